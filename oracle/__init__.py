@@ -1,0 +1,331 @@
+"""Plain CPU oracle for neighbor-restricted multi-head graph attention.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does, and
+the two share no code.  Graph loops live in ``oracle.c`` (plain C, fp64, OpenMP
+over rows); the dense steps (projections, the global linear branch, the gate,
+LayerNorm) are written here with numpy in float64, a matmul being the only
+library primitive used as a step.
+
+Conventions.  An edge e: u -> v has source u (keys, values) and target v
+(query, softmax group).  Node tensors are [N, H, C]; heads are contiguous
+chunks of the feature axis and are normalised independently.
+
+Parity status of each function (what pins it) is listed in its docstring.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_oracle.so")
+_lib = None
+
+SLOPE = 0.2  # LeakyReLU negative slope of the GAT score
+LN_EPS = 1e-5
+GLOBAL_EPS = 1e-6
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into _oracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.orc_coo_to_csr.argtypes = [i32, i64, P, P, P, P, P]
+        L.orc_coo_to_csr.restype = ctypes.c_int
+        L.orc_local_fwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, f64, f64, P, i64, P, P]
+        L.orc_local_fwd.restype = None
+        L.orc_local_bwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, P, P, P, f64, f64, P, P,
+                                    P, i64, P, P, i64, P, P]
+        L.orc_local_bwd.restype = None
+        L.orc_edge_values.argtypes = [i32, P, P, i64, P]
+        L.orc_edge_values.restype = None
+        L.orc_edge_values_bwd.argtypes = [i32, i32, P, P, P, P]
+        L.orc_edge_values_bwd.restype = None
+        L.orc_threads.argtypes = []
+        L.orc_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def threads() -> int:
+    return int(lib().orc_threads())
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+# --------------------------------------------------------------------------- CSR
+
+
+def coo_to_csr(n: int, key, other):
+    """Stable counting sort by key: (row_ptr[n+1], col[E] = other[eid], eid[E]).
+
+    Tinymesh "Sparse attention experiment", section "Target softmax" (reductions
+    traverse the destination CSR; COO order is kept).  Pinned by a library stable
+    argsort and the histogram closed form."""
+    key, other = _i32(key), _i32(other)
+    e = key.shape[0]
+    row_ptr = np.zeros(n + 1, np.int32)
+    col = np.zeros(e, np.int32)
+    eid = np.zeros(e, np.int32)
+    rc = lib().orc_coo_to_csr(n, e, _p(key), _p(other), _p(row_ptr), _p(col), _p(eid))
+    if rc != 0:
+        raise ValueError("edge endpoint out of range")
+    return row_ptr, col, eid
+
+
+class Graph:
+    """Fixed topology: the COO list and both CSRs the oracle derives from it."""
+
+    def __init__(self, n: int, src, dst):
+        self.n = int(n)
+        self.src, self.dst = _i32(src), _i32(dst)
+        self.row_ptr, self.col, self.eid = coo_to_csr(self.n, self.dst, self.src)
+        self.row_ptr_s, self.col_s, self.eid_s = coo_to_csr(self.n, self.src, self.dst)
+
+    @property
+    def e(self) -> int:
+        return int(self.src.shape[0])
+
+
+# --------------------------------------------------------------------------- local attention
+
+
+def _rows(rows):
+    if rows is None:
+        return None, None
+    r = _i32(rows)
+    return r, r.shape[0]
+
+
+def local_fwd_dot(q, k, v, g: Graph, scale: float, rows=None):
+    """Dot-product local branch ("Gated Local-Global Graph Attention", Key formulas, L_i):
+    per destination and head, softmax over in-edges of scale * q_v.k_u, weights applied
+    to v_u.  Returns out [R,H,C] and lse [R,H] (R = len(rows) or N).
+
+    Pinned by: masked scaled_dot_product_attention on dense graphs (library), the
+    complete-graph reduction to dense multi-head attention, and invariants."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, hh, c = q.shape
+    r, nr = _rows(rows)
+    nr = n if r is None else nr
+    out = np.empty((nr, hh, c), np.float64)
+    lse = np.empty((nr, hh), np.float64)
+    lib().orc_local_fwd(0, n, hh, c, _p(q), _p(k), _p(v), _p(g.row_ptr), _p(g.col), scale, 0.0, _p(r), nr,
+                        _p(out), _p(lse))
+    return out, lse
+
+
+def local_fwd_add(s_src, s_dst, hf, g: Graph, slope: float = SLOPE, rows=None):
+    """GAT additive local attention (Tinymesh "Sparse attention experiment", sections
+    "Composition" and "Multiple heads are composition"): score LeakyReLU(s_src[u] + s_dst[v]),
+    target softmax, weighted sum of hf[u].  Pinned by the two exact witnesses."""
+    s_src, s_dst, hf = _f64(s_src), _f64(s_dst), _f64(hf)
+    n, hh, c = hf.shape
+    r, nr = _rows(rows)
+    nr = n if r is None else nr
+    out = np.empty((nr, hh, c), np.float64)
+    lse = np.empty((nr, hh), np.float64)
+    lib().orc_local_fwd(1, n, hh, c, _p(s_dst), _p(s_src), _p(hf), _p(g.row_ptr), _p(g.col), 0.0, slope, _p(r),
+                        nr, _p(out), _p(lse))
+    return out, lse
+
+
+def _local_bwd(mode, qs, ks, val, d_out, g: Graph, scale, slope, rows_d, rows_s):
+    qs, ks, val, d_out = _f64(qs), _f64(ks), _f64(val), _f64(d_out)
+    n, hh, c = val.shape
+    w = c if mode == 0 else 1
+    rd, nd = _rows(rows_d)
+    rs, ns = _rows(rows_s)
+    nd = n if rd is None else nd
+    ns = n if rs is None else ns
+    lse = np.empty((n, hh), np.float64)
+    dd = np.empty((n, hh), np.float64)
+    d_qs = np.empty((nd, hh, w), np.float64)
+    d_ks = np.empty((ns, hh, w), np.float64)
+    d_val = np.empty((ns, hh, c), np.float64)
+    lib().orc_local_bwd(mode, n, hh, c, _p(qs), _p(ks), _p(val), _p(d_out), _p(g.row_ptr), _p(g.col),
+                        _p(g.row_ptr_s), _p(g.col_s), scale, slope, _p(lse), _p(dd), _p(rd), nd, _p(d_qs), _p(rs),
+                        ns, _p(d_ks), _p(d_val))
+    if mode == 1:
+        d_qs, d_ks = d_qs[..., 0], d_ks[..., 0]
+    return dict(lse=lse, D=dd, d_q=d_qs, d_k=d_ks, d_v=d_val)
+
+
+def local_bwd_dot(q, k, v, d_out, g: Graph, scale: float, rows_d=None, rows_s=None):
+    """First-order gradients of sum(out * d_out) for the dot-product branch: dq over the
+    destination CSR, dk and dv over the CSR by source.  Softmax gradient with the detached
+    maximum (Tinymesh "Target softmax").  Pinned by autograd through masked dense attention
+    (library) and central finite differences of local_fwd_dot."""
+    return _local_bwd(0, q, k, v, d_out, g, scale, 0.0, rows_d, rows_s)
+
+
+def local_bwd_add(s_src, s_dst, hf, d_out, g: Graph, slope: float = SLOPE, rows_d=None, rows_s=None):
+    """Gradients for the additive branch: d s_dst (destination CSR), d s_src and the
+    aggregation part of d hf (CSR by source).  Pinned by the exact witnesses and by
+    autograd through the dense formulation."""
+    r = _local_bwd(1, s_dst, s_src, hf, d_out, g, 0.0, slope, rows_d, rows_s)
+    return dict(lse=r["lse"], D=r["D"], d_s_dst=r["d_q"], d_s_src=r["d_k"], d_hf=r["d_v"])
+
+
+# --------------------------------------------------------------------------- endpoint projection
+
+
+def edge_values(x, endpoint):
+    """out[e] = x[endpoint[e]] (Tinymesh "Endpoint projection").  Pinned by numpy indexing."""
+    x = _f64(x)
+    n = x.shape[0]
+    w = int(np.prod(x.shape[1:])) if x.ndim > 1 else 1
+    ep = _i32(endpoint)
+    out = np.empty((ep.shape[0], w), np.float64)
+    lib().orc_edge_values(w, _p(x.reshape(n, w)), _p(ep), ep.shape[0], _p(out))
+    return out.reshape((ep.shape[0],) + x.shape[1:])
+
+
+def edge_values_bwd(d_edge, endpoint, n: int):
+    """dx[u] = sum of d_edge[e] over edges with endpoint[e] == u, via the CSR keyed by the
+    endpoint (Tinymesh "Endpoint projection").  Pinned by numpy's unbuffered add.at."""
+    d_edge = _f64(d_edge)
+    e = d_edge.shape[0]
+    w = int(np.prod(d_edge.shape[1:])) if d_edge.ndim > 1 else 1
+    row_ptr, _, eid = coo_to_csr(n, endpoint, np.zeros(e, np.int32))
+    dx = np.empty((n, w), np.float64)
+    lib().orc_edge_values_bwd(n, w, _p(row_ptr), _p(eid), _p(d_edge.reshape(e, w)), _p(dx))
+    return dx.reshape((n,) + d_edge.shape[1:])
+
+
+# --------------------------------------------------------------------------- GAT layer
+
+
+def gat_coefficients(x, w, a_s, a_t):
+    """H = X W viewed as [N,K,C]; s_src[n,k] = a_s[k].H[n,k]; s_dst with a_t (Tinymesh
+    "Composition": one source and one target coefficient per node and head)."""
+    x, w, a_s, a_t = _f64(x), _f64(w), _f64(a_s), _f64(a_t)
+    hh, c = a_s.shape
+    hf = (x @ w).reshape(x.shape[0], hh, c)
+    s_src = (hf * a_s[None]).sum(-1)
+    s_dst = (hf * a_t[None]).sum(-1)
+    return hf, s_src, s_dst
+
+
+def gat_forward(x, w, a_s, a_t, g: Graph, slope: float = SLOPE):
+    """Multi-head GAT layer output [N, K*C] (heads concatenated) plus intermediates."""
+    hf, s_src, s_dst = gat_coefficients(x, w, a_s, a_t)
+    out, lse = local_fwd_add(s_src, s_dst, hf, g, slope)
+    return dict(out=out.reshape(out.shape[0], -1), hf=hf, s_src=s_src, s_dst=s_dst, lse=lse)
+
+
+def gat_backward(x, w, a_s, a_t, d_out, g: Graph, slope: float = SLOPE):
+    """dX, dW, da_s, da_t of sum(out * d_out).  Chain: the local backward gives d s_src,
+    d s_dst and the aggregation part of dH; the coefficient map adds a_s d s_src + a_t d s_dst;
+    then dW = X^T dH and dX = dH W^T."""
+    x, w, a_s, a_t = _f64(x), _f64(w), _f64(a_s), _f64(a_t)
+    hf, s_src, s_dst = gat_coefficients(x, w, a_s, a_t)
+    n, hh, c = hf.shape
+    r = local_bwd_add(s_src, s_dst, hf, _f64(d_out).reshape(n, hh, c), g, slope)
+    d_hf = r["d_hf"] + a_s[None] * r["d_s_src"][..., None] + a_t[None] * r["d_s_dst"][..., None]
+    da_s = (r["d_s_src"][..., None] * hf).sum(0)
+    da_t = (r["d_s_dst"][..., None] * hf).sum(0)
+    dh = d_hf.reshape(n, hh * c)
+    return dict(d_x=dh @ w.T, d_w=x.T @ dh, d_a_s=da_s, d_a_t=da_t, d_hf=d_hf, d_s_src=r["d_s_src"],
+                d_s_dst=r["d_s_dst"])
+
+
+# --------------------------------------------------------------------------- gated local-global layer
+
+
+def phi(x):
+    """phi = elu + 1 ("Gated Local-Global Graph Attention", Implementation notes)."""
+    x = _f64(x)
+    return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def global_linear(q, k, v, eps: float = GLOBAL_EPS):
+    """Global branch per head ("Gated Local-Global Graph Attention", Key formulas, G_i):
+    S = sum_j phi(k_j) v_j^T [H,r,r], z = sum_j phi(k_j) [H,r],
+    G_i = phi(q_i)^T S / (phi(q_i)^T z + eps) [N,H,r].
+    Pinned by the dense O(N^2) kernelised form."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    pq, pk = phi(q), phi(k)
+    s = np.einsum("nhi,nhj->hij", pk, v)
+    z = pk.sum(0)
+    num = np.einsum("nhi,hij->nhj", pq, s)
+    den = np.einsum("nhi,hi->nh", pq, z) + eps
+    return s, z, num / den[..., None]
+
+
+def gate(x, w_g, b_g):
+    """g_i = sigmoid(x_i . w_g + b_g), one scalar per node (Key formulas)."""
+    t = _f64(x) @ _f64(w_g) + float(b_g)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-t))
+
+
+def combine(gv, loc, glob):
+    """Y_i = g_i L_i + (1 - g_i) G_i (Key formulas)."""
+    gv = _f64(gv)[:, None]
+    return gv * _f64(loc) + (1.0 - gv) * _f64(glob)
+
+
+def layer_norm(a, gamma, beta, eps: float = LN_EPS):
+    """Textbook LayerNorm over the last axis with biased variance."""
+    a = _f64(a)
+    mu = a.mean(-1, keepdims=True)
+    var = ((a - mu) ** 2).mean(-1, keepdims=True)
+    return _f64(gamma) * (a - mu) / np.sqrt(var + eps) + _f64(beta)
+
+
+def gated_layer(p: dict, g: Graph, heads: int, eps: float = GLOBAL_EPS, rows=None):
+    """The full layer of "Gated Local-Global Graph Attention" (Implementation notes, item 2):
+    Q,K,V = X W_{Q,K,V}; local masked softmax per head; phi = elu+1 global branch;
+    g = sigmoid(X w_g + b_g); out = LayerNorm(X + W_o(g L + (1-g) G)).
+    ``rows`` restricts the per-node outputs (the global statistics S, z always use all
+    nodes).  Returns a dict of every intermediate, in float64."""
+    x = _f64(p["x"])
+    n, d = x.shape
+    r = d // heads
+    q = (x @ _f64(p["w_q"])).reshape(n, heads, r)
+    k = (x @ _f64(p["w_k"])).reshape(n, heads, r)
+    v = (x @ _f64(p["w_v"])).reshape(n, heads, r)
+    loc, lse = local_fwd_dot(q, k, v, g, 1.0 / np.sqrt(r), rows=rows)
+    pk = phi(k)
+    s = np.einsum("nhi,nhj->hij", pk, v)
+    z = pk.sum(0)
+    xr = x if rows is None else x[np.asarray(rows)]
+    qr = q if rows is None else q[np.asarray(rows)]
+    pq = phi(qr)
+    glob = np.einsum("nhi,hij->nhj", pq, s) / (np.einsum("nhi,hi->nh", pq, z) + eps)[..., None]
+    gv = gate(xr, p["w_g"], p["b_g"])
+    y = combine(gv, loc.reshape(-1, d), glob.reshape(-1, d))
+    pre = xr + y @ _f64(p["w_o"])
+    out = layer_norm(pre, p["gamma"], p["beta"])
+    return dict(q=q, k=k, v=v, local=loc.reshape(-1, d), lse=lse, S=s, z=z, glob=glob.reshape(-1, d), gate=gv, y=y,
+                pre=pre, out=out)
