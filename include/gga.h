@@ -1,0 +1,244 @@
+/*
+ * gga.h -- C ABI of libgga, neighbor-restricted multi-head graph attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Graph.  A directed multigraph on n nodes given as a COO edge list of int32
+ *   (src[e], dst[e]).  Edge e: u -> v has source u and target v (Tinymesh
+ *   "Sparse attention experiment", section "Endpoint projection").  The source
+ *   provides keys and values, the target provides the query and owns the
+ *   softmax group (the in-edges of v).  Self-loops are ordinary edges that the
+ *   caller adds; the library never adds, removes, deduplicates or reorders
+ *   edges (section "Composition": no silent topology change).  Duplicate edges
+ *   each contribute their own softmax term.
+ * CSR.  row_ptr[n+1], col[E], eid[E] as built by gga_coo_to_csr: row v holds
+ *   the edges whose key is v, in ascending COO index; eid is that COO index and
+ *   col the other endpoint.
+ * Node tensors.  Row-major [n, H, C] with heads as contiguous chunks of the
+ *   feature axis ("ag_multihead_attention", Details: head h is rows
+ *   h*d_k .. (h+1)*d_k-1); node scores are [n, H].  Outputs are fp32.
+ * Memory.  Every pointer is a device pointer owned by the caller.  The library
+ *   never allocates, frees or retains device memory; scratch comes from a
+ *   caller buffer `ws` of at least the size the matching *_workspace query
+ *   returns (a NULL ws is allowed when that size is 0).  Inputs are never
+ *   written.  Pointers to node tensors must be 16-byte aligned.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *   enqueues work on it: no call synchronises or copies device -> host.
+ * Errors.  Arguments are checked on the host before anything is enqueued; on a
+ *   failed check the call returns a nonzero status and enqueues nothing.  Edge
+ *   index ranges are not checked by the compute calls (they would need a device
+ *   read): run gga_validate_coo on untrusted input first.  A HIP launch error is
+ *   returned as GGA_EHIP.  n == 0 or E == 0 are valid and return GGA_OK.
+ * Threads.  Calls are re-entrant; there is no mutable global state beyond a
+ *   per-device cache of device properties.
+ */
+#ifndef GGA_H
+#define GGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GGA_ABI_VERSION 1
+
+/* status codes */
+#define GGA_OK 0
+#define GGA_EINVAL 1       /* null pointer with a nonzero size, negative size, misalignment */
+#define GGA_ERANGE 2       /* a size beyond what int32 indexing supports */
+#define GGA_EUNSUPPORTED 3 /* dtype, score mode or shape this build does not handle */
+#define GGA_EWORKSPACE 4   /* workspace or plan buffer smaller than its query says */
+#define GGA_EHIP 5         /* a HIP runtime call or kernel launch failed */
+
+/* storage type of node tensors */
+#define GGA_F32 0
+#define GGA_BF16 1
+
+/* score of edge u -> v */
+#define GGA_SCORE_DOT 0      /* scale * q[v,h,:] . k[u,h,:] */
+#define GGA_SCORE_ADDITIVE 1 /* LeakyReLU(s_src[u,h] + s_dst[v,h]) */
+
+int gga_abi_version(void);
+const char *gga_status_string(int status);
+
+/*
+ * Count COO entries whose src or dst lies outside [0, n).  Writes the count to the
+ * device int *d_bad (the call clears it first).  The only check of index range.
+ */
+int gga_validate_coo(int32_t n, int64_t e, const int32_t *src, const int32_t *dst, int32_t *d_bad, void *stream);
+
+/*
+ * COO -> CSR by `key` with a stable counting sort (Tinymesh "Sparse attention
+ * experiment", section "Target softmax": the segment reductions traverse the
+ * destination CSR and gathers keep the original COO order).
+ *   key = dst, other = src: the CSR by destination used by the forward pass.
+ *   key = src, other = dst: the CSR by source used by the backward pass.
+ * Outputs row_ptr[n+1], col[e] (= other[eid]) and eid[e]; within a row eid
+ * ascends.  The result is a pure function of the input (bit-exact, no
+ * dependence on scheduling).  Keys outside [0, n) are skipped in the row
+ * counts; the outputs are then unspecified but every write stays in bounds.
+ * e must be < 2^31.
+ */
+size_t gga_coo_to_csr_workspace(int32_t n, int64_t e);
+int gga_coo_to_csr(int32_t n, int64_t e, const int32_t *key, const int32_t *other, int32_t *row_ptr, int32_t *col,
+                   int32_t *eid, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Degree-bucket plan of a CSR, built once per fixed topology.  Rows with few
+ * edges are processed by one wavefront each; longer rows by a workgroup; rows
+ * longer than one chunk are split into chunks whose partial softmax states are
+ * merged in a fixed order, so that high-degree rows do not serialise (Tinymesh
+ * "Sparse attention experiment", section "Target softmax", which notes that
+ * high-degree rows serialise in a plain pull kernel).  The plan is an opaque
+ * device buffer of gga_plan_bytes(n, e) bytes; it depends only on row_ptr.
+ */
+size_t gga_plan_bytes(int32_t n, int64_t e);
+size_t gga_plan_workspace(int32_t n, int64_t e);
+int gga_plan_build(int32_t n, int64_t e, const int32_t *row_ptr, void *plan, size_t plan_bytes, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* Shape and mode of a local attention call. */
+typedef struct gga_local_desc {
+    int32_t n;            /* nodes */
+    int32_t heads;        /* H */
+    int64_t e;            /* edges (length of col) */
+    int32_t head_dim;     /* C (r): per-head width */
+    int32_t score;        /* GGA_SCORE_DOT or GGA_SCORE_ADDITIVE */
+    int32_t dtype;        /* storage type of q, k, v (dot) or of v (additive) */
+    float scale;          /* dot: multiplier of q.k, usually 1/sqrt(C) */
+    float negative_slope; /* additive: LeakyReLU slope, usually 0.2 */
+    int32_t reserved;     /* must be 0 */
+} gga_local_desc;
+
+/*
+ * Local attention forward ("Gated Local-Global Graph Attention", Key formulas,
+ * local branch L_i; Tinymesh "Sparse attention experiment", sections
+ * "Composition", "Multiple heads are composition" and "Target softmax").
+ * For every target v and head h, over the in-edges e: u -> v of the CSR by
+ * destination:
+ *   dot:      s_e = scale * q[v,h,:] . k[u,h,:]      (qs = q, ks = k: [n,H,C])
+ *   additive: s_e = LeakyReLU(s_src[u,h] + s_dst[v,h]) (qs = s_dst, ks = s_src:
+ *             fp32 [n,H])
+ *   alpha_e = exp(s_e - max) / sum exp(s - max)       (per v, h)
+ *   out[v,h,:] = sum_e alpha_e v[u,h,:]               (fp32 [n,H,C])
+ *   lse[v,h] = log sum_e exp(s_e)                     (fp32 [n,H]; may be NULL)
+ * A row with no in-edges gets out = 0 and lse = -inf.  Heads are normalised
+ * independently and concatenated.  `plan` comes from gga_plan_build on the same
+ * row_ptr.  Deterministic: the same inputs give bit-identical outputs.
+ */
+size_t gga_local_attn_fwd_workspace(const gga_local_desc *d);
+int gga_local_attn_fwd(const gga_local_desc *d, const void *qs, const void *ks, const void *v,
+                       const int32_t *row_ptr, const int32_t *col, const void *plan, float *out, float *lse,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Local attention backward: first-order gradients of sum(out * d_out), with the
+ * softmax maximum treated as a constant (Tinymesh "Sparse attention experiment",
+ * section "Target softmax").  With d_alpha_e = d_out[v,h,:] . v[u,h,:],
+ * D[v,h] = sum_e alpha_e d_alpha_e and ds_e = alpha_e (d_alpha_e - D[v,h]):
+ *   dot:      d_qs = dq[v] = sum_{e into v} ds_e scale k[u]          fp32 [n,H,C]
+ *             d_ks = dk[u] = sum_{e out of u} ds_e scale q[v]        fp32 [n,H,C]
+ *   additive: d_qs = d s_dst[v] = sum_{e into v} ds_e LeakyReLU'(z_e) fp32 [n,H]
+ *             d_ks = d s_src[u] = sum_{e out of u} ds_e LeakyReLU'(z_e)
+ *   both:     d_v[u] = sum_{e out of u} alpha_e d_out[v]              fp32 [n,H,C]
+ * Sums over the edges out of u walk the CSR by source (row_ptr_s, col_s with
+ * plan_s), grouping edge gradients by the selected endpoint (section "Endpoint
+ * projection", backward), so no floating-point atomics are used and results are
+ * deterministic.  `out` and `lse` are the forward's outputs.
+ */
+size_t gga_local_attn_bwd_workspace(const gga_local_desc *d);
+int gga_local_attn_bwd(const gga_local_desc *d, const void *qs, const void *ks, const void *v, const float *out,
+                       const float *lse, const float *d_out, const int32_t *row_ptr, const int32_t *col,
+                       const void *plan, const int32_t *row_ptr_s, const int32_t *col_s, const void *plan_s,
+                       float *d_qs, float *d_ks, float *d_v, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Endpoint projection (Tinymesh "Sparse attention experiment", section
+ * "Endpoint projection"): out[e,:] = x[endpoint[e],:] for a node field x of
+ * [n, width] elements of `dtype`; out is [e, width] of the same dtype.  Pass
+ * endpoint = src for "source", dst for "target".
+ */
+int gga_edge_values(int32_t n, int32_t width, int32_t dtype, const void *x, int64_t e, const int32_t *endpoint,
+                    void *out, void *stream);
+
+/*
+ * Its backward: dx[u,:] = sum of d_edge[e,:] over the edges whose selected
+ * endpoint is u, as a row sum over the CSR keyed by that endpoint (row_ptr, eid
+ * from gga_coo_to_csr with key = endpoint).  fp32, deterministic.
+ */
+int gga_edge_values_bwd(int32_t n, int32_t width, int64_t e, const int32_t *row_ptr, const int32_t *eid,
+                        const float *d_edge, float *dx, void *stream);
+
+/*
+ * GAT node coefficients (Tinymesh "Sparse attention experiment", section
+ * "Composition": one source and one target coefficient per node and head):
+ *   s_src[n,h] = sum_c a_s[h,c] hf[n,h,c],  s_dst[n,h] = sum_c a_t[h,c] hf[n,h,c]
+ * hf fp32 [n,H,C]; a_s, a_t fp32 [H,C]; outputs fp32 [n,H].
+ */
+int gga_gat_coef_fwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf, const float *a_s,
+                     const float *a_t, float *s_src, float *s_dst, void *stream);
+
+/*
+ * Backward of the coefficients, joined with the aggregation gradient d_hf_attn
+ * from gga_local_attn_bwd (additive mode):
+ *   d_hf[n,h,c] = d_hf_attn[n,h,c] + a_s[h,c] d_s_src[n,h] + a_t[h,c] d_s_dst[n,h]
+ *   d_a_s[h,c] = sum_n d_s_src[n,h] hf[n,h,c],  d_a_t likewise with d_s_dst.
+ * The sums over n use a fixed two-level order (deterministic).  d_hf may alias
+ * d_hf_attn.
+ */
+size_t gga_gat_coef_bwd_workspace(int32_t n, int32_t heads, int32_t head_dim);
+int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf, const float *a_s,
+                     const float *a_t, const float *d_hf_attn, const float *d_s_src, const float *d_s_dst,
+                     float *d_hf, float *d_a_s, float *d_a_t, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dense fp32 product on the matrix cores: c[m,n] = op(a) op(b) (+ bias[n]),
+ * op(a) = a [m,k] or, with trans_a, a stored [k,m]; op(b) = b [k,n] or, with
+ * trans_b, b stored [n,k].  Row-major, fp32 in and out, fp32 accumulation.
+ * Used for the projections Q = X W_Q, K, V, the output map W_o, the GAT map
+ * X W and its gradients X^T dH, dH W^T ("Gated Local-Global Graph Attention",
+ * Mathematical statement; Tinymesh "Composition").  bias may be NULL.
+ */
+int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float *a, const float *b,
+               const float *bias, float *c, void *stream);
+
+/*
+ * Global linear-attention branch ("Gated Local-Global Graph Attention", Key
+ * formulas G_i, S, z; Implementation notes item 2: phi = elu + 1), per head h:
+ *   S[h] = sum_j phi(k[j,h,:]) v[j,h,:]^T   fp32 [H,r,r]
+ *   z[h] = sum_j phi(k[j,h,:])              fp32 [H,r]
+ *   g[i,h,:] = phi(q[i,h,:])^T S[h] / (phi(q[i,h,:]) . z[h] + eps)   fp32 [n,H,r]
+ * q, k, v fp32 [n,H,r].  The sums over j use a fixed split order
+ * (deterministic).  s_out and z_out may be NULL.
+ */
+size_t gga_global_linear_workspace(int32_t n, int32_t heads, int32_t r);
+int gga_global_linear_fwd(int32_t n, int32_t heads, int32_t r, const float *q, const float *k, const float *v,
+                          float eps, float *s_out, float *z_out, float *g_out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * Node gate and combination ("Gated Local-Global Graph Attention", Key formulas):
+ *   gate[i] = sigmoid(x[i,:] . w_g + b_g)          (x fp32 [n,d], w_g fp32 [d])
+ *   y[i,:] = gate[i] l[i,:] + (1 - gate[i]) g[i,:]   (l, g, y fp32 [n,width])
+ * gate_out may be NULL.
+ */
+int gga_gated_combine(int32_t n, int32_t d, const float *x, const float *w_g, float b_g, int32_t width,
+                      const float *l, const float *g, float *gate_out, float *y, void *stream);
+
+/*
+ * Residual and LayerNorm of the layer output ("Gated Local-Global Graph
+ * Attention", Implementation notes item 2: LayerNorm(X + Wo(...))):
+ *   a = x + y;  out = gamma (a - mean(a)) / sqrt(var(a) + eps) + beta
+ * over the last axis of width d, biased variance; all fp32 [n,d], gamma/beta [d].
+ */
+int gga_add_layernorm(int32_t n, int32_t d, const float *x, const float *y, const float *gamma, const float *beta,
+                      float eps, float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GGA_H */

@@ -1,0 +1,317 @@
+"""Python binding of libgga: neighbor-restricted multi-head graph attention on MI355X.
+
+Every function here has the name of the C entry point it wraps (include/gga.h) and
+only marshals arguments: torch tensors become device pointers, the current HIP
+stream is passed along, output and workspace tensors are allocated with torch when
+the caller does not supply them, and a nonzero status raises GGAError.  All
+arithmetic runs in the HIP kernels of libgga.so; importing this package fails if
+the library has not been built (``python sparse_graph_attention_amd/build.py``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgga.so")
+
+GGA_OK, GGA_EINVAL, GGA_ERANGE, GGA_EUNSUPPORTED, GGA_EWORKSPACE, GGA_EHIP = range(6)
+GGA_F32, GGA_BF16 = 0, 1
+GGA_SCORE_DOT, GGA_SCORE_ADDITIVE = 0, 1
+
+
+class GGAError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        self.status = status
+        super().__init__(f"{name} failed: {gga_status_string(status)} ({status})")
+
+
+class gga_local_desc(ctypes.Structure):
+    _fields_ = [
+        ("n", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("e", ctypes.c_int64),
+        ("head_dim", ctypes.c_int32),
+        ("score", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("negative_slope", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_graph_attention_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    D = ctypes.POINTER(gga_local_desc)
+    sig = {
+        "gga_abi_version": ([], ctypes.c_int),
+        "gga_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "gga_validate_coo": ([i32, i64, P, P, P, P], ctypes.c_int),
+        "gga_coo_to_csr_workspace": ([i32, i64], sz),
+        "gga_coo_to_csr": ([i32, i64, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_plan_bytes": ([i32, i64], sz),
+        "gga_plan_workspace": ([i32, i64], sz),
+        "gga_plan_build": ([i32, i64, P, P, sz, P, sz, P], ctypes.c_int),
+        "gga_local_attn_fwd_workspace": ([D], sz),
+        "gga_local_attn_fwd": ([D, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_local_attn_bwd_workspace": ([D], sz),
+        "gga_local_attn_bwd": ([D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_edge_values": ([i32, i32, i32, P, i64, P, P, P], ctypes.c_int),
+        "gga_edge_values_bwd": ([i32, i32, i64, P, P, P, P, P], ctypes.c_int),
+        "gga_gat_coef_fwd": ([i32, i32, i32, P, P, P, P, P, P], ctypes.c_int),
+        "gga_gat_coef_bwd_workspace": ([i32, i32, i32], sz),
+        "gga_gat_coef_bwd": ([i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_linear": ([i32, i32, i32, i32, i32, P, P, P, P, P], ctypes.c_int),
+        "gga_global_linear_workspace": ([i32, i32, i32], sz),
+        "gga_global_linear_fwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_gated_combine": ([i32, i32, P, P, f32, i32, P, P, P, P, P], ctypes.c_int),
+        "gga_add_layernorm": ([i32, i32, P, P, P, P, f32, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+# --------------------------------------------------------------------------- marshalling helpers
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return ctypes.c_void_p(t)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(name: str, rc: int) -> None:
+    if rc != GGA_OK:
+        raise GGAError(name, rc)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise GGAError("workspace", GGA_EWORKSPACE)
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GGA_F32
+    if t.dtype == torch.bfloat16:
+        return GGA_BF16
+    raise GGAError(f"dtype {t.dtype}", GGA_EUNSUPPORTED)
+
+
+def gga_abi_version() -> int:
+    return int(lib.gga_abi_version())
+
+
+def gga_status_string(status: int) -> str:
+    return lib.gga_status_string(int(status)).decode()
+
+
+# --------------------------------------------------------------------------- graph
+
+
+def gga_validate_coo(n: int, src: torch.Tensor, dst: torch.Tensor, d_bad=None, stream=None) -> torch.Tensor:
+    d_bad = torch.empty(1, dtype=torch.int32, device=src.device) if d_bad is None else d_bad
+    _check("gga_validate_coo", lib.gga_validate_coo(n, src.numel(), _ptr(src), _ptr(dst), _ptr(d_bad),
+                                                    _stream(stream)))
+    return d_bad
+
+
+def gga_coo_to_csr(n: int, key: torch.Tensor, other: torch.Tensor, row_ptr=None, col=None, eid=None, ws=None,
+                   stream=None):
+    e = key.numel()
+    dev = key.device
+    row_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev) if row_ptr is None else row_ptr
+    col = torch.empty(e, dtype=torch.int32, device=dev) if col is None else col
+    eid = torch.empty(e, dtype=torch.int32, device=dev) if eid is None else eid
+    nb = lib.gga_coo_to_csr_workspace(n, e)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_coo_to_csr", lib.gga_coo_to_csr(n, e, _ptr(key), _ptr(other), _ptr(row_ptr), _ptr(col), _ptr(eid),
+                                                _ptr(ws), nb, _stream(stream)))
+    return row_ptr, col, eid
+
+
+def gga_plan_build(n: int, e: int, row_ptr: torch.Tensor, plan=None, ws=None, stream=None) -> torch.Tensor:
+    dev = row_ptr.device
+    pb = lib.gga_plan_bytes(n, e)
+    plan = torch.empty(pb, dtype=torch.uint8, device=dev) if plan is None else plan
+    wb = lib.gga_plan_workspace(n, e)
+    ws = _workspace(wb, dev, ws)
+    _check("gga_plan_build", lib.gga_plan_build(n, e, _ptr(row_ptr), _ptr(plan), plan.numel(), _ptr(ws), wb,
+                                                _stream(stream)))
+    return plan
+
+
+class Topology:
+    """A fixed graph on the device: the CSR by destination with its plan and, when
+    ``backward`` is set, the CSR by source with its plan (built by the entry points
+    above; this class only keeps the tensors together)."""
+
+    def __init__(self, n: int, src: torch.Tensor, dst: torch.Tensor, backward: bool = False, stream=None):
+        self.n = int(n)
+        self.e = int(src.numel())
+        self.src, self.dst = src, dst
+        self.row_ptr, self.col, self.eid = gga_coo_to_csr(n, dst, src, stream=stream)
+        self.plan = gga_plan_build(n, self.e, self.row_ptr, stream=stream)
+        self.row_ptr_s = self.col_s = self.eid_s = self.plan_s = None
+        if backward:
+            self.build_source_csr(stream)
+
+    def build_source_csr(self, stream=None):
+        self.row_ptr_s, self.col_s, self.eid_s = gga_coo_to_csr(self.n, self.src, self.dst, stream=stream)
+        self.plan_s = gga_plan_build(self.n, self.e, self.row_ptr_s, stream=stream)
+
+
+# --------------------------------------------------------------------------- local attention
+
+
+def make_desc(n, e, heads, head_dim, score, dtype, scale=None, negative_slope=0.2) -> gga_local_desc:
+    if scale is None:
+        scale = head_dim ** -0.5 if head_dim > 0 else 1.0
+    return gga_local_desc(n, heads, e, head_dim, score, dtype, scale, negative_slope, 0)
+
+
+def gga_local_attn_fwd(desc: gga_local_desc, qs, ks, v, row_ptr, col, plan, out=None, lse=None, want_lse=True,
+                       ws=None, stream=None):
+    dev = v.device
+    if out is None:
+        out = torch.empty(desc.n, desc.heads, desc.head_dim, dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(desc.n, desc.heads, dtype=torch.float32, device=dev)
+    nb = lib.gga_local_attn_fwd_workspace(ctypes.byref(desc))
+    ws = _workspace(nb, dev, ws)
+    _check("gga_local_attn_fwd", lib.gga_local_attn_fwd(ctypes.byref(desc), _ptr(qs), _ptr(ks), _ptr(v),
+                                                        _ptr(row_ptr), _ptr(col), _ptr(plan), _ptr(out), _ptr(lse),
+                                                        _ptr(ws), nb, _stream(stream)))
+    return out, lse
+
+
+def gga_local_attn_bwd(desc: gga_local_desc, qs, ks, v, out, lse, d_out, topo: Topology, d_qs=None, d_ks=None,
+                       d_v=None, ws=None, stream=None):
+    dev = v.device
+    qs_shape = (desc.n, desc.heads, desc.head_dim) if desc.score == GGA_SCORE_DOT else (desc.n, desc.heads)
+    d_qs = torch.empty(qs_shape, dtype=torch.float32, device=dev) if d_qs is None else d_qs
+    d_ks = torch.empty(qs_shape, dtype=torch.float32, device=dev) if d_ks is None else d_ks
+    d_v = torch.empty(desc.n, desc.heads, desc.head_dim, dtype=torch.float32, device=dev) if d_v is None else d_v
+    nb = lib.gga_local_attn_bwd_workspace(ctypes.byref(desc))
+    ws = _workspace(nb, dev, ws)
+    _check("gga_local_attn_bwd", lib.gga_local_attn_bwd(
+        ctypes.byref(desc), _ptr(qs), _ptr(ks), _ptr(v), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(topo.row_ptr),
+        _ptr(topo.col), _ptr(topo.plan), _ptr(topo.row_ptr_s), _ptr(topo.col_s), _ptr(topo.plan_s), _ptr(d_qs),
+        _ptr(d_ks), _ptr(d_v), _ptr(ws), nb, _stream(stream)))
+    return d_qs, d_ks, d_v
+
+
+# --------------------------------------------------------------------------- endpoint projection, GAT
+
+
+def gga_edge_values(x: torch.Tensor, endpoint: torch.Tensor, out=None, stream=None):
+    n = x.shape[0]
+    width = x.numel() // max(n, 1) if n else (x.shape[1] if x.dim() > 1 else 1)
+    e = endpoint.numel()
+    out = torch.empty((e,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device) if out is None else out
+    _check("gga_edge_values", lib.gga_edge_values(n, width, _dtype_code(x), _ptr(x), e, _ptr(endpoint), _ptr(out),
+                                                  _stream(stream)))
+    return out
+
+
+def gga_edge_values_bwd(n: int, d_edge: torch.Tensor, row_ptr, eid, dx=None, stream=None):
+    e = d_edge.shape[0]
+    width = d_edge.numel() // max(e, 1) if e else (d_edge.shape[1] if d_edge.dim() > 1 else 1)
+    dx = torch.empty((n,) + tuple(d_edge.shape[1:]), dtype=torch.float32, device=d_edge.device) if dx is None else dx
+    _check("gga_edge_values_bwd", lib.gga_edge_values_bwd(n, width, e, _ptr(row_ptr), _ptr(eid), _ptr(d_edge),
+                                                          _ptr(dx), _stream(stream)))
+    return dx
+
+
+def gga_gat_coef_fwd(hf: torch.Tensor, a_s: torch.Tensor, a_t: torch.Tensor, s_src=None, s_dst=None, stream=None):
+    n, heads, c = hf.shape
+    s_src = torch.empty(n, heads, dtype=torch.float32, device=hf.device) if s_src is None else s_src
+    s_dst = torch.empty(n, heads, dtype=torch.float32, device=hf.device) if s_dst is None else s_dst
+    _check("gga_gat_coef_fwd", lib.gga_gat_coef_fwd(n, heads, c, _ptr(hf), _ptr(a_s), _ptr(a_t), _ptr(s_src),
+                                                    _ptr(s_dst), _stream(stream)))
+    return s_src, s_dst
+
+
+def gga_gat_coef_bwd(hf, a_s, a_t, d_hf_attn, d_s_src, d_s_dst, d_hf=None, d_a_s=None, d_a_t=None, ws=None,
+                     stream=None):
+    n, heads, c = hf.shape
+    dev = hf.device
+    d_hf = torch.empty_like(hf) if d_hf is None else d_hf
+    d_a_s = torch.empty(heads, c, dtype=torch.float32, device=dev) if d_a_s is None else d_a_s
+    d_a_t = torch.empty(heads, c, dtype=torch.float32, device=dev) if d_a_t is None else d_a_t
+    nb = lib.gga_gat_coef_bwd_workspace(n, heads, c)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_gat_coef_bwd", lib.gga_gat_coef_bwd(n, heads, c, _ptr(hf), _ptr(a_s), _ptr(a_t), _ptr(d_hf_attn),
+                                                    _ptr(d_s_src), _ptr(d_s_dst), _ptr(d_hf), _ptr(d_a_s),
+                                                    _ptr(d_a_t), _ptr(ws), nb, _stream(stream)))
+    return d_hf, d_a_s, d_a_t
+
+
+# --------------------------------------------------------------------------- dense steps
+
+
+def gga_linear(a: torch.Tensor, b: torch.Tensor, bias=None, trans_a=False, trans_b=False, out=None, stream=None):
+    m = a.shape[1] if trans_a else a.shape[0]
+    k = a.shape[0] if trans_a else a.shape[1]
+    n = b.shape[0] if trans_b else b.shape[1]
+    out = torch.empty(m, n, dtype=torch.float32, device=a.device) if out is None else out
+    _check("gga_linear", lib.gga_linear(m, k, n, int(trans_a), int(trans_b), _ptr(a), _ptr(b), _ptr(bias), _ptr(out),
+                                        _stream(stream)))
+    return out
+
+
+def gga_global_linear_fwd(q, k, v, eps=1e-6, s_out=None, z_out=None, g_out=None, ws=None, stream=None):
+    n, heads, r = q.shape
+    dev = q.device
+    s_out = torch.empty(heads, r, r, dtype=torch.float32, device=dev) if s_out is None else s_out
+    z_out = torch.empty(heads, r, dtype=torch.float32, device=dev) if z_out is None else z_out
+    g_out = torch.empty(n, heads, r, dtype=torch.float32, device=dev) if g_out is None else g_out
+    nb = lib.gga_global_linear_workspace(n, heads, r)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_global_linear_fwd", lib.gga_global_linear_fwd(n, heads, r, _ptr(q), _ptr(k), _ptr(v), eps,
+                                                              _ptr(s_out), _ptr(z_out), _ptr(g_out), _ptr(ws), nb,
+                                                              _stream(stream)))
+    return s_out, z_out, g_out
+
+
+def gga_gated_combine(x, w_g, b_g: float, l, g, gate_out=None, y=None, stream=None):
+    n, d = x.shape
+    width = l.numel() // max(n, 1)
+    y = torch.empty(n, width, dtype=torch.float32, device=x.device) if y is None else y
+    gate_out = torch.empty(n, dtype=torch.float32, device=x.device) if gate_out is None else gate_out
+    _check("gga_gated_combine", lib.gga_gated_combine(n, d, _ptr(x), _ptr(w_g), float(b_g), width, _ptr(l), _ptr(g),
+                                                      _ptr(gate_out), _ptr(y), _stream(stream)))
+    return gate_out, y
+
+
+def gga_add_layernorm(x, y, gamma, beta, eps=1e-5, out=None, stream=None):
+    n, d = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _check("gga_add_layernorm", lib.gga_add_layernorm(n, d, _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), eps,
+                                                      _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,204 @@
+// COO -> CSR by key: a stable least-significant-digit radix sort of (key, COO index).
+//
+// Each pass sorts by 8 bits of the key.  A pass is stable by construction: a tile's
+// items are ranked in their original order (wave ballots give the rank among equal
+// digits inside a wave, per-wave counts in LDS order the waves, a running per-digit
+// count orders the rounds) and tiles are ordered by a digit-major exclusive scan of
+// per-tile histograms.  The result therefore equals a stable sort, independent of
+// scheduling: within a row the COO indices ascend, bit-exact across runs and devices.
+// No atomics decide a position; the only global atomics count row lengths.
+#include "common.hpp"
+
+namespace gga {
+
+namespace {
+
+constexpr int kRsThreads = 256;
+constexpr int kRsItems = 16;
+constexpr int kRsTile = kRsThreads * kRsItems;  // 4096 edges per tile
+constexpr int kRsBins = 256;
+constexpr int kRsWaves = kRsThreads / 64;
+
+__global__ void count_keys(const int32_t* __restrict__ key, int64_t e, int32_t n, int32_t* __restrict__ cnt,
+                           int32_t* __restrict__ bad) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < e; i += (int64_t)gridDim.x * blockDim.x) {
+        int32_t k = key[i];
+        if ((uint32_t)k < (uint32_t)n)
+            atomicAdd(&cnt[k], 1);
+        else if (bad)
+            atomicAdd(bad, 1);
+    }
+}
+
+__global__ void count_bad(const int32_t* __restrict__ a, const int32_t* __restrict__ b, int64_t e, int32_t n,
+                          int32_t* __restrict__ bad) {
+    int local = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < e; i += (int64_t)gridDim.x * blockDim.x)
+        local += ((uint32_t)a[i] >= (uint32_t)n) + ((uint32_t)b[i] >= (uint32_t)n);
+    if (local) atomicAdd(bad, local);
+}
+
+__global__ void radix_upsweep(const int32_t* __restrict__ keys, int64_t e, int shift, uint32_t mask,
+                              int32_t* __restrict__ hist, int64_t nblocks) {
+    __shared__ int cnt[kRsBins];
+    cnt[threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kRsTile;
+#pragma unroll 4
+    for (int k = 0; k < kRsItems; k++) {
+        int64_t i = base + k * kRsThreads + threadIdx.x;
+        if (i < e) atomicAdd(&cnt[((uint32_t)keys[i] >> shift) & mask], 1);
+    }
+    __syncthreads();
+    hist[(int64_t)threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
+}
+
+// vals_in == nullptr means the identity (COO index); keys_out may be nullptr on the last pass.
+__global__ void radix_downsweep(const int32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
+                                int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int64_t e, int shift,
+                                int bits, const int32_t* __restrict__ offsets, int64_t nblocks) {
+    __shared__ int run[kRsBins];
+    __shared__ int wc[kRsWaves][kRsBins];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t mask = (1u << bits) - 1u;
+    run[tid] = offsets[(int64_t)tid * nblocks + blockIdx.x];
+    const int64_t base = (int64_t)blockIdx.x * kRsTile;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int r = 0; r < kRsItems; r++) {
+        const int64_t i = base + r * kRsThreads + tid;
+        const bool valid = i < e;
+        const int32_t key = valid ? keys_in[i] : 0;
+        const int32_t val = valid ? (vals_in ? vals_in[i] : (int32_t)i) : 0;
+        const uint32_t d = ((uint32_t)key >> shift) & mask;
+#pragma unroll
+        for (int w = 0; w < kRsWaves; w++) wc[w][tid] = 0;
+        __syncthreads();
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < bits; b++) {
+            const bool bit = (d >> b) & 1u;
+            const uint64_t bb = __ballot(bit);
+            peers &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & lt);
+        if (valid && rank == 0) wc[wave][d] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int pos = run[d] + rank;
+            for (int w = 0; w < wave; w++) pos += wc[w][d];
+            if (keys_out) keys_out[pos] = key;
+            vals_out[pos] = val;
+        }
+        __syncthreads();
+        int add = 0;
+#pragma unroll
+        for (int w = 0; w < kRsWaves; w++) add += wc[w][tid];
+        run[tid] += add;
+        __syncthreads();
+    }
+}
+
+__global__ void gather_col(const int32_t* __restrict__ other, const int32_t* __restrict__ eid, int64_t e,
+                           int32_t* __restrict__ col) {
+    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < e; p += (int64_t)gridDim.x * blockDim.x)
+        col[p] = other[eid[p]];
+}
+
+int key_bits(int32_t n) {
+    if (n <= 1) return 0;
+    uint32_t m = (uint32_t)(n - 1);
+    return 32 - __builtin_clz(m);
+}
+
+struct CsrWs {
+    int32_t* cnt;
+    int32_t* hist;
+    int32_t* scan;
+    int32_t* keys_tmp;
+    int32_t* vals_tmp;
+    size_t bytes;
+};
+
+CsrWs carve(void* ws, int32_t n, int64_t e) {
+    Carver c(ws);
+    CsrWs w;
+    int64_t nblocks = (e + kRsTile - 1) / kRsTile;
+    int64_t hist_n = (int64_t)kRsBins * nblocks;
+    w.cnt = c.take<int32_t>((size_t)n + 1);
+    w.hist = c.take<int32_t>((size_t)hist_n);
+    size_t sc = scan_workspace_elems(hist_n > n ? hist_n : n);
+    w.scan = c.take<int32_t>(sc);
+    w.keys_tmp = c.take<int32_t>((size_t)e);
+    w.vals_tmp = c.take<int32_t>((size_t)e);
+    w.bytes = c.bytes();
+    return w;
+}
+
+int grid_for(int64_t n) {
+    int64_t b = (n + 255) / 256;
+    if (b < 1) b = 1;
+    if (b > 16384) b = 16384;
+    return (int)b;
+}
+
+}  // namespace
+
+}  // namespace gga
+
+using namespace gga;
+
+extern "C" size_t gga_coo_to_csr_workspace(int32_t n, int64_t e) {
+    if (n < 0 || e < 0 || e >= (int64_t)INT32_MAX) return 0;
+    return carve(nullptr, n, e).bytes;
+}
+
+extern "C" int gga_validate_coo(int32_t n, int64_t e, const int32_t* src, const int32_t* dst, int32_t* d_bad,
+                                void* stream) {
+    if (n < 0 || e < 0) return GGA_EINVAL;
+    if (!d_bad || (e > 0 && (!src || !dst))) return GGA_EINVAL;
+    hipStream_t s = as_stream(stream);
+    fill_i32(d_bad, 1, 0, s);
+    if (e > 0) count_bad<<<grid_for(e), 256, 0, s>>>(src, dst, e, n, d_bad);
+    return launch_status();
+}
+
+extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const int32_t* other, int32_t* row_ptr,
+                              int32_t* col, int32_t* eid, void* ws, size_t ws_bytes, void* stream) {
+    if (n < 0 || e < 0) return GGA_EINVAL;
+    if (e >= (int64_t)INT32_MAX) return GGA_ERANGE;
+    if (!row_ptr) return GGA_EINVAL;
+    if (e > 0 && (!key || !other || !col || !eid)) return GGA_EINVAL;
+    CsrWs w = carve(nullptr, n, e);
+    if (ws_bytes < w.bytes || (w.bytes > 0 && !ws)) return GGA_EWORKSPACE;
+    w = carve(ws, n, e);
+    hipStream_t s = as_stream(stream);
+
+    // row_ptr: histogram of valid keys, exclusive scan, total at row_ptr[n]
+    fill_i32(w.cnt, (int64_t)n + 1, 0, s);
+    if (e > 0 && n > 0) count_keys<<<grid_for(e), 256, 0, s>>>(key, e, n, w.cnt, nullptr);
+    exclusive_scan_i32(w.cnt, row_ptr, n, row_ptr + n, w.scan, s);
+    if (e == 0) return launch_status();
+
+    const int64_t nblocks = (e + kRsTile - 1) / kRsTile;
+    const int bits_total = key_bits(n);
+    const int passes = bits_total == 0 ? 1 : (bits_total + 7) / 8;
+    const int last = passes - 1;
+    int32_t* kbuf[2] = {w.keys_tmp, col};  // col is free until the final gather
+    int32_t* vbuf[2];
+    vbuf[last & 1] = eid;
+    vbuf[(last & 1) ^ 1] = w.vals_tmp;
+    for (int p = 0; p < passes; p++) {
+        const int shift = 8 * p;
+        const int bits = bits_total == 0 ? 0 : ((bits_total - shift) < 8 ? (bits_total - shift) : 8);
+        const uint32_t mask = (1u << bits) - 1u;
+        const int32_t* kin = p == 0 ? key : kbuf[(p - 1) & 1];
+        const int32_t* vin = p == 0 ? nullptr : vbuf[(p - 1) & 1];
+        int32_t* kout = p == last ? nullptr : kbuf[p & 1];
+        int32_t* vout = vbuf[p & 1];
+        radix_upsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, e, shift, mask, w.hist, nblocks);
+        exclusive_scan_i32(w.hist, w.hist, (int64_t)kRsBins * nblocks, nullptr, w.scan, s);
+        radix_downsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, vin, kout, vout, e, shift, bits, w.hist,
+                                                                  nblocks);
+    }
+    gather_col<<<grid_for(e), 256, 0, s>>>(other, eid, e, col);
+    return launch_status();
+}

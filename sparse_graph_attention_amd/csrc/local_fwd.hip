@@ -1,0 +1,520 @@
+// Fused local attention forward: per target row, gather source rows, score, online
+// softmax and weighted aggregation in one pass ("Gated Local-Global Graph Attention",
+// Key formulas, local branch; Tinymesh "Sparse attention experiment", sections
+// "Target softmax" and "Multiple heads are composition").
+//
+// Lane layout.  A row of W = H*C elements is covered by LPR lanes holding EPL elements
+// each (16-byte loads on the fast path), HDP lanes per head (padded to a power of two),
+// and NS slots per lane when one wavefront is not wide enough.  The 64/LPR groups of a
+// wavefront take different edges of the same row; their states are merged at the end.
+// Scores are kept in log2 units (the score multiplier includes log2(e)), so the
+// softmax uses exp2.  No floating-point atomics: every sum has a fixed order.
+#include "plan.hpp"
+
+namespace gga {
+
+namespace {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kFwdWaves = 4;
+constexpr int kFwdThreads = 64 * kFwdWaves;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct FwdParams {
+    const void* qs;
+    const void* ks;
+    const void* v;
+    const int32_t* row_ptr;
+    const int32_t* col;
+    const PlanHeader* hdr;
+    const int32_t* light;
+    const int4* chunks;
+    const int4* heavy;
+    float* out;
+    float* lse;
+    float* part;
+    int32_t n, H, C, W;
+    int32_t lpr_log2;
+    int32_t part_stride;
+    float score_mul;
+    float slope;
+    int32_t chunk_blocks;
+};
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int EPL>
+__device__ __forceinline__ void store_f32(float* dst, const float* f) {
+    if constexpr (EPL == 8) {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+        reinterpret_cast<float4*>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+    } else if constexpr (EPL == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) dst[i] = f[i];
+    }
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_f32(const float* src, float* f) {
+    if constexpr (EPL == 8) {
+        float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else if constexpr (EPL == 4) {
+        float4 a = *reinterpret_cast<const float4*>(src);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) f[i] = src[i];
+    }
+}
+
+template <typename T, int EPL, int HDP, int NS, int MODE>
+struct FwdRow {
+    using V = Vec<T, EPL>;
+    using raw_t = typename V::raw_t;
+    static constexpr int kUMax = 8 / NS;
+
+    // geometry
+    int lane, g, G, U, EIT, lpr;
+    int off[NS], head[NS];
+    bool ok[NS], lead[NS];
+    // state
+    float m[NS], l[NS], acc[NS][EPL];
+    // destination-side operand
+    float qf[NS][EPL];
+    float sd[NS];
+
+    __device__ __forceinline__ void geometry(const FwdParams& p) {
+        lane = threadIdx.x & 63;
+        lpr = 1 << p.lpr_log2;
+        G = 64 >> p.lpr_log2;
+        g = lane >> p.lpr_log2;
+        U = G >= kUMax ? 1 : kUMax / G;
+        EIT = G * U;
+        const int li = lane & (lpr - 1);
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const int j = s * 64 + li;
+            head[s] = j / HDP;
+            const int sub = j % HDP;
+            ok[s] = head[s] < p.H && sub * EPL < p.C;
+            off[s] = head[s] * p.C + sub * EPL;
+            lead[s] = sub == 0;
+        }
+    }
+
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            m[s] = kNegInf;
+            l[s] = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPL; i++) acc[s][i] = 0.f;
+        }
+    }
+
+    __device__ __forceinline__ void load_target(const FwdParams& p, int32_t v) {
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            if constexpr (MODE == GGA_SCORE_DOT) {
+                raw_t r{};
+                if (ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.qs) + (size_t)v * p.W + off[s]);
+                V::widen(r, qf[s]);
+            } else {
+                sd[s] = ok[s] ? static_cast<const float*>(p.qs)[(size_t)v * p.H + head[s]] : 0.f;
+            }
+        }
+    }
+
+    // Edges at positions beg + start + k*stride + (g + G*j), j < U, for k = 0, 1, ...
+    __device__ __forceinline__ void run(const FwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                        int32_t stride) {
+        const T* __restrict__ kp = static_cast<const T*>(p.ks);
+        const T* __restrict__ vp = static_cast<const T*>(p.v);
+        const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
+        for (int32_t base = beg + start; base < end; base += stride) {
+            const int32_t colv = (lane < EIT && base + lane < end) ? p.col[base + lane] : 0;
+            int32_t u[kUMax];
+            bool ev[kUMax];
+#pragma unroll
+            for (int j = 0; j < kUMax; j++) {
+                if (j < U) {
+                    const int idx = g + G * j;
+                    u[j] = __shfl(colv, idx, 64);
+                    ev[j] = base + idx < end;
+                } else {
+                    u[j] = 0;
+                    ev[j] = false;
+                }
+            }
+            raw_t kr[kUMax][NS], vr[kUMax][NS];
+            float ss[kUMax][NS];
+#pragma unroll
+            for (int j = 0; j < kUMax; j++) {
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    kr[j][s] = raw_t{};
+                    vr[j][s] = raw_t{};
+                    ss[j][s] = 0.f;
+                    if (ev[j] && ok[s]) {
+                        const size_t ro = (size_t)u[j] * p.W + off[s];
+                        if constexpr (MODE == GGA_SCORE_DOT)
+                            kr[j][s] = *reinterpret_cast<const raw_t*>(kp + ro);
+                        else
+                            ss[j][s] = ssrc[(size_t)u[j] * p.H + head[s]];
+                        vr[j][s] = *reinterpret_cast<const raw_t*>(vp + ro);
+                    }
+                }
+            }
+            float sc[kUMax][NS];
+#pragma unroll
+            for (int j = 0; j < kUMax; j++) {
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    if (j < U) {
+                        float t;
+                        if constexpr (MODE == GGA_SCORE_DOT) {
+                            float f[EPL];
+                            V::widen(kr[j][s], f);
+                            float d = 0.f;
+#pragma unroll
+                            for (int i = 0; i < EPL; i++) d = fmaf(qf[s][i], f[i], d);
+                            t = group_sum<HDP>(d) * p.score_mul;
+                        } else {
+                            float z = ss[j][s] + sd[s];
+                            z = z > 0.f ? z : z * p.slope;
+                            t = z * p.score_mul;
+                        }
+                        sc[j][s] = ev[j] ? t : kNegInf;
+                    } else {
+                        sc[j][s] = kNegInf;
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
+                float mx = kNegInf;
+#pragma unroll
+                for (int j = 0; j < kUMax; j++) mx = fmaxf(mx, sc[j][s]);
+                const float mn = fmaxf(m[s], mx);
+                if (mn > kNegInf) {
+                    const float corr = fexp2(m[s] - mn);
+                    l[s] *= corr;
+#pragma unroll
+                    for (int i = 0; i < EPL; i++) acc[s][i] *= corr;
+#pragma unroll
+                    for (int j = 0; j < kUMax; j++) {
+                        if (j < U) {
+                            const float pj = fexp2(sc[j][s] - mn);
+                            float f[EPL];
+                            V::widen(vr[j][s], f);
+                            l[s] += pj;
+#pragma unroll
+                            for (int i = 0; i < EPL; i++) acc[s][i] = fmaf(pj, f[i], acc[s][i]);
+                        }
+                    }
+                    m[s] = mn;
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void fold(float mo, float lo, const float* ao, int s) {
+        const float mn = fmaxf(m[s], mo);
+        if (mn > kNegInf) {
+            const float a = fexp2(m[s] - mn), b = fexp2(mo - mn);
+            l[s] = l[s] * a + lo * b;
+#pragma unroll
+            for (int i = 0; i < EPL; i++) acc[s][i] = acc[s][i] * a + ao[i] * b;
+            m[s] = mn;
+        }
+    }
+
+    // Butterfly over the G groups of the wavefront; group 0 ends with the whole state.
+    __device__ __forceinline__ void merge_groups() {
+        for (int o = lpr; o < 64; o <<= 1) {
+#pragma unroll
+            for (int s = 0; s < NS; s++) {
+                const float mo = __shfl_xor(m[s], o, 64);
+                const float lo = __shfl_xor(l[s], o, 64);
+                float ao[EPL];
+#pragma unroll
+                for (int i = 0; i < EPL; i++) ao[i] = __shfl_xor(acc[s][i], o, 64);
+                fold(mo, lo, ao, s);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void write_final(const FwdParams& p, int32_t v) {
+        if (g != 0) return;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            if (!ok[s]) continue;
+            const float inv = l[s] > 0.f ? 1.0f / l[s] : 0.f;
+            float o[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; i++) o[i] = acc[s][i] * inv;
+            store_f32<EPL>(p.out + (size_t)v * p.W + off[s], o);
+            if (lead[s] && p.lse)
+                p.lse[(size_t)v * p.H + head[s]] = l[s] > 0.f ? (m[s] + __log2f(l[s])) * kLn2 : kNegInf;
+        }
+    }
+
+    __device__ __forceinline__ void write_partial(const FwdParams& p, int32_t slot) {
+        if (g != 0) return;
+        float* sp = p.part + (size_t)slot * p.part_stride;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            if (!ok[s]) continue;
+            store_f32<EPL>(sp + off[s], acc[s]);
+            if (lead[s]) {
+                sp[p.W + head[s]] = m[s];
+                sp[p.W + p.H + head[s]] = l[s];
+            }
+        }
+    }
+};
+
+template <typename T, int EPL, int HDP, int NS, int MODE>
+__global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
+    using Row = FwdRow<T, EPL, HDP, NS, MODE>;
+    Row r;
+    r.geometry(p);
+    const int wave = threadIdx.x >> 6;
+    if ((int)blockIdx.x < p.chunk_blocks) {
+        // one workgroup per chunk of a long row; the four wavefronts interleave the
+        // chunk's edges and their states are folded in wavefront order
+        __shared__ float sm[kFwdWaves][NS][64][EPL + 2];
+        const int nch = p.hdr->n_chunks;
+        for (int c = blockIdx.x; c < nch; c += p.chunk_blocks) {
+            const int4 ch = p.chunks[c];
+            r.reset();
+            r.load_target(p, ch.x);
+            r.run(p, ch.y, ch.z, wave * r.EIT, kFwdWaves * r.EIT);
+            r.merge_groups();
+            if (wave > 0) {
+#pragma unroll
+                for (int s = 0; s < NS; s++) {
+                    sm[wave][s][r.lane][0] = r.m[s];
+                    sm[wave][s][r.lane][1] = r.l[s];
+#pragma unroll
+                    for (int i = 0; i < EPL; i++) sm[wave][s][r.lane][2 + i] = r.acc[s][i];
+                }
+            }
+            __syncthreads();
+            if (wave == 0) {
+                for (int w = 1; w < kFwdWaves; w++) {
+#pragma unroll
+                    for (int s = 0; s < NS; s++) {
+                        float ao[EPL];
+#pragma unroll
+                        for (int i = 0; i < EPL; i++) ao[i] = sm[w][s][r.lane][2 + i];
+                        r.fold(sm[w][s][r.lane][0], sm[w][s][r.lane][1], ao, s);
+                    }
+                }
+                if (ch.w < 0)
+                    r.write_final(p, ch.x);
+                else
+                    r.write_partial(p, ch.w);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+    const int li = (blockIdx.x - p.chunk_blocks) * kFwdWaves + wave;
+    if (li >= p.hdr->n_light) return;
+    const int32_t v = p.light[li];
+    r.reset();
+    r.load_target(p, v);
+    r.run(p, p.row_ptr[v], p.row_ptr[v + 1], 0, r.EIT);
+    r.merge_groups();
+    r.write_final(p, v);
+}
+
+// Folds the partial states of each heavy row in slot order.
+__global__ __launch_bounds__(kFwdThreads) void local_fwd_merge(FwdParams p) {
+    const int lane = threadIdx.x & 63;
+    const int nh = p.hdr->n_heavy;
+    for (int hr = blockIdx.x * kFwdWaves + (threadIdx.x >> 6); hr < nh; hr += gridDim.x * kFwdWaves) {
+        const int4 hv = p.heavy[hr];
+        for (int x = lane; x < p.W; x += 64) {
+            const int h = x / p.C;
+            float m = kNegInf, l = 0.f, a = 0.f;
+            for (int i = 0; i < hv.z; i++) {
+                const float* sp = p.part + (size_t)(hv.y + i) * p.part_stride;
+                const float mi = sp[p.W + h], li = sp[p.W + p.H + h], ai = sp[x];
+                const float mn = fmaxf(m, mi);
+                if (mn > kNegInf) {
+                    const float ca = fexp2(m - mn), cb = fexp2(mi - mn);
+                    l = l * ca + li * cb;
+                    a = a * ca + ai * cb;
+                    m = mn;
+                }
+            }
+            p.out[(size_t)hv.x * p.W + x] = l > 0.f ? a * (1.0f / l) : 0.f;
+            if (p.lse && x - h * p.C == 0)
+                p.lse[(size_t)hv.x * p.H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+struct Shape {
+    int epl, hdp, ns, lpr_log2;
+};
+
+int next_pow2(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) r++;
+    return r;
+}
+
+// Picks the lane layout; returns false for shapes this build does not handle.
+bool pick_shape(int H, int C, int dtype, Shape* sh) {
+    const int vec = dtype == GGA_BF16 ? 8 : 4;
+    sh->epl = (C % vec == 0) ? vec : 1;
+    const int per_head = C / sh->epl;
+    sh->hdp = next_pow2(per_head);
+    if (sh->hdp > 64) return false;
+    const int lanes = H * sh->hdp;
+    if (lanes <= 64) {
+        sh->ns = 1;
+        sh->lpr_log2 = ilog2(next_pow2(lanes));
+    } else {
+        sh->ns = (lanes + 63) / 64;
+        sh->lpr_log2 = 6;
+        if (sh->ns > 2 || sh->epl == 1) return false;
+    }
+    return true;
+}
+
+size_t part_stride(int H, int C) { return align_up((size_t)H * C + 2 * (size_t)H, 8); }
+
+template <typename T, int EPL, int HDP, int NS, int MODE>
+void launch(const FwdParams& p, unsigned grid, int64_t max_heavy, hipStream_t s) {
+    local_fwd_kernel<T, EPL, HDP, NS, MODE><<<grid, kFwdThreads, 0, s>>>(p);
+    if (max_heavy > 0) {
+        int64_t mb = (max_heavy + kFwdWaves - 1) / kFwdWaves;
+        unsigned mg = (unsigned)(mb < 1024 ? mb : 1024);
+        local_fwd_merge<<<mg, kFwdThreads, 0, s>>>(p);
+    }
+}
+
+template <typename T, int EPL, int MODE>
+bool dispatch_hdp(const Shape& sh, const FwdParams& p, unsigned grid, int64_t mh, hipStream_t s) {
+#define GGA_CASE(HD)                                                              \
+    case HD:                                                                      \
+        if (sh.ns == 1)                                                           \
+            launch<T, EPL, HD, 1, MODE>(p, grid, mh, s);                          \
+        else if constexpr (EPL > 1)                                               \
+            launch<T, EPL, HD, 2, MODE>(p, grid, mh, s);                          \
+        else                                                                      \
+            return false;                                                         \
+        return true;
+    switch (sh.hdp) {
+        GGA_CASE(1)
+        GGA_CASE(2)
+        GGA_CASE(4)
+        GGA_CASE(8)
+        GGA_CASE(16)
+        GGA_CASE(32)
+        GGA_CASE(64)
+        default:
+            return false;
+    }
+#undef GGA_CASE
+}
+
+template <int MODE>
+bool dispatch(int dtype, const Shape& sh, const FwdParams& p, unsigned grid, int64_t mh, hipStream_t s) {
+    if (dtype == GGA_BF16) {
+        if (sh.epl == 8) return dispatch_hdp<uint16_t, 8, MODE>(sh, p, grid, mh, s);
+        return dispatch_hdp<uint16_t, 1, MODE>(sh, p, grid, mh, s);
+    }
+    if (sh.epl == 4) return dispatch_hdp<float, 4, MODE>(sh, p, grid, mh, s);
+    return dispatch_hdp<float, 1, MODE>(sh, p, grid, mh, s);
+}
+
+int check_desc(const gga_local_desc* d) {
+    if (!d) return GGA_EINVAL;
+    if (d->n < 0 || d->e < 0 || d->heads < 1 || d->head_dim < 1 || d->reserved != 0) return GGA_EINVAL;
+    if (d->e >= (int64_t)INT32_MAX) return GGA_ERANGE;
+    if ((int64_t)d->n * d->heads * d->head_dim >= ((int64_t)1 << 40)) return GGA_ERANGE;
+    if (d->score != GGA_SCORE_DOT && d->score != GGA_SCORE_ADDITIVE) return GGA_EUNSUPPORTED;
+    if (d->dtype != GGA_F32 && d->dtype != GGA_BF16) return GGA_EUNSUPPORTED;
+    Shape sh;
+    if (!pick_shape(d->heads, d->head_dim, d->dtype, &sh)) return GGA_EUNSUPPORTED;
+    return GGA_OK;
+}
+
+}  // namespace
+
+}  // namespace gga
+
+using namespace gga;
+
+extern "C" size_t gga_local_attn_fwd_workspace(const gga_local_desc* d) {
+    if (check_desc(d) != GGA_OK) return 0;
+    PlanBounds b = plan_bounds(d->e);
+    return align_up((size_t)b.max_slots * part_stride(d->heads, d->head_dim) * sizeof(float), 256);
+}
+
+extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
+                                  const int32_t* row_ptr, const int32_t* col, const void* plan, float* out,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    if (d->n == 0) return GGA_OK;
+    if (!row_ptr || !plan || !out || !qs) return GGA_EINVAL;
+    if (d->e > 0 && (!col || !ks || !v)) return GGA_EINVAL;
+    if (!aligned16(out) || !aligned16(qs) || (ks && !aligned16(ks)) || (v && !aligned16(v))) return GGA_EINVAL;
+    const size_t need = gga_local_attn_fwd_workspace(d);
+    if (ws_bytes < need || (need > 0 && !ws)) return GGA_EWORKSPACE;
+    Shape sh;
+    pick_shape(d->heads, d->head_dim, d->dtype, &sh);
+
+    PlanView pv = plan_view(const_cast<void*>(plan), d->n, d->e);
+    PlanBounds b = plan_bounds(d->e);
+    FwdParams p{};
+    p.qs = qs;
+    p.ks = ks;
+    p.v = v;
+    p.row_ptr = row_ptr;
+    p.col = col;
+    p.hdr = pv.hdr;
+    p.light = pv.light;
+    p.chunks = pv.chunks;
+    p.heavy = pv.heavy;
+    p.out = out;
+    p.lse = lse;
+    p.part = static_cast<float*>(ws);
+    p.n = d->n;
+    p.H = d->heads;
+    p.C = d->head_dim;
+    p.W = d->heads * d->head_dim;
+    p.lpr_log2 = sh.lpr_log2;
+    p.part_stride = (int32_t)part_stride(d->heads, d->head_dim);
+    const float log2e = 1.44269504088896340736f;
+    p.score_mul = d->score == GGA_SCORE_DOT ? d->scale * log2e : log2e;
+    p.slope = d->negative_slope;
+    const int64_t cb = b.max_chunks < 2048 ? b.max_chunks : 2048;
+    p.chunk_blocks = d->e > kLightEdges ? (int32_t)cb : 0;
+    const int64_t light_blocks = ((int64_t)d->n + kFwdWaves - 1) / kFwdWaves;
+    const int64_t grid = p.chunk_blocks + light_blocks;
+    if (grid >= ((int64_t)1 << 31)) return GGA_ERANGE;
+    const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;
+    hipStream_t s = as_stream(stream);
+    bool ok = d->score == GGA_SCORE_DOT ? dispatch<GGA_SCORE_DOT>(d->dtype, sh, p, (unsigned)grid, mh, s)
+                                        : dispatch<GGA_SCORE_ADDITIVE>(d->dtype, sh, p, (unsigned)grid, mh, s);
+    if (!ok) return GGA_EUNSUPPORTED;
+    return launch_status();
+}

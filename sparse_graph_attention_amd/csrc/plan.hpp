@@ -1,0 +1,61 @@
+// Layout of the degree-bucket plan (an opaque device buffer to callers).
+#pragma once
+
+#include "common.hpp"
+
+namespace gga {
+
+// Rows with at most kLightEdges in-edges are processed by one wavefront each.  Longer
+// rows are cut into chunks of at most kChunkEdges edges, one workgroup per chunk; when
+// a row has more than one chunk, each chunk leaves a partial softmax state in a slot and
+// a merge kernel folds the row's slots in slot order.
+constexpr int kLightEdges = 64;
+constexpr int kChunkEdges = 1024;
+
+struct PlanHeader {
+    int32_t n_light;   // rows in the light list
+    int32_t n_chunks;  // entries of the chunk table
+    int32_t n_heavy;   // rows cut into more than one chunk
+    int32_t n_slots;   // partial-state slots used by those rows
+    int32_t n;         // rows the plan was built for
+    int32_t light_edges;
+    int32_t chunk_edges;
+    int32_t magic;
+};
+
+constexpr int32_t kPlanMagic = 0x67676150;
+
+struct PlanBounds {
+    int64_t max_chunks, max_heavy, max_slots;
+};
+
+inline PlanBounds plan_bounds(int64_t e) {
+    PlanBounds b;
+    b.max_chunks = e / (kLightEdges + 1) + e / kChunkEdges + 1;
+    b.max_heavy = e / (kChunkEdges + 1) + 1;
+    b.max_slots = e / kChunkEdges + e / (kChunkEdges + 1) + 1;
+    return b;
+}
+
+// Device views into a plan buffer.
+struct PlanView {
+    PlanHeader* hdr;
+    int32_t* light;  // [n]
+    int4* chunks;    // [max_chunks]: row, begin, end, slot (-1: chunk is the whole row)
+    int4* heavy;     // [max_heavy]: row, first slot, slot count, 0
+    size_t bytes;
+};
+
+inline PlanView plan_view(void* plan, int32_t n, int64_t e) {
+    PlanBounds b = plan_bounds(e);
+    Carver c(plan);
+    PlanView v;
+    v.hdr = c.take<PlanHeader>(1);
+    v.light = c.take<int32_t>((size_t)n);
+    v.chunks = c.take<int4>((size_t)b.max_chunks);
+    v.heavy = c.take<int4>((size_t)b.max_heavy);
+    v.bytes = c.bytes();
+    return v;
+}
+
+}  // namespace gga

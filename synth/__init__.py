@@ -232,3 +232,19 @@ def gated_layer_inputs(n: int, d: int = 256, ident: int = 4):
     gamma = np.ones(d, np.float32)
     beta = np.zeros(d, np.float32)
     return dict(x=x, w_q=ws[0], w_k=ws[1], w_v=ws[2], w_o=ws[3], w_g=w_g, b_g=b_g, gamma=gamma, beta=beta)
+
+
+def mixed_degree_graph(n: int, seed: int, hubs=(3000, 1025, 700, 65), background: int = 4, isolated: int = 3):
+    """Test graph exercising every degree bucket: a uniform background of about
+    ``background`` in-edges per node plus a self-loop, nodes 0..len(hubs)-1 given the
+    listed extra in-degrees, and the last ``isolated`` nodes left with no in-edge."""
+    rng = _rng(9100, seed)
+    live = n - isolated
+    m = background * live
+    src = [rng.integers(0, n, size=m, dtype=np.int32), np.arange(live, dtype=np.int32)]
+    dst = [rng.integers(0, live, size=m, dtype=np.int32), np.arange(live, dtype=np.int32)]
+    for i, d in enumerate(hubs):
+        if i < live:
+            src.append(rng.integers(0, n, size=d, dtype=np.int32))
+            dst.append(np.full(d, i, np.int32))
+    return _shuffle(np.concatenate(src), np.concatenate(dst), rng)
