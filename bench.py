@@ -28,6 +28,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 
+# HBM bytes per forward launch counted by rocprofv3 (FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00,
+# factors from a plain 1 GiB copy) for the kernel as of the committed profile summary
+# profiles/local_fwd_dot_n1m_h8_r64_bf16.md; None once the kernel changes.
+COUNTED_TRAFFIC_GB = 39.95
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -161,7 +166,7 @@ def main() -> int:
         "csr_build_ms": csr_ms,
         "plan_build_ms": plan_ms,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": COUNTED_TRAFFIC_GB,
                      "kernel": "local_fwd_kernel (+ heavy-row merge launch)", "alg_bytes_per_launch": alg,
                      "launch_ms": kern_ms},
         "cpu_baseline": cpu,
