@@ -1,0 +1,105 @@
+// Host entry point of the local attention backward (kernels in local_bwd_impl.hpp).
+#include "local_bwd_impl.hpp"
+#include "shape.hpp"
+
+namespace gga {
+namespace {
+
+struct BwdWs {
+    float* D;
+    float* part_a;
+    float* part_b;
+    int32_t stride_a, stride_b;
+    size_t bytes;
+};
+
+BwdWs carve_bwd(void* ws, const gga_local_desc* d) {
+    const PlanBounds b = plan_bounds(d->e);
+    const int64_t W = (int64_t)d->heads * d->head_dim;
+    const int64_t wk = d->score == GGA_SCORE_DOT ? W : d->heads;
+    BwdWs w;
+    w.stride_a = (int32_t)align_up((size_t)wk, 8);
+    w.stride_b = (int32_t)(align_up((size_t)wk, 8) + align_up((size_t)W, 8));
+    Carver c(ws);
+    w.D = c.take<float>((size_t)d->n * d->heads);
+    w.part_a = c.take<float>((size_t)b.max_slots * w.stride_a);
+    w.part_b = c.take<float>((size_t)b.max_slots * w.stride_b);
+    w.bytes = c.bytes();
+    return w;
+}
+
+}  // namespace
+}  // namespace gga
+
+using namespace gga;
+
+extern "C" size_t gga_local_attn_bwd_workspace(const gga_local_desc* d) {
+    if (check_desc(d) != GGA_OK) return 0;
+    return carve_bwd(nullptr, d).bytes;
+}
+
+extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
+                                  const float* out, const float* lse, const float* d_out, const int32_t* row_ptr,
+                                  const int32_t* col, const void* plan, const int32_t* row_ptr_s,
+                                  const int32_t* col_s, const void* plan_s, float* d_qs, float* d_ks, float* d_v,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    if (d->n == 0) return GGA_OK;
+    if (!qs || !out || !lse || !d_out || !row_ptr || !plan || !row_ptr_s || !plan_s || !d_qs || !d_ks || !d_v)
+        return GGA_EINVAL;
+    if (d->e > 0 && (!ks || !v || !col || !col_s)) return GGA_EINVAL;
+    for (const void* p : {qs, ks, v, (const void*)out, (const void*)d_out, (const void*)d_qs, (const void*)d_ks,
+                          (const void*)d_v})
+        if (p && !aligned16(p)) return GGA_EINVAL;
+    const BwdWs need = carve_bwd(nullptr, d);
+    if (ws_bytes < need.bytes || !ws) return GGA_EWORKSPACE;
+    const BwdWs w = carve_bwd(ws, d);
+    hipStream_t s = as_stream(stream);
+    const int64_t W = (int64_t)d->heads * d->head_dim;
+    const int64_t wk = d->score == GGA_SCORE_DOT ? W : d->heads;
+    if (d->e == 0) {
+        fill_f32(d_qs, (int64_t)d->n * wk, 0.f, s);
+        fill_f32(d_ks, (int64_t)d->n * wk, 0.f, s);
+        fill_f32(d_v, (int64_t)d->n * W, 0.f, s);
+        return launch_status();
+    }
+    Shape sh;
+    pick_shape(d->heads, d->head_dim, d->dtype, &sh);
+    const PlanBounds b = plan_bounds(d->e);
+    const PlanView pa = plan_view(const_cast<void*>(plan), d->n, d->e);
+    const PlanView pb = plan_view(const_cast<void*>(plan_s), d->n, d->e);
+    const int64_t cb = b.max_chunks < 2048 ? b.max_chunks : 2048;
+    BwdParams p{};
+    p.qs = qs;
+    p.ks = ks;
+    p.v = v;
+    p.out = out;
+    p.lse = lse;
+    p.dout = d_out;
+    p.d_qs = d_qs;
+    p.d_ks = d_ks;
+    p.d_v = d_v;
+    p.D = w.D;
+    p.a = BwdCsr{row_ptr, col, pa.hdr, pa.light, pa.chunks, pa.heavy, w.part_a, w.stride_a,
+                 d->e > kLightEdges ? (int32_t)cb : 0};
+    p.b = BwdCsr{row_ptr_s, col_s, pb.hdr, pb.light, pb.chunks, pb.heavy, w.part_b, w.stride_b,
+                 d->e > kLightEdges ? (int32_t)cb : 0};
+    p.n = d->n;
+    p.H = d->heads;
+    p.C = d->head_dim;
+    p.W = (int32_t)W;
+    p.lpr_log2 = sh.lpr_log2;
+    p.scale = d->scale;
+    p.score_mul = d->score == GGA_SCORE_DOT ? d->scale * kLog2e : kLog2e;
+    p.slope = d->negative_slope;
+    const int64_t light_blocks = ((int64_t)d->n + kBwdWaves - 1) / kBwdWaves;
+    const int64_t ga = p.a.chunk_blocks + light_blocks, gb = p.b.chunk_blocks + light_blocks;
+    if (ga >= ((int64_t)1 << 31) || gb >= ((int64_t)1 << 31)) return GGA_ERANGE;
+    const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;
+    const bool ok = d->dtype == GGA_BF16
+                        ? launch_bwd_bf16(p, sh.epl, sh.hdp, sh.ns, d->score, (unsigned)ga, (unsigned)gb, mh, s)
+                        : launch_bwd_f32(p, sh.epl, sh.hdp, sh.ns, d->score, (unsigned)ga, (unsigned)gb, mh, s);
+    if (!ok) return GGA_EUNSUPPORTED;
+    return launch_status();
+}

@@ -10,6 +10,7 @@
 // Scores are kept in log2 units (the score multiplier includes log2(e)), so the
 // softmax uses exp2.  No floating-point atomics: every sum has a fixed order.
 #include "plan.hpp"
+#include "shape.hpp"
 
 namespace gga {
 
@@ -362,41 +363,6 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_merge(FwdParams p) {
 
 // ---------------------------------------------------------------- host side
 
-struct Shape {
-    int epl, hdp, ns, lpr_log2;
-};
-
-int next_pow2(int x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
-
-int ilog2(int x) {
-    int r = 0;
-    while ((1 << r) < x) r++;
-    return r;
-}
-
-// Picks the lane layout; returns false for shapes this build does not handle.
-bool pick_shape(int H, int C, int dtype, Shape* sh) {
-    const int vec = dtype == GGA_BF16 ? 8 : 4;
-    sh->epl = (C % vec == 0) ? vec : 1;
-    const int per_head = C / sh->epl;
-    sh->hdp = next_pow2(per_head);
-    if (sh->hdp > 64) return false;
-    const int lanes = H * sh->hdp;
-    if (lanes <= 64) {
-        sh->ns = 1;
-        sh->lpr_log2 = ilog2(next_pow2(lanes));
-    } else {
-        sh->ns = (lanes + 63) / 64;
-        sh->lpr_log2 = 6;
-        if (sh->ns > 2 || sh->epl == 1) return false;
-    }
-    return true;
-}
-
 size_t part_stride(int H, int C) { return align_up((size_t)H * C + 2 * (size_t)H, 8); }
 
 template <typename T, int EPL, int HDP, int NS, int MODE>
@@ -442,18 +408,6 @@ bool dispatch(int dtype, const Shape& sh, const FwdParams& p, unsigned grid, int
     }
     if (sh.epl == 4) return dispatch_hdp<float, 4, MODE>(sh, p, grid, mh, s);
     return dispatch_hdp<float, 1, MODE>(sh, p, grid, mh, s);
-}
-
-int check_desc(const gga_local_desc* d) {
-    if (!d) return GGA_EINVAL;
-    if (d->n < 0 || d->e < 0 || d->heads < 1 || d->head_dim < 1 || d->reserved != 0) return GGA_EINVAL;
-    if (d->e >= (int64_t)INT32_MAX) return GGA_ERANGE;
-    if ((int64_t)d->n * d->heads * d->head_dim >= ((int64_t)1 << 40)) return GGA_ERANGE;
-    if (d->score != GGA_SCORE_DOT && d->score != GGA_SCORE_ADDITIVE) return GGA_EUNSUPPORTED;
-    if (d->dtype != GGA_F32 && d->dtype != GGA_BF16) return GGA_EUNSUPPORTED;
-    Shape sh;
-    if (!pick_shape(d->heads, d->head_dim, d->dtype, &sh)) return GGA_EUNSUPPORTED;
-    return GGA_OK;
 }
 
 }  // namespace

@@ -1,11 +1,6 @@
 // Entry points whose kernels are not written yet: they report GGA_EUNSUPPORTED.
 #include "common.hpp"
 
-extern "C" size_t gga_local_attn_bwd_workspace(const gga_local_desc*) { return 0; }
-extern "C" int gga_local_attn_bwd(const gga_local_desc*, const void*, const void*, const void*, const float*,
-                                  const float*, const float*, const int32_t*, const int32_t*, const void*,
-                                  const int32_t*, const int32_t*, const void*, float*, float*, float*, void*, size_t,
-                                  void*) { return GGA_EUNSUPPORTED; }
 extern "C" int gga_edge_values(int32_t, int32_t, int32_t, const void*, int64_t, const int32_t*, void*, void*) {
     return GGA_EUNSUPPORTED;
 }

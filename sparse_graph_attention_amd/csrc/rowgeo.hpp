@@ -1,0 +1,77 @@
+// Lane geometry of a node row inside a wavefront, shared by the row kernels.
+//
+// A row of W = H*C elements is covered by LPR lanes holding EPL consecutive elements
+// each; a head spans HDP lanes (C/EPL rounded up to a power of two; surplus lanes hold
+// nothing); when H*HDP > 64 each lane holds NS slots, slot s covering row lanes
+// s*64 .. s*64+63.  The 64/LPR groups of lanes in a wavefront work on different edges
+// of the same row.
+#pragma once
+
+#include "common.hpp"
+
+namespace gga {
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int EPL>
+__device__ __forceinline__ void store_f32(float* dst, const float* f) {
+    if constexpr (EPL == 8) {
+        reinterpret_cast<float4*>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
+        reinterpret_cast<float4*>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
+    } else if constexpr (EPL == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) dst[i] = f[i];
+    }
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_f32(const float* src, float* f) {
+    if constexpr (EPL == 8) {
+        const float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else if constexpr (EPL == 4) {
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) f[i] = src[i];
+    }
+}
+
+template <int EPL, int HDP, int NS>
+struct RowGeo {
+    int lane, g, G, lpr;
+    int off[NS], head[NS];
+    bool ok[NS], lead[NS];
+
+    __device__ __forceinline__ void init(int lpr_log2, int H, int C) {
+        lane = threadIdx.x & 63;
+        lpr = 1 << lpr_log2;
+        G = 64 >> lpr_log2;
+        g = lane >> lpr_log2;
+        const int li = lane & (lpr - 1);
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+            const int j = s * 64 + li;
+            head[s] = j / HDP;
+            const int sub = j % HDP;
+            ok[s] = head[s] < H && sub * EPL < C;
+            off[s] = head[s] * C + sub * EPL;
+            lead[s] = sub == 0;
+        }
+    }
+};
+
+// Sum of a value over the G edge groups of a wavefront (butterfly from LPR up to 32).
+__device__ __forceinline__ float sum_groups(float x, int lpr) {
+    for (int o = lpr; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+}  // namespace gga
