@@ -200,10 +200,13 @@ int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf
  * trans_b, b stored [n,k].  Row-major, fp32 in and out, fp32 accumulation.
  * Used for the projections Q = X W_Q, K, V, the output map W_o, the GAT map
  * X W and its gradients X^T dH, dH W^T ("Gated Local-Global Graph Attention",
- * Mathematical statement; Tinymesh "Composition").  bias may be NULL.
+ * Mathematical statement; Tinymesh "Composition").  bias may be NULL.  When
+ * the output is small and k long, k is split into a fixed number of ranges
+ * whose partial products (in `ws`) are added in range order: deterministic.
  */
+size_t gga_linear_workspace(int32_t m, int32_t k, int32_t n);
 int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float *a, const float *b,
-               const float *bias, float *c, void *stream);
+               const float *bias, float *c, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Global linear-attention branch ("Gated Local-Global Graph Attention", Key

@@ -67,7 +67,8 @@ def _load() -> ctypes.CDLL:
         "gga_gat_coef_fwd": ([i32, i32, i32, P, P, P, P, P, P], ctypes.c_int),
         "gga_gat_coef_bwd_workspace": ([i32, i32, i32], sz),
         "gga_gat_coef_bwd": ([i32, i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
-        "gga_linear": ([i32, i32, i32, i32, i32, P, P, P, P, P], ctypes.c_int),
+        "gga_linear_workspace": ([i32, i32, i32], sz),
+        "gga_linear": ([i32, i32, i32, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_global_linear_workspace": ([i32, i32, i32], sz),
         "gga_global_linear_fwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
         "gga_gated_combine": ([i32, i32, P, P, f32, i32, P, P, P, P, P], ctypes.c_int),
@@ -275,13 +276,16 @@ def gga_gat_coef_bwd(hf, a_s, a_t, d_hf_attn, d_s_src, d_s_dst, d_hf=None, d_a_s
 # --------------------------------------------------------------------------- dense steps
 
 
-def gga_linear(a: torch.Tensor, b: torch.Tensor, bias=None, trans_a=False, trans_b=False, out=None, stream=None):
+def gga_linear(a: torch.Tensor, b: torch.Tensor, bias=None, trans_a=False, trans_b=False, out=None, ws=None,
+               stream=None):
     m = a.shape[1] if trans_a else a.shape[0]
     k = a.shape[0] if trans_a else a.shape[1]
     n = b.shape[0] if trans_b else b.shape[1]
     out = torch.empty(m, n, dtype=torch.float32, device=a.device) if out is None else out
+    nb = lib.gga_linear_workspace(m, k, n)
+    ws = _workspace(nb, a.device, ws)
     _check("gga_linear", lib.gga_linear(m, k, n, int(trans_a), int(trans_b), _ptr(a), _ptr(b), _ptr(bias), _ptr(out),
-                                        _stream(stream)))
+                                        _ptr(ws), nb, _stream(stream)))
     return out
 
 

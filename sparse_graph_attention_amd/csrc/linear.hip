@@ -1,0 +1,240 @@
+// Dense fp32 product on the matrix cores (v_mfma_f32_16x16x4_f32): c = op(a) op(b) (+ bias).
+//
+// Workgroup tile 128x128, four wavefronts each owning 64x64 (4x4 MFMA tiles of 16x16),
+// K staged through LDS 16 at a time with double buffering.  LDS holds both operands
+// k-major ([k][m] and [k][n]) so each MFMA operand read is 16 consecutive floats per
+// quarter-wavefront.  When the output has few tiles and K is long, K is split into a
+// fixed number of ranges whose partial products are added in range order by a second
+// kernel, so results do not depend on scheduling.
+#include "common.hpp"
+
+namespace gga {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, KT = 16;
+constexpr int LDS_STRIDE = BM + 16;  // 144 floats: successive k rows start 16 banks apart
+
+struct GemmArgs {
+    const float* a;
+    const float* b;
+    const float* bias;
+    float* c;
+    int32_t M, K, N, lda, ldb;
+    int32_t trans_a, trans_b;
+    int32_t kchunk;  // K range per split
+};
+
+// Loads 4 consecutive floats of a row starting at column c0, zero beyond `lim` columns.
+__device__ __forceinline__ float4 load4(const float* row, int64_t c0, int64_t lim, bool vec_ok) {
+    if (vec_ok && c0 + 3 < lim) return *reinterpret_cast<const float4*>(row + c0);
+    float4 r;
+    r.x = c0 + 0 < lim ? row[c0 + 0] : 0.f;
+    r.y = c0 + 1 < lim ? row[c0 + 1] : 0.f;
+    r.z = c0 + 2 < lim ? row[c0 + 2] : 0.f;
+    r.w = c0 + 3 < lim ? row[c0 + 3] : 0.f;
+    return r;
+}
+
+// One operand tile (128 along m or n, KT along k) into registers: two float4 per thread.
+// `kmajor_src`: the operand is stored with k as its row index (a transposed / b plain).
+__device__ __forceinline__ void fetch_tile(const float* src, int ld, bool kmajor_src, int64_t o0, int64_t olim,
+                                           int64_t k0, int64_t klim, bool vec_ok, float4 (&r)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int f = threadIdx.x + 256 * q;
+        if (kmajor_src) {
+            const int kr = f / 32, c4 = f % 32;
+            const int64_t k = k0 + kr;
+            if (k < klim)
+                r[q] = load4(src + k * ld, o0 + c4 * 4, olim, vec_ok);
+            else
+                r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            const int orow = f / 4, c4 = f % 4;
+            const int64_t o = o0 + orow;
+            if (o < olim)
+                r[q] = load4(src + o * ld, k0 + c4 * 4, klim, vec_ok);
+            else
+                r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+}
+
+__device__ __forceinline__ void stash_tile(float* lds, bool kmajor_src, const float4 (&r)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int f = threadIdx.x + 256 * q;
+        if (kmajor_src) {
+            const int kr = f / 32, c4 = f % 32;
+            *reinterpret_cast<float4*>(lds + kr * LDS_STRIDE + c4 * 4) = r[q];
+        } else {
+            const int orow = f / 4, c4 = f % 4;
+            lds[(c4 * 4 + 0) * LDS_STRIDE + orow] = r[q].x;
+            lds[(c4 * 4 + 1) * LDS_STRIDE + orow] = r[q].y;
+            lds[(c4 * 4 + 2) * LDS_STRIDE + orow] = r[q].z;
+            lds[(c4 * 4 + 3) * LDS_STRIDE + orow] = r[q].w;
+        }
+    }
+}
+
+// grid: (ceil(N/BN), ceil(M/BM), splits).  With splits > 1, c points at the partial buffer
+// [splits][M][N] and bias is ignored.
+__global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
+    __shared__ float As[2][KT * LDS_STRIDE];
+    __shared__ float Bs[2][KT * LDS_STRIDE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+    const int64_t kb = (int64_t)blockIdx.z * g.kchunk;
+    const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+    const bool a_km = g.trans_a != 0;   // a stored [K][M]
+    const bool b_km = g.trans_b == 0;   // b stored [K][N]
+    const bool a_vec = (g.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
+    const bool b_vec = (g.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(g.b) & 15) == 0;
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (int)((ke - kb + KT - 1) / KT);
+    float4 ra[2], rb[2];
+    if (nk > 0) {
+        fetch_tile(g.a, g.lda, a_km, m0, g.M, kb, ke, a_vec, ra);
+        fetch_tile(g.b, g.ldb, b_km, n0, g.N, kb, ke, b_vec, rb);
+        stash_tile(As[0], a_km, ra);
+        stash_tile(Bs[0], b_km, rb);
+    }
+    __syncthreads();
+    for (int t = 0; t < nk; t++) {
+        const int cur = t & 1;
+        if (t + 1 < nk) {
+            const int64_t k0 = kb + (int64_t)(t + 1) * KT;
+            fetch_tile(g.a, g.lda, a_km, m0, g.M, k0, ke, a_vec, ra);
+            fetch_tile(g.b, g.ldb, b_km, n0, g.N, k0, ke, b_vec, rb);
+        }
+        const float* as = As[cur];
+        const float* bs = Bs[cur];
+#pragma unroll
+        for (int kk = 0; kk < KT / 4; kk++) {
+            const int kr = kk * 4 + (lane >> 4);
+            float af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) af[i] = as[kr * LDS_STRIDE + wm * 64 + i * 16 + (lane & 15)];
+#pragma unroll
+            for (int j = 0; j < 4; j++) bf[j] = bs[kr * LDS_STRIDE + wn * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (t + 1 < nk) {
+            stash_tile(As[cur ^ 1], a_km, ra);
+            stash_tile(Bs[cur ^ 1], b_km, rb);
+        }
+        __syncthreads();
+    }
+
+    float* cbase = g.c + (int64_t)blockIdx.z * g.M * g.N;
+    const bool add_bias = g.bias != nullptr && gridDim.z == 1;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+        if (col >= g.N) continue;
+        const float bv = add_bias ? g.bias[col] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int64_t row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+                if (row < g.M) cbase[row * g.N + col] = acc[i][j][r] + bv;
+            }
+        }
+    }
+}
+
+__global__ void splitk_reduce(const float* __restrict__ part, int splits, int64_t mn, int32_t N,
+                              const float* __restrict__ bias, float* __restrict__ c) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < mn; i += (int64_t)gridDim.x * blockDim.x) {
+        float s = 0.f;
+        for (int z = 0; z < splits; z++) s += part[z * mn + i];
+        c[i] = s + (bias ? bias[i % N] : 0.f);
+    }
+}
+
+struct Split {
+    int splits;
+    int32_t kchunk;
+};
+
+Split pick_split(int32_t m, int32_t k, int32_t n) {
+    const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    Split s{1, k};
+    if (tiles < 256 && k > 1024) {
+        int64_t want = (1024 + tiles - 1) / tiles;
+        int64_t by_k = k / 512;
+        int64_t sp = want < by_k ? want : by_k;
+        if (sp > 64) sp = 64;
+        if (sp > 1) {
+            int64_t kc = (k + sp - 1) / sp;
+            kc = (kc + KT - 1) / KT * KT;
+            s.kchunk = (int32_t)kc;
+            s.splits = (int)((k + kc - 1) / kc);
+        }
+    }
+    if (s.kchunk < 1) s.kchunk = 1;
+    return s;
+}
+
+}  // namespace
+}  // namespace gga
+
+using namespace gga;
+
+extern "C" size_t gga_linear_workspace(int32_t m, int32_t k, int32_t n) {
+    if (m < 0 || k < 0 || n < 0) return 0;
+    const Split s = pick_split(m, k, n);
+    if (s.splits <= 1) return 0;
+    return align_up((size_t)s.splits * m * n * sizeof(float), 256);
+}
+
+extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float* a,
+                          const float* b, const float* bias, float* c, void* ws, size_t ws_bytes, void* stream) {
+    if (m < 0 || k < 0 || n < 0) return GGA_EINVAL;
+    if (m == 0 || n == 0) return GGA_OK;
+    if (!c || (k > 0 && (!a || !b))) return GGA_EINVAL;
+    if ((int64_t)m * n >= ((int64_t)1 << 40)) return GGA_ERANGE;
+    hipStream_t s = as_stream(stream);
+    const Split sp = pick_split(m, k, n);
+    const size_t need = gga_linear_workspace(m, k, n);
+    if (ws_bytes < need || (need > 0 && !ws)) return GGA_EWORKSPACE;
+    GemmArgs g{};
+    g.a = a;
+    g.b = b;
+    g.bias = bias;
+    g.M = m;
+    g.K = k;
+    g.N = n;
+    g.lda = trans_a ? m : k;
+    g.ldb = trans_b ? k : n;
+    g.trans_a = trans_a != 0;
+    g.trans_b = trans_b != 0;
+    g.kchunk = sp.kchunk;
+    const int64_t gy = (m + BM - 1) / BM, gx = (n + BN - 1) / BN;
+    if (gy > 65535) return GGA_ERANGE;
+    if (sp.splits > 1) {
+        g.c = static_cast<float*>(ws);
+        gemm_f32_mfma<<<dim3((unsigned)gx, (unsigned)gy, (unsigned)sp.splits), 256, 0, s>>>(g);
+        const int64_t mn = (int64_t)m * n;
+        int64_t blocks = (mn + 255) / 256;
+        if (blocks > 65536) blocks = 65536;
+        splitk_reduce<<<(unsigned)blocks, 256, 0, s>>>(static_cast<const float*>(ws), sp.splits, mn, n, bias, c);
+    } else {
+        g.c = c;
+        gemm_f32_mfma<<<dim3((unsigned)gx, (unsigned)gy, 1), 256, 0, s>>>(g);
+    }
+    return launch_status();
+}

@@ -1,0 +1,69 @@
+"""The two layers the pages build from the primitives, as sequences of libgga calls.
+
+Nothing here computes: each function only orders entry points of the C ABI and hands
+tensors from one to the next.
+
+- GAT layer (Tinymesh "Sparse attention experiment", sections "Composition" and
+  "Multiple heads are composition"): H = X W, per-node coefficients, additive scores,
+  target softmax, weighted sum, heads concatenated; and its first-order gradients.
+- Gated local-global layer ("Gated Local-Global Graph Attention", Implementation notes
+  item 2): Q, K, V projections, local masked softmax, phi = elu+1 global branch, node
+  gate, W_o, residual LayerNorm.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, Topology, gga_add_layernorm, gga_gat_coef_bwd,
+               gga_gat_coef_fwd, gga_gated_combine, gga_global_linear_fwd, gga_linear, gga_local_attn_bwd,
+               gga_local_attn_fwd, make_desc)
+
+
+def gat_forward(x: torch.Tensor, w: torch.Tensor, a_s: torch.Tensor, a_t: torch.Tensor, topo: Topology,
+                negative_slope: float = 0.2):
+    """Returns a dict with out [N, K*C] and the intermediates the backward needs."""
+    n = x.shape[0]
+    heads, c = a_s.shape
+    hf = gga_linear(x, w).view(n, heads, c)
+    s_src, s_dst = gga_gat_coef_fwd(hf, a_s, a_t)
+    desc = make_desc(n, topo.e, heads, c, GGA_SCORE_ADDITIVE, GGA_F32, 1.0, negative_slope)
+    out, lse = gga_local_attn_fwd(desc, s_dst, s_src, hf, topo.row_ptr, topo.col, topo.plan)
+    return dict(out=out.view(n, heads * c), hf=hf, s_src=s_src, s_dst=s_dst, lse=lse, desc=desc, out3=out)
+
+
+def gat_backward(x, w, a_s, a_t, d_out: torch.Tensor, fwd: dict, topo: Topology):
+    """dX, dW, da_s, da_t of sum(out * d_out) (Tinymesh "Evidence and limits": first-order
+    gradients).  topo must hold the CSR by source (Topology(..., backward=True))."""
+    n = x.shape[0]
+    heads, c = a_s.shape
+    d3 = d_out.reshape(n, heads, c)
+    d_sdst, d_ssrc, d_hf_attn = gga_local_attn_bwd(fwd["desc"], fwd["s_dst"], fwd["s_src"], fwd["hf"], fwd["out3"],
+                                                   fwd["lse"], d3, topo)
+    d_hf, d_a_s, d_a_t = gga_gat_coef_bwd(fwd["hf"], a_s, a_t, d_hf_attn, d_ssrc, d_sdst)
+    dh = d_hf.view(n, heads * c)
+    d_w = gga_linear(x, dh, trans_a=True)
+    d_x = gga_linear(dh, w, trans_b=True)
+    return dict(d_x=d_x, d_w=d_w, d_a_s=d_a_s, d_a_t=d_a_t, d_hf=d_hf, d_s_src=d_ssrc, d_s_dst=d_sdst)
+
+
+def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, ln_eps: float = 1e-5,
+                        dtype: int = GGA_F32):
+    """p: x [N,d], w_q, w_k, w_v, w_o [d,d], w_g [d], b_g (float), gamma, beta [d]."""
+    x = p["x"]
+    n, d = x.shape
+    r = d // heads
+    q = gga_linear(x, p["w_q"]).view(n, heads, r)
+    k = gga_linear(x, p["w_k"]).view(n, heads, r)
+    v = gga_linear(x, p["w_v"]).view(n, heads, r)
+    desc = make_desc(n, topo.e, heads, r, GGA_SCORE_DOT, dtype, r ** -0.5)
+    loc, lse = gga_local_attn_fwd(desc, q, k, v, topo.row_ptr, topo.col, topo.plan)
+    s, z, glob = gga_global_linear_fwd(q, k, v, eps)
+    gate, y = gga_gated_combine(x, p["w_g"], p["b_g"], loc.view(n, d), glob.view(n, d))
+    zo = gga_linear(y, p["w_o"])
+    out = gga_add_layernorm(x, zo, p["gamma"], p["beta"], ln_eps)
+    return dict(q=q, k=k, v=v, local=loc.view(n, d), lse=lse, S=s, z=z, glob=glob.view(n, d), gate=gate, y=y,
+                out=out)
+
+
+__all__ = ["gat_forward", "gat_backward", "gated_layer_forward", "GGA_BF16"]

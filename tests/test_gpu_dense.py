@@ -1,0 +1,100 @@
+"""GPU parity of the dense steps: the fp32 MFMA product, the global linear branch, the
+node gate / combination and the residual LayerNorm, against the oracle (fp64)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    import sparse_graph_attention_amd as m
+
+    return m
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("m,k,n,ta,tb,bias", [
+    (1, 1, 1, 0, 0, False), (7, 5, 3, 0, 0, True), (128, 128, 128, 0, 0, False), (300, 257, 130, 0, 0, True),
+    (300, 257, 130, 1, 0, False), (300, 257, 130, 0, 1, True), (300, 257, 130, 1, 1, False),
+    (128, 170000, 64, 1, 0, False),   # X^T dH of the GAT workload: split over k
+    (170000, 64, 128, 0, 1, False),   # dH W^T
+    (4096, 256, 256, 0, 0, False), (33, 0, 17, 0, 0, True),
+])
+def test_linear(g, m, k, n, ta, tb, bias):
+    print(f"linear m={m} k={k} n={n} ta={ta} tb={tb}", flush=True)
+    rng = np.random.default_rng(m + k + n)
+    a = rng.standard_normal((k, m) if ta else (m, k)).astype(np.float32)
+    b = rng.standard_normal((n, k) if tb else (k, n)).astype(np.float32)
+    bv = rng.standard_normal(n).astype(np.float32) if bias else None
+    c = g.gga_linear(_t(a), _t(b), None if bv is None else _t(bv), trans_a=bool(ta), trans_b=bool(tb))
+    torch.cuda.synchronize()
+    ref = (a.T if ta else a).astype(np.float64) @ (b.T if tb else b).astype(np.float64)
+    if bv is not None:
+        ref = ref + bv
+    # fp32 accumulation over k terms of size ~1: allow sqrt(k) growth of the absolute error
+    assert_close(c.cpu().numpy(), ref, "f32", "c", atol=1e-5 * max(1.0, np.sqrt(k)))
+
+
+def test_linear_deterministic(g):
+    rng = np.random.default_rng(3)
+    a, b = _t(rng.standard_normal((50000, 128))), _t(rng.standard_normal((50000, 64)))
+    c1 = g.gga_linear(a, b, trans_a=True)
+    c2 = g.gga_linear(a, b, trans_a=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("n,h,r", [(1, 1, 16), (1000, 2, 16), (5000, 4, 64), (3001, 3, 32), (777, 2, 48),
+                                   (500, 2, 5), (20000, 1, 8)])
+def test_global_linear(g, n, h, r):
+    print(f"global n={n} h={h} r={r}", flush=True)
+    rng = np.random.default_rng(n + r)
+    q, k, v = (rng.standard_normal((n, h, r)).astype(np.float32) * 0.5 for _ in range(3))
+    s, z, gg = g.gga_global_linear_fwd(_t(q), _t(k), _t(v), 1e-6)
+    torch.cuda.synchronize()
+    rs, rz, rg = oracle.global_linear(q, k, v, 1e-6)
+    assert_close(s.cpu().numpy(), rs, "f32", "S", atol=1e-5 * np.sqrt(n))
+    assert_close(z.cpu().numpy(), rz, "f32", "z", atol=1e-5 * np.sqrt(n))
+    assert_close(gg.cpu().numpy(), rg, "f32", "G")
+
+
+def test_gate_combine_and_limits(g):
+    rng = np.random.default_rng(5)
+    n, d, w = 1000, 256, 256
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    wg = (rng.standard_normal(d) * 0.1).astype(np.float32)
+    loc, glob = rng.standard_normal((n, w)).astype(np.float32), rng.standard_normal((n, w)).astype(np.float32)
+    for b_g in (0.3, 80.0, -80.0):
+        gate, y = g.gga_gated_combine(_t(x), _t(wg), b_g, _t(loc), _t(glob))
+        torch.cuda.synchronize()
+        rg = oracle.gate(x, wg, b_g)
+        assert_close(gate.cpu().numpy(), rg, "f32", "gate")
+        assert_close(y.cpu().numpy(), oracle.combine(rg, loc, glob), "f32", "y")
+    # odd widths take the scalar path
+    x2 = rng.standard_normal((37, 5)).astype(np.float32)
+    wg2 = rng.standard_normal(5).astype(np.float32)
+    l2, g2 = rng.standard_normal((37, 3)).astype(np.float32), rng.standard_normal((37, 3)).astype(np.float32)
+    gate, y = g.gga_gated_combine(_t(x2), _t(wg2), -0.2, _t(l2), _t(g2))
+    torch.cuda.synchronize()
+    rg = oracle.gate(x2, wg2, -0.2)
+    assert_close(y.cpu().numpy(), oracle.combine(rg, l2, g2), "f32", "y")
+
+
+@pytest.mark.parametrize("n,d", [(1, 4), (1000, 256), (333, 1024), (50, 100), (10, 3000)])
+def test_add_layernorm(g, n, d):
+    rng = np.random.default_rng(n + d)
+    x = (rng.standard_normal((n, d)) * 2 + 1).astype(np.float32)
+    y = rng.standard_normal((n, d)).astype(np.float32)
+    gm, bt = rng.standard_normal(d).astype(np.float32), rng.standard_normal(d).astype(np.float32)
+    out = g.gga_add_layernorm(_t(x), _t(y), _t(gm), _t(bt), 1e-5)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), oracle.layer_norm(x.astype(np.float64) + y, gm, bt), "f32", "ln")
