@@ -1,16 +1,25 @@
 #!/usr/bin/env python3
-"""Benchmark of the local graph-attention forward on one MI355X.
+"""Benchmark of neighbor-restricted graph attention on one MI355X.
 
-Workload: the 1M-node dot-product configuration -- N = 2^20 nodes, every node with
-16 in-edges drawn uniformly plus one self-loop (E = 17 N = 17,825,792), H = 8 heads of
-r = 64, q/k/v stored as bf16 (N(0,1) rounded to nearest even), fp32 accumulation and
-fp32 output, score scale 1/sqrt(64).  A step is one fused forward pass (out and lse)
-over the resident inputs; the CSR build and the degree plan are per-topology work and
-are timed and reported separately.
+Default workload (the headline): the 1M-node dot-product configuration -- N = 2^20
+nodes, each with 16 in-edges drawn uniformly plus one self-loop (E = 17 N =
+17,825,792), H = 8 heads of r = 64, q/k/v stored as bf16 (N(0,1) rounded to nearest
+even), fp32 accumulation and fp32 output, score scale 1/sqrt(64).  A step is one fused
+forward pass (out and lse) over inputs already resident in HBM.  The CSR build and the
+degree plan are per-topology work, timed and reported separately.
 
-Prints one JSON line with the throughput in GEdges/s, the roofline of the forward
-kernel (algorithmic HBM bytes per launch over the launch time measured with HIP events
-on the launch stream), and the CPU oracle timed on this host over the same workload.
+Other workloads (``--workload``), each printed as its own line when asked for:
+  5  heavy-tailed 2M-node graph, H = 8, C = 32, bf16: a step is forward + backward
+     (dQ over the CSR by destination, dK and dV over the CSR by source)
+  2  170k-node power-law GAT layer, Fin = 128 -> 8 heads x 8, fp32: a step is the
+     layer forward + its first-order gradients (dX, dW, da_s, da_t)
+  4  262k-node gated local-global layer, d = 256, 4 heads of 64, fp32: a step is the
+     layer forward
+  1  tiny 1024-node dot-product graph, H = 1, r = 16, fp32: forward
+
+Prints one JSON line: throughput in GEdges/s, the roofline of the dominant kernel call
+(algorithmic HBM bytes per launch over the launch time measured with HIP events on the
+launch stream) and the CPU oracle timed on this host over the same work.
 """
 
 from __future__ import annotations
@@ -27,26 +36,316 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 
-# HBM bytes per forward launch counted by rocprofv3 (FETCH_SIZE x 2.00 + WRITE_SIZE x 1.00,
-# factors from a plain 1 GiB copy) for the kernel as of the committed profile summary
+# HBM bytes per forward launch on the default workload counted by rocprofv3 (FETCH_SIZE x 2.00
+# + WRITE_SIZE x 1.00, factors from a plain 1 GiB copy), for the kernel as of the summary in
 # profiles/local_fwd_dot_n1m_h8_r64_bf16.md; None once the kernel changes.
 COUNTED_TRAFFIC_GB = 39.95
+
+METRIC = "GEdges/s (x heads) for local graph-attention fwd; achieved HBM GB/s vs peak"
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def fwd_bytes(n: int, e: int, heads: int, c: int, esz: int, with_lse: bool) -> int:
-    """Algorithmic HBM bytes of one forward launch of the per-destination pull method:
-    q once, one key row and one value row per edge, col per edge, row_ptr, out once,
-    lse once."""
+def fwd_bytes(n, e, heads, c, esz, with_lse=True) -> int:
+    """Forward, per launch: q once, one key row and one value row per edge, col per edge,
+    row_ptr, out once (fp32), lse once (fp32)."""
     w = heads * c
-    b = n * w * esz + e * (2 * w * esz + 4) + 4 * (n + 1) + n * w * 4
-    if with_lse:
-        b += n * heads * 4
-    return b
+    return n * w * esz + e * (2 * w * esz + 4) + 4 * (n + 1) + n * w * 4 + (n * heads * 4 if with_lse else 0)
+
+
+def bwd_bytes(n, e, heads, c, esz) -> int:
+    """Backward, per call.  Pass A (CSR by destination): per edge a key and a value row and
+    col; per node q, dO, out, lse, row_ptr, and dq and D written.  Pass B (CSR by source):
+    per edge a query row, a dO row, lse and D of the target, and col; per node k, v,
+    row_ptr, and dk, dv written."""
+    w = heads * c
+    a = e * (2 * w * esz + 4) + n * (w * esz + 8 * w + 4 * heads + 4) + n * (4 * w + 4 * heads)
+    b = e * (w * esz + 4 * w + 8 * heads + 4) + n * (2 * w * esz + 4) + n * 8 * w
+    return a + b
+
+
+class Timer:
+    """Times `steps` calls of step() after `warmup` untimed ones: wall clock between two
+    device synchronisations, plus HIP events (on the launch stream) around named phases."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.events = {}
+
+    def mark(self, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(self.stream)
+        self.events.setdefault(name, []).append(ev)
+
+    def run(self, step, steps, warmup):
+        for _ in range(warmup):
+            step(None)
+        self.events = {}
+        self.torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            step(self)
+        self.torch.cuda.synchronize()
+        wall = (time.perf_counter() - t) * 1e3 / steps
+        return wall
+
+    def phase_ms(self, a, b):
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(self.events[a], self.events[b])]))
+
+
+def _mark(tm, name):
+    if tm is not None:
+        tm.mark(name)
+
+
+def per_topology(g, torch, n, src_d, dst_d, backward=False):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    row_ptr, col, eid = g.gga_coo_to_csr(n, dst_d, src_d)
+    ev[1].record()
+    plan = g.gga_plan_build(n, int(src_d.numel()), row_ptr)
+    ev[2].record()
+    topo = g.Topology.__new__(g.Topology)
+    topo.n, topo.e, topo.src, topo.dst = n, int(src_d.numel()), src_d, dst_d
+    topo.row_ptr, topo.col, topo.eid, topo.plan = row_ptr, col, eid, plan
+    topo.row_ptr_s = topo.col_s = topo.eid_s = topo.plan_s = None
+    torch.cuda.synchronize()
+    t = {"csr_build_ms": ev[0].elapsed_time(ev[1]), "plan_build_ms": ev[1].elapsed_time(ev[2])}
+    if backward:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        topo.build_source_csr()
+        e1.record()
+        torch.cuda.synchronize()
+        t["source_csr_and_plan_ms"] = e0.elapsed_time(e1)
+    return topo, t
+
+
+def bf16_dev(torch, bits, shape, dev):
+    return torch.from_numpy(bits.view(np.int16).reshape(shape)).to(dev).view(torch.bfloat16)
+
+
+def roofline(bound, achieved, peak, unit, traffic=None, **extra):
+    r = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "traffic": traffic}
+    r.update(extra)
+    return r
+
+
+def record(args, name, value, ms_step, dtype, config, roof, cpu, extra):
+    rec = {"metric": METRIC, "value": value, "unit": "GEdges/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+           "config": dict({"workload": name, "global_batch": 1, "parallelism": "single GPU"}, **config),
+           "roofline": roof, "cpu_baseline": cpu}
+    rec.update(extra)
+    return rec
+
+
+# --------------------------------------------------------------------------- workloads
+
+
+def bench_dot_forward(args, g, torch, synth, ident):
+    w = synth.WORKLOADS[ident]
+    n, heads, c = w.n, w.heads, w.head_dim
+    dev = torch.device("cuda:0")
+    src, dst = synth.workload_graph(ident)
+    e = int(src.size)
+    log(f"workload {w.name}: n={n} e={e} H={heads} C={c} {w.dtype}")
+    hosts = [synth.node_tensor(ident, i, (n, heads, c)) for i in range(3)]
+    if w.dtype == "bf16":
+        bits = [synth.to_bf16_bits(x) for x in hosts]
+        hosts = [synth.bf16_bits_to_f32(b).reshape(n, heads, c) for b in bits]
+        q, k, v = (bf16_dev(torch, b, (n, heads, c), dev) for b in bits)
+        code, esz = g.GGA_BF16, 2
+    else:
+        q, k, v = (torch.from_numpy(x).to(dev) for x in hosts)
+        code, esz = g.GGA_F32, 4
+    topo, tt = per_topology(g, torch, n, torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev))
+    desc = g.make_desc(n, e, heads, c, g.GGA_SCORE_DOT, code, 1.0 / np.sqrt(c))
+    out = torch.empty(n, heads, c, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, heads, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(g.lib.gga_local_attn_fwd_workspace(g.ctypes.byref(desc)), 1), dtype=torch.uint8, device=dev)
+
+    def step(tm):
+        _mark(tm, "f0")
+        g.gga_local_attn_fwd(desc, q, k, v, topo.row_ptr, topo.col, topo.plan, out=out, lse=lse, ws=ws)
+        _mark(tm, "f1")
+
+    tm = Timer(torch, torch.cuda.current_stream())
+    ms = tm.run(step, args.steps, args.warmup)
+    kms = tm.phase_ms("f0", "f1")
+    alg = fwd_bytes(n, e, heads, c, esz)
+    ach = alg / (kms * 1e-3) / 1e9
+    log(f"fwd: {ms:.3f} ms/step (launch avg {kms:.3f} ms), {ach:.0f} GB/s algorithmic; {tt}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        h64 = [x.astype(np.float64) for x in hosts]
+        og = oracle.Graph(n, src, dst)
+        t1 = time.perf_counter()
+        oracle.local_fwd_dot(h64[0], h64[1], h64[2], og, 1.0 / np.sqrt(c))
+        dt = time.perf_counter() - t1
+        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the whole forward of this workload ({e} edges, all {n} rows), fp64, {dt:.1f} s"}
+        log(f"cpu oracle: {dt:.2f} s with {oracle.threads()} threads")
+    traffic = COUNTED_TRAFFIC_GB if ident == 3 else None
+    roof = roofline("hbm", ach, HBM_PEAK_GBS, "GB/s", traffic, kernel="local_fwd_kernel (+ heavy-row merge launch)",
+                    alg_bytes_per_launch=alg, launch_ms=kms)
+    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "storage": f"{w.dtype} q/k/v, fp32 out/lse",
+           "seq_len": n}
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, w.dtype, cfg, roof, cpu,
+                  dict(tt, gedge_heads_per_s=e * heads / (ms * 1e-3) / 1e9, hbm_gbs_algorithmic=ach))
+
+
+def bench_heavy_tail(args, g, torch, synth):
+    ident = 5
+    w = synth.WORKLOADS[ident]
+    n, heads, c = w.n, w.heads, w.head_dim
+    dev = torch.device("cuda:0")
+    src, dst = synth.workload_graph(ident)
+    e = int(src.size)
+    log(f"workload {w.name}: n={n} e={e}")
+    bits = [synth.to_bf16_bits(synth.node_tensor(ident, i, (n, heads, c))) for i in range(3)]
+    q, k, v = (bf16_dev(torch, b, (n, heads, c), dev) for b in bits)
+    d_out_h = synth.node_tensor(ident, 0, (n, heads, c), stream=synth.GRADS)
+    d_out = torch.from_numpy(d_out_h).to(dev)
+    topo, tt = per_topology(g, torch, n, torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), True)
+    desc = g.make_desc(n, e, heads, c, g.GGA_SCORE_DOT, g.GGA_BF16, 1.0 / np.sqrt(c))
+    out = torch.empty(n, heads, c, dtype=torch.float32, device=dev)
+    lse = torch.empty(n, heads, dtype=torch.float32, device=dev)
+    grads = [torch.empty(n, heads, c, dtype=torch.float32, device=dev) for _ in range(3)]
+    wsf = torch.empty(max(g.lib.gga_local_attn_fwd_workspace(g.ctypes.byref(desc)), 1), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(g.lib.gga_local_attn_bwd_workspace(g.ctypes.byref(desc)), dtype=torch.uint8, device=dev)
+
+    def step(tm):
+        _mark(tm, "f0")
+        g.gga_local_attn_fwd(desc, q, k, v, topo.row_ptr, topo.col, topo.plan, out=out, lse=lse, ws=wsf)
+        _mark(tm, "f1")
+        g.gga_local_attn_bwd(desc, q, k, v, out, lse, d_out, topo, d_qs=grads[0], d_ks=grads[1], d_v=grads[2],
+                             ws=wsb)
+        _mark(tm, "b1")
+
+    tm = Timer(torch, torch.cuda.current_stream())
+    ms = tm.run(step, args.steps, args.warmup)
+    fms, bms = tm.phase_ms("f0", "f1"), tm.phase_ms("f1", "b1")
+    fa, ba = fwd_bytes(n, e, heads, c, 2), bwd_bytes(n, e, heads, c, 2)
+    log(f"step {ms:.3f} ms: fwd {fms:.3f} ms ({fa / fms / 1e6:.0f} GB/s), bwd {bms:.3f} ms "
+        f"({ba / bms / 1e6:.0f} GB/s); {tt}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        h64 = [synth.bf16_bits_to_f32(b).reshape(n, heads, c).astype(np.float64) for b in bits]
+        og = oracle.Graph(n, src, dst)
+        t1 = time.perf_counter()
+        oracle.local_fwd_dot(h64[0], h64[1], h64[2], og, 1.0 / np.sqrt(c))
+        oracle.local_bwd_dot(h64[0], h64[1], h64[2], d_out_h, og, 1.0 / np.sqrt(c))
+        dt = time.perf_counter() - t1
+        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the whole step (forward + backward, {e} edges), fp64, {dt:.1f} s"}
+        log(f"cpu oracle: {dt:.2f} s")
+    roof = roofline("hbm", ba / (bms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", None,
+                    kernel="bwd_dst_kernel + bwd_src_kernel (+ merges), one call", alg_bytes_per_launch=ba,
+                    launch_ms=bms)
+    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "storage": "bf16 q/k/v, fp32 grads",
+           "step": "forward + backward", "seq_len": n}
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "bf16", cfg, roof, cpu,
+                  dict(tt, fwd_ms=fms, bwd_ms=bms, fwd_gbs_algorithmic=fa / fms / 1e6,
+                       bwd_gbs_algorithmic=ba / bms / 1e6))
+
+
+def bench_gat(args, g, torch, synth):
+    from sparse_graph_attention_amd import layers
+
+    ident = 2
+    w = synth.WORKLOADS[ident]
+    n, heads, c = w.n, w.heads, w.head_dim
+    dev = torch.device("cuda:0")
+    src, dst = synth.workload_graph(ident)
+    e = int(src.size)
+    log(f"workload {w.name}: n={n} e={e}")
+    x, wt, a_s, a_t, d_out = synth.gat_inputs(n)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    xd, wd, asd, atd, dod = t(x), t(wt), t(a_s), t(a_t), t(d_out)
+    topo, tt = per_topology(g, torch, n, t(src), t(dst), True)
+
+    def step(tm):
+        _mark(tm, "f0")
+        f = layers.gat_forward(xd, wd, asd, atd, topo)
+        _mark(tm, "f1")
+        layers.gat_backward(xd, wd, asd, atd, dod, f, topo)
+        _mark(tm, "b1")
+
+    tm = Timer(torch, torch.cuda.current_stream())
+    ms = tm.run(step, args.steps, args.warmup)
+    fms, bms = tm.phase_ms("f0", "f1"), tm.phase_ms("f1", "b1")
+    log(f"step {ms:.3f} ms: fwd {fms:.3f} ms, bwd {bms:.3f} ms; {tt}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        og = oracle.Graph(n, src, dst)
+        t1 = time.perf_counter()
+        oracle.gat_forward(x, wt, a_s, a_t, og)
+        oracle.gat_backward(x, wt, a_s, a_t, d_out, og)
+        dt = time.perf_counter() - t1
+        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the whole step (layer forward + first-order gradients), fp64, {dt:.1f} s"}
+    fa = fwd_bytes(n, e, heads, c, 4) + n * heads * 8 * 2  # + s_src, s_dst per edge side
+    roof = roofline("hbm", fa / (fms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", None,
+                    kernel="layer forward (GEMM, coefficients, fused local forward)", alg_bytes_per_launch=fa,
+                    launch_ms=fms)
+    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "fin": w.fin, "storage": "fp32",
+           "step": "forward + first-order gradients", "seq_len": n}
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
+
+
+def bench_layer(args, g, torch, synth):
+    from sparse_graph_attention_amd import layers
+
+    ident = 4
+    w = synth.WORKLOADS[ident]
+    n, heads, c, d = w.n, w.heads, w.head_dim, w.d_model
+    dev = torch.device("cuda:0")
+    src, dst = synth.workload_graph(ident)
+    e = int(src.size)
+    log(f"workload {w.name}: n={n} e={e}")
+    p = synth.gated_layer_inputs(n, d=d)
+    pd = {k: (torch.from_numpy(np.ascontiguousarray(v)).to(dev) if isinstance(v, np.ndarray) else v)
+          for k, v in p.items()}
+    topo, tt = per_topology(g, torch, n, torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev))
+
+    def step(tm):
+        _mark(tm, "f0")
+        layers.gated_layer_forward(pd, topo, heads)
+        _mark(tm, "f1")
+
+    tm = Timer(torch, torch.cuda.current_stream())
+    ms = tm.run(step, args.steps, args.warmup)
+    flops = 2.0 * n * d * d * 4 + 4.0 * n * heads * c * c  # Q, K, V, W_o; S and phi(Q) S
+    log(f"layer {ms:.3f} ms ({flops / ms / 1e9:.1f} TFLOP/s over the dense contractions); {tt}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        og = oracle.Graph(n, src, dst)
+        t1 = time.perf_counter()
+        oracle.gated_layer(p, og, heads)
+        dt = time.perf_counter() - t1
+        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the whole layer forward, fp64 (numpy matmuls for the projections), {dt:.1f} s"}
+    roof = roofline("mfma", flops / (ms * 1e-3) / 1e12, MFMA_F32_PEAK_TFLOPS, "TFLOP/s", None,
+                    kernel="whole layer (GEMMs dominate the flops)", flops_per_step=flops, launch_ms=ms)
+    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "d_model": d, "storage": "fp32",
+           "step": "layer forward", "seq_len": n}
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, tt)
 
 
 def main() -> int:
@@ -54,6 +353,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -68,109 +368,21 @@ def main() -> int:
     import sparse_graph_attention_amd as g
     import synth
 
-    ident = 3
-    w = synth.WORKLOADS[ident]
-    n, heads, c = w.n, w.heads, w.head_dim
-    dev = torch.device("cuda:0")
-    t0 = time.time()
-    src, dst = synth.workload_graph(ident)
-    e = int(src.size)
-    log(f"workload {w.name}: n={n} e={e} H={heads} C={c} bf16 (graph {time.time() - t0:.1f}s)")
-    bits = [synth.to_bf16_bits(synth.node_tensor(ident, i, (n, heads, c))) for i in range(3)]
-    q, k, v = (torch.from_numpy(b.view(np.int16).reshape(n, heads, c)).to(dev).view(torch.bfloat16) for b in bits)
-    src_d = torch.from_numpy(src).to(dev)
-    dst_d = torch.from_numpy(dst).to(dev)
-    log(f"inputs resident ({time.time() - t0:.1f}s)")
-
-    stream = torch.cuda.current_stream()
-    # per-topology work: CSR by destination and the degree plan
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    row_ptr, col, eid = g.gga_coo_to_csr(n, dst_d, src_d)
-    ev[1].record(stream)
-    plan = g.gga_plan_build(n, e, row_ptr)
-    ev[2].record(stream)
-    torch.cuda.synchronize()
-    csr_ms, plan_ms = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
-
-    desc = g.make_desc(n, e, heads, c, g.GGA_SCORE_DOT, g.GGA_BF16, 1.0 / np.sqrt(c))
-    out = torch.empty(n, heads, c, dtype=torch.float32, device=dev)
-    lse = torch.empty(n, heads, dtype=torch.float32, device=dev)
-    ws_bytes = g.lib.gga_local_attn_fwd_workspace(g.ctypes.byref(desc))
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-
-    def step():
-        g.gga_local_attn_fwd(desc, q, k, v, row_ptr, col, plan, out=out, lse=lse, ws=ws)
-
-    for _ in range(args.warmup):
-        step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    launch_ms = [s.elapsed_time(x) for s, x in zip(starts, ends)]
-    ms_step = wall * 1e3 / args.steps
-    kern_ms = float(np.mean(launch_ms))
-    log(f"fwd: wall {ms_step:.3f} ms/step, launch avg {kern_ms:.3f} ms (min {min(launch_ms):.3f}, "
-        f"max {max(launch_ms):.3f}); csr {csr_ms:.2f} ms, plan {plan_ms:.2f} ms")
-
-    alg = fwd_bytes(n, e, heads, c, 2, True)
-    achieved = alg / (kern_ms * 1e-3) / 1e9
-
+    if args.workload in (1, 3):
+        rec = bench_dot_forward(args, g, torch, synth, args.workload)
+    elif args.workload == 5:
+        rec = bench_heavy_tail(args, g, torch, synth)
+    elif args.workload == 2:
+        rec = bench_gat(args, g, torch, synth)
+    else:
+        rec = bench_layer(args, g, torch, synth)
     if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
         b = torch.empty_like(a)
         for _ in range(3):
             b.copy_(a)
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-
-        hosts = [synth.bf16_bits_to_f32(b).reshape(n, heads, c).astype(np.float64) for b in bits]
-        og = oracle.Graph(n, src, dst)
-        t1 = time.perf_counter()
-        oracle.local_fwd_dot(hosts[0], hosts[1], hosts[2], og, 1.0 / np.sqrt(c))
-        dt = time.perf_counter() - t1
-        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the whole forward of this workload ({e} edges, all {n} rows), fp64, {dt:.1f} s"}
-        log(f"cpu oracle: {dt:.2f} s with {oracle.threads()} threads")
-
-    rec = {
-        "metric": "GEdges/s (x heads) for local graph-attention fwd; achieved HBM GB/s vs peak",
-        "value": e / (ms_step * 1e-3) / 1e9,
-        "unit": "GEdges/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": w.name, "nodes": n, "edges": e, "heads": heads, "head_dim": c,
-                   "in_degree": "16 uniform + 1 self-loop", "storage": "bf16 q/k/v, fp32 out/lse",
-                   "global_batch": 1, "seq_len": n, "parallelism": "single GPU"},
-        "gedge_heads_per_s": e * heads / (ms_step * 1e-3) / 1e9,
-        "hbm_gbs_algorithmic": achieved,
-        "csr_build_ms": csr_ms,
-        "plan_build_ms": plan_ms,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": COUNTED_TRAFFIC_GB,
-                     "kernel": "local_fwd_kernel (+ heavy-row merge launch)", "alg_bytes_per_launch": alg,
-                     "launch_ms": kern_ms},
-        "cpu_baseline": cpu,
-    }
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -188,6 +188,13 @@ struct PassA {
     }
 
     __device__ __forceinline__ void write_final(const BwdParams& p, int32_t v) {
+        if constexpr (MODE == GGA_SCORE_DOT) {
+            if (geo.exact) {  // all lanes take part (the row store exchanges chunks)
+                store_row_nt<EPL>(p.d_qs + (size_t)v * p.W, acc[0], geo.lpr, geo.lane, geo.g);
+                if (geo.g == 0 && geo.lead[0]) p.D[(size_t)v * p.H + geo.head[0]] = Dh[0];
+                return;
+            }
+        }
         if (geo.g != 0) return;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
@@ -363,6 +370,15 @@ struct PassB {
     }
 
     __device__ __forceinline__ void write_final(const BwdParams& p, int32_t u) {
+        if (geo.exact) {  // all lanes take part (the row store exchanges chunks)
+            if constexpr (MODE == GGA_SCORE_DOT) {
+                store_row_nt<EPL>(p.d_ks + (size_t)u * p.W, dk[0], geo.lpr, geo.lane, geo.g);
+            } else {
+                if (geo.g == 0 && geo.lead[0]) p.d_ks[(size_t)u * p.H + geo.head[0]] = dk[0][0];
+            }
+            store_row_nt<EPL>(p.d_v + (size_t)u * p.W, dv[0], geo.lpr, geo.lane, geo.g);
+            return;
+        }
         write_to(p, p.d_ks + (size_t)u * dk_width(p), p.d_v + (size_t)u * p.W);
     }
 

@@ -10,16 +10,15 @@
 // Scores are kept in log2 units (the score multiplier includes log2(e)), so the
 // softmax uses exp2.  No floating-point atomics: every sum has a fixed order.
 #include "plan.hpp"
+#include "rowgeo.hpp"
 #include "shape.hpp"
 
 namespace gga {
 
 namespace {
 
-constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kFwdWaves = 4;
 constexpr int kFwdThreads = 64 * kFwdWaves;
-constexpr float kNegInf = -__builtin_huge_valf();
 
 struct FwdParams {
     const void* qs;
@@ -42,42 +41,13 @@ struct FwdParams {
     int32_t chunk_blocks;
 };
 
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <int EPL>
-__device__ __forceinline__ void store_f32(float* dst, const float* f) {
-    if constexpr (EPL == 8) {
-        reinterpret_cast<float4*>(dst)[0] = make_float4(f[0], f[1], f[2], f[3]);
-        reinterpret_cast<float4*>(dst)[1] = make_float4(f[4], f[5], f[6], f[7]);
-    } else if constexpr (EPL == 4) {
-        *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < EPL; i++) dst[i] = f[i];
-    }
-}
-
-template <int EPL>
-__device__ __forceinline__ void load_f32(const float* src, float* f) {
-    if constexpr (EPL == 8) {
-        float4 a = reinterpret_cast<const float4*>(src)[0], b = reinterpret_cast<const float4*>(src)[1];
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    } else if constexpr (EPL == 4) {
-        float4 a = *reinterpret_cast<const float4*>(src);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    } else {
-#pragma unroll
-        for (int i = 0; i < EPL; i++) f[i] = src[i];
-    }
-}
-
 template <typename T, int EPL, int HDP, int NS, int MODE>
 struct FwdRow {
     using V = Vec<T, EPL>;
     using raw_t = typename V::raw_t;
     static constexpr int kUMax = 8 / NS;
 
-    // geometry
+    RowGeo<EPL, HDP, NS> geo;
     int lane, g, G, U, EIT, lpr;
     int off[NS], head[NS];
     bool ok[NS], lead[NS];
@@ -88,21 +58,19 @@ struct FwdRow {
     float sd[NS];
 
     __device__ __forceinline__ void geometry(const FwdParams& p) {
-        lane = threadIdx.x & 63;
-        lpr = 1 << p.lpr_log2;
-        G = 64 >> p.lpr_log2;
-        g = lane >> p.lpr_log2;
+        geo.init(p.lpr_log2, p.H, p.C);
+        lane = geo.lane;
+        lpr = geo.lpr;
+        G = geo.G;
+        g = geo.g;
         U = G >= kUMax ? 1 : kUMax / G;
         EIT = G * U;
-        const int li = lane & (lpr - 1);
 #pragma unroll
         for (int s = 0; s < NS; s++) {
-            const int j = s * 64 + li;
-            head[s] = j / HDP;
-            const int sub = j % HDP;
-            ok[s] = head[s] < p.H && sub * EPL < p.C;
-            off[s] = head[s] * p.C + sub * EPL;
-            lead[s] = sub == 0;
+            off[s] = geo.off[s];
+            head[s] = geo.head[s];
+            ok[s] = geo.ok[s];
+            lead[s] = geo.lead[s];
         }
     }
 
@@ -249,6 +217,17 @@ struct FwdRow {
     }
 
     __device__ __forceinline__ void write_final(const FwdParams& p, int32_t v) {
+        if (geo.exact) {
+            // every lane takes part in the row store (it exchanges chunks across lanes)
+            const float inv = l[0] > 0.f ? 1.0f / l[0] : 0.f;
+            float o[EPL];
+#pragma unroll
+            for (int i = 0; i < EPL; i++) o[i] = acc[0][i] * inv;
+            store_row_nt<EPL>(p.out + (size_t)v * p.W, o, lpr, lane, g);
+            if (g == 0 && lead[0] && p.lse)
+                p.lse[(size_t)v * p.H + head[0]] = l[0] > 0.f ? (m[0] + __log2f(l[0])) * kLn2 : kNegInf;
+            return;
+        }
         if (g != 0) return;
 #pragma unroll
         for (int s = 0; s < NS; s++) {

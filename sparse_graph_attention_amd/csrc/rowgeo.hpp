@@ -49,6 +49,8 @@ struct RowGeo {
     int lane, g, G, lpr;
     int off[NS], head[NS];
     bool ok[NS], lead[NS];
+    bool exact;  // one slot, and the lpr lanes of a group cover the row exactly
+
 
     __device__ __forceinline__ void init(int lpr_log2, int H, int C) {
         lane = threadIdx.x & 63;
@@ -65,8 +67,45 @@ struct RowGeo {
             off[s] = head[s] * C + sub * EPL;
             lead[s] = sub == 0;
         }
+        exact = NS == 1 && lpr == H * HDP && HDP * EPL == C;
     }
 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Stores a node's output row held by the lanes of group 0 (lane l holds elements
+// [l*EPL, (l+1)*EPL) of a row of lpr*EPL floats) with non-temporal stores that each cover
+// consecutive 16-byte chunks of the row.  With 8 floats per lane the chunks are first
+// exchanged across lanes so that one store instruction writes a contiguous 1 KiB instead
+// of half of every cache line twice.  All 64 lanes must call it (it shuffles).
+template <int EPL>
+__device__ __forceinline__ void store_row_nt(float* row, const float* vals, int lpr, int lane, int g) {
+    if constexpr (EPL == 8) {
+        const int nchunks = lpr * 2;
+        for (int base = 0; base < nchunks; base += 64) {
+            const int c = base + lane;
+            const int srcl = (c >> 1) & 63;
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                a[i] = __shfl(vals[i], srcl, 64);
+                b[i] = __shfl(vals[4 + i], srcl, 64);
+            }
+            if (c < nchunks) {
+                const f32x4 val = (c & 1) ? f32x4{b[0], b[1], b[2], b[3]} : f32x4{a[0], a[1], a[2], a[3]};
+                __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(row) + c);
+            }
+        }
+    } else if constexpr (EPL == 4) {
+        if (g == 0)
+            __builtin_nontemporal_store(f32x4{vals[0], vals[1], vals[2], vals[3]},
+                                        reinterpret_cast<f32x4*>(row) + lane);
+    } else {
+        if (g == 0)
+#pragma unroll
+            for (int i = 0; i < EPL; i++) __builtin_nontemporal_store(vals[i], row + lane * EPL + i);
+    }
+}
 
 // Sum of a value over the G edge groups of a wavefront (butterfly from LPR up to 32).
 __device__ __forceinline__ float sum_groups(float x, int lpr) {
