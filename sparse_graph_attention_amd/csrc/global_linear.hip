@@ -14,89 +14,112 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// N consecutive floats (N = 1..4) in one load; p must be 4*N-byte aligned (16 for N = 3).
+template <int N>
+__device__ __forceinline__ void load_n(const float* p, float* out) {
+    if constexpr (N == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        out[0] = t.x; out[1] = t.y; out[2] = t.z; out[3] = t.w;
+    } else if constexpr (N == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        out[0] = t.x; out[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i++) out[i] = p[i];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void store_n(float* p, const float* v) {
+    if constexpr (N == 4) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i++) p[i] = v[i];
+    }
+}
+
+// Number of node ranges of the statistics (a function of n only, so the order of the
+// sums is fixed): ranges of at least 256 nodes, at most 1024 ranges.
 int row_ranges(int32_t n) {
-    int64_t nb = ((int64_t)n + 1023) / 1024;
+    int64_t nb = ((int64_t)n + 255) / 256;
     if (nb < 1) nb = 1;
-    if (nb > 256) nb = 256;
+    if (nb > 1024) nb = 1024;
     return (int)nb;
 }
 
-// ---- statistics, matrix-core path.  grid (nb, H); block: 4 wavefronts splitting the
-// range's rows four ways, folded in wavefront order.
+// ---- statistics, matrix-core path.  grid nb; a workgroup owns one node range and has one
+// wavefront per head (up to 16; more heads loop), so the wavefronts of a workgroup read the
+// same rows together.  Each step takes 4 rows (lane / 16); four steps are loaded before any
+// is multiplied.
 template <int TR>
-__global__ __launch_bounds__(256) void stats_mfma(int32_t n, int32_t H, int32_t rows_per, const float* __restrict__ k,
-                                                  const float* __restrict__ v, float* __restrict__ part) {
+__global__ __launch_bounds__(1024) void stats_mfma(int32_t n, int32_t H, int32_t rows_per, const float* __restrict__ k,
+                                                   const float* __restrict__ v, float* __restrict__ part) {
     constexpr int R = TR * 16;
-    __shared__ float sm[3][64][TR * TR * 4 + TR];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int h = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int64_t W = (int64_t)H * R;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per;
     const int64_t r1 = r0 + rows_per < n ? r0 + rows_per : n;
-    v4f acc[TR][TR];
-    float zacc[TR];
+    for (int h = wave; h < H; h += nw) {
+        v4f acc[TR][TR];
+        float zacc[TR];
 #pragma unroll
-    for (int i = 0; i < TR; i++) {
-        zacc[i] = 0.f;
+        for (int i = 0; i < TR; i++) {
+            zacc[i] = 0.f;
 #pragma unroll
-        for (int j = 0; j < TR; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-    for (int64_t base = r0 + wave * 4; base < r1; base += 16) {
-        const int64_t row = base + (lane >> 4);
-        const bool ok = row < r1;
-        float a[TR], b[TR];
+            for (int j = 0; j < TR; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        // Feature order inside a head is permuted: MFMA tile u, position p <-> feature
+        // TR*p + u, so lane p loads its TR features of a row as one vector.
+        for (int64_t base = r0; base < r1; base += 16) {
+            float a[4][TR], b[4][TR];
 #pragma unroll
-        for (int t = 0; t < TR; t++) {
-            const int64_t o = row * W + h * R + t * 16 + (lane & 15);
-            a[t] = ok ? phi(k[o]) : 0.f;
-            b[t] = ok ? v[o] : 0.f;
-            zacc[t] += a[t];
+            for (int st = 0; st < 4; st++) {
+                const int64_t row = base + st * 4 + (lane >> 4);
+                if (row < r1) {
+                    const int64_t o = row * W + h * R + TR * (lane & 15);
+                    load_n<TR>(k + o, a[st]);
+                    load_n<TR>(v + o, b[st]);
+#pragma unroll
+                    for (int t = 0; t < TR; t++) a[st][t] = phi(a[st][t]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < TR; t++) a[st][t] = b[st][t] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int st = 0; st < 4; st++) {
+#pragma unroll
+                for (int t = 0; t < TR; t++) zacc[t] += a[st][t];
+#pragma unroll
+                for (int i = 0; i < TR; i++)
+#pragma unroll
+                    for (int j = 0; j < TR; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[st][i], b[st][j], acc[i][j], 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int i = 0; i < TR; i++)
+        for (int t = 0; t < TR; t++) {
+            zacc[t] += __shfl_xor(zacc[t], 16, 64);
+            zacc[t] += __shfl_xor(zacc[t], 32, 64);
+        }
+        float* out = part + ((int64_t)blockIdx.x * H + h) * (R * R + R);
+        // acc[i][j][q] of lane l is S[TR*pi + i][TR*pj + j] with pi = (l/16)*4 + q, pj = l%16
 #pragma unroll
-            for (int j = 0; j < TR; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+        for (int q = 0; q < 4; q++) {
+            const int pi = (lane >> 4) * 4 + q, pj = lane & 15;
 #pragma unroll
-    for (int t = 0; t < TR; t++) {
-        zacc[t] += __shfl_xor(zacc[t], 16, 64);
-        zacc[t] += __shfl_xor(zacc[t], 32, 64);
-    }
-    if (wave > 0) {
+            for (int i = 0; i < TR; i++) {
+                float row[TR];
 #pragma unroll
-        for (int i = 0; i < TR; i++)
-#pragma unroll
-            for (int j = 0; j < TR; j++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) sm[wave - 1][lane][(i * TR + j) * 4 + q] = acc[i][j][q];
-#pragma unroll
-        for (int t = 0; t < TR; t++) sm[wave - 1][lane][TR * TR * 4 + t] = zacc[t];
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    for (int w = 0; w < 3; w++) {
-#pragma unroll
-        for (int i = 0; i < TR; i++)
-#pragma unroll
-            for (int j = 0; j < TR; j++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) acc[i][j][q] += sm[w][lane][(i * TR + j) * 4 + q];
-#pragma unroll
-        for (int t = 0; t < TR; t++) zacc[t] += sm[w][lane][TR * TR * 4 + t];
-    }
-    float* out = part + ((int64_t)blockIdx.x * H + h) * (R * R + R);
-#pragma unroll
-    for (int i = 0; i < TR; i++)
-#pragma unroll
-        for (int j = 0; j < TR; j++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int ii = i * 16 + (lane >> 4) * 4 + q, jj = j * 16 + (lane & 15);
-                out[ii * R + jj] = acc[i][j][q];
+                for (int j = 0; j < TR; j++) row[j] = acc[i][j][q];
+                store_n<TR>(out + (TR * pi + i) * R + TR * pj, row);
             }
-    if (lane < 16)
-#pragma unroll
-        for (int t = 0; t < TR; t++) out[R * R + t * 16 + lane] = zacc[t];
+        }
+        if (lane < 16) store_n<TR>(out + R * R + TR * lane, zacc);
+    }
 }
 
 // ---- statistics, scalar path (any r).  grid (nb, H); threads over the r*r + r outputs.
@@ -121,76 +144,104 @@ __global__ __launch_bounds__(256) void stats_scalar(int32_t n, int32_t H, int32_
     }
 }
 
-// Adds the range partials in range order: S and z into ws (and s_out / z_out if given).
-__global__ void stats_reduce(int nb, int32_t H, int32_t R, const float* __restrict__ part, float* __restrict__ s,
-                             float* __restrict__ z, float* __restrict__ s_out, float* __restrict__ z_out) {
+// Adds the range partials: a workgroup of 16 wavefronts owns 64 consecutive outputs,
+// wavefront w adds ranges w, w+16, ... and the 16 sums are added in wavefront order.
+// Writes S and z into the workspace (and s_out / z_out if given).
+__global__ __launch_bounds__(1024) void stats_reduce(int nb, int32_t H, int32_t R, const float* __restrict__ part,
+                                                     float* __restrict__ s, float* __restrict__ z,
+                                                     float* __restrict__ s_out, float* __restrict__ z_out) {
+    __shared__ float sm[16][64];
     const int per = R * R + R;
-    for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < (int64_t)H * per;
-         x += (int64_t)gridDim.x * blockDim.x) {
-        const int h = (int)(x / per), e = (int)(x % per);
-        float a = 0.f;
-        for (int b = 0; b < nb; b++) a += part[((int64_t)b * H + h) * per + e];
-        if (e < R * R) {
-            s[(int64_t)h * R * R + e] = a;
-            if (s_out) s_out[(int64_t)h * R * R + e] = a;
-        } else {
-            z[(int64_t)h * R + e - R * R] = a;
-            if (z_out) z_out[(int64_t)h * R + e - R * R] = a;
-        }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t x = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t tot = (int64_t)H * per;
+    const int h = (int)(x / per), e = (int)(x % per);
+    float a = 0.f;
+    if (x < tot)
+        for (int b = wave; b < nb; b += 16) a += part[((int64_t)b * H + h) * per + e];
+    sm[wave][lane] = a;
+    __syncthreads();
+    if (wave != 0 || x >= tot) return;
+    float t = 0.f;
+    for (int w = 0; w < 16; w++) t += sm[w][lane];
+    if (e < R * R) {
+        s[(int64_t)h * R * R + e] = t;
+        if (s_out) s_out[(int64_t)h * R * R + e] = t;
+    } else {
+        z[(int64_t)h * R + e - R * R] = t;
+        if (z_out) z_out[(int64_t)h * R + e - R * R] = t;
     }
 }
 
-// ---- G = phi(Q) S / (phi(Q) z + eps), matrix-core path.  grid (ceil(n/64), H): a block
-// stages 64 rows of phi(q) and S[h] in LDS; wavefront w computes rows w*16 .. w*16+15.
+// ---- G = phi(Q) S / (phi(Q) z + eps), matrix-core path.  One wavefront per head (up to
+// 16 per workgroup; the workgroup's wavefronts read the same rows), looping over 16-row
+// tiles.  The contraction index is permuted so that in MFMA step t the lane group
+// gq = lane/16 supplies k = gq*(R/4) + t: each lane's A operands over the R/4 steps are
+// then R/4 consecutive elements of its row (16-byte loads), and its B operands S[k][j] are
+// held in registers for the whole loop.
 template <int TR>
-__global__ __launch_bounds__(256) void apply_mfma(int32_t n, int32_t H, float eps, const float* __restrict__ q,
-                                                  const float* __restrict__ s, const float* __restrict__ z,
-                                                  float* __restrict__ g) {
+__global__ __launch_bounds__(1024) void apply_mfma(int32_t n, int32_t H, float eps, const float* __restrict__ q,
+                                                   const float* __restrict__ s, const float* __restrict__ z,
+                                                   float* __restrict__ g) {
     constexpr int R = TR * 16;
-    __shared__ float Qs[64][R + 1];
-    __shared__ float Ss[R][R + 4];
-    __shared__ float den[64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int h = blockIdx.y;
+    constexpr int KQ = R / 4;  // MFMA steps per row tile
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int gq = lane >> 4, li = lane & 15;
     const int64_t W = (int64_t)H * R;
-    const int64_t n0 = (int64_t)blockIdx.x * 64;
-    for (int e = threadIdx.x; e < R * R; e += 256) Ss[e / R][e % R] = s[(int64_t)h * R * R + e];
-    for (int e = threadIdx.x; e < 64 * R; e += 256) {
-        const int rr = e / R, c = e % R;
-        const int64_t row = n0 + rr;
-        Qs[rr][c] = row < n ? phi(q[row * W + h * R + c]) : 0.f;
-    }
-    __syncthreads();
-    {
-        const int rr = threadIdx.x >> 2, part = threadIdx.x & 3;
-        float d = 0.f;
-        for (int c = part; c < R; c += 4) d = fmaf(Qs[rr][c], z[(int64_t)h * R + c], d);
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        if (part == 0) den[rr] = d + eps;
-    }
-    __syncthreads();
-    v4f acc[TR];
+    const int64_t tiles = ((int64_t)n + 15) / 16;
+    for (int h = wave; h < H; h += nw) {
+        float sreg[KQ][TR], zreg[KQ];
+        // output columns are permuted too: MFMA tile j, position li <-> column TR*li + j, so
+        // each lane ends with TR consecutive outputs of a row (one vector store)
 #pragma unroll
-    for (int j = 0; j < TR; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < KQ; t++) {
+            const int kk = gq * KQ + t;
+            zreg[t] = z[(int64_t)h * R + kk];
 #pragma unroll
-    for (int k4 = 0; k4 < R / 4; k4++) {
-        const int kk = k4 * 4 + (lane >> 4);
-        const float a = Qs[wave * 16 + (lane & 15)][kk];
-#pragma unroll
-        for (int j = 0; j < TR; j++) {
-            const float b = Ss[kk][j * 16 + (lane & 15)];
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+            for (int j = 0; j < TR; j++) sreg[t][j] = s[((int64_t)h * R + kk) * R + TR * li + j];
         }
-    }
+        for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+            const int64_t row = tile * 16 + li;
+            float a[KQ];
+            if (row < n) {
+                const float4* qp = reinterpret_cast<const float4*>(q + row * W + h * R + gq * KQ);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; q4++) {
-        const int rr = wave * 16 + (lane >> 4) * 4 + q4;
-        const int64_t row = n0 + rr;
-        if (row >= n) continue;
-        const float inv = 1.0f / den[rr];
+                for (int c = 0; c < KQ / 4; c++) {
+                    const float4 t4 = qp[c];
+                    a[4 * c + 0] = phi(t4.x);
+                    a[4 * c + 1] = phi(t4.y);
+                    a[4 * c + 2] = phi(t4.z);
+                    a[4 * c + 3] = phi(t4.w);
+                }
+            } else {
 #pragma unroll
-        for (int j = 0; j < TR; j++) g[row * W + h * R + j * 16 + (lane & 15)] = acc[j][q4] * inv;
+                for (int t = 0; t < KQ; t++) a[t] = 0.f;
+            }
+            float d = 0.f;
+#pragma unroll
+            for (int t = 0; t < KQ; t++) d = fmaf(a[t], zreg[t], d);
+            d += __shfl_xor(d, 16, 64);
+            d += __shfl_xor(d, 32, 64);  // every lane li now holds the dot for row tile*16 + li
+            v4f acc[TR];
+#pragma unroll
+            for (int j = 0; j < TR; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < KQ; t++)
+#pragma unroll
+                for (int j = 0; j < TR; j++) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], sreg[t][j], acc[j], 0, 0, 0);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; q4++) {
+                const int rr = gq * 4 + q4;  // output row of this lane within the tile
+                const float inv = 1.0f / (__shfl(d, rr, 64) + eps);
+                const int64_t orow = tile * 16 + rr;
+                if (orow < n) {
+                    float o[TR];
+#pragma unroll
+                    for (int j = 0; j < TR; j++) o[j] = acc[j][q4] * inv;
+                    store_n<TR>(g + orow * W + h * R + TR * li, o);
+                }
+            }
+        }
     }
 }
 
@@ -253,32 +304,34 @@ extern "C" int gga_global_linear_fwd(int32_t n, int32_t heads, int32_t r, const 
     hipStream_t s = as_stream(stream);
     const int nb = row_ranges(n);
     const int32_t rows_per = (int32_t)((((int64_t)n + nb - 1) / nb + 15) / 16 * 16);
-    const bool mfma = r % 16 == 0 && r <= 64;
+    const bool mfma = r % 16 == 0 && r <= 64 && aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_out);
+    const int wpb = heads < 16 ? heads : 16;  // wavefronts (heads) per workgroup
     if (n > 0) {
-        const dim3 grid((unsigned)nb, (unsigned)heads);
         if (mfma) {
+            const unsigned grid = (unsigned)nb, threads = 64u * wpb;
             switch (r / 16) {
-                case 1: stats_mfma<1><<<grid, 256, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
-                case 2: stats_mfma<2><<<grid, 256, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
-                case 3: stats_mfma<3><<<grid, 256, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
-                default: stats_mfma<4><<<grid, 256, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
+                case 1: stats_mfma<1><<<grid, threads, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
+                case 2: stats_mfma<2><<<grid, threads, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
+                case 3: stats_mfma<3><<<grid, threads, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
+                default: stats_mfma<4><<<grid, threads, 0, s>>>(n, heads, rows_per, k, v, w.part); break;
             }
         } else {
-            stats_scalar<<<grid, 256, 0, s>>>(n, heads, r, rows_per, k, v, w.part);
+            stats_scalar<<<dim3((unsigned)nb, (unsigned)heads), 256, 0, s>>>(n, heads, r, rows_per, k, v, w.part);
         }
     } else {
         fill_f32(w.part, (int64_t)nb * heads * (r * r + r), 0.f, s);
     }
     const int64_t tot = (int64_t)heads * (r * r + r);
-    stats_reduce<<<(unsigned)((tot + 255) / 256), 256, 0, s>>>(nb, heads, r, w.part, w.s, w.z, s_out, z_out);
+    stats_reduce<<<(unsigned)((tot + 63) / 64), 1024, 0, s>>>(nb, heads, r, w.part, w.s, w.z, s_out, z_out);
     if (n > 0) {
         if (mfma) {
-            const dim3 grid((unsigned)(((int64_t)n + 63) / 64), (unsigned)heads);
+            int64_t tiles = ((int64_t)n + 15) / 16;
+            const unsigned grid = (unsigned)(tiles < 2048 ? tiles : 2048), threads = 64u * wpb;
             switch (r / 16) {
-                case 1: apply_mfma<1><<<grid, 256, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
-                case 2: apply_mfma<2><<<grid, 256, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
-                case 3: apply_mfma<3><<<grid, 256, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
-                default: apply_mfma<4><<<grid, 256, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
+                case 1: apply_mfma<1><<<grid, threads, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
+                case 2: apply_mfma<2><<<grid, threads, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
+                case 3: apply_mfma<3><<<grid, threads, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
+                default: apply_mfma<4><<<grid, threads, 0, s>>>(n, heads, eps, q, w.s, w.z, g_out); break;
             }
         } else {
             int64_t blocks = ((int64_t)n * heads * r + 255) / 256;

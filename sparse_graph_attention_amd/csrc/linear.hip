@@ -1,10 +1,10 @@
 // Dense fp32 product on the matrix cores (v_mfma_f32_16x16x4_f32): c = op(a) op(b) (+ bias).
 //
-// Workgroup tile 128x128, four wavefronts each owning 64x64 (4x4 MFMA tiles of 16x16),
-// K staged through LDS 16 at a time with double buffering.  LDS holds both operands
+// Workgroup tile 128 x BN (BN = 128, or 64 when n <= 64), four wavefronts each owning
+// 64 x BN/2 (MFMA tiles of 16x16), K staged through LDS 16 at a time with double buffering.  LDS holds both operands
 // k-major ([k][m] and [k][n]) so each MFMA operand read is 16 consecutive floats per
 // quarter-wavefront.  When the output has few tiles and K is long, K is split into a
-// fixed number of ranges whose partial products are added in range order by a second
+// fixed number of ranges whose partial products are added in a fixed order by a second
 // kernel, so results do not depend on scheduling.
 #include "common.hpp"
 
@@ -13,8 +13,7 @@ namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 128, KT = 16;
-constexpr int LDS_STRIDE = BM + 16;  // 144 floats: successive k rows start 16 banks apart
+constexpr int BM = 128, KT = 16;
 
 struct GemmArgs {
     const float* a;
@@ -37,22 +36,23 @@ __device__ __forceinline__ float4 load4(const float* row, int64_t c0, int64_t li
     return r;
 }
 
-// One operand tile (128 along m or n, KT along k) into registers: two float4 per thread.
+// One operand tile (TW along m or n, KT along k) into registers: TW*KT/1024 float4 per thread.
 // `kmajor_src`: the operand is stored with k as its row index (a transposed / b plain).
+template <int TW>
 __device__ __forceinline__ void fetch_tile(const float* src, int ld, bool kmajor_src, int64_t o0, int64_t olim,
-                                           int64_t k0, int64_t klim, bool vec_ok, float4 (&r)[2]) {
+                                           int64_t k0, int64_t klim, bool vec_ok, float4 (&r)[TW * KT / 1024]) {
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
+    for (int q = 0; q < TW * KT / 1024; q++) {
         const int f = threadIdx.x + 256 * q;
         if (kmajor_src) {
-            const int kr = f / 32, c4 = f % 32;
+            const int kr = f / (TW / 4), c4 = f % (TW / 4);
             const int64_t k = k0 + kr;
             if (k < klim)
                 r[q] = load4(src + k * ld, o0 + c4 * 4, olim, vec_ok);
             else
                 r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         } else {
-            const int orow = f / 4, c4 = f % 4;
+            const int orow = f / (KT / 4), c4 = f % (KT / 4);
             const int64_t o = o0 + orow;
             if (o < olim)
                 r[q] = load4(src + o * ld, k0 + c4 * 4, klim, vec_ok);
@@ -62,28 +62,38 @@ __device__ __forceinline__ void fetch_tile(const float* src, int ld, bool kmajor
     }
 }
 
-__device__ __forceinline__ void stash_tile(float* lds, bool kmajor_src, const float4 (&r)[2]) {
+// LDS row stride of a k-major tile of width TW: successive k rows start 16 banks apart.
+template <int TW>
+constexpr int lds_stride() { return TW + 16; }
+
+template <int TW>
+__device__ __forceinline__ void stash_tile(float* lds, bool kmajor_src, const float4 (&r)[TW * KT / 1024]) {
+    constexpr int S = lds_stride<TW>();
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
+    for (int q = 0; q < TW * KT / 1024; q++) {
         const int f = threadIdx.x + 256 * q;
         if (kmajor_src) {
-            const int kr = f / 32, c4 = f % 32;
-            *reinterpret_cast<float4*>(lds + kr * LDS_STRIDE + c4 * 4) = r[q];
+            const int kr = f / (TW / 4), c4 = f % (TW / 4);
+            *reinterpret_cast<float4*>(lds + kr * S + c4 * 4) = r[q];
         } else {
-            const int orow = f / 4, c4 = f % 4;
-            lds[(c4 * 4 + 0) * LDS_STRIDE + orow] = r[q].x;
-            lds[(c4 * 4 + 1) * LDS_STRIDE + orow] = r[q].y;
-            lds[(c4 * 4 + 2) * LDS_STRIDE + orow] = r[q].z;
-            lds[(c4 * 4 + 3) * LDS_STRIDE + orow] = r[q].w;
+            const int orow = f / (KT / 4), c4 = f % (KT / 4);
+            lds[(c4 * 4 + 0) * S + orow] = r[q].x;
+            lds[(c4 * 4 + 1) * S + orow] = r[q].y;
+            lds[(c4 * 4 + 2) * S + orow] = r[q].z;
+            lds[(c4 * 4 + 3) * S + orow] = r[q].w;
         }
     }
 }
 
 // grid: (ceil(N/BN), ceil(M/BM), splits).  With splits > 1, c points at the partial buffer
-// [splits][M][N] and bias is ignored.
+// [splits][M][N] and bias is ignored.  Wavefront w owns rows (w/2)*64 .. +64 and columns
+// (w%2)*BN/2 .. +BN/2 of the workgroup tile: 4 x TJ MFMA tiles of 16 x 16.
+template <int BN>
 __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
-    __shared__ float As[2][KT * LDS_STRIDE];
-    __shared__ float Bs[2][KT * LDS_STRIDE];
+    constexpr int SA = lds_stride<BM>(), SB = lds_stride<BN>();
+    constexpr int TJ = BN / 32;
+    __shared__ float As[2][KT * SA];
+    __shared__ float Bs[2][KT * SB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
@@ -94,46 +104,46 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
     const bool a_vec = (g.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
     const bool b_vec = (g.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(g.b) & 15) == 0;
 
-    v4f acc[4][4];
+    v4f acc[4][TJ];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (int)((ke - kb + KT - 1) / KT);
-    float4 ra[2], rb[2];
+    float4 ra[BM * KT / 1024], rb[BN * KT / 1024];
     if (nk > 0) {
-        fetch_tile(g.a, g.lda, a_km, m0, g.M, kb, ke, a_vec, ra);
-        fetch_tile(g.b, g.ldb, b_km, n0, g.N, kb, ke, b_vec, rb);
-        stash_tile(As[0], a_km, ra);
-        stash_tile(Bs[0], b_km, rb);
+        fetch_tile<BM>(g.a, g.lda, a_km, m0, g.M, kb, ke, a_vec, ra);
+        fetch_tile<BN>(g.b, g.ldb, b_km, n0, g.N, kb, ke, b_vec, rb);
+        stash_tile<BM>(As[0], a_km, ra);
+        stash_tile<BN>(Bs[0], b_km, rb);
     }
     __syncthreads();
     for (int t = 0; t < nk; t++) {
         const int cur = t & 1;
         if (t + 1 < nk) {
             const int64_t k0 = kb + (int64_t)(t + 1) * KT;
-            fetch_tile(g.a, g.lda, a_km, m0, g.M, k0, ke, a_vec, ra);
-            fetch_tile(g.b, g.ldb, b_km, n0, g.N, k0, ke, b_vec, rb);
+            fetch_tile<BM>(g.a, g.lda, a_km, m0, g.M, k0, ke, a_vec, ra);
+            fetch_tile<BN>(g.b, g.ldb, b_km, n0, g.N, k0, ke, b_vec, rb);
         }
         const float* as = As[cur];
         const float* bs = Bs[cur];
 #pragma unroll
         for (int kk = 0; kk < KT / 4; kk++) {
             const int kr = kk * 4 + (lane >> 4);
-            float af[4], bf[4];
+            float af[4], bf[TJ];
 #pragma unroll
-            for (int i = 0; i < 4; i++) af[i] = as[kr * LDS_STRIDE + wm * 64 + i * 16 + (lane & 15)];
+            for (int i = 0; i < 4; i++) af[i] = as[kr * SA + wm * 64 + i * 16 + (lane & 15)];
 #pragma unroll
-            for (int j = 0; j < 4; j++) bf[j] = bs[kr * LDS_STRIDE + wn * 64 + j * 16 + (lane & 15)];
+            for (int j = 0; j < TJ; j++) bf[j] = bs[kr * SB + wn * (BN / 2) + j * 16 + (lane & 15)];
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
         if (t + 1 < nk) {
-            stash_tile(As[cur ^ 1], a_km, ra);
-            stash_tile(Bs[cur ^ 1], b_km, rb);
+            stash_tile<BM>(As[cur ^ 1], a_km, ra);
+            stash_tile<BN>(Bs[cur ^ 1], b_km, rb);
         }
         __syncthreads();
     }
@@ -141,8 +151,8 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
     float* cbase = g.c + (int64_t)blockIdx.z * g.M * g.N;
     const bool add_bias = g.bias != nullptr && gridDim.z == 1;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t col = n0 + wn * 64 + j * 16 + (lane & 15);
+    for (int j = 0; j < TJ; j++) {
+        const int64_t col = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
         if (col >= g.N) continue;
         const float bv = add_bias ? g.bias[col] : 0.f;
 #pragma unroll
@@ -156,12 +166,23 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
     }
 }
 
-__global__ void splitk_reduce(const float* __restrict__ part, int splits, int64_t mn, int32_t N,
-                              const float* __restrict__ bias, float* __restrict__ c) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < mn; i += (int64_t)gridDim.x * blockDim.x) {
-        float s = 0.f;
-        for (int z = 0; z < splits; z++) s += part[z * mn + i];
-        c[i] = s + (bias ? bias[i % N] : 0.f);
+// c = sum over the splits of the partial products (in split order) + bias.  A workgroup of
+// 16 wavefronts owns 64 consecutive outputs: wavefront w adds splits w, w+16, ... and the
+// 16 running sums are then added in wavefront order.
+__global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ part, int splits, int64_t mn,
+                                                      int32_t N, const float* __restrict__ bias, float* __restrict__ c) {
+    __shared__ float sm[16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+    float s = 0.f;
+    if (i < mn)
+        for (int z = wave; z < splits; z += 16) s += part[(int64_t)z * mn + i];
+    sm[wave][lane] = s;
+    __syncthreads();
+    if (wave == 0 && i < mn) {
+        float t = 0.f;
+        for (int w = 0; w < 16; w++) t += sm[w][lane];
+        c[i] = t + (bias ? bias[i % N] : 0.f);
     }
 }
 
@@ -170,14 +191,19 @@ struct Split {
     int32_t kchunk;
 };
 
+int pick_bn(int32_t n) { return n <= 64 ? 64 : 128; }
+
+// Output tiles below 512: split k so that about 2048 workgroups run, each with at least 256
+// values of k (a fixed function of the shape, so the summation order is too).
 Split pick_split(int32_t m, int32_t k, int32_t n) {
-    const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const int bn = pick_bn(n);
+    const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + bn - 1) / bn);
     Split s{1, k};
-    if (tiles < 256 && k > 1024) {
-        int64_t want = (1024 + tiles - 1) / tiles;
-        int64_t by_k = k / 512;
+    if (tiles < 512 && k > 1024) {
+        int64_t want = (2048 + tiles - 1) / tiles;
+        int64_t by_k = k / 256;
         int64_t sp = want < by_k ? want : by_k;
-        if (sp > 64) sp = 64;
+        if (sp > 1024) sp = 1024;
         if (sp > 1) {
             int64_t kc = (k + sp - 1) / sp;
             kc = (kc + KT - 1) / KT * KT;
@@ -223,18 +249,19 @@ extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int3
     g.trans_a = trans_a != 0;
     g.trans_b = trans_b != 0;
     g.kchunk = sp.kchunk;
-    const int64_t gy = (m + BM - 1) / BM, gx = (n + BN - 1) / BN;
+    const int bn = pick_bn(n);
+    const int64_t gy = (m + BM - 1) / BM, gx = (n + bn - 1) / bn;
     if (gy > 65535) return GGA_ERANGE;
+    g.c = sp.splits > 1 ? static_cast<float*>(ws) : c;
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)sp.splits);
+    if (bn == 64)
+        gemm_f32_mfma<64><<<grid, 256, 0, s>>>(g);
+    else
+        gemm_f32_mfma<128><<<grid, 256, 0, s>>>(g);
     if (sp.splits > 1) {
-        g.c = static_cast<float*>(ws);
-        gemm_f32_mfma<<<dim3((unsigned)gx, (unsigned)gy, (unsigned)sp.splits), 256, 0, s>>>(g);
         const int64_t mn = (int64_t)m * n;
-        int64_t blocks = (mn + 255) / 256;
-        if (blocks > 65536) blocks = 65536;
-        splitk_reduce<<<(unsigned)blocks, 256, 0, s>>>(static_cast<const float*>(ws), sp.splits, mn, n, bias, c);
-    } else {
-        g.c = c;
-        gemm_f32_mfma<<<dim3((unsigned)gx, (unsigned)gy, 1), 256, 0, s>>>(g);
+        splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(static_cast<const float*>(ws), sp.splits, mn, n,
+                                                                bias, c);
     }
     return launch_status();
 }
