@@ -103,6 +103,8 @@ def _mark(tm, name):
 
 
 def per_topology(g, torch, n, src_d, dst_d, backward=False):
+    # one untimed build first, so the timed one sees loaded kernels and a warm allocator
+    g.Topology(n, src_d, dst_d, backward=backward)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     torch.cuda.synchronize()
     ev[0].record()

@@ -6,7 +6,9 @@
 // count orders the rounds) and tiles are ordered by a digit-major exclusive scan of
 // per-tile histograms.  The result therefore equals a stable sort, independent of
 // scheduling: within a row the COO indices ascend, bit-exact across runs and devices.
-// No atomics decide a position; the only global atomics count row lengths.
+// Each tile's items are staged in LDS in digit order before they are written, so the
+// scatter writes contiguous runs.  row_ptr comes from the segment boundaries of the
+// sorted keys; no atomics take part in the build.
 #include "common.hpp"
 
 namespace gga {
@@ -18,17 +20,6 @@ constexpr int kRsItems = 16;
 constexpr int kRsTile = kRsThreads * kRsItems;  // 4096 edges per tile
 constexpr int kRsBins = 256;
 constexpr int kRsWaves = kRsThreads / 64;
-
-__global__ void count_keys(const int32_t* __restrict__ key, int64_t e, int32_t n, int32_t* __restrict__ cnt,
-                           int32_t* __restrict__ bad) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < e; i += (int64_t)gridDim.x * blockDim.x) {
-        int32_t k = key[i];
-        if ((uint32_t)k < (uint32_t)n)
-            atomicAdd(&cnt[k], 1);
-        else if (bad)
-            atomicAdd(bad, 1);
-    }
-}
 
 __global__ void count_bad(const int32_t* __restrict__ a, const int32_t* __restrict__ b, int64_t e, int32_t n,
                           int32_t* __restrict__ bad) {
@@ -53,22 +44,51 @@ __global__ void radix_upsweep(const int32_t* __restrict__ keys, int64_t e, int s
     hist[(int64_t)threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// vals_in == nullptr means the identity (COO index); keys_out may be nullptr on the last pass.
-__global__ void radix_downsweep(const int32_t* __restrict__ keys_in, const int32_t* __restrict__ vals_in,
-                                int32_t* __restrict__ keys_out, int32_t* __restrict__ vals_out, int64_t e, int shift,
-                                int bits, const int32_t* __restrict__ offsets, int64_t nblocks) {
-    __shared__ int run[kRsBins];
+// vals_in == nullptr means the identity (COO index).  `offsets` is the digit-major exclusive
+// scan of the per-tile digit counts (offsets[d * nblocks + b]); `total` = e.
+__global__ __launch_bounds__(kRsThreads) void radix_downsweep(const int32_t* __restrict__ keys_in,
+                                                              const int32_t* __restrict__ vals_in,
+                                                              int32_t* __restrict__ keys_out,
+                                                              int32_t* __restrict__ vals_out, int64_t e, int shift,
+                                                              int bits, const int32_t* __restrict__ offsets,
+                                                              int64_t nblocks) {
+    __shared__ int run[kRsBins];    // items of each digit placed so far in this tile
+    __shared__ int tdo[kRsBins];    // tile-local start of each digit
+    __shared__ int gbase[kRsBins];  // global start of each digit's run of this tile
     __shared__ int wc[kRsWaves][kRsBins];
+    __shared__ int wtot[kRsWaves];
+    __shared__ int32_t skey[kRsTile];
+    __shared__ int32_t sval[kRsTile];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint32_t mask = (1u << bits) - 1u;
-    run[tid] = offsets[(int64_t)tid * nblocks + blockIdx.x];
     const int64_t base = (int64_t)blockIdx.x * kRsTile;
+    const int tile_n = (int)((e - base) < kRsTile ? (e - base) : kRsTile);
+    // this tile's count of digit tid, from the scan's neighbour (the scan is over a flat array)
+    const int64_t oi = (int64_t)tid * nblocks + blockIdx.x;
+    const int g0 = offsets[oi];
+    const int g1 = (oi + 1 < (int64_t)kRsBins * nblocks) ? offsets[oi + 1] : (int)e;
+    const int cnt = g1 - g0;
+    gbase[tid] = g0;
+    run[tid] = 0;
+    {  // exclusive scan of the tile counts over the digits
+        int x = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wtot[wave] = x;
+        __syncthreads();
+        int before = 0;
+        for (int w = 0; w < wave; w++) before += wtot[w];
+        tdo[tid] = before + x - cnt;
+    }
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int r = 0; r < kRsItems; r++) {
-        const int64_t i = base + r * kRsThreads + tid;
-        const bool valid = i < e;
-        const int32_t key = valid ? keys_in[i] : 0;
-        const int32_t val = valid ? (vals_in ? vals_in[i] : (int32_t)i) : 0;
+        const int li = r * kRsThreads + tid;
+        const bool valid = li < tile_n;
+        const int32_t key = valid ? keys_in[base + li] : 0;
+        const int32_t val = valid ? (vals_in ? vals_in[base + li] : (int32_t)(base + li)) : 0;
         const uint32_t d = ((uint32_t)key >> shift) & mask;
 #pragma unroll
         for (int w = 0; w < kRsWaves; w++) wc[w][tid] = 0;
@@ -83,17 +103,39 @@ __global__ void radix_downsweep(const int32_t* __restrict__ keys_in, const int32
         if (valid && rank == 0) wc[wave][d] = __popcll(peers);
         __syncthreads();
         if (valid) {
-            int pos = run[d] + rank;
+            int pos = tdo[d] + run[d] + rank;
             for (int w = 0; w < wave; w++) pos += wc[w][d];
-            if (keys_out) keys_out[pos] = key;
-            vals_out[pos] = val;
+            skey[pos] = key;
+            sval[pos] = val;
         }
         __syncthreads();
         int add = 0;
 #pragma unroll
         for (int w = 0; w < kRsWaves; w++) add += wc[w][tid];
         run[tid] += add;
-        __syncthreads();
+    }
+    __syncthreads();
+    // the tile now sits in LDS in (digit, original order); write each digit's run contiguously
+    for (int li = tid; li < tile_n; li += kRsThreads) {
+        const int32_t key = skey[li];
+        const uint32_t d = ((uint32_t)key >> shift) & mask;
+        const int pos = gbase[d] + (li - tdo[d]);
+        if (keys_out) keys_out[pos] = key;
+        vals_out[pos] = sval[li];
+    }
+}
+
+// row_ptr from the sorted keys: row_ptr[v] = first position whose key is >= v.  Position p
+// writes the rows v in (key[p-1], key[p]] (clamped to [0, n]); every write is in bounds even
+// when keys are out of range.
+__global__ void row_ptr_from_sorted(const int32_t* __restrict__ skeys, int64_t e, int32_t n,
+                                    int32_t* __restrict__ row_ptr) {
+    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p <= e; p += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t kp = p > 0 ? (int64_t)skeys[p - 1] : -1;
+        const int64_t kc = p < e ? (int64_t)skeys[p] : (int64_t)n;
+        const int64_t lo = kp + 1 < 0 ? 0 : kp + 1;
+        const int64_t hi = kc < n ? kc : n;
+        for (int64_t v = lo; v <= hi; v++) row_ptr[v] = (int32_t)p;
     }
 }
 
@@ -110,7 +152,6 @@ int key_bits(int32_t n) {
 }
 
 struct CsrWs {
-    int32_t* cnt;
     int32_t* hist;
     int32_t* scan;
     int32_t* keys_tmp;
@@ -123,7 +164,6 @@ CsrWs carve(void* ws, int32_t n, int64_t e) {
     CsrWs w;
     int64_t nblocks = (e + kRsTile - 1) / kRsTile;
     int64_t hist_n = (int64_t)kRsBins * nblocks;
-    w.cnt = c.take<int32_t>((size_t)n + 1);
     w.hist = c.take<int32_t>((size_t)hist_n);
     size_t sc = scan_workspace_elems(hist_n > n ? hist_n : n);
     w.scan = c.take<int32_t>(sc);
@@ -172,11 +212,10 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
     w = carve(ws, n, e);
     hipStream_t s = as_stream(stream);
 
-    // row_ptr: histogram of valid keys, exclusive scan, total at row_ptr[n]
-    fill_i32(w.cnt, (int64_t)n + 1, 0, s);
-    if (e > 0 && n > 0) count_keys<<<grid_for(e), 256, 0, s>>>(key, e, n, w.cnt, nullptr);
-    exclusive_scan_i32(w.cnt, row_ptr, n, row_ptr + n, w.scan, s);
-    if (e == 0) return launch_status();
+    if (e == 0 || n == 0) {
+        fill_i32(row_ptr, (int64_t)n + 1, 0, s);
+        if (e == 0) return launch_status();
+    }
 
     const int64_t nblocks = (e + kRsTile - 1) / kRsTile;
     const int bits_total = key_bits(n);
@@ -192,13 +231,14 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
         const uint32_t mask = (1u << bits) - 1u;
         const int32_t* kin = p == 0 ? key : kbuf[(p - 1) & 1];
         const int32_t* vin = p == 0 ? nullptr : vbuf[(p - 1) & 1];
-        int32_t* kout = p == last ? nullptr : kbuf[p & 1];
+        int32_t* kout = kbuf[p & 1];
         int32_t* vout = vbuf[p & 1];
         radix_upsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, e, shift, mask, w.hist, nblocks);
         exclusive_scan_i32(w.hist, w.hist, (int64_t)kRsBins * nblocks, nullptr, w.scan, s);
         radix_downsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, vin, kout, vout, e, shift, bits, w.hist,
                                                                   nblocks);
     }
+    if (n > 0) row_ptr_from_sorted<<<grid_for(e + 1), 256, 0, s>>>(kbuf[last & 1], e, n, row_ptr);
     gather_col<<<grid_for(e), 256, 0, s>>>(other, eid, e, col);
     return launch_status();
 }
