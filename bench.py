@@ -41,7 +41,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 # HBM bytes per forward launch on the default workload counted by rocprofv3 (FETCH_SIZE x 2.00
 # + WRITE_SIZE x 1.00, factors from a plain 1 GiB copy), for the kernel as of the summary in
 # profiles/local_fwd_dot_n1m_h8_r64_bf16.md; None once the kernel changes.
-COUNTED_TRAFFIC_GB = 39.95
+COUNTED_TRAFFIC_GB = 39.93
 
 METRIC = "GEdges/s (x heads) for local graph-attention fwd; achieved HBM GB/s vs peak"
 
