@@ -182,9 +182,26 @@ def bench_dot_forward(args, g, torch, synth, ident):
     tm = Timer(torch, torch.cuda.current_stream())
     ms = tm.run(step, args.steps, args.warmup)
     kms = tm.phase_ms("f0", "f1")
+    # the same step captured once in a HIP graph and replayed (launch overhead amortised)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(None)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(None)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     alg = fwd_bytes(n, e, heads, c, esz)
     ach = alg / (kms * 1e-3) / 1e9
-    log(f"fwd: {ms:.3f} ms/step (launch avg {kms:.3f} ms), {ach:.0f} GB/s algorithmic; {tt}")
+    log(f"fwd: {ms:.3f} ms/step (launch avg {kms:.3f} ms, graph replay {graph_ms:.4f} ms), "
+        f"{ach:.0f} GB/s algorithmic; {tt}")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -203,7 +220,8 @@ def bench_dot_forward(args, g, torch, synth, ident):
     cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "storage": f"{w.dtype} q/k/v, fp32 out/lse",
            "seq_len": n}
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, w.dtype, cfg, roof, cpu,
-                  dict(tt, gedge_heads_per_s=e * heads / (ms * 1e-3) / 1e9, hbm_gbs_algorithmic=ach))
+                  dict(tt, gedge_heads_per_s=e * heads / (ms * 1e-3) / 1e9, hbm_gbs_algorithmic=ach,
+                       graph_replay_ms_per_step=graph_ms))
 
 
 def bench_heavy_tail(args, g, torch, synth):
