@@ -1,10 +1,10 @@
 // Dense fp32 product on the matrix cores (v_mfma_f32_16x16x4_f32): c = op(a) op(b) (+ bias).
 //
-// Workgroup tile 128 x BN (BN = 128, or 64 when n <= 64), four wavefronts each owning
-// 64 x BN/2 (MFMA tiles of 16x16), K staged through LDS 16 at a time with double buffering.  LDS holds both operands
-// k-major ([k][m] and [k][n]) so each MFMA operand read is 16 consecutive floats per
-// quarter-wavefront.  When the output has few tiles and K is long, K is split into a
-// fixed number of ranges whose partial products are added in a fixed order by a second
+// Workgroup tile 128 x BN (BN = 128, or 64 when n <= 64), eight wavefronts each owning
+// 64 x BN/4 (MFMA tiles of 16x16), K staged through LDS 16 at a time with double buffering.
+// LDS holds both operands as [row][k]; with the contraction index permuted inside a tile,
+// each lane reads its operands for four MFMA steps with one 16-byte LDS read.  When the
+// output has few tiles and K is long, K is split into a fixed number of ranges whose partial products are added in a fixed order by a second
 // kernel, so results do not depend on scheduling.
 #include "common.hpp"
 
@@ -36,66 +36,99 @@ __device__ __forceinline__ float4 load4(const float* row, int64_t c0, int64_t li
     return r;
 }
 
-// One operand tile (TW along m or n, KT along k) into registers: TW*KT/1024 float4 per thread.
+constexpr int kGemmThreads = 512;  // 8 wavefronts: 2 along m x 4 along n
+
+// Number of float4 a thread moves for an operand tile of width TW (along m or n) x KT.
+template <int TW>
+constexpr int tile_q() { return (TW * KT / 4 + kGemmThreads - 1) / kGemmThreads; }
+
+// One operand tile (TW along m or n, KT along k) into registers.
 // `kmajor_src`: the operand is stored with k as its row index (a transposed / b plain).
 template <int TW>
 __device__ __forceinline__ void fetch_tile(const float* src, int ld, bool kmajor_src, int64_t o0, int64_t olim,
-                                           int64_t k0, int64_t klim, bool vec_ok, float4 (&r)[TW * KT / 1024]) {
+                                           int64_t k0, int64_t klim, bool vec_ok, float4 (&r)[tile_q<TW>()]) {
 #pragma unroll
-    for (int q = 0; q < TW * KT / 1024; q++) {
-        const int f = threadIdx.x + 256 * q;
+    for (int q = 0; q < tile_q<TW>(); q++) {
+        const int f = threadIdx.x + kGemmThreads * q;
+        r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (f >= TW * KT / 4) continue;
         if (kmajor_src) {
-            const int kr = f / (TW / 4), c4 = f % (TW / 4);
+            // k fastest across threads: the transposing LDS store then hits consecutive banks
+            const int kr = f % KT, c4 = f / KT;
             const int64_t k = k0 + kr;
-            if (k < klim)
-                r[q] = load4(src + k * ld, o0 + c4 * 4, olim, vec_ok);
-            else
-                r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k < klim) r[q] = load4(src + k * ld, o0 + c4 * 4, olim, vec_ok);
         } else {
             const int orow = f / (KT / 4), c4 = f % (KT / 4);
             const int64_t o = o0 + orow;
-            if (o < olim)
-                r[q] = load4(src + o * ld, k0 + c4 * 4, klim, vec_ok);
-            else
-                r[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (o < olim) r[q] = load4(src + o * ld, k0 + c4 * 4, klim, vec_ok);
         }
     }
 }
 
-// LDS row stride of a k-major tile of width TW: successive k rows start 16 banks apart.
-template <int TW>
-constexpr int lds_stride() { return TW + 16; }
+// LDS holds each operand tile as [row][k] (rows along m or n), KT + 4 floats per row.
+constexpr int LDS_ROW = KT + 4;
 
+// A k-major source is transposed on its way into LDS; otherwise rows are copied as
+// 16-byte vectors.
 template <int TW>
-__device__ __forceinline__ void stash_tile(float* lds, bool kmajor_src, const float4 (&r)[TW * KT / 1024]) {
-    constexpr int S = lds_stride<TW>();
+__device__ __forceinline__ void stash_tile(float* lds, bool kmajor_src, const float4 (&r)[tile_q<TW>()]) {
 #pragma unroll
-    for (int q = 0; q < TW * KT / 1024; q++) {
-        const int f = threadIdx.x + 256 * q;
+    for (int q = 0; q < tile_q<TW>(); q++) {
+        const int f = threadIdx.x + kGemmThreads * q;
+        if (f >= TW * KT / 4) continue;
         if (kmajor_src) {
-            const int kr = f / (TW / 4), c4 = f % (TW / 4);
-            *reinterpret_cast<float4*>(lds + kr * S + c4 * 4) = r[q];
+            const int kr = f % KT, c4 = f / KT;
+            lds[(c4 * 4 + 0) * LDS_ROW + kr] = r[q].x;
+            lds[(c4 * 4 + 1) * LDS_ROW + kr] = r[q].y;
+            lds[(c4 * 4 + 2) * LDS_ROW + kr] = r[q].z;
+            lds[(c4 * 4 + 3) * LDS_ROW + kr] = r[q].w;
         } else {
             const int orow = f / (KT / 4), c4 = f % (KT / 4);
-            lds[(c4 * 4 + 0) * S + orow] = r[q].x;
-            lds[(c4 * 4 + 1) * S + orow] = r[q].y;
-            lds[(c4 * 4 + 2) * S + orow] = r[q].z;
-            lds[(c4 * 4 + 3) * S + orow] = r[q].w;
+            *reinterpret_cast<float4*>(lds + orow * LDS_ROW + c4 * 4) = r[q];
+        }
+    }
+}
+
+// MFMAs of one KT-deep LDS tile into a wavefront's 64 x (BN/4) accumulators.  The
+// contraction index is permuted inside the tile: MFMA step t takes, in the k slot of lane
+// group g = lane/16, the element k = 4g + t, so each lane's operands for the four steps are
+// four consecutive k of one row -- one 16-byte LDS read per operand tile.
+template <int BN>
+__device__ __forceinline__ void mfma_tile(const float* as, const float* bs, int wm, int wn, int lane,
+                                          v4f (&acc)[4][BN / 64]) {
+    constexpr int TJ = BN / 64;
+    const int kq = (lane >> 4) * 4;
+    float4 af[4], bf[TJ];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        af[i] = *reinterpret_cast<const float4*>(as + (wm * 64 + i * 16 + (lane & 15)) * LDS_ROW + kq);
+#pragma unroll
+    for (int j = 0; j < TJ; j++)
+        bf[j] = *reinterpret_cast<const float4*>(bs + (wn * (BN / 4) + j * 16 + (lane & 15)) * LDS_ROW + kq);
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float av = st == 0 ? af[i].x : st == 1 ? af[i].y : st == 2 ? af[i].z : af[i].w;
+#pragma unroll
+            for (int j = 0; j < TJ; j++) {
+                const float bv = st == 0 ? bf[j].x : st == 1 ? bf[j].y : st == 2 ? bf[j].z : bf[j].w;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[i][j], 0, 0, 0);
+            }
         }
     }
 }
 
 // grid: (ceil(N/BN), ceil(M/BM), splits).  With splits > 1, c points at the partial buffer
-// [splits][M][N] and bias is ignored.  Wavefront w owns rows (w/2)*64 .. +64 and columns
-// (w%2)*BN/2 .. +BN/2 of the workgroup tile: 4 x TJ MFMA tiles of 16 x 16.
+// [splits][M][N] and bias is ignored.  Wavefront w owns rows (w/4)*64 .. +64 and columns
+// (w%4)*BN/4 .. +BN/4 of the workgroup tile.
 template <int BN>
-__global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
-    constexpr int SA = lds_stride<BM>(), SB = lds_stride<BN>();
-    constexpr int TJ = BN / 32;
-    __shared__ float As[2][KT * SA];
-    __shared__ float Bs[2][KT * SB];
+__global__ __launch_bounds__(kGemmThreads) void gemm_f32_mfma(GemmArgs g) {
+    constexpr int TJ = BN / 64;
+    __shared__ float As[2][BM * LDS_ROW];
+    __shared__ float Bs[2][BN * LDS_ROW];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
     const int64_t kb = (int64_t)blockIdx.z * g.kchunk;
     const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
@@ -111,7 +144,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
         for (int j = 0; j < TJ; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (int)((ke - kb + KT - 1) / KT);
-    float4 ra[BM * KT / 1024], rb[BN * KT / 1024];
+    float4 ra[tile_q<BM>()], rb[tile_q<BN>()];
     if (nk > 0) {
         fetch_tile<BM>(g.a, g.lda, a_km, m0, g.M, kb, ke, a_vec, ra);
         fetch_tile<BN>(g.b, g.ldb, b_km, n0, g.N, kb, ke, b_vec, rb);
@@ -126,21 +159,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
             fetch_tile<BM>(g.a, g.lda, a_km, m0, g.M, k0, ke, a_vec, ra);
             fetch_tile<BN>(g.b, g.ldb, b_km, n0, g.N, k0, ke, b_vec, rb);
         }
-        const float* as = As[cur];
-        const float* bs = Bs[cur];
-#pragma unroll
-        for (int kk = 0; kk < KT / 4; kk++) {
-            const int kr = kk * 4 + (lane >> 4);
-            float af[4], bf[TJ];
-#pragma unroll
-            for (int i = 0; i < 4; i++) af[i] = as[kr * SA + wm * 64 + i * 16 + (lane & 15)];
-#pragma unroll
-            for (int j = 0; j < TJ; j++) bf[j] = bs[kr * SB + wn * (BN / 2) + j * 16 + (lane & 15)];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < TJ; j++) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+        mfma_tile<BN>(As[cur], Bs[cur], wm, wn, lane, acc);
         if (t + 1 < nk) {
             stash_tile<BM>(As[cur ^ 1], a_km, ra);
             stash_tile<BN>(Bs[cur ^ 1], b_km, rb);
@@ -152,7 +171,7 @@ __global__ __launch_bounds__(256) void gemm_f32_mfma(GemmArgs g) {
     const bool add_bias = g.bias != nullptr && gridDim.z == 1;
 #pragma unroll
     for (int j = 0; j < TJ; j++) {
-        const int64_t col = n0 + wn * (BN / 2) + j * 16 + (lane & 15);
+        const int64_t col = n0 + wn * (BN / 4) + j * 16 + (lane & 15);
         if (col >= g.N) continue;
         const float bv = add_bias ? g.bias[col] : 0.f;
 #pragma unroll
@@ -255,9 +274,9 @@ extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int3
     g.c = sp.splits > 1 ? static_cast<float*>(ws) : c;
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)sp.splits);
     if (bn == 64)
-        gemm_f32_mfma<64><<<grid, 256, 0, s>>>(g);
+        gemm_f32_mfma<64><<<grid, kGemmThreads, 0, s>>>(g);
     else
-        gemm_f32_mfma<128><<<grid, 256, 0, s>>>(g);
+        gemm_f32_mfma<128><<<grid, kGemmThreads, 0, s>>>(g);
     if (sp.splits > 1) {
         const int64_t mn = (int64_t)m * n;
         splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(static_cast<const float*>(ws), sp.splits, mn, n,
