@@ -329,3 +329,79 @@ def gated_layer(p: dict, g: Graph, heads: int, eps: float = GLOBAL_EPS, rows=Non
     out = layer_norm(pre, p["gamma"], p["beta"])
     return dict(q=q, k=k, v=v, local=loc.reshape(-1, d), lse=lse, S=s, z=z, glob=glob.reshape(-1, d), gate=gv, y=y,
                 pre=pre, out=out)
+
+
+# --------------------------------------------------------------------------- gated layer backward
+
+
+def phi_grad(x):
+    """d phi / dx for phi = elu + 1: 1 for x > 0, exp(x) otherwise."""
+    x = _f64(x)
+    return np.where(x > 0.0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def layer_norm_bwd(a, gamma, d_out, eps: float = LN_EPS):
+    """Backward of out = gamma (a - mu)/sqrt(var + eps) + beta over the last axis:
+    returns d a, d gamma, d beta (textbook LayerNorm derivative)."""
+    a, gamma, d_out = _f64(a), _f64(gamma), _f64(d_out)
+    mu = a.mean(-1, keepdims=True)
+    inv = 1.0 / np.sqrt(((a - mu) ** 2).mean(-1, keepdims=True) + eps)
+    xh = (a - mu) * inv
+    dxh = d_out * gamma
+    da = inv * (dxh - dxh.mean(-1, keepdims=True) - xh * (dxh * xh).mean(-1, keepdims=True))
+    return da, (d_out * xh).sum(0), d_out.sum(0)
+
+
+def global_linear_bwd(q, k, v, d_g, eps: float = GLOBAL_EPS):
+    """Backward of the global branch G_i = phi(q_i)^T S / (phi(q_i)^T z + eps), S = sum_j
+    phi(k_j) v_j^T, z = sum_j phi(k_j) ("Gated Local-Global Graph Attention", Key
+    formulas), per head, by the chain rule: with num_i = phi(q_i)^T S and den_i the
+    denominator, d num_i = dG_i / den_i and d den_i = -(dG_i . G_i) / den_i; then
+    d phi(q_i) = S d num_i + z d den_i, dS = sum_i phi(q_i) d num_i^T, dz = sum_i phi(q_i) d den_i,
+    d phi(k_j) = dS v_j + dz, dv_j = dS^T phi(k_j), and dq = d phi(q) phi'(q), dk likewise."""
+    q, k, v, d_g = _f64(q), _f64(k), _f64(v), _f64(d_g)
+    pq, pk = phi(q), phi(k)
+    s = np.einsum("nhi,nhj->hij", pk, v)
+    z = pk.sum(0)
+    num = np.einsum("nhi,hij->nhj", pq, s)
+    den = np.einsum("nhi,hi->nh", pq, z) + eps
+    gg = num / den[..., None]
+    dnum = d_g / den[..., None]
+    dden = -(d_g * gg).sum(-1) / den
+    dpq = np.einsum("hij,nhj->nhi", s, dnum) + z[None] * dden[..., None]
+    ds = np.einsum("nhi,nhj->hij", pq, dnum)
+    dz = np.einsum("nhi,nh->hi", pq, dden)
+    dpk = np.einsum("hij,nhj->nhi", ds, v) + dz[None]
+    dv = np.einsum("hij,nhi->nhj", ds, pk)
+    return dict(d_q=dpq * phi_grad(q), d_k=dpk * phi_grad(k), d_v=dv, d_S=ds, d_z=dz)
+
+
+def gated_layer_backward(p: dict, g: Graph, heads: int, d_out, eps: float = GLOBAL_EPS, ln_eps: float = LN_EPS):
+    """First-order gradients of sum(out * d_out) for the gated local-global layer (the
+    forward of gated_layer): dX and the gradients of W_Q, W_K, W_V, W_o, w_g, b_g, gamma,
+    beta.  Chain: LayerNorm -> residual and W_o -> gate and combination -> local branch
+    (local_bwd_dot) and global branch (global_linear_bwd) -> projections."""
+    f = gated_layer(p, g, heads, eps)
+    x = _f64(p["x"])
+    n, d = x.shape
+    r = d // heads
+    d_pre, d_gamma, d_beta = layer_norm_bwd(f["pre"], p["gamma"], d_out, ln_eps)
+    dy = d_pre @ _f64(p["w_o"]).T
+    d_wo = f["y"].T @ d_pre
+    gv = f["gate"][:, None]
+    d_loc = gv * dy
+    d_glob = (1.0 - gv) * dy
+    d_gate = (dy * (f["local"] - f["glob"])).sum(-1)
+    d_t = d_gate * f["gate"] * (1.0 - f["gate"])
+    d_wg = x.T @ d_t
+    d_bg = d_t.sum()
+    loc = local_bwd_dot(f["q"], f["k"], f["v"], d_loc.reshape(n, heads, r), g, 1.0 / np.sqrt(r))
+    glb = global_linear_bwd(f["q"], f["k"], f["v"], d_glob.reshape(n, heads, r), eps)
+    dq = (loc["d_q"] + glb["d_q"]).reshape(n, d)
+    dk = (loc["d_k"] + glb["d_k"]).reshape(n, d)
+    dv = (loc["d_v"] + glb["d_v"]).reshape(n, d)
+    d_x = d_pre + np.outer(d_t, _f64(p["w_g"])) + dq @ _f64(p["w_q"]).T + dk @ _f64(p["w_k"]).T + \
+        dv @ _f64(p["w_v"]).T
+    return dict(d_x=d_x, d_w_q=x.T @ dq, d_w_k=x.T @ dk, d_w_v=x.T @ dv, d_w_o=d_wo, d_w_g=d_wg, d_b_g=d_bg,
+                d_gamma=d_gamma, d_beta=d_beta, d_pre=d_pre, d_y=dy, d_local=d_loc, d_glob=d_glob, d_gate=d_gate,
+                d_t=d_t, d_q=dq, d_k=dk, d_v=dv, fwd=f)
