@@ -240,6 +240,60 @@ int gga_gated_combine(int32_t n, int32_t d, const float *x, const float *w_g, fl
 int gga_add_layernorm(int32_t n, int32_t d, const float *x, const float *y, const float *gamma, const float *beta,
                       float eps, float *out, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of the gated local-global layer ("Gated Local-Global Graph
+ * Attention", Implementation notes item 2), first-order gradients of
+ * sum(out * d_out).  The local branch's gradient is gga_local_attn_bwd.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * c[m,n] += op(a) op(b): gga_linear accumulating into c instead of overwriting it
+ * (same shapes, layouts, workspace and determinism).  Used to add the projection
+ * gradients dQ W_Q^T, dK W_K^T, dV W_V^T into dX.
+ */
+int gga_linear_accumulate(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float *a,
+                          const float *b, float *c, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Backward of out = LayerNorm(x + y) over rows of width d (gga_add_layernorm):
+ *   d_pre[i,:] = rstd (g - mean(g) - xhat mean(g xhat)),  g = d_out gamma,
+ *   d_gamma = sum_i d_out xhat,  d_beta = sum_i d_out
+ * with xhat and rstd recomputed from x + y.  d_pre is the gradient of x + y (so of both
+ * x and y).  The sums over rows use a fixed two-level order (deterministic).  fp32.
+ */
+size_t gga_add_layernorm_bwd_workspace(int32_t n, int32_t d);
+int gga_add_layernorm_bwd(int32_t n, int32_t d, const float *x, const float *y, const float *gamma, float eps,
+                          const float *d_out, float *d_pre, float *d_gamma, float *d_beta, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the gate and combination (gga_gated_combine), with g_i recomputed:
+ *   d_l = g dY,  d_g = (1 - g) dY,  dt_i = g_i (1 - g_i) sum_c dY[i,c] (l[i,c] - g[i,c])
+ *   d_x_out = d_x_in + dt w_g^T   (d_x_out may alias d_x_in)
+ *   d_w_g = sum_i dt_i x_i,  d_b_g = sum_i dt_i   (fixed two-level order)
+ * x [n,d]; l, g_glob, d_y, d_l, d_g [n,width]; d_w_g [d]; d_b_g one float.
+ */
+size_t gga_gated_combine_bwd_workspace(int32_t n, int32_t d);
+int gga_gated_combine_bwd(int32_t n, int32_t d, const float *x, const float *w_g, float b_g, int32_t width,
+                          const float *l, const float *g_glob, const float *d_y, float *d_l, float *d_g,
+                          const float *d_x_in, float *d_x_out, float *d_w_g, float *d_b_g, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/*
+ * Backward of the global branch (gga_global_linear_fwd), per head, given its S and z:
+ *   num_i = phi(q_i)^T S, den_i = phi(q_i) . z + eps, G_i = num_i / den_i,
+ *   d num_i = dG_i / den_i, d den_i = -(dG_i . G_i) / den_i,
+ *   d phi(q_i) = S d num_i + z d den_i,  dS = sum_i phi(q_i) d num_i^T,  dz = sum_i phi(q_i) d den_i,
+ *   d phi(k_j) = dS v_j + dz,  d v_j = dS^T phi(k_j),  phi'(x) = 1 (x > 0) or e^x.
+ * The results are ADDED to d_q, d_k, d_v (fp32 [n,H,r]), so the local branch's
+ * gradients can be written there first.  Requires r <= 64.  dS, dz sums over nodes use
+ * a fixed range order (deterministic).
+ */
+size_t gga_global_linear_bwd_workspace(int32_t n, int32_t heads, int32_t r);
+int gga_global_linear_bwd(int32_t n, int32_t heads, int32_t r, const float *q, const float *k, const float *v,
+                          float eps, const float *s, const float *z, const float *d_g, float *d_q, float *d_k,
+                          float *d_v, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -275,10 +275,11 @@ def global_linear(q, k, v, eps: float = GLOBAL_EPS):
     Pinned by the dense O(N^2) kernelised form."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     pq, pk = phi(q), phi(k)
-    s = np.einsum("nhi,nhj->hij", pk, v)
+    # per-head products as batched matrix products over the head axis ([H, ., .] operands)
+    s = pk.transpose(1, 2, 0) @ v.transpose(1, 0, 2)  # S[h] = phi(K_h)^T V_h
     z = pk.sum(0)
-    num = np.einsum("nhi,hij->nhj", pq, s)
-    den = np.einsum("nhi,hi->nh", pq, z) + eps
+    num = (pq.transpose(1, 0, 2) @ s).transpose(1, 0, 2)  # num[i, h] = phi(q_ih)^T S[h]
+    den = (pq * z[None]).sum(-1) + eps
     return s, z, num / den[..., None]
 
 
@@ -317,12 +318,13 @@ def gated_layer(p: dict, g: Graph, heads: int, eps: float = GLOBAL_EPS, rows=Non
     v = (x @ _f64(p["w_v"])).reshape(n, heads, r)
     loc, lse = local_fwd_dot(q, k, v, g, 1.0 / np.sqrt(r), rows=rows)
     pk = phi(k)
-    s = np.einsum("nhi,nhj->hij", pk, v)
+    s = pk.transpose(1, 2, 0) @ v.transpose(1, 0, 2)  # S[h] = phi(K_h)^T V_h
     z = pk.sum(0)
     xr = x if rows is None else x[np.asarray(rows)]
     qr = q if rows is None else q[np.asarray(rows)]
     pq = phi(qr)
-    glob = np.einsum("nhi,hij->nhj", pq, s) / (np.einsum("nhi,hi->nh", pq, z) + eps)[..., None]
+    num = (pq.transpose(1, 0, 2) @ s).transpose(1, 0, 2)  # phi(q_i)^T S[h]
+    glob = num / ((pq * z[None]).sum(-1) + eps)[..., None]
     gv = gate(xr, p["w_g"], p["b_g"])
     y = combine(gv, loc.reshape(-1, d), glob.reshape(-1, d))
     pre = xr + y @ _f64(p["w_o"])
@@ -361,18 +363,21 @@ def global_linear_bwd(q, k, v, d_g, eps: float = GLOBAL_EPS):
     d phi(k_j) = dS v_j + dz, dv_j = dS^T phi(k_j), and dq = d phi(q) phi'(q), dk likewise."""
     q, k, v, d_g = _f64(q), _f64(k), _f64(v), _f64(d_g)
     pq, pk = phi(q), phi(k)
-    s = np.einsum("nhi,nhj->hij", pk, v)
+    # per-head products as batched matrix products over the head axis; t() moves the node
+    # axis behind the head axis ([N, H, r] -> [H, N, r]) and back
+    t = lambda a: a.transpose(1, 0, 2)  # noqa: E731
+    s = pk.transpose(1, 2, 0) @ t(v)  # S[h] = phi(K_h)^T V_h
     z = pk.sum(0)
-    num = np.einsum("nhi,hij->nhj", pq, s)
-    den = np.einsum("nhi,hi->nh", pq, z) + eps
+    num = t(t(pq) @ s)
+    den = (pq * z[None]).sum(-1) + eps
     gg = num / den[..., None]
     dnum = d_g / den[..., None]
     dden = -(d_g * gg).sum(-1) / den
-    dpq = np.einsum("hij,nhj->nhi", s, dnum) + z[None] * dden[..., None]
-    ds = np.einsum("nhi,nhj->hij", pq, dnum)
-    dz = np.einsum("nhi,nh->hi", pq, dden)
-    dpk = np.einsum("hij,nhj->nhi", ds, v) + dz[None]
-    dv = np.einsum("hij,nhi->nhj", ds, pk)
+    dpq = t(t(dnum) @ s.transpose(0, 2, 1)) + z[None] * dden[..., None]  # S dnum_i
+    ds = pq.transpose(1, 2, 0) @ t(dnum)  # sum_i phi(q_i) dnum_i^T
+    dz = (pq * dden[..., None]).sum(0)
+    dpk = t(t(v) @ ds.transpose(0, 2, 1)) + dz[None]  # dS v_j + dz
+    dv = t(t(pk) @ ds)  # dS^T phi(k_j)
     return dict(d_q=dpq * phi_grad(q), d_k=dpk * phi_grad(k), d_v=dv, d_S=ds, d_z=dz)
 
 

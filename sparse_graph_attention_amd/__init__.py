@@ -73,6 +73,13 @@ def _load() -> ctypes.CDLL:
         "gga_global_linear_fwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
         "gga_gated_combine": ([i32, i32, P, P, f32, i32, P, P, P, P, P], ctypes.c_int),
         "gga_add_layernorm": ([i32, i32, P, P, P, P, f32, P, P], ctypes.c_int),
+        "gga_linear_accumulate": ([i32, i32, i32, i32, i32, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_add_layernorm_bwd_workspace": ([i32, i32], sz),
+        "gga_add_layernorm_bwd": ([i32, i32, P, P, P, f32, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_gated_combine_bwd_workspace": ([i32, i32], sz),
+        "gga_gated_combine_bwd": ([i32, i32, P, P, f32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_global_linear_bwd_workspace": ([i32, i32, i32], sz),
+        "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -114,6 +121,14 @@ def _workspace(nbytes: int, device, ws=None):
             raise GGAError("workspace", GGA_EWORKSPACE)
         return ws
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _row_width(t: torch.Tensor) -> int:
+    """Elements per row of a node tensor [N, ...]."""
+    w = 1
+    for s in t.shape[1:]:
+        w *= int(s)
+    return w
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -305,7 +320,7 @@ def gga_global_linear_fwd(q, k, v, eps=1e-6, s_out=None, z_out=None, g_out=None,
 
 def gga_gated_combine(x, w_g, b_g: float, l, g, gate_out=None, y=None, stream=None):
     n, d = x.shape
-    width = l.numel() // max(n, 1)
+    width = _row_width(l)
     y = torch.empty(n, width, dtype=torch.float32, device=x.device) if y is None else y
     gate_out = torch.empty(n, dtype=torch.float32, device=x.device) if gate_out is None else gate_out
     _check("gga_gated_combine", lib.gga_gated_combine(n, d, _ptr(x), _ptr(w_g), float(b_g), width, _ptr(l), _ptr(g),
@@ -319,3 +334,62 @@ def gga_add_layernorm(x, y, gamma, beta, eps=1e-5, out=None, stream=None):
     _check("gga_add_layernorm", lib.gga_add_layernorm(n, d, _ptr(x), _ptr(y), _ptr(gamma), _ptr(beta), eps,
                                                       _ptr(out), _stream(stream)))
     return out
+
+
+# --------------------------------------------------------------------------- layer backward
+
+
+def gga_linear_accumulate(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, trans_a=False, trans_b=False, ws=None,
+                          stream=None):
+    m = a.shape[1] if trans_a else a.shape[0]
+    k = a.shape[0] if trans_a else a.shape[1]
+    n = b.shape[0] if trans_b else b.shape[1]
+    nb = lib.gga_linear_workspace(m, k, n)
+    ws = _workspace(nb, a.device, ws)
+    _check("gga_linear_accumulate", lib.gga_linear_accumulate(m, k, n, int(trans_a), int(trans_b), _ptr(a), _ptr(b),
+                                                              _ptr(out), _ptr(ws), nb, _stream(stream)))
+    return out
+
+
+def gga_add_layernorm_bwd(x, y, gamma, d_out, eps=1e-5, d_pre=None, d_gamma=None, d_beta=None, ws=None, stream=None):
+    n, d = x.shape
+    dev = x.device
+    d_pre = torch.empty_like(x) if d_pre is None else d_pre
+    d_gamma = torch.empty(d, dtype=torch.float32, device=dev) if d_gamma is None else d_gamma
+    d_beta = torch.empty(d, dtype=torch.float32, device=dev) if d_beta is None else d_beta
+    nb = lib.gga_add_layernorm_bwd_workspace(n, d)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_add_layernorm_bwd", lib.gga_add_layernorm_bwd(n, d, _ptr(x), _ptr(y), _ptr(gamma), eps, _ptr(d_out),
+                                                              _ptr(d_pre), _ptr(d_gamma), _ptr(d_beta), _ptr(ws), nb,
+                                                              _stream(stream)))
+    return d_pre, d_gamma, d_beta
+
+
+def gga_gated_combine_bwd(x, w_g, b_g: float, l, g, d_y, d_x_in, d_l=None, d_g=None, d_x_out=None, d_w_g=None,
+                          d_b_g=None, ws=None, stream=None):
+    n, d = x.shape
+    dev = x.device
+    width = _row_width(l)
+    d_l = torch.empty(n, width, dtype=torch.float32, device=dev) if d_l is None else d_l
+    d_g = torch.empty(n, width, dtype=torch.float32, device=dev) if d_g is None else d_g
+    d_x_out = torch.empty_like(x) if d_x_out is None else d_x_out
+    d_w_g = torch.empty(d, dtype=torch.float32, device=dev) if d_w_g is None else d_w_g
+    d_b_g = torch.empty(1, dtype=torch.float32, device=dev) if d_b_g is None else d_b_g
+    nb = lib.gga_gated_combine_bwd_workspace(n, d)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_gated_combine_bwd", lib.gga_gated_combine_bwd(n, d, _ptr(x), _ptr(w_g), float(b_g), width, _ptr(l),
+                                                              _ptr(g), _ptr(d_y), _ptr(d_l), _ptr(d_g), _ptr(d_x_in),
+                                                              _ptr(d_x_out), _ptr(d_w_g), _ptr(d_b_g), _ptr(ws), nb,
+                                                              _stream(stream)))
+    return d_l, d_g, d_x_out, d_w_g, d_b_g
+
+
+def gga_global_linear_bwd(q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None):
+    """Adds the global branch's gradients into d_q, d_k, d_v (all [n, H, r] fp32)."""
+    n, heads, r = q.shape
+    nb = lib.gga_global_linear_bwd_workspace(n, heads, r)
+    ws = _workspace(nb, q.device, ws)
+    _check("gga_global_linear_bwd", lib.gga_global_linear_bwd(n, heads, r, _ptr(q), _ptr(k), _ptr(v), eps, _ptr(s),
+                                                              _ptr(z), _ptr(d_g), _ptr(d_q), _ptr(d_k), _ptr(d_v),
+                                                              _ptr(ws), nb, _stream(stream)))
+    return d_q, d_k, d_v

@@ -1,4 +1,5 @@
-// Dense fp32 product on the matrix cores (v_mfma_f32_16x16x4_f32): c = op(a) op(b) (+ bias).
+// Dense fp32 product on the matrix cores (v_mfma_f32_16x16x4_f32): c = op(a) op(b) (+ bias),
+// or c += op(a) op(b).
 //
 // Workgroup tile 128 x BN (BN = 128, or 64 when n <= 64), eight wavefronts each owning
 // 64 x BN/4 (MFMA tiles of 16x16), K staged through LDS 16 at a time with double buffering.
@@ -23,6 +24,7 @@ struct GemmArgs {
     int32_t M, K, N, lda, ldb;
     int32_t trans_a, trans_b;
     int32_t kchunk;  // K range per split
+    int32_t accumulate;  // add into c instead of overwriting it
 };
 
 // Loads 4 consecutive floats of a row starting at column c0, zero beyond `lim` columns.
@@ -179,17 +181,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_mfma(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const int64_t row = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-                if (row < g.M) cbase[row * g.N + col] = acc[i][j][r] + bv;
+                if (row >= g.M) continue;
+                const float prev = (g.accumulate && gridDim.z == 1) ? cbase[row * g.N + col] : 0.f;
+                cbase[row * g.N + col] = prev + (acc[i][j][r] + bv);
             }
         }
     }
 }
 
-// c = sum over the splits of the partial products (in split order) + bias.  A workgroup of
+// c = (c if accumulating) + (sum over the splits of the partial products (in split order) + bias).  A workgroup of
 // 16 wavefronts owns 64 consecutive outputs: wavefront w adds splits w, w+16, ... and the
 // 16 running sums are then added in wavefront order.
 __global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ part, int splits, int64_t mn,
-                                                      int32_t N, const float* __restrict__ bias, float* __restrict__ c) {
+                                                      int32_t N, const float* __restrict__ bias, int accumulate,
+                                                      float* __restrict__ c) {
     __shared__ float sm[16][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t i = (int64_t)blockIdx.x * 64 + lane;
@@ -201,7 +206,8 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ 
     if (wave == 0 && i < mn) {
         float t = 0.f;
         for (int w = 0; w < 16; w++) t += sm[w][lane];
-        c[i] = t + (bias ? bias[i % N] : 0.f);
+        const float prev = accumulate ? c[i] : 0.f;
+        c[i] = prev + (t + (bias ? bias[i % N] : 0.f));
     }
 }
 
@@ -246,8 +252,10 @@ extern "C" size_t gga_linear_workspace(int32_t m, int32_t k, int32_t n) {
     return align_up((size_t)s.splits * m * n * sizeof(float), 256);
 }
 
-extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float* a,
-                          const float* b, const float* bias, float* c, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+int linear_impl(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float* a, const float* b,
+                const float* bias, float* c, int accumulate, void* ws, size_t ws_bytes, void* stream) {
     if (m < 0 || k < 0 || n < 0) return GGA_EINVAL;
     if (m == 0 || n == 0) return GGA_OK;
     if (!c || (k > 0 && (!a || !b))) return GGA_EINVAL;
@@ -268,6 +276,7 @@ extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int3
     g.trans_a = trans_a != 0;
     g.trans_b = trans_b != 0;
     g.kchunk = sp.kchunk;
+    g.accumulate = accumulate;
     const int bn = pick_bn(n);
     const int64_t gy = (m + BM - 1) / BM, gx = (n + bn - 1) / bn;
     if (gy > 65535) return GGA_ERANGE;
@@ -280,7 +289,20 @@ extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int3
     if (sp.splits > 1) {
         const int64_t mn = (int64_t)m * n;
         splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(static_cast<const float*>(ws), sp.splits, mn, n,
-                                                                bias, c);
+                                                                bias, accumulate, c);
     }
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float* a,
+                          const float* b, const float* bias, float* c, void* ws, size_t ws_bytes, void* stream) {
+    return linear_impl(m, k, n, trans_a, trans_b, a, b, bias, c, 0, ws, ws_bytes, stream);
+}
+
+extern "C" int gga_linear_accumulate(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b,
+                                     const float* a, const float* b, float* c, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    return linear_impl(m, k, n, trans_a, trans_b, a, b, nullptr, c, 1, ws, ws_bytes, stream);
 }

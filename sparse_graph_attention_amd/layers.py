@@ -15,8 +15,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, Topology, gga_add_layernorm, gga_gat_coef_bwd,
-               gga_gat_coef_fwd, gga_gated_combine, gga_global_linear_fwd, gga_linear, gga_local_attn_bwd,
+from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, Topology, gga_add_layernorm,
+               gga_add_layernorm_bwd, gga_gat_coef_bwd, gga_gat_coef_fwd, gga_gated_combine, gga_gated_combine_bwd,
+               gga_global_linear_bwd, gga_global_linear_fwd, gga_linear, gga_linear_accumulate, gga_local_attn_bwd,
                gga_local_attn_fwd, make_desc)
 
 
@@ -62,8 +63,34 @@ def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, 
     gate, y = gga_gated_combine(x, p["w_g"], p["b_g"], loc.view(n, d), glob.view(n, d))
     zo = gga_linear(y, p["w_o"])
     out = gga_add_layernorm(x, zo, p["gamma"], p["beta"], ln_eps)
-    return dict(q=q, k=k, v=v, local=loc.view(n, d), lse=lse, S=s, z=z, glob=glob.view(n, d), gate=gate, y=y,
-                out=out)
+    return dict(q=q, k=k, v=v, local=loc.view(n, d), local3=loc, lse=lse, S=s, z=z, glob=glob.view(n, d), gate=gate,
+                y=y, zo=zo, out=out, desc=desc)
 
 
-__all__ = ["gat_forward", "gat_backward", "gated_layer_forward", "GGA_BF16"]
+def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: torch.Tensor, eps: float = 1e-6,
+                         ln_eps: float = 1e-5):
+    """First-order gradients of sum(out * d_out) for every input and parameter of the gated
+    local-global layer, from the forward's intermediates.  topo must hold the CSR by source
+    (Topology(..., backward=True)); the forward must have run in fp32."""
+    x = p["x"]
+    n, d = x.shape
+    r = d // heads
+    d_pre, d_gamma, d_beta = gga_add_layernorm_bwd(x, fwd["zo"], p["gamma"], d_out, ln_eps)
+    d_y = gga_linear(d_pre, p["w_o"], trans_b=True)
+    d_wo = gga_linear(fwd["y"], d_pre, trans_a=True)
+    d_loc, d_glob, d_x, d_wg, d_bg = gga_gated_combine_bwd(x, p["w_g"], p["b_g"], fwd["local"], fwd["glob"], d_y,
+                                                           d_pre)
+    d_q, d_k, d_v = gga_local_attn_bwd(fwd["desc"], fwd["q"], fwd["k"], fwd["v"], fwd["local3"], fwd["lse"],
+                                       d_loc.view(n, heads, r), topo)
+    gga_global_linear_bwd(fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"], d_glob.view(n, heads, r), d_q, d_k, d_v,
+                          eps)
+    grads = dict(d_w_o=d_wo, d_w_g=d_wg, d_b_g=d_bg, d_gamma=d_gamma, d_beta=d_beta)
+    for name, g in (("q", d_q), ("k", d_k), ("v", d_v)):
+        g2 = g.view(n, d)
+        grads["d_w_" + name] = gga_linear(x, g2, trans_a=True)
+        gga_linear_accumulate(g2, p["w_" + name], d_x, trans_b=True)
+    grads["d_x"] = d_x
+    return grads
+
+
+__all__ = ["gat_forward", "gat_backward", "gated_layer_forward", "gated_layer_backward", "GGA_BF16"]
