@@ -338,34 +338,43 @@ def bench_layer(args, g, torch, synth):
     e = int(src.size)
     log(f"workload {w.name}: n={n} e={e}")
     p = synth.gated_layer_inputs(n, d=d)
+    d_out = synth.node_tensor(ident, 7, (n, d))
     pd = {k: (torch.from_numpy(np.ascontiguousarray(v)).to(dev) if isinstance(v, np.ndarray) else v)
           for k, v in p.items()}
-    topo, tt = per_topology(g, torch, n, torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev))
+    dod = torch.from_numpy(d_out).to(dev)
+    topo, tt = per_topology(g, torch, n, torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), True)
 
     def step(tm):
         _mark(tm, "f0")
-        layers.gated_layer_forward(pd, topo, heads)
+        f = layers.gated_layer_forward(pd, topo, heads)
         _mark(tm, "f1")
+        layers.gated_layer_backward(pd, f, topo, heads, dod)
+        _mark(tm, "b1")
 
     tm = Timer(torch, torch.cuda.current_stream())
     ms = tm.run(step, args.steps, args.warmup)
-    flops = 2.0 * n * d * d * 4 + 4.0 * n * heads * c * c  # Q, K, V, W_o; S and phi(Q) S
-    log(f"layer {ms:.3f} ms ({flops / ms / 1e9:.1f} TFLOP/s over the dense contractions); {tt}")
+    fms, bms = tm.phase_ms("f0", "f1"), tm.phase_ms("f1", "b1")
+    # dense contractions: 4 forward and 8 backward n x d x d products; the global branch's
+    # per-head r x r contractions (2 forward, 5 backward)
+    flops = 2.0 * n * d * d * 12 + 2.0 * n * heads * c * c * 7
+    log(f"step {ms:.3f} ms: fwd {fms:.3f} ms, bwd {bms:.3f} ms ({flops / ms / 1e9:.1f} TFLOP/s over the dense "
+        f"contractions); {tt}")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
 
         og = oracle.Graph(n, src, dst)
         t1 = time.perf_counter()
-        oracle.gated_layer(p, og, heads)
+        oracle.gated_layer_backward(p, og, heads, d_out)
         dt = time.perf_counter() - t1
         cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the whole layer forward, fp64 (numpy matmuls for the projections), {dt:.1f} s"}
+               "sample": f"the whole step (layer forward + first-order gradients), fp64 (numpy matmuls for the "
+                         f"dense products), {dt:.1f} s"}
     roof = roofline("mfma", flops / (ms * 1e-3) / 1e12, MFMA_F32_PEAK_TFLOPS, "TFLOP/s", None,
-                    kernel="whole layer (GEMMs dominate the flops)", flops_per_step=flops, launch_ms=ms)
+                    kernel="whole layer step (fp32 GEMMs dominate the flops)", flops_per_step=flops, launch_ms=ms)
     cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "d_model": d, "storage": "fp32",
-           "step": "layer forward", "seq_len": n}
-    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, tt)
+           "step": "layer forward + first-order gradients", "seq_len": n}
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
 
 
 def main() -> int:
