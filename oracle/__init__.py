@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.orc_edge_values.restype = None
         L.orc_edge_values_bwd.argtypes = [i32, i32, P, P, P, P]
         L.orc_edge_values_bwd.restype = None
+        L.orc_batch_edges.argtypes = [i32, P, P, P, P, P, P]
+        L.orc_batch_edges.restype = i64
         L.orc_threads.argtypes = []
         L.orc_threads.restype = ctypes.c_int
         _lib = L
@@ -100,6 +102,24 @@ def coo_to_csr(n: int, key, other):
     if rc != 0:
         raise ValueError("edge endpoint out of range")
     return row_ptr, col, eid
+
+
+def batch_edges(node_ptr, edge_ptr, src_local, dst_local):
+    """Packs a batch of B graphs into one block-diagonal graph over the packed node axis
+    (Gated Local-Global Graph Attention, Implementation notes note 1: batched X with one
+    sparse adjacency list per graph).  Graph b owns nodes node_ptr[b] .. node_ptr[b+1]-1
+    and COO entries edge_ptr[b] .. edge_ptr[b+1]-1, whose endpoints are local ids in
+    [0, n_b); they become local id + node_ptr[b].  An endpoint outside [0, n_b) is written
+    as -1 and counted.  Returns (src, dst, bad).  Pinned by the block-diagonal assembly of
+    per-graph adjacency matrices (library)."""
+    node_ptr, edge_ptr = _i32(node_ptr), _i32(edge_ptr)
+    src_local, dst_local = _i32(src_local), _i32(dst_local)
+    e = src_local.shape[0]
+    src = np.empty(e, np.int32)
+    dst = np.empty(e, np.int32)
+    bad = lib().orc_batch_edges(node_ptr.shape[0] - 1, _p(node_ptr), _p(edge_ptr), _p(src_local), _p(dst_local),
+                                _p(src), _p(dst))
+    return src, dst, int(bad)
 
 
 class Graph:
@@ -283,6 +303,27 @@ def global_linear(q, k, v, eps: float = GLOBAL_EPS):
     return s, z, num / den[..., None]
 
 
+def global_linear_seg(q, k, v, node_ptr, eps: float = GLOBAL_EPS):
+    """The global branch over a batch of graphs packed along the node axis: graph b owns
+    rows node_ptr[b] .. node_ptr[b+1]-1 and its statistics S_b, z_b sum over its own nodes
+    only, so G_i = phi(q_i)^T S_b / (phi(q_i)^T z_b + eps) for i in graph b (Key formulas,
+    per graph of the batch).  A graph with no node has S_b = 0, z_b = 0.
+    Returns S [B,H,r,r], z [B,H,r], G [N,H,r].  Pinned by the dense kernelised form with a
+    same-graph mask."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, hh, r = q.shape
+    ptr = np.asarray(node_ptr, np.int64)
+    b = ptr.shape[0] - 1
+    s = np.zeros((b, hh, r, r))
+    z = np.zeros((b, hh, r))
+    glob = np.zeros((n, hh, r))
+    for i in range(b):
+        lo, hi = int(ptr[i]), int(ptr[i + 1])
+        if hi > lo:
+            s[i], z[i], glob[lo:hi] = global_linear(q[lo:hi], k[lo:hi], v[lo:hi], eps)
+    return s, z, glob
+
+
 def gate(x, w_g, b_g):
     """g_i = sigmoid(x_i . w_g + b_g), one scalar per node (Key formulas)."""
     t = _f64(x) @ _f64(w_g) + float(b_g)
@@ -304,12 +345,16 @@ def layer_norm(a, gamma, beta, eps: float = LN_EPS):
     return _f64(gamma) * (a - mu) / np.sqrt(var + eps) + _f64(beta)
 
 
-def gated_layer(p: dict, g: Graph, heads: int, eps: float = GLOBAL_EPS, rows=None):
+def gated_layer(p: dict, g: Graph, heads: int, eps: float = GLOBAL_EPS, rows=None, node_ptr=None):
     """The full layer of "Gated Local-Global Graph Attention" (Implementation notes, item 2):
     Q,K,V = X W_{Q,K,V}; local masked softmax per head; phi = elu+1 global branch;
     g = sigmoid(X w_g + b_g); out = LayerNorm(X + W_o(g L + (1-g) G)).
     ``rows`` restricts the per-node outputs (the global statistics S, z always use all
-    nodes).  Returns a dict of every intermediate, in float64."""
+    nodes).  ``node_ptr`` [B+1] makes the input a batch of B graphs packed along the node
+    axis (Implementation notes, note 1: a batched X with one adjacency list per graph): the
+    graph g must then be the block-diagonal union (batch_edges) and S, z are per graph
+    (global_linear_seg), shape [B, H, r, r] and [B, H, r].  Returns a dict of every
+    intermediate, in float64."""
     x = _f64(p["x"])
     n, d = x.shape
     r = d // heads
@@ -317,14 +362,19 @@ def gated_layer(p: dict, g: Graph, heads: int, eps: float = GLOBAL_EPS, rows=Non
     k = (x @ _f64(p["w_k"])).reshape(n, heads, r)
     v = (x @ _f64(p["w_v"])).reshape(n, heads, r)
     loc, lse = local_fwd_dot(q, k, v, g, 1.0 / np.sqrt(r), rows=rows)
-    pk = phi(k)
-    s = pk.transpose(1, 2, 0) @ v.transpose(1, 0, 2)  # S[h] = phi(K_h)^T V_h
-    z = pk.sum(0)
     xr = x if rows is None else x[np.asarray(rows)]
-    qr = q if rows is None else q[np.asarray(rows)]
-    pq = phi(qr)
-    num = (pq.transpose(1, 0, 2) @ s).transpose(1, 0, 2)  # phi(q_i)^T S[h]
-    glob = num / ((pq * z[None]).sum(-1) + eps)[..., None]
+    if node_ptr is None:
+        pk = phi(k)
+        s = pk.transpose(1, 2, 0) @ v.transpose(1, 0, 2)  # S[h] = phi(K_h)^T V_h
+        z = pk.sum(0)
+        qr = q if rows is None else q[np.asarray(rows)]
+        pq = phi(qr)
+        num = (pq.transpose(1, 0, 2) @ s).transpose(1, 0, 2)  # phi(q_i)^T S[h]
+        glob = num / ((pq * z[None]).sum(-1) + eps)[..., None]
+    else:
+        s, z, glob = global_linear_seg(q, k, v, node_ptr, eps)
+        if rows is not None:
+            glob = glob[np.asarray(rows)]
     gv = gate(xr, p["w_g"], p["b_g"])
     y = combine(gv, loc.reshape(-1, d), glob.reshape(-1, d))
     pre = xr + y @ _f64(p["w_o"])
@@ -381,12 +431,35 @@ def global_linear_bwd(q, k, v, d_g, eps: float = GLOBAL_EPS):
     return dict(d_q=dpq * phi_grad(q), d_k=dpk * phi_grad(k), d_v=dv, d_S=ds, d_z=dz)
 
 
-def gated_layer_backward(p: dict, g: Graph, heads: int, d_out, eps: float = GLOBAL_EPS, ln_eps: float = LN_EPS):
+def global_linear_seg_bwd(q, k, v, d_g, node_ptr, eps: float = GLOBAL_EPS):
+    """Backward of global_linear_seg: global_linear_bwd on each graph of the batch
+    (graphs share no statistics, so their gradients are independent).  Returns d_q, d_k,
+    d_v [N,H,r] and d_S [B,H,r,r], d_z [B,H,r].  Pinned by autograd through the masked dense
+    kernelised form."""
+    q, k, v, d_g = _f64(q), _f64(k), _f64(v), _f64(d_g)
+    n, hh, r = q.shape
+    ptr = np.asarray(node_ptr, np.int64)
+    b = ptr.shape[0] - 1
+    out = dict(d_q=np.zeros((n, hh, r)), d_k=np.zeros((n, hh, r)), d_v=np.zeros((n, hh, r)),
+               d_S=np.zeros((b, hh, r, r)), d_z=np.zeros((b, hh, r)))
+    for i in range(b):
+        lo, hi = int(ptr[i]), int(ptr[i + 1])
+        if hi > lo:
+            res = global_linear_bwd(q[lo:hi], k[lo:hi], v[lo:hi], d_g[lo:hi], eps)
+            for key in ("d_q", "d_k", "d_v"):
+                out[key][lo:hi] = res[key]
+            out["d_S"][i], out["d_z"][i] = res["d_S"], res["d_z"]
+    return out
+
+
+def gated_layer_backward(p: dict, g: Graph, heads: int, d_out, eps: float = GLOBAL_EPS, ln_eps: float = LN_EPS,
+                         node_ptr=None):
     """First-order gradients of sum(out * d_out) for the gated local-global layer (the
     forward of gated_layer): dX and the gradients of W_Q, W_K, W_V, W_o, w_g, b_g, gamma,
     beta.  Chain: LayerNorm -> residual and W_o -> gate and combination -> local branch
-    (local_bwd_dot) and global branch (global_linear_bwd) -> projections."""
-    f = gated_layer(p, g, heads, eps)
+    (local_bwd_dot) and global branch (global_linear_bwd, per graph with node_ptr) ->
+    projections."""
+    f = gated_layer(p, g, heads, eps, node_ptr=node_ptr)
     x = _f64(p["x"])
     n, d = x.shape
     r = d // heads
@@ -401,7 +474,10 @@ def gated_layer_backward(p: dict, g: Graph, heads: int, d_out, eps: float = GLOB
     d_wg = x.T @ d_t
     d_bg = d_t.sum()
     loc = local_bwd_dot(f["q"], f["k"], f["v"], d_loc.reshape(n, heads, r), g, 1.0 / np.sqrt(r))
-    glb = global_linear_bwd(f["q"], f["k"], f["v"], d_glob.reshape(n, heads, r), eps)
+    if node_ptr is None:
+        glb = global_linear_bwd(f["q"], f["k"], f["v"], d_glob.reshape(n, heads, r), eps)
+    else:
+        glb = global_linear_seg_bwd(f["q"], f["k"], f["v"], d_glob.reshape(n, heads, r), node_ptr, eps)
     dq = (loc["d_q"] + glb["d_q"]).reshape(n, d)
     dk = (loc["d_k"] + glb["d_k"]).reshape(n, d)
     dv = (loc["d_v"] + glb["d_v"]).reshape(n, d)

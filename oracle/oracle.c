@@ -291,6 +291,28 @@ void orc_edge_values_bwd(int32_t n, int32_t w, const int32_t *row_ptr, const int
     }
 }
 
+/*
+ * A batch of graphs packed into one block-diagonal graph ("Gated Local-Global Graph
+ * Attention", Implementation notes note 1: batched X with one adjacency list per graph).
+ * Graph b owns nodes node_ptr[b] .. node_ptr[b+1]-1 and COO entries edge_ptr[b] ..
+ * edge_ptr[b+1]-1 with local endpoint ids; each becomes id + node_ptr[b], or -1 when the
+ * id is outside [0, n_b).  Returns the number of such endpoints.
+ */
+int64_t orc_batch_edges(int32_t b, const int32_t *node_ptr, const int32_t *edge_ptr, const int32_t *src_local,
+                        const int32_t *dst_local, int32_t *src, int32_t *dst) {
+    int64_t bad = 0;
+    for (int32_t g = 0; g < b; g++) {
+        const int32_t nb = node_ptr[g + 1] - node_ptr[g];
+        for (int64_t i = edge_ptr[g]; i < edge_ptr[g + 1]; i++) {
+            const int32_t s = src_local[i], d = dst_local[i];
+            src[i] = (s >= 0 && s < nb) ? s + node_ptr[g] : -1;
+            dst[i] = (d >= 0 && d < nb) ? d + node_ptr[g] : -1;
+            bad += (src[i] < 0) + (dst[i] < 0);
+        }
+    }
+    return bad;
+}
+
 int orc_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);

@@ -175,6 +175,7 @@ class Workload:
     score: str  # "dot" or "additive"
     fin: int = 0  # GAT input width
     d_model: int = 0  # gated layer model width
+    batch: int = 1  # graphs packed along the node axis (n nodes in all)
 
 
 WORKLOADS = {
@@ -183,6 +184,7 @@ WORKLOADS = {
     3: Workload(3, "dot-uniform16-n1m-h8-r64-bf16", 1 << 20, 8, 64, "bf16", "dot"),
     4: Workload(4, "gated-layer-n262k-d256-h4", 1 << 18, 4, 64, "f32", "dot", d_model=256),
     5: Workload(5, "dot-zipf1.8-n2m-h8-c32-bf16", 1 << 21, 8, 32, "bf16", "dot"),
+    6: Workload(6, "gated-layer-batch64-n4096-d256-h4", 1 << 18, 4, 64, "f32", "dot", d_model=256, batch=64),
 }
 
 
@@ -203,6 +205,34 @@ def workload_graph(ident: int, n: int | None = None):
     if ident == 5:
         return power_law(n, 31.0, 0.8, 50_000, rng)
     raise KeyError(ident)
+
+
+def batch_of_graphs(sizes, degree: int, rng: np.random.Generator):
+    """A batch of graphs, one adjacency list each: graph b has sizes[b] nodes, degree * n_b
+    uniform (src, dst) pairs over its own nodes (duplicates allowed) plus one self-loop per
+    node, shuffled within the graph.  Returns node_ptr [B+1], edge_ptr [B+1] and the local
+    COO lists of all graphs, concatenated (int32)."""
+    sizes = [int(x) for x in sizes]
+    node_ptr = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    srcs, dsts, counts = [], [], []
+    for nb in sizes:
+        s, d = uniform_pairs(nb, degree * nb, rng) if nb > 0 else (np.zeros(0, np.int32), np.zeros(0, np.int32))
+        srcs.append(s)
+        dsts.append(d)
+        counts.append(s.shape[0])
+    edge_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return node_ptr, edge_ptr, np.concatenate(srcs).astype(np.int32), np.concatenate(dsts).astype(np.int32)
+
+
+def workload_batch(ident: int):
+    """The per-graph COO lists of a batched workload (equal graph sizes n / batch)."""
+    w = WORKLOADS[ident]
+    return batch_of_graphs([w.n // w.batch] * w.batch, 32, _rng(ident, TOPOLOGY))
+
+
+def ragged_batch(seed: int, sizes=(1, 0, 17, 300, 4096, 2, 1000, 0, 2500, 63)):
+    """Test batch with graphs of very different sizes, including empty ones."""
+    return batch_of_graphs(sizes, 8, _rng(9200, seed))
 
 
 def node_tensor(ident: int, which: int, shape, stream: int = NODES, std: float = 1.0) -> np.ndarray:
