@@ -294,6 +294,53 @@ int gga_global_linear_bwd(int32_t n, int32_t heads, int32_t r, const float *q, c
                           float eps, const float *s, const float *z, const float *d_g, float *d_q, float *d_k,
                           float *d_v, void *ws, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Batches of graphs ("Gated Local-Global Graph Attention", Implementation notes
+ * note 1: a batched node input with one sparse adjacency list per graph).  The
+ * graphs are packed along the node axis: graph b owns node rows node_ptr[b] ..
+ * node_ptr[b+1]-1 (node_ptr int32 [batch+1], device, node_ptr[0] = 0,
+ * non-decreasing, node_ptr[batch] = n; graphs may be empty).  The local branch
+ * needs nothing new: on the block-diagonal edge list below, every softmax already
+ * stays inside its graph.  The global branch's statistics become per graph.
+ * node_ptr and edge_ptr are not checked on the host (they are device arrays); a
+ * malformed one gives unspecified values but no access outside the buffers.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Pack per-graph COO lists into one block-diagonal COO list over the packed node
+ * axis: entries edge_ptr[b] .. edge_ptr[b+1]-1 (edge_ptr int32 [batch+1], device,
+ * edge_ptr[batch] = e) belong to graph b and hold local ids in [0, n_b); they
+ * become id + node_ptr[b].  An id outside [0, n_b) (or an entry outside every
+ * graph's range) is written as -1 and counted in *d_bad (cleared first).  COO
+ * order is kept.  src_local, dst_local, src, dst int32 [e].
+ */
+int gga_batch_edges(int32_t batch, const int32_t *node_ptr, const int32_t *edge_ptr, int64_t e,
+                    const int32_t *src_local, const int32_t *dst_local, int32_t *src, int32_t *dst, int32_t *d_bad,
+                    void *stream);
+
+/*
+ * Global branch per graph of a batch (gga_global_linear_fwd with the sums over j
+ * taken over the rows of i's graph):
+ *   S[b,h] = sum_{j in b} phi(k_j) v_j^T   fp32 [batch,H,r,r]
+ *   z[b,h] = sum_{j in b} phi(k_j)         fp32 [batch,H,r]
+ *   g[i,h,:] = phi(q_i)^T S[b,h] / (phi(q_i) . z[b,h] + eps)   for i in graph b.
+ * An empty graph has S = 0, z = 0.  Deterministic.  s_out and z_out may be NULL.
+ */
+size_t gga_global_linear_batch_workspace(int32_t n, int32_t batch, int32_t heads, int32_t r);
+int gga_global_linear_batch_fwd(int32_t n, int32_t batch, const int32_t *node_ptr, int32_t heads, int32_t r,
+                                const float *q, const float *k, const float *v, float eps, float *s_out, float *z_out,
+                                float *g_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Its backward (gga_global_linear_bwd per graph, with s [batch,H,r,r] and
+ * z [batch,H,r] from the forward): adds the gradients into d_q, d_k, d_v.
+ * Requires r <= 64.  Workspace: gga_global_linear_batch_workspace.
+ */
+int gga_global_linear_batch_bwd(int32_t n, int32_t batch, const int32_t *node_ptr, int32_t heads, int32_t r,
+                                const float *q, const float *k, const float *v, float eps, const float *s,
+                                const float *z, const float *d_g, float *d_q, float *d_k, float *d_v, void *ws,
+                                size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,11 @@ def _load() -> ctypes.CDLL:
         "gga_gated_combine_bwd": ([i32, i32, P, P, f32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_global_linear_bwd_workspace": ([i32, i32, i32], sz),
         "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_batch_edges": ([i32, P, P, i64, P, P, P, P, P, P], ctypes.c_int),
+        "gga_global_linear_batch_workspace": ([i32, i32, i32, i32], sz),
+        "gga_global_linear_batch_fwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_global_linear_batch_bwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P],
+                                        ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -392,4 +397,51 @@ def gga_global_linear_bwd(q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, 
     _check("gga_global_linear_bwd", lib.gga_global_linear_bwd(n, heads, r, _ptr(q), _ptr(k), _ptr(v), eps, _ptr(s),
                                                               _ptr(z), _ptr(d_g), _ptr(d_q), _ptr(d_k), _ptr(d_v),
                                                               _ptr(ws), nb, _stream(stream)))
+    return d_q, d_k, d_v
+
+
+# --------------------------------------------------------------------------- batches of graphs
+
+
+def gga_batch_edges(node_ptr: torch.Tensor, edge_ptr: torch.Tensor, src_local: torch.Tensor, dst_local: torch.Tensor,
+                    src=None, dst=None, d_bad=None, stream=None):
+    """Packs per-graph local COO lists into the block-diagonal list; returns (src, dst, d_bad)."""
+    batch = node_ptr.numel() - 1
+    e = src_local.numel()
+    dev = src_local.device
+    src = torch.empty(e, dtype=torch.int32, device=dev) if src is None else src
+    dst = torch.empty(e, dtype=torch.int32, device=dev) if dst is None else dst
+    d_bad = torch.empty(1, dtype=torch.int32, device=dev) if d_bad is None else d_bad
+    _check("gga_batch_edges", lib.gga_batch_edges(batch, _ptr(node_ptr), _ptr(edge_ptr), e, _ptr(src_local),
+                                                  _ptr(dst_local), _ptr(src), _ptr(dst), _ptr(d_bad),
+                                                  _stream(stream)))
+    return src, dst, d_bad
+
+
+def gga_global_linear_batch_fwd(node_ptr, q, k, v, eps=1e-6, s_out=None, z_out=None, g_out=None, ws=None,
+                                stream=None):
+    n, heads, r = q.shape
+    batch = node_ptr.numel() - 1
+    dev = q.device
+    s_out = torch.empty(batch, heads, r, r, dtype=torch.float32, device=dev) if s_out is None else s_out
+    z_out = torch.empty(batch, heads, r, dtype=torch.float32, device=dev) if z_out is None else z_out
+    g_out = torch.empty(n, heads, r, dtype=torch.float32, device=dev) if g_out is None else g_out
+    nb = lib.gga_global_linear_batch_workspace(n, batch, heads, r)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_global_linear_batch_fwd",
+           lib.gga_global_linear_batch_fwd(n, batch, _ptr(node_ptr), heads, r, _ptr(q), _ptr(k), _ptr(v), eps,
+                                           _ptr(s_out), _ptr(z_out), _ptr(g_out), _ptr(ws), nb, _stream(stream)))
+    return s_out, z_out, g_out
+
+
+def gga_global_linear_batch_bwd(node_ptr, q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None):
+    """Adds the per-graph global branch's gradients into d_q, d_k, d_v."""
+    n, heads, r = q.shape
+    batch = node_ptr.numel() - 1
+    nb = lib.gga_global_linear_batch_workspace(n, batch, heads, r)
+    ws = _workspace(nb, q.device, ws)
+    _check("gga_global_linear_batch_bwd",
+           lib.gga_global_linear_batch_bwd(n, batch, _ptr(node_ptr), heads, r, _ptr(q), _ptr(k), _ptr(v), eps,
+                                           _ptr(s), _ptr(z), _ptr(d_g), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(ws),
+                                           nb, _stream(stream)))
     return d_q, d_k, d_v

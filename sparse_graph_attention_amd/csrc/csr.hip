@@ -145,6 +145,37 @@ __global__ void gather_col(const int32_t* __restrict__ other, const int32_t* __r
         col[p] = other[eid[p]];
 }
 
+// Packs per-graph local COO ids into the block-diagonal list over the packed node axis.
+// Entry i belongs to the graph b with edge_ptr[b] <= i < edge_ptr[b+1] (binary search).
+__global__ void batch_edges_kernel(int32_t batch, const int32_t* __restrict__ node_ptr,
+                                   const int32_t* __restrict__ edge_ptr, int64_t e, const int32_t* __restrict__ sl,
+                                   const int32_t* __restrict__ dl, int32_t* __restrict__ src, int32_t* __restrict__ dst,
+                                   int32_t* __restrict__ bad) {
+    int local = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < e; i += (int64_t)gridDim.x * blockDim.x) {
+        int32_t lo = 0, hi = batch + 1;  // first index with edge_ptr > i
+        while (lo < hi) {
+            const int32_t mid = (lo + hi) >> 1;
+            if ((int64_t)edge_ptr[mid] <= i)
+                lo = mid + 1;
+            else
+                hi = mid;
+        }
+        const int32_t b = lo - 1;
+        int32_t s = -1, d = -1;
+        if (b >= 0 && b < batch) {
+            const int32_t base = node_ptr[b], nb = node_ptr[b + 1] - base;
+            const int32_t a = sl[i], c = dl[i];
+            if (a >= 0 && a < nb) s = a + base;
+            if (c >= 0 && c < nb) d = c + base;
+        }
+        src[i] = s;
+        dst[i] = d;
+        local += (s < 0) + (d < 0);
+    }
+    if (local) atomicAdd(bad, local);
+}
+
 int key_bits(int32_t n) {
     if (n <= 1) return 0;
     uint32_t m = (uint32_t)(n - 1);
@@ -240,5 +271,18 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
     }
     if (n > 0) row_ptr_from_sorted<<<grid_for(e + 1), 256, 0, s>>>(kbuf[last & 1], e, n, row_ptr);
     gather_col<<<grid_for(e), 256, 0, s>>>(other, eid, e, col);
+    return launch_status();
+}
+
+extern "C" int gga_batch_edges(int32_t batch, const int32_t* node_ptr, const int32_t* edge_ptr, int64_t e,
+                               const int32_t* src_local, const int32_t* dst_local, int32_t* src, int32_t* dst,
+                               int32_t* d_bad, void* stream) {
+    if (batch < 1 || e < 0) return GGA_EINVAL;
+    if (e >= (int64_t)INT32_MAX) return GGA_ERANGE;
+    if (!node_ptr || !edge_ptr || !d_bad || (e > 0 && (!src_local || !dst_local || !src || !dst))) return GGA_EINVAL;
+    hipStream_t s = as_stream(stream);
+    fill_i32(d_bad, 1, 0, s);
+    if (e > 0) batch_edges_kernel<<<grid_for(e), 256, 0, s>>>(batch, node_ptr, edge_ptr, e, src_local, dst_local, src,
+                                                              dst, d_bad);
     return launch_status();
 }

@@ -17,8 +17,9 @@ import torch
 
 from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, Topology, gga_add_layernorm,
                gga_add_layernorm_bwd, gga_gat_coef_bwd, gga_gat_coef_fwd, gga_gated_combine, gga_gated_combine_bwd,
-               gga_global_linear_bwd, gga_global_linear_fwd, gga_linear, gga_linear_accumulate, gga_local_attn_bwd,
-               gga_local_attn_fwd, make_desc)
+               gga_global_linear_batch_bwd, gga_global_linear_batch_fwd, gga_global_linear_bwd,
+               gga_global_linear_fwd, gga_linear, gga_linear_accumulate, gga_local_attn_bwd, gga_local_attn_fwd,
+               make_desc)
 
 
 def gat_forward(x: torch.Tensor, w: torch.Tensor, a_s: torch.Tensor, a_t: torch.Tensor, topo: Topology,
@@ -49,8 +50,11 @@ def gat_backward(x, w, a_s, a_t, d_out: torch.Tensor, fwd: dict, topo: Topology)
 
 
 def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, ln_eps: float = 1e-5,
-                        dtype: int = GGA_F32):
-    """p: x [N,d], w_q, w_k, w_v, w_o [d,d], w_g [d], b_g (float), gamma, beta [d]."""
+                        dtype: int = GGA_F32, node_ptr: torch.Tensor | None = None):
+    """p: x [N,d], w_q, w_k, w_v, w_o [d,d], w_g [d], b_g (float), gamma, beta [d].
+    node_ptr (int32 [B+1], device): the rows are a batch of B graphs packed along the node
+    axis, topo their block-diagonal union (gga_batch_edges); the global statistics are
+    then per graph."""
     x = p["x"]
     n, d = x.shape
     r = d // heads
@@ -59,7 +63,10 @@ def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, 
     v = gga_linear(x, p["w_v"]).view(n, heads, r)
     desc = make_desc(n, topo.e, heads, r, GGA_SCORE_DOT, dtype, r ** -0.5)
     loc, lse = gga_local_attn_fwd(desc, q, k, v, topo.row_ptr, topo.col, topo.plan)
-    s, z, glob = gga_global_linear_fwd(q, k, v, eps)
+    if node_ptr is None:
+        s, z, glob = gga_global_linear_fwd(q, k, v, eps)
+    else:
+        s, z, glob = gga_global_linear_batch_fwd(node_ptr, q, k, v, eps)
     gate, y = gga_gated_combine(x, p["w_g"], p["b_g"], loc.view(n, d), glob.view(n, d))
     zo = gga_linear(y, p["w_o"])
     out = gga_add_layernorm(x, zo, p["gamma"], p["beta"], ln_eps)
@@ -68,7 +75,7 @@ def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, 
 
 
 def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: torch.Tensor, eps: float = 1e-6,
-                         ln_eps: float = 1e-5):
+                         ln_eps: float = 1e-5, node_ptr: torch.Tensor | None = None):
     """First-order gradients of sum(out * d_out) for every input and parameter of the gated
     local-global layer, from the forward's intermediates.  topo must hold the CSR by source
     (Topology(..., backward=True)); the forward must have run in fp32."""
@@ -82,8 +89,12 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
                                                            d_pre)
     d_q, d_k, d_v = gga_local_attn_bwd(fwd["desc"], fwd["q"], fwd["k"], fwd["v"], fwd["local3"], fwd["lse"],
                                        d_loc.view(n, heads, r), topo)
-    gga_global_linear_bwd(fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"], d_glob.view(n, heads, r), d_q, d_k, d_v,
-                          eps)
+    if node_ptr is None:
+        gga_global_linear_bwd(fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"], d_glob.view(n, heads, r), d_q, d_k,
+                              d_v, eps)
+    else:
+        gga_global_linear_batch_bwd(node_ptr, fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"],
+                                    d_glob.view(n, heads, r), d_q, d_k, d_v, eps)
     grads = dict(d_w_o=d_wo, d_w_g=d_wg, d_b_g=d_bg, d_gamma=d_gamma, d_beta=d_beta)
     for name, g in (("q", d_q), ("k", d_k), ("v", d_v)):
         g2 = g.view(n, d)

@@ -3,6 +3,7 @@
 import numpy as np
 import torch
 
+import oracle
 import synth
 
 TOL = {"f32": dict(rtol=1e-4, atol=1e-5), "bf16": dict(rtol=2e-2, atol=1e-5)}
@@ -56,3 +57,33 @@ def assert_close(got, want, dtype: str, what: str, atol=None, rtol=None):
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; max abs err "
                            f"{err[finite].max():.3e}")
     return float(err[finite].max()) if finite.any() else 0.0
+
+
+def global_term_scales(q, k, v, d_g, eps, node_ptr=None):
+    """Per element, the sum of the magnitudes of the terms each gradient of the global branch
+    adds (S and dS taken as sums of |terms| over the nodes, since their own rounding error
+    scales with those): an fp32 evaluation is off by at most a small multiple of 2^-24 times
+    this, also where the terms cancel (one node: dq is only eps-sized)."""
+    q, k, v, d_g = (np.asarray(a, np.float64) for a in (q, k, v, d_g))
+    if node_ptr is not None:  # per graph of a batch
+        out = {nm: np.zeros(q.shape) for nm in ("d_q", "d_k", "d_v")}
+        for b in range(len(node_ptr) - 1):
+            lo, hi = int(node_ptr[b]), int(node_ptr[b + 1])
+            if hi > lo:
+                one = global_term_scales(q[lo:hi], k[lo:hi], v[lo:hi], d_g[lo:hi], eps)
+                for nm in out:
+                    out[nm][lo:hi] = one[nm]
+        return out
+    t = lambda a: a.transpose(1, 0, 2)  # noqa: E731
+    s, z, gg = oracle.global_linear(q, k, v, eps)
+    pq, pk = oracle.phi(q), oracle.phi(k)
+    s_abs = pk.transpose(1, 2, 0) @ t(np.abs(v))
+    den = (pq * z[None]).sum(-1) + eps
+    a_num = np.abs(d_g) / den[..., None]
+    a_den = (np.abs(d_g) * np.abs(gg)).sum(-1) / den
+    tq = (t(t(a_num) @ s_abs.transpose(0, 2, 1)) + z[None] * a_den[..., None]) * oracle.phi_grad(q)
+    ds_abs = pq.transpose(1, 2, 0) @ t(a_num)
+    dz_abs = (pq * a_den[..., None]).sum(0)
+    tk = (t(t(np.abs(v)) @ ds_abs.transpose(0, 2, 1)) + dz_abs[None]) * oracle.phi_grad(k)
+    tv = t(t(pk) @ ds_abs)
+    return dict(d_q=tq, d_k=tk, d_v=tv)

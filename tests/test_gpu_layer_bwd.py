@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import assert_close, i32
+from gpu_util import assert_close, global_term_scales, i32
 
 pytestmark = pytest.mark.gpu
 
@@ -85,27 +85,6 @@ def test_gated_combine_bwd_in_place(g):
     assert torch.equal(buf, ref)
 
 
-def _global_term_scales(q, k, v, d_g, eps):
-    """Per element, the sum of the magnitudes of the terms each gradient of the global branch
-    adds (S and dS taken as sums of |terms| over the nodes, since their own rounding error
-    scales with those): an fp32 evaluation is off by at most a small multiple of 2^-24 times
-    this, also where the terms cancel (one node: dq is only eps-sized)."""
-    t = lambda a: a.transpose(1, 0, 2)  # noqa: E731
-    q, k, v, d_g = (np.asarray(a, np.float64) for a in (q, k, v, d_g))
-    s, z, gg = oracle.global_linear(q, k, v, eps)
-    pq, pk = oracle.phi(q), oracle.phi(k)
-    s_abs = pk.transpose(1, 2, 0) @ t(np.abs(v))
-    den = (pq * z[None]).sum(-1) + eps
-    a_num = np.abs(d_g) / den[..., None]
-    a_den = (np.abs(d_g) * np.abs(gg)).sum(-1) / den
-    tq = (t(t(a_num) @ s_abs.transpose(0, 2, 1)) + z[None] * a_den[..., None]) * oracle.phi_grad(q)
-    ds_abs = pq.transpose(1, 2, 0) @ t(a_num)
-    dz_abs = (pq * a_den[..., None]).sum(0)
-    tk = (t(t(np.abs(v)) @ ds_abs.transpose(0, 2, 1)) + dz_abs[None]) * oracle.phi_grad(k)
-    tv = t(t(pk) @ ds_abs)
-    return dict(d_q=tq, d_k=tk, d_v=tv)
-
-
 @pytest.mark.parametrize("n,heads,r", [(1000, 4, 64), (997, 2, 48), (500, 8, 32), (77, 3, 16), (1, 1, 64),
                                        (600, 2, 24), (40, 5, 8), (300, 1, 64 - 1)])
 def test_global_linear_bwd(g, n, heads, r):
@@ -114,32 +93,22 @@ def test_global_linear_bwd(g, n, heads, r):
     print(f"global bwd n={n} H={heads} r={r}", flush=True)
     ref = oracle.global_linear_bwd(q, k, v, d_g, 1e-6)
     names = ("d_q", "d_k", "d_v")
-    # the kernels add into what is there: start from values of the gradients' own size, so
-    # that rounding the sum does not swamp the comparison
-    base = [_rand((n, heads, r), 24 + i, float(np.sqrt(np.mean(ref[nm] ** 2)))) for i, nm in enumerate(names)]
-    qd, kd, vd = _t(q), _t(k), _t(v)
+    qd, kd, vd, gd = _t(q), _t(k), _t(v), _t(d_g)
     s, z, _ = g.gga_global_linear_fwd(qd, kd, vd, 1e-6)
-    dq, dk, dv = (_t(b) for b in base)
-    g.gga_global_linear_bwd(qd, kd, vd, s, z, _t(d_g), dq, dk, dv, 1e-6)
+    grads = [torch.zeros(n, heads, r, device="cuda") for _ in names]
+    g.gga_global_linear_bwd(qd, kd, vd, s, z, gd, *grads, 1e-6)
+    # the kernels add into what is there: from a nonzero start the result is that start plus
+    # the same contribution (the addition may be fused with the last product, so the two
+    # differ by at most a rounding of each)
+    base = [_t(_rand((n, heads, r), 24 + i)) for i in range(3)]
+    acc = [b.clone() for b in base]
+    g.gga_global_linear_bwd(qd, kd, vd, s, z, gd, *acc, 1e-6)
     torch.cuda.synchronize()
-    scale = _global_term_scales(q, k, v, d_g, 1e-6)
-    for got, b, nm in zip((dq, dk, dv), base, names):
-        assert_close(got.cpu().numpy() - b, ref[nm], "f32", nm, atol=1e-5 * scale[nm])
-
-
-def test_global_linear_bwd_accumulates_exactly(g):
-    """With zero initial gradients the result equals a second call on the first's output
-    minus the first: the kernels add exactly once."""
-    n, heads, r = 400, 2, 32
-    q, k, v, d_g = (_t(_rand((n, heads, r), 30 + i)) for i in range(4))
-    s, z, _ = g.gga_global_linear_fwd(q, k, v, 1e-6)
-    z0 = [torch.zeros(n, heads, r, device="cuda") for _ in range(3)]
-    g.gga_global_linear_bwd(q, k, v, s, z, d_g, *z0, 1e-6)
-    again = [t.clone() for t in z0]
-    g.gga_global_linear_bwd(q, k, v, s, z, d_g, *again, 1e-6)
-    torch.cuda.synchronize()
-    for a, b in zip(z0, again):
-        assert torch.equal(b, a + a)
+    scale = global_term_scales(q, k, v, d_g, 1e-6)
+    for got, b, a, nm in zip(grads, base, acc, names):
+        assert_close(got.cpu().numpy(), ref[nm], "f32", nm, atol=1e-5 * scale[nm])
+        lim = 2.0 ** -23 * (b.abs() + 2 * got.abs())
+        assert bool(((a - (b + got)).abs() <= lim).all()), nm
 
 
 @pytest.mark.parametrize("m,k,n,ta,tb", [(300, 200, 150, False, True), (256, 5000, 64, True, False),
