@@ -14,7 +14,9 @@ Other workloads (``--workload``), each printed as its own line when asked for:
   2  170k-node power-law GAT layer, Fin = 128 -> 8 heads x 8, fp32: a step is the
      layer forward + its first-order gradients (dX, dW, da_s, da_t)
   4  262k-node gated local-global layer, d = 256, 4 heads of 64, fp32: a step is the
-     layer forward
+     layer forward + the gradients of every input and parameter
+  6  the same layer over a batch of 64 graphs of 4096 nodes packed along the node axis
+     (block-diagonal edges, per-graph global statistics): forward + gradients
   1  tiny 1024-node dot-product graph, H = 1, r = 16, fp32: forward
 
 Prints one JSON line: throughput in GEdges/s, the roofline of the dominant kernel call
@@ -327,28 +329,41 @@ def bench_gat(args, g, torch, synth):
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
 
 
-def bench_layer(args, g, torch, synth):
+def bench_layer(args, g, torch, synth, ident):
+    """The gated local-global layer, forward + gradients of every input and parameter; for a
+    batched workload the graphs are packed along the node axis (block-diagonal edges,
+    per-graph global statistics)."""
     from sparse_graph_attention_amd import layers
 
-    ident = 4
     w = synth.WORKLOADS[ident]
     n, heads, c, d = w.n, w.heads, w.head_dim, w.d_model
     dev = torch.device("cuda:0")
-    src, dst = synth.workload_graph(ident)
-    e = int(src.size)
-    log(f"workload {w.name}: n={n} e={e}")
-    p = synth.gated_layer_inputs(n, d=d)
+    node_ptr = node_ptr_d = None
+    if w.batch > 1:
+        node_ptr, edge_ptr, sl, dl = synth.workload_batch(ident)
+        node_ptr_d = torch.from_numpy(node_ptr).to(dev)
+        src_d, dst_d, bad = g.gga_batch_edges(node_ptr_d, torch.from_numpy(edge_ptr).to(dev),
+                                              torch.from_numpy(sl).to(dev), torch.from_numpy(dl).to(dev))
+        torch.cuda.synchronize()
+        if int(bad.item()) != 0:
+            raise RuntimeError("batch packing found ids outside their graph")
+    else:
+        src, dst = synth.workload_graph(ident)
+        src_d, dst_d = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+    e = int(src_d.numel())
+    log(f"workload {w.name}: n={n} e={e} graphs={w.batch}")
+    p = synth.gated_layer_inputs(n, d=d, ident=ident)
     d_out = synth.node_tensor(ident, 7, (n, d))
     pd = {k: (torch.from_numpy(np.ascontiguousarray(v)).to(dev) if isinstance(v, np.ndarray) else v)
           for k, v in p.items()}
     dod = torch.from_numpy(d_out).to(dev)
-    topo, tt = per_topology(g, torch, n, torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), True)
+    topo, tt = per_topology(g, torch, n, src_d, dst_d, True)
 
     def step(tm):
         _mark(tm, "f0")
-        f = layers.gated_layer_forward(pd, topo, heads)
+        f = layers.gated_layer_forward(pd, topo, heads, node_ptr=node_ptr_d)
         _mark(tm, "f1")
-        layers.gated_layer_backward(pd, f, topo, heads, dod)
+        layers.gated_layer_backward(pd, f, topo, heads, dod, node_ptr=node_ptr_d)
         _mark(tm, "b1")
 
     tm = Timer(torch, torch.cuda.current_stream())
@@ -363,17 +378,19 @@ def bench_layer(args, g, torch, synth):
     if not args.no_cpu_baseline:
         import oracle
 
+        if node_ptr is not None:
+            src, dst, _ = oracle.batch_edges(node_ptr, edge_ptr, sl, dl)
         og = oracle.Graph(n, src, dst)
         t1 = time.perf_counter()
-        oracle.gated_layer_backward(p, og, heads, d_out)
+        oracle.gated_layer_backward(p, og, heads, d_out, node_ptr=node_ptr)
         dt = time.perf_counter() - t1
         cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
                "sample": f"the whole step (layer forward + first-order gradients), fp64 (numpy matmuls for the "
                          f"dense products), {dt:.1f} s"}
     roof = roofline("mfma", flops / (ms * 1e-3) / 1e12, MFMA_F32_PEAK_TFLOPS, "TFLOP/s", None,
                     kernel="whole layer step (fp32 GEMMs dominate the flops)", flops_per_step=flops, launch_ms=ms)
-    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "d_model": d, "storage": "fp32",
-           "step": "layer forward + first-order gradients", "seq_len": n}
+    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "d_model": d, "graphs": w.batch,
+           "storage": "fp32", "step": "layer forward + first-order gradients", "seq_len": n}
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
 
 
@@ -382,7 +399,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -404,7 +421,7 @@ def main() -> int:
     elif args.workload == 2:
         rec = bench_gat(args, g, torch, synth)
     else:
-        rec = bench_layer(args, g, torch, synth)
+        rec = bench_layer(args, g, torch, synth, args.workload)
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
         b = torch.empty_like(a)

@@ -125,14 +125,15 @@ __device__ __forceinline__ int32_t owned_long(const Seg& sg, int64_t t, int64_t&
     return (lo >= a && lo < e && hi - lo > sg.rs) ? b : -1;
 }
 
-// The tiles owning a long graph, in tile order: list[0 .. *count).  One workgroup of 1024
-// threads; the number of tiles is at most 1024.
-__global__ __launch_bounds__(1024) void list_long(Seg sg, int64_t tiles, int32_t* __restrict__ list,
+// The long graphs in the order of their first tiles: list[0 .. *count) = (first tile,
+// graph, first row, end row).  One workgroup of 1024 threads; there are at most 1024 tiles.
+__global__ __launch_bounds__(1024) void list_long(Seg sg, int64_t tiles, int4* __restrict__ list,
                                                   int32_t* __restrict__ count) {
     __shared__ int wsum[16];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    int64_t lo, hi;
-    const int flag = (t < tiles && owned_long(sg, t, lo, hi) >= 0) ? 1 : 0;
+    int64_t lo = 0, hi = 0;
+    const int32_t b = t < tiles ? owned_long(sg, t, lo, hi) : -1;
+    const int flag = b >= 0 ? 1 : 0;
     int x = flag;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(1024) void list_long(Seg sg, int64_t tiles, int32_t
     __syncthreads();
     int before = 0;
     for (int w = 0; w < wave; w++) before += wsum[w];
-    if (flag) list[before + x - 1] = t;
+    if (flag) list[before + x - 1] = make_int4(t, b, (int)lo, (int)hi);
     if (t == 1023) count[0] = before + x;
 }
 
@@ -168,13 +169,13 @@ __device__ __forceinline__ void store_stats(float* sdst, float* zdst, const v4f 
     if (lane < 16) store_n<TR>(zdst + TR * lane, zacc);
 }
 
-// Matrix-core path.  grid (tiles); one wavefront per head (up to 16; more heads loop), so
+// Matrix-core path.  grid (tiles); one wavefront per head (up to 8; more heads loop), so
 // the wavefronts of a workgroup read the same rows.  Each step takes 4 rows (lane / 16);
 // four steps are loaded before any is multiplied.  Feature order inside a head is permuted:
 // MFMA tile u, position p <-> feature TR*p + u, so lane p loads its TR features of a row as
 // one vector.
 template <int TR>
-__global__ __launch_bounds__(1024) void stats_mfma(Seg sg, int32_t H, const float* __restrict__ k,
+__global__ __launch_bounds__(512) void stats_mfma(Seg sg, int32_t H, const float* __restrict__ k,
                                                    const float* __restrict__ v, float* __restrict__ part,
                                                    float* __restrict__ s, float* __restrict__ z) {
     constexpr int R = TR * 16;
@@ -262,13 +263,15 @@ __global__ __launch_bounds__(256) void stats_scalar(Seg sg, int32_t H, int32_t R
 }
 
 // Adds the pieces of each long graph in tile order.  grid (ceil(H*(r*r+r)/64), L): a
-// workgroup of 16 wavefronts owns 64 consecutive outputs of the graphs list[y], y =
-// blockIdx.y, blockIdx.y + L, ...; wavefront w adds tiles w, w+16, ... of the graph and the
-// 16 sums are added in wavefront order.
-__global__ __launch_bounds__(1024) void seg_reduce(Seg sg, int32_t H, int32_t R, const int32_t* __restrict__ list,
-                                                   const int32_t* __restrict__ count, const float* __restrict__ part,
-                                                   float* __restrict__ s, float* __restrict__ z) {
-    __shared__ float sm[16][64];
+// workgroup of NW wavefronts owns 64 consecutive outputs of the graphs list[y], y =
+// blockIdx.y, blockIdx.y + L, ...; wavefront w adds tiles w, w+NW, ... of the graph and the
+// NW sums are added in wavefront order.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void seg_reduce(Seg sg, int32_t H, int32_t R, const int4* __restrict__ list,
+                                                      const int32_t* __restrict__ count,
+                                                      const float* __restrict__ part, float* __restrict__ s,
+                                                      float* __restrict__ z) {
+    __shared__ float sm[NW][64];
     const int per = R * R + R;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t x = (int64_t)blockIdx.x * 64 + lane;
@@ -276,13 +279,13 @@ __global__ __launch_bounds__(1024) void seg_reduce(Seg sg, int32_t H, int32_t R,
     const int h = (int)(x / per), e = (int)(x % per);
     const int nl = count[0];
     for (int y = blockIdx.y; y < nl; y += gridDim.y) {
-        const int64_t t0 = list[y];
-        int64_t lo, hi;
-        const int32_t b = owned_long(sg, t0, lo, hi);
+        const int4 ent = list[y];
+        const int64_t t0 = ent.x, lo = ent.z, hi = ent.w;
+        const int32_t b = ent.y;
         const int64_t t1 = (hi - 1) / sg.rs;
         float a = 0.f;
         if (x < tot)
-            for (int64_t tt = t0 + wave; tt <= t1; tt += 16) {
+            for (int64_t tt = t0 + wave; tt <= t1; tt += NW) {
                 const int slot = (tt == t0 && lo != t0 * sg.rs) ? 1 : 0;
                 a += part[((tt * 2 + slot) * H + h) * per + e];
             }
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(1024) void seg_reduce(Seg sg, int32_t H, int32_t R,
         __syncthreads();
         if (wave == 0 && x < tot) {
             float acc = 0.f;
-            for (int w = 0; w < 16; w++) acc += sm[w][lane];
+            for (int w = 0; w < NW; w++) acc += sm[w][lane];
             if (e < R * R)
                 s[((int64_t)b * H + h) * R * R + e] = acc;
             else
@@ -302,14 +305,35 @@ __global__ __launch_bounds__(1024) void seg_reduce(Seg sg, int32_t H, int32_t R,
 
 // ---------------------------------------------------------------- G = phi(Q) S / (phi(Q) z + eps)
 
-// Matrix-core path.  grid (tiles); one wavefront per head (up to 16).  The contraction
-// index is permuted so that in MFMA step t the lane group gq = lane/16 supplies
-// k = gq*(R/4) + t: each lane's A operands over the R/4 steps are R/4 consecutive elements
-// of its row (16-byte loads), and its B operands S[k][j] are held in registers for the
-// whole piece.  Output columns are permuted too (MFMA tile j, position li <-> column
-// TR*li + j), so each lane ends with TR consecutive outputs of a row.
+// Matrix-core path.  grid (tiles), up to 8 wavefronts; wavefront w serves head w % hp and every P-th 16-row
+// tile of a piece from tile w / hp (hp = min(H, wavefronts), P = wavefronts / hp; more heads
+// than wavefronts loop).  The contraction index is permuted so that in MFMA step t the lane
+// group gq = lane/16 supplies k = gq*(R/4) + t: each lane's A operands over the R/4 steps are
+// R/4 consecutive elements of its row (16-byte loads), and its B operands S[k][j] are held in
+// registers for the whole piece.  Output columns are permuted too (MFMA tile j, position
+// li <-> column TR*li + j), so each lane ends with TR consecutive outputs of a row.  The
+// next tile's q is loaded before the current one is multiplied.
 template <int TR>
-__global__ __launch_bounds__(1024) void apply_mfma(Seg sg, int32_t H, float eps, const float* __restrict__ q,
+__device__ __forceinline__ void load_phi_row(const float* __restrict__ q, int64_t off, bool ok, float (&a)[TR * 4]) {
+    constexpr int KQ = TR * 4;
+    if (ok) {
+        const float4* qp = reinterpret_cast<const float4*>(q + off);
+#pragma unroll
+        for (int c = 0; c < KQ / 4; c++) {
+            const float4 t4 = qp[c];
+            a[4 * c + 0] = phi(t4.x);
+            a[4 * c + 1] = phi(t4.y);
+            a[4 * c + 2] = phi(t4.z);
+            a[4 * c + 3] = phi(t4.w);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < KQ; t++) a[t] = 0.f;
+    }
+}
+
+template <int TR>
+__global__ __launch_bounds__(512) void apply_mfma(Seg sg, int32_t H, float eps, const float* __restrict__ q,
                                                    const float* __restrict__ s, const float* __restrict__ z,
                                                    float* __restrict__ g) {
     constexpr int R = TR * 16;
@@ -317,8 +341,12 @@ __global__ __launch_bounds__(1024) void apply_mfma(Seg sg, int32_t H, float eps,
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int gq = lane >> 4, li = lane & 15;
     const int64_t W = (int64_t)H * R;
+    const int hp = H < nw ? H : nw;
+    const int P = nw / hp;
+    const int h0 = wave % hp, p0 = wave / hp;
+    if (p0 >= P) return;
     for_each_segment(sg, blockIdx.x, [&](int32_t b, int64_t r0, int64_t r1, int) {
-        for (int h = wave; h < H; h += nw) {
+        for (int h = h0; h < H; h += hp) {
             const float* sh = s + ((int64_t)b * H + h) * R * R;
             const float* zh = z + ((int64_t)b * H + h) * R;
             float sreg[KQ][TR], zreg[KQ];
@@ -329,23 +357,14 @@ __global__ __launch_bounds__(1024) void apply_mfma(Seg sg, int32_t H, float eps,
 #pragma unroll
                 for (int j = 0; j < TR; j++) sreg[t][j] = sh[kk * R + TR * li + j];
             }
-            for (int64_t row0 = r0; row0 < r1; row0 += 16) {
-                const int64_t row = row0 + li;
-                float a[KQ];
-                if (row < r1) {
-                    const float4* qp = reinterpret_cast<const float4*>(q + row * W + h * R + gq * KQ);
-#pragma unroll
-                    for (int c = 0; c < KQ / 4; c++) {
-                        const float4 t4 = qp[c];
-                        a[4 * c + 0] = phi(t4.x);
-                        a[4 * c + 1] = phi(t4.y);
-                        a[4 * c + 2] = phi(t4.z);
-                        a[4 * c + 3] = phi(t4.w);
-                    }
-                } else {
-#pragma unroll
-                    for (int t = 0; t < KQ; t++) a[t] = 0.f;
-                }
+            const int64_t col = h * R + gq * KQ;
+            float a[KQ];
+            int64_t row0 = r0 + 16 * p0;
+            load_phi_row<TR>(q, (row0 + li) * W + col, row0 + li < r1, a);
+            for (; row0 < r1; row0 += 16 * P) {
+                float an[KQ];
+                const int64_t nxt = row0 + 16 * P;
+                load_phi_row<TR>(q, (nxt + li) * W + col, nxt + li < r1, an);
                 float d = 0.f;
 #pragma unroll
                 for (int t = 0; t < KQ; t++) d = fmaf(a[t], zreg[t], d);
@@ -371,6 +390,8 @@ __global__ __launch_bounds__(1024) void apply_mfma(Seg sg, int32_t H, float eps,
                         store_n<TR>(g + orow * W + h * R + TR * li, o);
                     }
                 }
+#pragma unroll
+                for (int t = 0; t < KQ; t++) a[t] = an[t];
             }
         }
     });
@@ -818,7 +839,8 @@ struct GlWs {
     float* part;    // [2 * tiles][H][R*R + R] pieces of long graphs
     float* s;       // [batch][H][R*R]  S (forward) or dS (backward)
     float* z;       // [batch][H][R]    z or dz
-    int32_t* list;  // [tiles] tiles owning a long graph, then their count
+    int4* list;      // [tiles] long graphs (first tile, graph, rows)
+    int32_t* count;  // number of long graphs
     size_t bytes;
 };
 
@@ -829,19 +851,26 @@ GlWs carve_gl(void* ws, int32_t n, int32_t batch, int32_t H, int32_t R) {
     w.part = c.take<float>((size_t)(tiles > 0 ? 2 * tiles : 1) * H * (R * R + R));
     w.s = c.take<float>((size_t)batch * H * R * R);
     w.z = c.take<float>((size_t)batch * H * R);
-    w.list = c.take<int32_t>((size_t)tiles + 1);
+    w.list = c.take<int4>((size_t)(tiles > 0 ? tiles : 1));
+    w.count = c.take<int32_t>(1);
     w.bytes = c.bytes();
     return w;
 }
 
 void launch_list_and_reduce(const Seg& sg, int32_t H, int32_t R, const GlWs& w, float* s, float* z, hipStream_t st) {
     const int64_t tiles = tile_count(sg.n);
-    list_long<<<1, 1024, 0, st>>>(sg, tiles, w.list, w.list + tiles);
+    list_long<<<1, 1024, 0, st>>>(sg, tiles, w.list, w.count);
     const int64_t longest = tiles < sg.batch ? tiles : sg.batch;  // long graphs: at most one per tile
-    const unsigned gy = (unsigned)(longest < 64 ? (longest > 0 ? longest : 1) : 64);
     const int64_t tot = (int64_t)H * (R * R + R);
-    seg_reduce<<<dim3((unsigned)((tot + 63) / 64), gy), 1024, 0, st>>>(sg, H, R, w.list, w.list + tiles, w.part, s,
-                                                                         z);
+    const unsigned gx = (unsigned)((tot + 63) / 64);
+    // one graph: its (up to 1024) tiles over 16 wavefronts per output; a batch: 4 wavefronts
+    // and more graphs at once (a fixed choice per shape, so the order of the sums is too)
+    if (sg.batch == 1) {
+        seg_reduce<16><<<dim3(gx, 1), 1024, 0, st>>>(sg, H, R, w.list, w.count, w.part, s, z);
+    } else {
+        const unsigned gy = (unsigned)(longest < 256 ? (longest > 0 ? longest : 1) : 256);
+        seg_reduce<4><<<dim3(gx, gy), 256, 0, st>>>(sg, H, R, w.list, w.count, w.part, s, z);
+    }
 }
 
 bool mfma_ok(int32_t r) { return r % 16 == 0 && r <= 64; }
@@ -862,7 +891,7 @@ int gl_fwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
     const int64_t tiles = tile_count(sg.n);
     const bool mfma = mfma_ok(r) && aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_out) &&
                       aligned16(s) && aligned16(z);
-    const int wpb = heads < 16 ? heads : 16;  // wavefronts (heads) per workgroup
+    const int wpb = heads < 8 ? heads : 8;  // wavefronts (heads) per workgroup
     if (mfma) {
         const unsigned grid = (unsigned)tiles, threads = 64u * wpb;
         switch (r / 16) {
@@ -876,7 +905,9 @@ int gl_fwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
     }
     launch_list_and_reduce(sg, heads, r, w, s, z, st);
     if (mfma) {
-        const unsigned grid = (unsigned)tiles, threads = 64u * wpb;
+        // up to 8 wavefronts: every head, and as many row-tile streams per head as fit
+        const int per_head = heads < 8 ? 8 / heads : 1;
+        const unsigned grid = (unsigned)tiles, threads = 64u * (unsigned)(heads < 8 ? heads * per_head : 8);
         switch (r / 16) {
             case 1: apply_mfma<1><<<grid, threads, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
             case 2: apply_mfma<2><<<grid, threads, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
