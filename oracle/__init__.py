@@ -51,10 +51,10 @@ def lib() -> ctypes.CDLL:
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.orc_coo_to_csr.argtypes = [i32, i64, P, P, P, P, P]
         L.orc_coo_to_csr.restype = ctypes.c_int
-        L.orc_local_fwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, f64, f64, P, i64, P, P]
+        L.orc_local_fwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, f64, f64, P, P, P, i64, P, P]
         L.orc_local_fwd.restype = None
-        L.orc_local_bwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, P, P, P, f64, f64, P, P,
-                                    P, i64, P, P, i64, P, P]
+        L.orc_local_bwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, P, P, P, f64, f64, P, P, P, P,
+                                    P, P, P, i64, P, P, i64, P, P]
         L.orc_local_bwd.restype = None
         L.orc_edge_values.argtypes = [i32, P, P, i64, P]
         L.orc_edge_values.restype = None
@@ -159,29 +159,35 @@ def local_fwd_dot(q, k, v, g: Graph, scale: float, rows=None):
     nr = n if r is None else nr
     out = np.empty((nr, hh, c), np.float64)
     lse = np.empty((nr, hh), np.float64)
-    lib().orc_local_fwd(0, n, hh, c, _p(q), _p(k), _p(v), _p(g.row_ptr), _p(g.col), scale, 0.0, _p(r), nr,
-                        _p(out), _p(lse))
+    lib().orc_local_fwd(0, n, hh, c, _p(q), _p(k), _p(v), _p(g.row_ptr), _p(g.col), scale, 0.0, None, None, _p(r),
+                        nr, _p(out), _p(lse))
     return out, lse
 
 
-def local_fwd_add(s_src, s_dst, hf, g: Graph, slope: float = SLOPE, rows=None):
+def local_fwd_add(s_src, s_dst, hf, g: Graph, slope: float = SLOPE, rows=None, s_edge=None):
     """GAT additive local attention (Tinymesh "Sparse attention experiment", sections
     "Composition" and "Multiple heads are composition"): score LeakyReLU(s_src[u] + s_dst[v]),
-    target softmax, weighted sum of hf[u].  Pinned by the two exact witnesses."""
+    target softmax, weighted sum of hf[u].  With s_edge [E,H] (COO order) the logit gains
+    the edge's own term (learned edge features, as in the GATConv the page's reference
+    contract follows).  Pinned by the two exact witnesses; the edge term by the masked dense
+    formulation and by its equivalence to a per-source shift when sources are unique."""
     s_src, s_dst, hf = _f64(s_src), _f64(s_dst), _f64(hf)
     n, hh, c = hf.shape
     r, nr = _rows(rows)
     nr = n if r is None else nr
     out = np.empty((nr, hh, c), np.float64)
     lse = np.empty((nr, hh), np.float64)
-    lib().orc_local_fwd(1, n, hh, c, _p(s_dst), _p(s_src), _p(hf), _p(g.row_ptr), _p(g.col), 0.0, slope, _p(r),
-                        nr, _p(out), _p(lse))
+    se = None if s_edge is None else _f64(s_edge).reshape(-1, hh)
+    lib().orc_local_fwd(1, n, hh, c, _p(s_dst), _p(s_src), _p(hf), _p(g.row_ptr), _p(g.col), 0.0, slope, _p(se),
+                        _p(g.eid), _p(r), nr, _p(out), _p(lse))
     return out, lse
 
 
-def _local_bwd(mode, qs, ks, val, d_out, g: Graph, scale, slope, rows_d, rows_s):
+def _local_bwd(mode, qs, ks, val, d_out, g: Graph, scale, slope, rows_d, rows_s, s_edge=None):
     qs, ks, val, d_out = _f64(qs), _f64(ks), _f64(val), _f64(d_out)
     n, hh, c = val.shape
+    se = None if s_edge is None else _f64(s_edge).reshape(-1, hh)
+    d_edge = None if s_edge is None else np.zeros((g.e, hh), np.float64)
     w = c if mode == 0 else 1
     rd, nd = _rows(rows_d)
     rs, ns = _rows(rows_s)
@@ -193,11 +199,11 @@ def _local_bwd(mode, qs, ks, val, d_out, g: Graph, scale, slope, rows_d, rows_s)
     d_ks = np.empty((ns, hh, w), np.float64)
     d_val = np.empty((ns, hh, c), np.float64)
     lib().orc_local_bwd(mode, n, hh, c, _p(qs), _p(ks), _p(val), _p(d_out), _p(g.row_ptr), _p(g.col),
-                        _p(g.row_ptr_s), _p(g.col_s), scale, slope, _p(lse), _p(dd), _p(rd), nd, _p(d_qs), _p(rs),
-                        ns, _p(d_ks), _p(d_val))
+                        _p(g.row_ptr_s), _p(g.col_s), scale, slope, _p(se), _p(g.eid), _p(g.eid_s), _p(d_edge),
+                        _p(lse), _p(dd), _p(rd), nd, _p(d_qs), _p(rs), ns, _p(d_ks), _p(d_val))
     if mode == 1:
         d_qs, d_ks = d_qs[..., 0], d_ks[..., 0]
-    return dict(lse=lse, D=dd, d_q=d_qs, d_k=d_ks, d_v=d_val)
+    return dict(lse=lse, D=dd, d_q=d_qs, d_k=d_ks, d_v=d_val, d_edge=d_edge)
 
 
 def local_bwd_dot(q, k, v, d_out, g: Graph, scale: float, rows_d=None, rows_s=None):
@@ -208,12 +214,13 @@ def local_bwd_dot(q, k, v, d_out, g: Graph, scale: float, rows_d=None, rows_s=No
     return _local_bwd(0, q, k, v, d_out, g, scale, 0.0, rows_d, rows_s)
 
 
-def local_bwd_add(s_src, s_dst, hf, d_out, g: Graph, slope: float = SLOPE, rows_d=None, rows_s=None):
+def local_bwd_add(s_src, s_dst, hf, d_out, g: Graph, slope: float = SLOPE, rows_d=None, rows_s=None, s_edge=None):
     """Gradients for the additive branch: d s_dst (destination CSR), d s_src and the
-    aggregation part of d hf (CSR by source).  Pinned by the exact witnesses and by
-    autograd through the dense formulation."""
-    r = _local_bwd(1, s_dst, s_src, hf, d_out, g, 0.0, slope, rows_d, rows_s)
-    return dict(lse=r["lse"], D=r["D"], d_s_dst=r["d_q"], d_s_src=r["d_k"], d_hf=r["d_v"])
+    aggregation part of d hf (CSR by source); with an edge term also d s_edge [E,H] (COO
+    order; dz_e itself).  Pinned by the exact witnesses and by autograd through the dense
+    formulation."""
+    r = _local_bwd(1, s_dst, s_src, hf, d_out, g, 0.0, slope, rows_d, rows_s, s_edge)
+    return dict(lse=r["lse"], D=r["D"], d_s_dst=r["d_q"], d_s_src=r["d_k"], d_hf=r["d_v"], d_s_edge=r["d_edge"])
 
 
 # --------------------------------------------------------------------------- endpoint projection
@@ -256,27 +263,59 @@ def gat_coefficients(x, w, a_s, a_t):
     return hf, s_src, s_dst
 
 
-def gat_forward(x, w, a_s, a_t, g: Graph, slope: float = SLOPE):
-    """Multi-head GAT layer output [N, K*C] (heads concatenated) plus intermediates."""
+def edge_coefficients(f, w_e, a_e):
+    """Learned edge features of the score (GATConv with edge features, the reference contract
+    the Tinymesh page adopts; the page lists them as not yet covered): HE = F W_e viewed as
+    [E,K,C] (no bias) and s_edge[e,k] = a_e[k].HE[e,k], added to the edge's logit."""
+    f, w_e, a_e = _f64(f), _f64(w_e), _f64(a_e)
+    hh, c = a_e.shape
+    he = (f @ w_e).reshape(f.shape[0], hh, c)
+    return he, (he * a_e[None]).sum(-1)
+
+
+def gat_forward(x, w, a_s, a_t, g: Graph, slope: float = SLOPE, concat: bool = True, edge=None):
+    """Multi-head GAT layer output plus intermediates: heads concatenated [N, K*C], or with
+    concat=False averaged over heads [N, C] (head averaging, listed by the Tinymesh page
+    as not yet covered).  edge = dict(f [E,Fe] in COO order, w_e [Fe,K*C], a_e [K,C]) adds
+    the learned edge term to every logit."""
     hf, s_src, s_dst = gat_coefficients(x, w, a_s, a_t)
-    out, lse = local_fwd_add(s_src, s_dst, hf, g, slope)
-    return dict(out=out.reshape(out.shape[0], -1), hf=hf, s_src=s_src, s_dst=s_dst, lse=lse)
+    he = s_edge = None
+    if edge is not None:
+        he, s_edge = edge_coefficients(edge["f"], edge["w_e"], edge["a_e"])
+    out, lse = local_fwd_add(s_src, s_dst, hf, g, slope, s_edge=s_edge)
+    res = out.reshape(out.shape[0], -1) if concat else out.mean(1)
+    return dict(out=res, out3=out, hf=hf, s_src=s_src, s_dst=s_dst, lse=lse, he=he, s_edge=s_edge)
 
 
-def gat_backward(x, w, a_s, a_t, d_out, g: Graph, slope: float = SLOPE):
-    """dX, dW, da_s, da_t of sum(out * d_out).  Chain: the local backward gives d s_src,
-    d s_dst and the aggregation part of dH; the coefficient map adds a_s d s_src + a_t d s_dst;
-    then dW = X^T dH and dX = dH W^T."""
+def gat_backward(x, w, a_s, a_t, d_out, g: Graph, slope: float = SLOPE, concat: bool = True, edge=None):
+    """dX, dW, da_s, da_t (and with edge features dF, dW_e, da_e) of sum(out * d_out).
+    Chain: with head averaging each head receives d_out / K; the local backward gives
+    d s_src, d s_dst, d s_edge and the aggregation part of dH; the coefficient maps add
+    a_s d s_src + a_t d s_dst (and a_e d s_edge for HE); then dW = X^T dH, dX = dH W^T,
+    dW_e = F^T dHE, dF = dHE W_e^T."""
     x, w, a_s, a_t = _f64(x), _f64(w), _f64(a_s), _f64(a_t)
     hf, s_src, s_dst = gat_coefficients(x, w, a_s, a_t)
     n, hh, c = hf.shape
-    r = local_bwd_add(s_src, s_dst, hf, _f64(d_out).reshape(n, hh, c), g, slope)
+    if concat:
+        d3 = _f64(d_out).reshape(n, hh, c)
+    else:
+        d3 = np.repeat(_f64(d_out)[:, None, :] / hh, hh, axis=1)
+    he = s_edge = None
+    if edge is not None:
+        he, s_edge = edge_coefficients(edge["f"], edge["w_e"], edge["a_e"])
+    r = local_bwd_add(s_src, s_dst, hf, d3, g, slope, s_edge=s_edge)
     d_hf = r["d_hf"] + a_s[None] * r["d_s_src"][..., None] + a_t[None] * r["d_s_dst"][..., None]
     da_s = (r["d_s_src"][..., None] * hf).sum(0)
     da_t = (r["d_s_dst"][..., None] * hf).sum(0)
     dh = d_hf.reshape(n, hh * c)
-    return dict(d_x=dh @ w.T, d_w=x.T @ dh, d_a_s=da_s, d_a_t=da_t, d_hf=d_hf, d_s_src=r["d_s_src"],
-                d_s_dst=r["d_s_dst"])
+    res = dict(d_x=dh @ w.T, d_w=x.T @ dh, d_a_s=da_s, d_a_t=da_t, d_hf=d_hf, d_s_src=r["d_s_src"],
+               d_s_dst=r["d_s_dst"])
+    if edge is not None:
+        f, w_e, a_e = _f64(edge["f"]), _f64(edge["w_e"]), _f64(edge["a_e"])
+        d_se = r["d_s_edge"]
+        d_he = (d_se[..., None] * a_e[None]).reshape(f.shape[0], hh * c)
+        res.update(d_s_edge=d_se, d_a_e=(d_se[..., None] * he).sum(0), d_w_e=f.T @ d_he, d_f=d_he @ w_e.T)
+    return res
 
 
 # --------------------------------------------------------------------------- gated local-global layer

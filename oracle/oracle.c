@@ -91,18 +91,24 @@ static double add_logit(const double *s_src, const double *s_dst, int64_t v, int
 static double leaky(double z, double slope) { return z > 0.0 ? z : slope * z; }
 static double leaky_grad(double z, double slope) { return z > 0.0 ? 1.0 : slope; }
 
+/* Optional learned edge term of the additive logit (PyG GATConv with edge features, the
+ * reference contract the Tinymesh page adopts; the page lists edge-feature scoring as not
+ * yet covered): s_edge [E,H] in COO order, found through the CSR position's COO index. */
+static double edge_term(const double *s_edge, const int32_t *eid, int64_t p, int h, int hh) {
+    return s_edge ? s_edge[(size_t)eid[p] * hh + h] : 0.0;
+}
+
 /* Scores of all in-edges of v for head h, in CSR order. */
 static void row_scores(int mode, const double *qs, const double *ks, int64_t v, int h, int hh, int c,
-                       const int32_t *row_ptr, const int32_t *col, double scale, double slope, double *s,
-                       double *z) {
+                       const int32_t *row_ptr, const int32_t *col, double scale, double slope,
+                       const double *s_edge, const int32_t *eid, double *s) {
     int64_t b = row_ptr[v], e = row_ptr[v + 1];
     for (int64_t p = b; p < e; p++) {
         int64_t u = col[p];
         if (mode == 0) {
             s[p - b] = dot_score(qs, ks, v, u, h, hh, c, scale);
         } else {
-            double zz = add_logit(ks, qs, v, u, h, hh);
-            if (z) z[p - b] = zz;
+            double zz = add_logit(ks, qs, v, u, h, hh) + edge_term(s_edge, eid, p, h, hh);
             s[p - b] = leaky(zz, slope);
         }
     }
@@ -112,14 +118,16 @@ static void row_scores(int mode, const double *qs, const double *ks, int64_t v, 
  * Local attention forward for destination rows `rows` (all N if rows == NULL):
  * out[v,h,:] = sum_e alpha_e * val[u,h,:], lse[v,h] = log sum_e exp(s_e).
  * mode 0: dot product, qs = q [N,H,C], ks = k [N,H,C].
- * mode 1: additive,    qs = s_dst [N,H], ks = s_src [N,H].
+ * mode 1: additive,    qs = s_dst [N,H], ks = s_src [N,H]; with s_edge (COO [E,H],
+ *         NULL for none) and eid (the CSR's COO indices) the logit gains s_edge[e,h].
  * A row with no in-edges gets out = 0 and lse = -inf (isolated rows, Tinymesh
  * "Evidence and limits").  Heads are normalised independently and concatenated
  * (Tinymesh "Multiple heads are composition").
  */
 void orc_local_fwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs, const double *ks,
                    const double *val, const int32_t *row_ptr, const int32_t *col, double scale, double slope,
-                   const int32_t *rows, int64_t n_rows, double *out, double *lse) {
+                   const double *s_edge, const int32_t *eid, const int32_t *rows, int64_t n_rows, double *out,
+                   double *lse) {
     (void)n;
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t i = 0; i < n_rows; i++) {
@@ -134,7 +142,7 @@ void orc_local_fwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs,
                 lse[(size_t)i * hh + h] = -INFINITY;
                 continue;
             }
-            row_scores(mode, qs, ks, v, h, hh, c, row_ptr, col, scale, slope, s, NULL);
+            row_scores(mode, qs, ks, v, h, hh, c, row_ptr, col, scale, slope, s_edge, eid, s);
             lse[(size_t)i * hh + h] = row_softmax(s, deg, a);
             for (int64_t p = 0; p < deg; p++) {
                 const double *vu = val + ((size_t)col[b + p] * hh + h) * c;
@@ -162,6 +170,9 @@ void orc_local_fwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs,
  * Sums "out of u" walk the CSR by source, grouping edge gradients by the
  * selected endpoint (Tinymesh "Endpoint projection", backward).
  *
+ * With an edge term (mode 1, s_edge != NULL; eid / eid_s the COO indices of the CSR by
+ * destination / by source), d_edge[e,h] = dz_e (COO order) for the edges into `rows_d`.
+ *
  * Stage 1 computes, for every destination, lse and D = sum_e alpha_e d alpha_e
  * (written to lse_all / d_all, [N,H]).  Stage 2 fills d_qs for `rows_d`
  * (all if NULL), stage 3 fills d_ks and dval for `rows_s` (all if NULL);
@@ -170,6 +181,7 @@ void orc_local_fwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs,
 void orc_local_bwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs, const double *ks,
                    const double *val, const double *d_out, const int32_t *row_ptr, const int32_t *col,
                    const int32_t *row_ptr_s, const int32_t *col_s, double scale, double slope,
+                   const double *s_edge, const int32_t *eid, const int32_t *eid_s, double *d_edge,
                    double *lse_all, double *d_all, const int32_t *rows_d, int64_t n_rows_d, double *d_qs,
                    const int32_t *rows_s, int64_t n_rows_s, double *d_ks, double *d_val) {
     int qs_w = mode == 0 ? c : 1; /* width per head of qs / ks */
@@ -186,7 +198,7 @@ void orc_local_bwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs,
                 d_all[v * hh + h] = 0.0;
                 continue;
             }
-            row_scores(mode, qs, ks, v, h, hh, c, row_ptr, col, scale, slope, s, NULL);
+            row_scores(mode, qs, ks, v, h, hh, c, row_ptr, col, scale, slope, s_edge, eid, s);
             lse_all[v * hh + h] = row_softmax(s, deg, a);
             const double *g = d_out + ((size_t)v * hh + h) * c;
             double dsum = 0.0;
@@ -225,10 +237,11 @@ void orc_local_bwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs,
                     const double *ku = ks + ((size_t)u * hh + h) * c;
                     for (int j = 0; j < c; j++) dq[j] += ds * scale * ku[j];
                 } else {
-                    double z = add_logit(ks, qs, v, u, h, hh);
+                    double z = add_logit(ks, qs, v, u, h, hh) + edge_term(s_edge, eid, p, h, hh);
                     double al = exp(leaky(z, slope) - l);
                     double ds = al * (da - dd);
                     dq[0] += ds * leaky_grad(z, slope);
+                    if (d_edge) d_edge[(size_t)eid[p] * hh + h] = ds * leaky_grad(z, slope);
                 }
             }
         }
@@ -259,7 +272,7 @@ void orc_local_bwd(int mode, int32_t n, int32_t hh, int32_t c, const double *qs,
                     const double *qv = qs + ((size_t)v * hh + h) * c;
                     for (int j = 0; j < c; j++) dk[j] += ds * scale * qv[j];
                 } else {
-                    double z = add_logit(ks, qs, v, u, h, hh);
+                    double z = add_logit(ks, qs, v, u, h, hh) + edge_term(s_edge, eid_s, p, h, hh);
                     al = exp(leaky(z, slope) - l);
                     double ds = al * (da - dd);
                     dk[0] += ds * leaky_grad(z, slope);
