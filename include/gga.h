@@ -176,7 +176,8 @@ int gga_edge_values_bwd(int32_t n, int32_t width, int64_t e, const int32_t *row_
  * GAT node coefficients (Tinymesh "Sparse attention experiment", section
  * "Composition": one source and one target coefficient per node and head):
  *   s_src[n,h] = sum_c a_s[h,c] hf[n,h,c],  s_dst[n,h] = sum_c a_t[h,c] hf[n,h,c]
- * hf fp32 [n,H,C]; a_s, a_t fp32 [H,C]; outputs fp32 [n,H].
+ * hf fp32 [n,H,C]; a_s, a_t fp32 [H,C]; outputs fp32 [n,H].  a_t and s_dst may both
+ * be NULL (one coefficient per row, e.g. the edge term a_e . HE over edge rows).
  */
 int gga_gat_coef_fwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf, const float *a_s,
                      const float *a_t, float *s_src, float *s_dst, void *stream);
@@ -187,7 +188,8 @@ int gga_gat_coef_fwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf
  *   d_hf[n,h,c] = d_hf_attn[n,h,c] + a_s[h,c] d_s_src[n,h] + a_t[h,c] d_s_dst[n,h]
  *   d_a_s[h,c] = sum_n d_s_src[n,h] hf[n,h,c],  d_a_t likewise with d_s_dst.
  * The sums over n use a fixed two-level order (deterministic).  d_hf may alias
- * d_hf_attn.
+ * d_hf_attn.  d_hf_attn may be NULL (zero); a_t, d_s_dst and d_a_t may all be NULL
+ * (one coefficient per row).
  */
 size_t gga_gat_coef_bwd_workspace(int32_t n, int32_t heads, int32_t head_dim);
 int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf, const float *a_s,
@@ -340,6 +342,45 @@ int gga_global_linear_batch_bwd(int32_t n, int32_t batch, const int32_t *node_pt
                                 const float *q, const float *k, const float *v, float eps, const float *s,
                                 const float *z, const float *d_g, float *d_q, float *d_k, float *d_v, void *ws,
                                 size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * GAT variants the Tinymesh page ("Evidence and limits") lists as not yet
+ * covered, read as in the GATConv its "Reference contract" section follows:
+ * learned edge features in the score and head averaging.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Additive local attention with an edge term: for edge e: u -> v and head h the
+ * logit is z_e = s_src[u,h] + s_dst[v,h] + s_edge[e,h] before LeakyReLU (s_edge
+ * fp32 [e,H] in COO order, e.g. a_e . (F W_e) per head from gga_gat_coef_fwd on the
+ * edge features); otherwise as gga_local_attn_fwd in additive mode.  `eid` is the
+ * COO index of each CSR position (gga_coo_to_csr).  fp32 hf only (GGA_EUNSUPPORTED
+ * otherwise).  Deterministic.
+ */
+size_t gga_local_attn_fwd_edge_workspace(const gga_local_desc *d);
+int gga_local_attn_fwd_edge(const gga_local_desc *d, const float *s_dst, const float *s_src, const void *hf,
+                            const float *s_edge, const int32_t *row_ptr, const int32_t *col, const int32_t *eid,
+                            const void *plan, float *out, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Its backward (as gga_local_attn_bwd in additive mode, with the same logits), plus
+ * d_s_edge[e,h] = dz_e = ds_e LeakyReLU'(z_e), fp32 [e,H] in COO order.  eid and
+ * eid_s are the COO indices of the CSR by destination and by source.
+ */
+size_t gga_local_attn_bwd_edge_workspace(const gga_local_desc *d);
+int gga_local_attn_bwd_edge(const gga_local_desc *d, const float *s_dst, const float *s_src, const void *hf,
+                            const float *s_edge, const float *out, const float *lse, const float *d_out,
+                            const int32_t *row_ptr, const int32_t *col, const int32_t *eid, const void *plan,
+                            const int32_t *row_ptr_s, const int32_t *col_s, const int32_t *eid_s, const void *plan_s,
+                            float *d_s_dst, float *d_s_src, float *d_hf, float *d_s_edge, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * Head averaging: out[n,c] = (1/H) sum_h in[n,h,c] (in fp32 [n,H,C], out [n,C]), and
+ * its backward d_in[n,h,c] = d_out[n,c] / H.
+ */
+int gga_head_mean(int32_t n, int32_t heads, int32_t head_dim, const float *in, float *out, void *stream);
+int gga_head_mean_bwd(int32_t n, int32_t heads, int32_t head_dim, const float *d_out, float *d_in, void *stream);
 
 #ifdef __cplusplus
 }

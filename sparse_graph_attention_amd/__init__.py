@@ -81,6 +81,12 @@ def _load() -> ctypes.CDLL:
         "gga_global_linear_bwd_workspace": ([i32, i32, i32], sz),
         "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_batch_edges": ([i32, P, P, i64, P, P, P, P, P, P], ctypes.c_int),
+        "gga_local_attn_fwd_edge_workspace": ([D], sz),
+        "gga_local_attn_fwd_edge": ([D, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_local_attn_bwd_edge_workspace": ([D], sz),
+        "gga_local_attn_bwd_edge": ([D] + [P] * 20 + [sz, P], ctypes.c_int),
+        "gga_head_mean": ([i32, i32, i32, P, P, P], ctypes.c_int),
+        "gga_head_mean_bwd": ([i32, i32, i32, P, P, P], ctypes.c_int),
         "gga_global_linear_batch_workspace": ([i32, i32, i32, i32], sz),
         "gga_global_linear_batch_fwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
         "gga_global_linear_batch_bwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P],
@@ -269,10 +275,12 @@ def gga_edge_values_bwd(n: int, d_edge: torch.Tensor, row_ptr, eid, dx=None, str
     return dx
 
 
-def gga_gat_coef_fwd(hf: torch.Tensor, a_s: torch.Tensor, a_t: torch.Tensor, s_src=None, s_dst=None, stream=None):
+def gga_gat_coef_fwd(hf: torch.Tensor, a_s: torch.Tensor, a_t, s_src=None, s_dst=None, stream=None):
+    """a_t None: one coefficient per row (s_dst None)."""
     n, heads, c = hf.shape
     s_src = torch.empty(n, heads, dtype=torch.float32, device=hf.device) if s_src is None else s_src
-    s_dst = torch.empty(n, heads, dtype=torch.float32, device=hf.device) if s_dst is None else s_dst
+    if a_t is not None and s_dst is None:
+        s_dst = torch.empty(n, heads, dtype=torch.float32, device=hf.device)
     _check("gga_gat_coef_fwd", lib.gga_gat_coef_fwd(n, heads, c, _ptr(hf), _ptr(a_s), _ptr(a_t), _ptr(s_src),
                                                     _ptr(s_dst), _stream(stream)))
     return s_src, s_dst
@@ -284,7 +292,8 @@ def gga_gat_coef_bwd(hf, a_s, a_t, d_hf_attn, d_s_src, d_s_dst, d_hf=None, d_a_s
     dev = hf.device
     d_hf = torch.empty_like(hf) if d_hf is None else d_hf
     d_a_s = torch.empty(heads, c, dtype=torch.float32, device=dev) if d_a_s is None else d_a_s
-    d_a_t = torch.empty(heads, c, dtype=torch.float32, device=dev) if d_a_t is None else d_a_t
+    if a_t is not None and d_a_t is None:
+        d_a_t = torch.empty(heads, c, dtype=torch.float32, device=dev)
     nb = lib.gga_gat_coef_bwd_workspace(n, heads, c)
     ws = _workspace(nb, dev, ws)
     _check("gga_gat_coef_bwd", lib.gga_gat_coef_bwd(n, heads, c, _ptr(hf), _ptr(a_s), _ptr(a_t), _ptr(d_hf_attn),
@@ -445,3 +454,54 @@ def gga_global_linear_batch_bwd(node_ptr, q, k, v, s, z, d_g, d_q, d_k, d_v, eps
                                            _ptr(s), _ptr(z), _ptr(d_g), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(ws),
                                            nb, _stream(stream)))
     return d_q, d_k, d_v
+
+
+# --------------------------------------------------------------------------- GAT variants
+
+
+def gga_local_attn_fwd_edge(desc: gga_local_desc, s_dst, s_src, hf, s_edge, topo: Topology, out=None, lse=None,
+                            ws=None, stream=None):
+    """Additive local attention whose logits include s_edge [E,H] (COO order)."""
+    dev = hf.device
+    out = torch.empty(desc.n, desc.heads, desc.head_dim, dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty(desc.n, desc.heads, dtype=torch.float32, device=dev) if lse is None else lse
+    nb = lib.gga_local_attn_fwd_edge_workspace(ctypes.byref(desc))
+    ws = _workspace(nb, dev, ws)
+    _check("gga_local_attn_fwd_edge", lib.gga_local_attn_fwd_edge(
+        ctypes.byref(desc), _ptr(s_dst), _ptr(s_src), _ptr(hf), _ptr(s_edge), _ptr(topo.row_ptr), _ptr(topo.col),
+        _ptr(topo.eid), _ptr(topo.plan), _ptr(out), _ptr(lse), _ptr(ws), nb, _stream(stream)))
+    return out, lse
+
+
+def gga_local_attn_bwd_edge(desc: gga_local_desc, s_dst, s_src, hf, s_edge, out, lse, d_out, topo: Topology,
+                            d_s_dst=None, d_s_src=None, d_hf=None, d_s_edge=None, ws=None, stream=None):
+    """Returns d s_dst, d s_src, d hf (aggregation part) and d s_edge (COO order)."""
+    dev = hf.device
+    n, heads, c = desc.n, desc.heads, desc.head_dim
+    d_s_dst = torch.empty(n, heads, dtype=torch.float32, device=dev) if d_s_dst is None else d_s_dst
+    d_s_src = torch.empty(n, heads, dtype=torch.float32, device=dev) if d_s_src is None else d_s_src
+    d_hf = torch.empty(n, heads, c, dtype=torch.float32, device=dev) if d_hf is None else d_hf
+    d_s_edge = torch.empty(desc.e, heads, dtype=torch.float32, device=dev) if d_s_edge is None else d_s_edge
+    nb = lib.gga_local_attn_bwd_edge_workspace(ctypes.byref(desc))
+    ws = _workspace(nb, dev, ws)
+    _check("gga_local_attn_bwd_edge", lib.gga_local_attn_bwd_edge(
+        ctypes.byref(desc), _ptr(s_dst), _ptr(s_src), _ptr(hf), _ptr(s_edge), _ptr(out), _ptr(lse), _ptr(d_out),
+        _ptr(topo.row_ptr), _ptr(topo.col), _ptr(topo.eid), _ptr(topo.plan), _ptr(topo.row_ptr_s), _ptr(topo.col_s),
+        _ptr(topo.eid_s), _ptr(topo.plan_s), _ptr(d_s_dst), _ptr(d_s_src), _ptr(d_hf), _ptr(d_s_edge), _ptr(ws), nb,
+        _stream(stream)))
+    return d_s_dst, d_s_src, d_hf, d_s_edge
+
+
+def gga_head_mean(x: torch.Tensor, out=None, stream=None):
+    """x [n,H,C] -> mean over heads [n,C]."""
+    n, heads, c = x.shape
+    out = torch.empty(n, c, dtype=torch.float32, device=x.device) if out is None else out
+    _check("gga_head_mean", lib.gga_head_mean(n, heads, c, _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def gga_head_mean_bwd(d_out: torch.Tensor, heads: int, d_in=None, stream=None):
+    n, c = d_out.shape
+    d_in = torch.empty(n, heads, c, dtype=torch.float32, device=d_out.device) if d_in is None else d_in
+    _check("gga_head_mean_bwd", lib.gga_head_mean_bwd(n, heads, c, _ptr(d_out), _ptr(d_in), _stream(stream)))
+    return d_in

@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void edge_scatter_sum(int32_t n, int32_t width
     }
 }
 
-// s_src[n,h] = a_s[h,:] . hf[n,h,:],  s_dst[n,h] = a_t[h,:] . hf[n,h,:]
+// s_src[n,h] = a_s[h,:] . hf[n,h,:],  s_dst[n,h] = a_t[h,:] . hf[n,h,:] (skipped when
+// a_t is null: one coefficient per row, as for the edge term)
 __global__ void coef_fwd(int64_t nh, int32_t heads, int32_t c, const float* __restrict__ hf,
                          const float* __restrict__ a_s, const float* __restrict__ a_t, float* __restrict__ s_src,
                          float* __restrict__ s_dst) {
@@ -53,17 +54,18 @@ __global__ void coef_fwd(int64_t nh, int32_t heads, int32_t c, const float* __re
         for (int j = 0; j < c; j++) {
             const float v = row[j];
             ss = fmaf(a_s[h * c + j], v, ss);
-            st = fmaf(a_t[h * c + j], v, st);
+            if (a_t) st = fmaf(a_t[h * c + j], v, st);
         }
         s_src[i] = ss;
-        s_dst[i] = st;
+        if (a_t) s_dst[i] = st;
     }
 }
 
 constexpr int kCoefBlocks = 256;  // fixed split of the node axis for the coefficient gradients
 
 // d_hf = d_hf_attn + a_s d_s_src + a_t d_s_dst (elementwise), and per-block partial sums of
-// d_s_src * hf and d_s_dst * hf over a fixed node range.
+// d_s_src * hf and d_s_dst * hf over a fixed node range.  d_hf_attn may be null (zero); a_t
+// and d_s_dst may be null (one coefficient per row).
 __global__ __launch_bounds__(256) void coef_bwd_partial(int32_t n, int32_t heads, int32_t c,
                                                         const float* __restrict__ hf, const float* __restrict__ a_s,
                                                         const float* __restrict__ a_t,
@@ -84,12 +86,12 @@ __global__ __launch_bounds__(256) void coef_bwd_partial(int32_t n, int32_t heads
         float as_ = 0.f, at_ = 0.f;
         if (gi < groups) {
             const int h = x / c;
-            const float ws = a_s[x], wt = a_t[x];
+            const float ws = a_s[x], wt = a_t ? a_t[x] : 0.f;
             for (int64_t r = r0 + gi; r < r1; r += groups) {
                 const int64_t i = r * W + x;
                 const float v = hf[i];
-                const float gs = d_ss[r * heads + h], gt = d_sd[r * heads + h];
-                d_hf[i] = d_hf_attn[i] + ws * gs + wt * gt;
+                const float gs = d_ss[r * heads + h], gt = d_sd ? d_sd[r * heads + h] : 0.f;
+                d_hf[i] = (d_hf_attn ? d_hf_attn[i] : 0.f) + ws * gs + wt * gt;
                 as_ = fmaf(gs, v, as_);
                 at_ = fmaf(gt, v, at_);
             }
@@ -116,9 +118,36 @@ __global__ void coef_bwd_reduce(int32_t W, const float* __restrict__ part, float
                                 float* __restrict__ d_a_t) {
     for (int x = blockIdx.x * blockDim.x + threadIdx.x; x < 2 * W; x += gridDim.x * blockDim.x) {
         const int which = x / W, y = x % W;
+        if (which == 1 && !d_a_t) continue;
         float a = 0.f;
         for (int b = 0; b < kCoefBlocks; b++) a += part[((int64_t)b * 2 + which) * W + y];
         (which == 0 ? d_a_s : d_a_t)[y] = a;
+    }
+}
+
+// out[n, c] = (1/H) sum_h in[n, h, c] (heads averaged, in head order)
+__global__ void head_mean_kernel(int64_t nc, int32_t heads, int32_t c, const float* __restrict__ in,
+                                 float* __restrict__ out) {
+    const float inv = 1.0f / (float)heads;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nc; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = i / c;
+        const int j = (int)(i - n * c);
+        const float* row = in + n * heads * c + j;
+        float a = 0.f;
+        for (int h = 0; h < heads; h++) a += row[(int64_t)h * c];
+        out[i] = a * inv;
+    }
+}
+
+// d_in[n, h, c] = d_out[n, c] / H
+__global__ void head_mean_bwd_kernel(int64_t total, int32_t heads, int32_t c, const float* __restrict__ d_out,
+                                     float* __restrict__ d_in) {
+    const float inv = 1.0f / (float)heads;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t n = i / ((int64_t)heads * c);
+        const int j = (int)(i % c);
+        d_in[i] = d_out[n * c + j] * inv;
     }
 }
 
@@ -176,7 +205,7 @@ extern "C" int gga_gat_coef_fwd(int32_t n, int32_t heads, int32_t head_dim, cons
                                 const float* a_t, float* s_src, float* s_dst, void* stream) {
     if (n < 0 || heads < 1 || head_dim < 1) return GGA_EINVAL;
     if (n == 0) return GGA_OK;
-    if (!hf || !a_s || !a_t || !s_src || !s_dst) return GGA_EINVAL;
+    if (!hf || !a_s || !s_src || (a_t != nullptr) != (s_dst != nullptr)) return GGA_EINVAL;
     const int64_t nh = (int64_t)n * heads;
     coef_fwd<<<grid_for(nh, 256), 256, 0, as_stream(stream)>>>(nh, heads, head_dim, hf, a_s, a_t, s_src, s_dst);
     return launch_status();
@@ -191,8 +220,10 @@ extern "C" int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, cons
                                 const float* a_t, const float* d_hf_attn, const float* d_s_src, const float* d_s_dst,
                                 float* d_hf, float* d_a_s, float* d_a_t, void* ws, size_t ws_bytes, void* stream) {
     if (n < 0 || heads < 1 || head_dim < 1) return GGA_EINVAL;
-    if (!a_s || !a_t || !d_a_s || !d_a_t) return GGA_EINVAL;
-    if (n > 0 && (!hf || !d_hf_attn || !d_s_src || !d_s_dst || !d_hf)) return GGA_EINVAL;
+    if (!a_s || !d_a_s) return GGA_EINVAL;
+    const bool tgt = a_t != nullptr;  // the target side is all present or all absent
+    if (tgt != (d_a_t != nullptr) || (n > 0 && tgt != (d_s_dst != nullptr))) return GGA_EINVAL;
+    if (n > 0 && (!hf || !d_s_src || !d_hf)) return GGA_EINVAL;
     const size_t need = gga_gat_coef_bwd_workspace(n, heads, head_dim);
     if (ws_bytes < need || !ws) return GGA_EWORKSPACE;
     hipStream_t s = as_stream(stream);
@@ -201,5 +232,24 @@ extern "C" int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, cons
     coef_bwd_partial<<<kCoefBlocks, 256, 0, s>>>(n, heads, head_dim, hf, a_s, a_t, d_hf_attn, d_s_src, d_s_dst, d_hf,
                                                  part);
     coef_bwd_reduce<<<grid_for(2 * W, 256), 256, 0, s>>>(W, part, d_a_s, d_a_t);
+    return launch_status();
+}
+
+extern "C" int gga_head_mean(int32_t n, int32_t heads, int32_t head_dim, const float* in, float* out, void* stream) {
+    if (n < 0 || heads < 1 || head_dim < 1) return GGA_EINVAL;
+    if (n == 0) return GGA_OK;
+    if (!in || !out) return GGA_EINVAL;
+    const int64_t nc = (int64_t)n * head_dim;
+    head_mean_kernel<<<grid_for(nc, 256), 256, 0, as_stream(stream)>>>(nc, heads, head_dim, in, out);
+    return launch_status();
+}
+
+extern "C" int gga_head_mean_bwd(int32_t n, int32_t heads, int32_t head_dim, const float* d_out, float* d_in,
+                                 void* stream) {
+    if (n < 0 || heads < 1 || head_dim < 1) return GGA_EINVAL;
+    if (n == 0) return GGA_OK;
+    if (!d_out || !d_in) return GGA_EINVAL;
+    const int64_t total = (int64_t)n * heads * head_dim;
+    head_mean_bwd_kernel<<<grid_for(total, 256), 256, 0, as_stream(stream)>>>(total, heads, head_dim, d_out, d_in);
     return launch_status();
 }

@@ -28,24 +28,31 @@ BwdWs carve_bwd(void* ws, const gga_local_desc* d) {
     return w;
 }
 
-}  // namespace
-}  // namespace gga
+struct EdgeWs {
+    float* se_a;  // edge term in the order of the CSR by destination
+    float* se_b;  // ... by source
+    float* dz_a;  // dz_e in the order of the CSR by destination
+};
 
-using namespace gga;
-
-extern "C" size_t gga_local_attn_bwd_workspace(const gga_local_desc* d) {
-    if (check_desc(d) != GGA_OK) return 0;
-    return carve_bwd(nullptr, d).bytes;
+EdgeWs carve_edge(void* base, const gga_local_desc* d) {
+    Carver c(base);
+    EdgeWs w;
+    w.se_a = c.take<float>((size_t)d->e * d->heads);
+    w.se_b = c.take<float>((size_t)d->e * d->heads);
+    w.dz_a = c.take<float>((size_t)d->e * d->heads);
+    return w;
 }
 
-extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
-                                  const float* out, const float* lse, const float* d_out, const int32_t* row_ptr,
-                                  const int32_t* col, const void* plan, const int32_t* row_ptr_s,
-                                  const int32_t* col_s, const void* plan_s, float* d_qs, float* d_ks, float* d_v,
-                                  void* ws, size_t ws_bytes, void* stream) {
-    int st = check_desc(d);
-    if (st != GGA_OK) return st;
-    if (d->n == 0) return GGA_OK;
+size_t edge_ws_bytes(const gga_local_desc* d) {
+    Carver c(nullptr);
+    for (int i = 0; i < 3; i++) c.take<float>((size_t)d->e * d->heads);
+    return c.bytes();
+}
+
+int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void* v, const float* out,
+             const float* lse, const float* d_out, const int32_t* row_ptr, const int32_t* col, const void* plan,
+             const int32_t* row_ptr_s, const int32_t* col_s, const void* plan_s, float* d_qs, float* d_ks,
+             float* d_v, const EdgeWs* ew, void* ws, size_t ws_bytes, hipStream_t s) {
     if (!qs || !out || !lse || !d_out || !row_ptr || !plan || !row_ptr_s || !plan_s || !d_qs || !d_ks || !d_v)
         return GGA_EINVAL;
     if (d->e > 0 && (!ks || !v || !col || !col_s)) return GGA_EINVAL;
@@ -55,7 +62,6 @@ extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const
     const BwdWs need = carve_bwd(nullptr, d);
     if (ws_bytes < need.bytes || !ws) return GGA_EWORKSPACE;
     const BwdWs w = carve_bwd(ws, d);
-    hipStream_t s = as_stream(stream);
     const int64_t W = (int64_t)d->heads * d->head_dim;
     const int64_t wk = d->score == GGA_SCORE_DOT ? W : d->heads;
     if (d->e == 0) {
@@ -93,13 +99,74 @@ extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const
     p.scale = d->scale;
     p.score_mul = d->score == GGA_SCORE_DOT ? d->scale * kLog2e : kLog2e;
     p.slope = d->negative_slope;
+    int mode = d->score;
+    if (ew) {
+        p.se_a = ew->se_a;
+        p.se_b = ew->se_b;
+        p.dz_a = ew->dz_a;
+        mode = kScoreAddEdge;
+    }
     const int64_t light_blocks = ((int64_t)d->n + kBwdWaves - 1) / kBwdWaves;
     const int64_t ga = p.a.chunk_blocks + light_blocks, gb = p.b.chunk_blocks + light_blocks;
     if (ga >= ((int64_t)1 << 31) || gb >= ((int64_t)1 << 31)) return GGA_ERANGE;
     const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;
     const bool ok = d->dtype == GGA_BF16
-                        ? launch_bwd_bf16(p, sh.epl, sh.hdp, sh.ns, d->score, (unsigned)ga, (unsigned)gb, mh, s)
-                        : launch_bwd_f32(p, sh.epl, sh.hdp, sh.ns, d->score, (unsigned)ga, (unsigned)gb, mh, s);
+                        ? launch_bwd_bf16(p, sh.epl, sh.hdp, sh.ns, mode, (unsigned)ga, (unsigned)gb, mh, s)
+                        : launch_bwd_f32(p, sh.epl, sh.hdp, sh.ns, mode, (unsigned)ga, (unsigned)gb, mh, s);
     if (!ok) return GGA_EUNSUPPORTED;
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace gga
+
+using namespace gga;
+
+extern "C" size_t gga_local_attn_bwd_workspace(const gga_local_desc* d) {
+    if (check_desc(d) != GGA_OK) return 0;
+    return carve_bwd(nullptr, d).bytes;
+}
+
+extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
+                                  const float* out, const float* lse, const float* d_out, const int32_t* row_ptr,
+                                  const int32_t* col, const void* plan, const int32_t* row_ptr_s,
+                                  const int32_t* col_s, const void* plan_s, float* d_qs, float* d_ks, float* d_v,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    if (d->n == 0) return GGA_OK;
+    return bwd_impl(d, qs, ks, v, out, lse, d_out, row_ptr, col, plan, row_ptr_s, col_s, plan_s, d_qs, d_ks, d_v,
+                    nullptr, ws, ws_bytes, as_stream(stream));
+}
+
+extern "C" size_t gga_local_attn_bwd_edge_workspace(const gga_local_desc* d) {
+    if (check_desc(d) != GGA_OK) return 0;
+    return carve_bwd(nullptr, d).bytes + edge_ws_bytes(d);
+}
+
+extern "C" int gga_local_attn_bwd_edge(const gga_local_desc* d, const float* s_dst, const float* s_src,
+                                       const void* hf, const float* s_edge, const float* out, const float* lse,
+                                       const float* d_out, const int32_t* row_ptr, const int32_t* col,
+                                       const int32_t* eid, const void* plan, const int32_t* row_ptr_s,
+                                       const int32_t* col_s, const int32_t* eid_s, const void* plan_s,
+                                       float* d_s_dst, float* d_s_src, float* d_hf, float* d_s_edge, void* ws,
+                                       size_t ws_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    if (d->score != GGA_SCORE_ADDITIVE || d->dtype != GGA_F32) return GGA_EUNSUPPORTED;
+    if (d->n == 0) return GGA_OK;
+    if (d->e > 0 && (!s_edge || !eid || !eid_s || !d_s_edge)) return GGA_EINVAL;
+    if (ws_bytes < gga_local_attn_bwd_edge_workspace(d) || !ws) return GGA_EWORKSPACE;
+    hipStream_t s = as_stream(stream);
+    const size_t main_bytes = carve_bwd(nullptr, d).bytes;
+    const EdgeWs ew = carve_edge(static_cast<char*>(ws) + main_bytes, d);
+    if (d->e > 0) {
+        gather_rows_f32(s_edge, eid, d->e, d->heads, ew.se_a, s);
+        gather_rows_f32(s_edge, eid_s, d->e, d->heads, ew.se_b, s);
+    }
+    st = bwd_impl(d, s_dst, s_src, hf, out, lse, d_out, row_ptr, col, plan, row_ptr_s, col_s, plan_s, d_s_dst,
+                  d_s_src, d_hf, d->e > 0 ? &ew : nullptr, ws, main_bytes, s);
+    if (st != GGA_OK) return st;
+    if (d->e > 0) scatter_rows_f32(ew.dz_a, eid, d->e, d->heads, d_s_edge, s);  // CSR order -> COO order
     return launch_status();
 }

@@ -10,6 +10,8 @@
 // Long rows of either CSR are cut into chunks whose partial sums are added in slot order.
 #pragma once
 
+#include <type_traits>
+
 #include "plan.hpp"
 #include "rowgeo.hpp"
 
@@ -47,6 +49,11 @@ struct BwdParams {
     float scale;      // dot: score scale
     float score_mul;  // multiplier taking a raw score to log2 units
     float slope;
+    // kScoreAddEdge: the edge term of the logit in the order of each CSR, and dz_e out in
+    // the order of the CSR by destination
+    const float* se_a;
+    const float* se_b;
+    float* dz_a;
 };
 
 // Launchers, one per storage type (instantiated in local_bwd_f32.hip / local_bwd_bf16.hip).
@@ -138,10 +145,13 @@ struct PassA {
                     ss[j][s] = 0.f;
                     if (ev[j] && geo.ok[s]) {
                         const size_t ro = (size_t)u[j] * p.W + geo.off[s];
-                        if constexpr (MODE == GGA_SCORE_DOT)
+                        if constexpr (MODE == GGA_SCORE_DOT) {
                             kr[j][s] = *reinterpret_cast<const raw_t*>(kp + ro);
-                        else
+                        } else {
                             ss[j][s] = ssrc[(size_t)u[j] * p.H + geo.head[s]];
+                            if constexpr (MODE == kScoreAddEdge)
+                                ss[j][s] += p.se_a[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]];
+                        }
                         vr[j][s] = *reinterpret_cast<const raw_t*>(vp + ro);
                     }
                 }
@@ -174,6 +184,11 @@ struct PassA {
                         const float al = fexp2(sc - l2[s]);
                         const float ds = ev[j] ? al * (da - Dh[s]) : 0.f;
                         acc[s][0] = fmaf(ds, z > 0.f ? 1.f : p.slope, acc[s][0]);
+                        if constexpr (MODE == kScoreAddEdge) {
+                            if (ev[j] && geo.ok[s] && geo.lead[s])
+                                p.dz_a[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]] =
+                                    ds * (z > 0.f ? 1.f : p.slope);
+                        }
                     }
                 }
             }
@@ -297,10 +312,13 @@ struct PassB {
                     if (ev[j] && geo.ok[s]) {
                         const size_t ro = (size_t)t[j] * p.W + geo.off[s];
                         const size_t hi = (size_t)t[j] * p.H + geo.head[s];
-                        if constexpr (MODE == GGA_SCORE_DOT)
+                        if constexpr (MODE == GGA_SCORE_DOT) {
                             qr[j][s] = *reinterpret_cast<const raw_t*>(qp + ro);
-                        else
+                        } else {
                             sj[j][s] = sdst[hi];
+                            if constexpr (MODE == kScoreAddEdge)
+                                sj[j][s] += p.se_b[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]];
+                        }
                         load_f32<EPL>(p.dout + ro, gr[j][s]);
                         lj[j][s] = p.lse[hi];
                         dj[j][s] = p.D[hi];
@@ -566,6 +584,13 @@ bool launch_bwd_dtype(const BwdParams& p, int epl, int hdp, int ns, int mode, un
     if (mode == GGA_SCORE_DOT) {
         if (epl == VEC) return launch_bwd_hdp<T, VEC, GGA_SCORE_DOT>(p, hdp, ns, ga, gb, mh, s);
         return launch_bwd_hdp<T, 1, GGA_SCORE_DOT>(p, hdp, ns, ga, gb, mh, s);
+    }
+    if (mode == kScoreAddEdge) {  // fp32 node tensors only
+        if constexpr (std::is_same<T, float>::value) {
+            if (epl == VEC) return launch_bwd_hdp<T, VEC, kScoreAddEdge>(p, hdp, ns, ga, gb, mh, s);
+            return launch_bwd_hdp<T, 1, kScoreAddEdge>(p, hdp, ns, ga, gb, mh, s);
+        }
+        return false;
     }
     if (epl == VEC) return launch_bwd_hdp<T, VEC, GGA_SCORE_ADDITIVE>(p, hdp, ns, ga, gb, mh, s);
     return launch_bwd_hdp<T, 1, GGA_SCORE_ADDITIVE>(p, hdp, ns, ga, gb, mh, s);

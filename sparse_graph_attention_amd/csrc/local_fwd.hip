@@ -39,6 +39,7 @@ struct FwdParams {
     float score_mul;
     float slope;
     int32_t chunk_blocks;
+    const float* se;  // kScoreAddEdge: edge term of the logit, CSR order [E, H]
 };
 
 template <typename T, int EPL, int HDP, int NS, int MODE>
@@ -129,10 +130,13 @@ struct FwdRow {
                     ss[j][s] = 0.f;
                     if (ev[j] && ok[s]) {
                         const size_t ro = (size_t)u[j] * p.W + off[s];
-                        if constexpr (MODE == GGA_SCORE_DOT)
+                        if constexpr (MODE == GGA_SCORE_DOT) {
                             kr[j][s] = *reinterpret_cast<const raw_t*>(kp + ro);
-                        else
+                        } else {
                             ss[j][s] = ssrc[(size_t)u[j] * p.H + head[s]];
+                            if constexpr (MODE == kScoreAddEdge)
+                                ss[j][s] += p.se[(size_t)(base + g + G * j) * p.H + head[s]];
+                        }
                         vr[j][s] = *reinterpret_cast<const raw_t*>(vp + ro);
                     }
                 }
@@ -389,28 +393,26 @@ bool dispatch(int dtype, const Shape& sh, const FwdParams& p, unsigned grid, int
     return dispatch_hdp<float, 1, MODE>(sh, p, grid, mh, s);
 }
 
-}  // namespace
+// The additive score with an edge term: fp32 node tensors only.
+bool dispatch_edge(int dtype, const Shape& sh, const FwdParams& p, unsigned grid, int64_t mh, hipStream_t s) {
+    if (dtype != GGA_F32) return false;
+    if (sh.epl == 4) return dispatch_hdp<float, 4, kScoreAddEdge>(sh, p, grid, mh, s);
+    return dispatch_hdp<float, 1, kScoreAddEdge>(sh, p, grid, mh, s);
+}
 
-}  // namespace gga
-
-using namespace gga;
-
-extern "C" size_t gga_local_attn_fwd_workspace(const gga_local_desc* d) {
-    if (check_desc(d) != GGA_OK) return 0;
+size_t fwd_part_bytes(const gga_local_desc* d) {
     PlanBounds b = plan_bounds(d->e);
     return align_up((size_t)b.max_slots * part_stride(d->heads, d->head_dim) * sizeof(float), 256);
 }
 
-extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
-                                  const int32_t* row_ptr, const int32_t* col, const void* plan, float* out,
-                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
-    int st = check_desc(d);
-    if (st != GGA_OK) return st;
-    if (d->n == 0) return GGA_OK;
+// The forward with an optional edge term `se` (CSR order); ws holds the split-row partials.
+int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void* v, const int32_t* row_ptr,
+             const int32_t* col, const void* plan, float* out, float* lse, const float* se, void* ws,
+             size_t ws_bytes, hipStream_t s) {
     if (!row_ptr || !plan || !out || !qs) return GGA_EINVAL;
     if (d->e > 0 && (!col || !ks || !v)) return GGA_EINVAL;
     if (!aligned16(out) || !aligned16(qs) || (ks && !aligned16(ks)) || (v && !aligned16(v))) return GGA_EINVAL;
-    const size_t need = gga_local_attn_fwd_workspace(d);
+    const size_t need = fwd_part_bytes(d);
     if (ws_bytes < need || (need > 0 && !ws)) return GGA_EWORKSPACE;
     Shape sh;
     pick_shape(d->heads, d->head_dim, d->dtype, &sh);
@@ -430,6 +432,7 @@ extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const
     p.out = out;
     p.lse = lse;
     p.part = static_cast<float*>(ws);
+    p.se = se;
     p.n = d->n;
     p.H = d->heads;
     p.C = d->head_dim;
@@ -445,9 +448,55 @@ extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const
     const int64_t grid = p.chunk_blocks + light_blocks;
     if (grid >= ((int64_t)1 << 31)) return GGA_ERANGE;
     const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;
-    hipStream_t s = as_stream(stream);
-    bool ok = d->score == GGA_SCORE_DOT ? dispatch<GGA_SCORE_DOT>(d->dtype, sh, p, (unsigned)grid, mh, s)
-                                        : dispatch<GGA_SCORE_ADDITIVE>(d->dtype, sh, p, (unsigned)grid, mh, s);
+    bool ok;
+    if (se)
+        ok = dispatch_edge(d->dtype, sh, p, (unsigned)grid, mh, s);
+    else if (d->score == GGA_SCORE_DOT)
+        ok = dispatch<GGA_SCORE_DOT>(d->dtype, sh, p, (unsigned)grid, mh, s);
+    else
+        ok = dispatch<GGA_SCORE_ADDITIVE>(d->dtype, sh, p, (unsigned)grid, mh, s);
     if (!ok) return GGA_EUNSUPPORTED;
     return launch_status();
+}
+
+}  // namespace
+
+}  // namespace gga
+
+using namespace gga;
+
+extern "C" size_t gga_local_attn_fwd_workspace(const gga_local_desc* d) {
+    if (check_desc(d) != GGA_OK) return 0;
+    return fwd_part_bytes(d);
+}
+
+extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
+                                  const int32_t* row_ptr, const int32_t* col, const void* plan, float* out,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    if (d->n == 0) return GGA_OK;
+    return fwd_impl(d, qs, ks, v, row_ptr, col, plan, out, lse, nullptr, ws, ws_bytes, as_stream(stream));
+}
+
+extern "C" size_t gga_local_attn_fwd_edge_workspace(const gga_local_desc* d) {
+    if (check_desc(d) != GGA_OK) return 0;
+    return fwd_part_bytes(d) + align_up((size_t)d->e * d->heads * sizeof(float), 256);
+}
+
+extern "C" int gga_local_attn_fwd_edge(const gga_local_desc* d, const float* s_dst, const float* s_src,
+                                       const void* hf, const float* s_edge, const int32_t* row_ptr,
+                                       const int32_t* col, const int32_t* eid, const void* plan, float* out,
+                                       float* lse, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    if (d->score != GGA_SCORE_ADDITIVE || d->dtype != GGA_F32) return GGA_EUNSUPPORTED;
+    if (d->n == 0) return GGA_OK;
+    if (d->e > 0 && (!s_edge || !eid)) return GGA_EINVAL;
+    const size_t part = fwd_part_bytes(d);
+    if (ws_bytes < gga_local_attn_fwd_edge_workspace(d) || !ws) return GGA_EWORKSPACE;
+    hipStream_t s = as_stream(stream);
+    float* se = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
+    gather_rows_f32(s_edge, eid, d->e, d->heads, se, s);  // COO order -> CSR order
+    return fwd_impl(d, s_dst, s_src, hf, row_ptr, col, plan, out, lse, d->e > 0 ? se : nullptr, ws, part, s);
 }

@@ -17,36 +17,59 @@ import torch
 
 from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, Topology, gga_add_layernorm,
                gga_add_layernorm_bwd, gga_gat_coef_bwd, gga_gat_coef_fwd, gga_gated_combine, gga_gated_combine_bwd,
+               gga_head_mean, gga_head_mean_bwd, gga_local_attn_bwd_edge, gga_local_attn_fwd_edge,
                gga_global_linear_batch_bwd, gga_global_linear_batch_fwd, gga_global_linear_bwd,
                gga_global_linear_fwd, gga_linear, gga_linear_accumulate, gga_local_attn_bwd, gga_local_attn_fwd,
                make_desc)
 
 
 def gat_forward(x: torch.Tensor, w: torch.Tensor, a_s: torch.Tensor, a_t: torch.Tensor, topo: Topology,
-                negative_slope: float = 0.2):
-    """Returns a dict with out [N, K*C] and the intermediates the backward needs."""
+                negative_slope: float = 0.2, concat: bool = True, edge: dict | None = None):
+    """Returns a dict with out (heads concatenated [N, K*C], or averaged [N, C] with
+    concat=False) and the intermediates the backward needs.  edge = dict(f [E, Fe] in COO
+    order, w_e [Fe, K*C], a_e [K, C]) adds the learned edge term a_e . (F W_e) to every
+    logit."""
     n = x.shape[0]
     heads, c = a_s.shape
     hf = gga_linear(x, w).view(n, heads, c)
     s_src, s_dst = gga_gat_coef_fwd(hf, a_s, a_t)
     desc = make_desc(n, topo.e, heads, c, GGA_SCORE_ADDITIVE, GGA_F32, 1.0, negative_slope)
-    out, lse = gga_local_attn_fwd(desc, s_dst, s_src, hf, topo.row_ptr, topo.col, topo.plan)
-    return dict(out=out.view(n, heads * c), hf=hf, s_src=s_src, s_dst=s_dst, lse=lse, desc=desc, out3=out)
+    he = s_edge = None
+    if edge is None:
+        out, lse = gga_local_attn_fwd(desc, s_dst, s_src, hf, topo.row_ptr, topo.col, topo.plan)
+    else:
+        he = gga_linear(edge["f"], edge["w_e"]).view(topo.e, heads, c)
+        s_edge, _ = gga_gat_coef_fwd(he, edge["a_e"], None)
+        out, lse = gga_local_attn_fwd_edge(desc, s_dst, s_src, hf, s_edge, topo)
+    res = out.view(n, heads * c) if concat else gga_head_mean(out)
+    return dict(out=res, hf=hf, s_src=s_src, s_dst=s_dst, lse=lse, desc=desc, out3=out, he=he, s_edge=s_edge)
 
 
-def gat_backward(x, w, a_s, a_t, d_out: torch.Tensor, fwd: dict, topo: Topology):
-    """dX, dW, da_s, da_t of sum(out * d_out) (Tinymesh "Evidence and limits": first-order
-    gradients).  topo must hold the CSR by source (Topology(..., backward=True))."""
+def gat_backward(x, w, a_s, a_t, d_out: torch.Tensor, fwd: dict, topo: Topology, concat: bool = True,
+                 edge: dict | None = None):
+    """dX, dW, da_s, da_t (and with edge features dF, dW_e, da_e) of sum(out * d_out)
+    (Tinymesh "Evidence and limits": first-order gradients).  topo must hold the CSR by
+    source (Topology(..., backward=True))."""
     n = x.shape[0]
     heads, c = a_s.shape
-    d3 = d_out.reshape(n, heads, c)
-    d_sdst, d_ssrc, d_hf_attn = gga_local_attn_bwd(fwd["desc"], fwd["s_dst"], fwd["s_src"], fwd["hf"], fwd["out3"],
-                                                   fwd["lse"], d3, topo)
+    d3 = d_out.reshape(n, heads, c) if concat else gga_head_mean_bwd(d_out, heads)
+    res = {}
+    if edge is None:
+        d_sdst, d_ssrc, d_hf_attn = gga_local_attn_bwd(fwd["desc"], fwd["s_dst"], fwd["s_src"], fwd["hf"],
+                                                       fwd["out3"], fwd["lse"], d3, topo)
+    else:
+        d_sdst, d_ssrc, d_hf_attn, d_se = gga_local_attn_bwd_edge(fwd["desc"], fwd["s_dst"], fwd["s_src"], fwd["hf"],
+                                                                  fwd["s_edge"], fwd["out3"], fwd["lse"], d3, topo)
+        d_he, d_a_e, _ = gga_gat_coef_bwd(fwd["he"], edge["a_e"], None, None, d_se, None)
+        dhe = d_he.view(topo.e, heads * c)
+        res.update(d_s_edge=d_se, d_a_e=d_a_e, d_w_e=gga_linear(edge["f"], dhe, trans_a=True),
+                   d_f=gga_linear(dhe, edge["w_e"], trans_b=True))
     d_hf, d_a_s, d_a_t = gga_gat_coef_bwd(fwd["hf"], a_s, a_t, d_hf_attn, d_ssrc, d_sdst)
     dh = d_hf.view(n, heads * c)
     d_w = gga_linear(x, dh, trans_a=True)
     d_x = gga_linear(dh, w, trans_b=True)
-    return dict(d_x=d_x, d_w=d_w, d_a_s=d_a_s, d_a_t=d_a_t, d_hf=d_hf, d_s_src=d_ssrc, d_s_dst=d_sdst)
+    res.update(d_x=d_x, d_w=d_w, d_a_s=d_a_s, d_a_t=d_a_t, d_hf=d_hf, d_s_src=d_ssrc, d_s_dst=d_sdst)
+    return res
 
 
 def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, ln_eps: float = 1e-5,

@@ -185,6 +185,7 @@ WORKLOADS = {
     4: Workload(4, "gated-layer-n262k-d256-h4", 1 << 18, 4, 64, "f32", "dot", d_model=256),
     5: Workload(5, "dot-zipf1.8-n2m-h8-c32-bf16", 1 << 21, 8, 32, "bf16", "dot"),
     6: Workload(6, "gated-layer-batch64-n4096-d256-h4", 1 << 18, 4, 64, "f32", "dot", d_model=256, batch=64),
+    7: Workload(7, "gat-edgefeat-mean-powerlaw-n170k", 170_000, 8, 8, "f32", "additive", fin=128),
 }
 
 
@@ -196,8 +197,8 @@ def workload_graph(ident: int, n: int | None = None):
     rng = _rng(ident, TOPOLOGY)
     if ident == 1:
         return erdos_renyi(n, 8.0 / (n - 1), rng)
-    if ident == 2:
-        return power_law(n, 14.0, 1.1, 10_000, rng)
+    if ident in (2, 7):  # the edge-feature variant runs on the same graph
+        return power_law(n, 14.0, 1.1, 10_000, _rng(2, TOPOLOGY))
     if ident == 3:
         return fixed_in_degree(n, 16, rng)
     if ident == 4:
@@ -250,6 +251,16 @@ def gat_inputs(n: int, fin: int = 128, heads: int = 8, ch: int = 8, ident: int =
     a_t = normal_f32(heads * ch, ident, WEIGHTS, 2, std=0.1).reshape(heads, ch)
     d_out = node_tensor(ident, 0, (n, heads * ch), stream=GRADS)
     return x, w, a_s, a_t, d_out
+
+
+def gat_edge_inputs(e: int, fe: int = 16, heads: int = 8, ch: int = 8, ident: int = 7):
+    """Learned edge features of the GAT score: F ~ N(0,1) [e, fe] (COO order), W_e
+    Glorot-uniform [fe, heads*ch], a_e ~ N(0, 0.1^2) [heads, ch]."""
+    f = normal_f32(e * fe, ident, NODES, 1).reshape(e, fe)
+    lim = float(np.sqrt(6.0 / (fe + heads * ch)))
+    w_e = uniform_f32(fe * heads * ch, -lim, lim, ident, WEIGHTS, 3).reshape(fe, heads * ch)
+    a_e = normal_f32(heads * ch, ident, WEIGHTS, 4, std=0.1).reshape(heads, ch)
+    return dict(f=f, w_e=w_e, a_e=a_e)
 
 
 def gated_layer_inputs(n: int, d: int = 256, ident: int = 4):
