@@ -17,6 +17,8 @@ Other workloads (``--workload``), each printed as its own line when asked for:
      layer forward + the gradients of every input and parameter
   6  the same layer over a batch of 64 graphs of 4096 nodes packed along the node axis
      (block-diagonal edges, per-graph global statistics): forward + gradients
+  7  the 170k-node GAT layer with 16 learned features per edge in the score and the
+     heads averaged: forward + first-order gradients
   1  tiny 1024-node dot-product graph, H = 1, r = 16, fp32: forward
 
 Prints one JSON line: throughput in GEdges/s, the roofline of the dominant kernel call
@@ -283,10 +285,11 @@ def bench_heavy_tail(args, g, torch, synth):
                        bwd_gbs_algorithmic=ba / bms / 1e6))
 
 
-def bench_gat(args, g, torch, synth):
+def bench_gat(args, g, torch, synth, ident):
+    """The GAT layer, forward + first-order gradients; the edge-feature workload adds 16
+    learned features per edge to every logit and averages the heads."""
     from sparse_graph_attention_amd import layers
 
-    ident = 2
     w = synth.WORKLOADS[ident]
     n, heads, c = w.n, w.heads, w.head_dim
     dev = torch.device("cuda:0")
@@ -295,14 +298,20 @@ def bench_gat(args, g, torch, synth):
     log(f"workload {w.name}: n={n} e={e}")
     x, wt, a_s, a_t, d_out = synth.gat_inputs(n)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    concat, edge, edge_d = True, None, None
+    if ident == 7:
+        concat = False
+        edge = synth.gat_edge_inputs(e)
+        edge_d = {k: t(v) for k, v in edge.items()}
+        d_out = synth.node_tensor(ident, 0, (n, c), stream=synth.GRADS)
     xd, wd, asd, atd, dod = t(x), t(wt), t(a_s), t(a_t), t(d_out)
     topo, tt = per_topology(g, torch, n, t(src), t(dst), True)
 
     def step(tm):
         _mark(tm, "f0")
-        f = layers.gat_forward(xd, wd, asd, atd, topo)
+        f = layers.gat_forward(xd, wd, asd, atd, topo, concat=concat, edge=edge_d)
         _mark(tm, "f1")
-        layers.gat_backward(xd, wd, asd, atd, dod, f, topo)
+        layers.gat_backward(xd, wd, asd, atd, dod, f, topo, concat=concat, edge=edge_d)
         _mark(tm, "b1")
 
     tm = Timer(torch, torch.cuda.current_stream())
@@ -315,16 +324,23 @@ def bench_gat(args, g, torch, synth):
 
         og = oracle.Graph(n, src, dst)
         t1 = time.perf_counter()
-        oracle.gat_forward(x, wt, a_s, a_t, og)
-        oracle.gat_backward(x, wt, a_s, a_t, d_out, og)
+        oracle.gat_forward(x, wt, a_s, a_t, og, concat=concat, edge=edge)
+        oracle.gat_backward(x, wt, a_s, a_t, d_out, og, concat=concat, edge=edge)
         dt = time.perf_counter() - t1
         cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
                "sample": f"the whole step (layer forward + first-order gradients), fp64, {dt:.1f} s"}
     fa = fwd_bytes(n, e, heads, c, 4) + n * heads * 8 * 2  # + s_src, s_dst per edge side
+    if edge is not None:
+        fe = edge["f"].shape[1]
+        # per edge: its feature row read, s_edge = F G written, permuted to CSR order (read +
+        # write) and read by the attention kernel
+        fa += e * (4 * fe + 4 * 4 * heads)
     roof = roofline("hbm", fa / (fms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", None,
-                    kernel="layer forward (GEMM, coefficients, fused local forward)", alg_bytes_per_launch=fa,
+                    kernel="layer forward (GEMMs, coefficients, fused local forward)", alg_bytes_per_launch=fa,
                     launch_ms=fms)
     cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "fin": w.fin, "storage": "fp32",
+           "heads_combined": "concatenated" if concat else "averaged",
+           "edge_features": 0 if edge is None else int(edge["f"].shape[1]),
            "step": "forward + first-order gradients", "seq_len": n}
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
 
@@ -399,7 +415,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -418,8 +434,8 @@ def main() -> int:
         rec = bench_dot_forward(args, g, torch, synth, args.workload)
     elif args.workload == 5:
         rec = bench_heavy_tail(args, g, torch, synth)
-    elif args.workload == 2:
-        rec = bench_gat(args, g, torch, synth)
+    elif args.workload in (2, 7):
+        rec = bench_gat(args, g, torch, synth, args.workload)
     else:
         rec = bench_layer(args, g, torch, synth, args.workload)
     if args.copy_calibration:

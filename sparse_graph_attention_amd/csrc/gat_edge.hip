@@ -46,22 +46,47 @@ __global__ __launch_bounds__(256) void edge_scatter_sum(int32_t n, int32_t width
 // a_t is null: one coefficient per row, as for the edge term)
 __global__ void coef_fwd(int64_t nh, int32_t heads, int32_t c, const float* __restrict__ hf,
                          const float* __restrict__ a_s, const float* __restrict__ a_t, float* __restrict__ s_src,
-                         float* __restrict__ s_dst) {
+                         float* __restrict__ s_dst, int vec) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nh; i += (int64_t)gridDim.x * blockDim.x) {
         const int h = (int)(i % heads);
         const float* row = hf + i * c;
         float ss = 0.f, st = 0.f;
-        for (int j = 0; j < c; j++) {
-            const float v = row[j];
-            ss = fmaf(a_s[h * c + j], v, ss);
-            if (a_t) st = fmaf(a_t[h * c + j], v, st);
+        if (vec) {  // c % 4 == 0, 16-byte aligned rows: the wavefront reads whole rows in 16-byte pieces
+            for (int j = 0; j < c; j += 4) {
+                const float4 v = *reinterpret_cast<const float4*>(row + j);
+                const float* as = a_s + h * c + j;
+                ss = fmaf(as[0], v.x, ss);
+                ss = fmaf(as[1], v.y, ss);
+                ss = fmaf(as[2], v.z, ss);
+                ss = fmaf(as[3], v.w, ss);
+                if (a_t) {
+                    const float* at = a_t + h * c + j;
+                    st = fmaf(at[0], v.x, st);
+                    st = fmaf(at[1], v.y, st);
+                    st = fmaf(at[2], v.z, st);
+                    st = fmaf(at[3], v.w, st);
+                }
+            }
+        } else {
+            for (int j = 0; j < c; j++) {
+                const float v = row[j];
+                ss = fmaf(a_s[h * c + j], v, ss);
+                if (a_t) st = fmaf(a_t[h * c + j], v, st);
+            }
         }
         s_src[i] = ss;
         if (a_t) s_dst[i] = st;
     }
 }
 
-constexpr int kCoefBlocks = 256;  // fixed split of the node axis for the coefficient gradients
+// Fixed split of the row axis for the coefficient gradients: ranges of about 512 rows, at
+// least 1 and at most 4096 of them (a function of n, so the order of the sums is too).
+inline int coef_blocks(int64_t n) {
+    int64_t b = (n + 511) / 512;
+    if (b < 1) b = 1;
+    if (b > 4096) b = 4096;
+    return (int)b;
+}
 
 // d_hf = d_hf_attn + a_s d_s_src + a_t d_s_dst (elementwise), and per-block partial sums of
 // d_s_src * hf and d_s_dst * hf over a fixed node range.  d_hf_attn may be null (zero); a_t
@@ -74,7 +99,7 @@ __global__ __launch_bounds__(256) void coef_bwd_partial(int32_t n, int32_t heads
                                                         const float* __restrict__ d_sd, float* __restrict__ d_hf,
                                                         float* __restrict__ part) {
     const int W = heads * c;
-    const int64_t rows_per = ((int64_t)n + kCoefBlocks - 1) / kCoefBlocks;
+    const int64_t rows_per = ((int64_t)n + gridDim.x - 1) / gridDim.x;
     const int64_t r0 = blockIdx.x * rows_per;
     const int64_t r1 = r0 + rows_per < n ? r0 + rows_per : n;
     __shared__ float sm[2][256];
@@ -114,15 +139,23 @@ __global__ __launch_bounds__(256) void coef_bwd_partial(int32_t n, int32_t heads
     }
 }
 
-__global__ void coef_bwd_reduce(int32_t W, const float* __restrict__ part, float* __restrict__ d_a_s,
-                                float* __restrict__ d_a_t) {
-    for (int x = blockIdx.x * blockDim.x + threadIdx.x; x < 2 * W; x += gridDim.x * blockDim.x) {
-        const int which = x / W, y = x % W;
-        if (which == 1 && !d_a_t) continue;
-        float a = 0.f;
-        for (int b = 0; b < kCoefBlocks; b++) a += part[((int64_t)b * 2 + which) * W + y];
-        (which == 0 ? d_a_s : d_a_t)[y] = a;
+// One workgroup per output: thread t adds ranges t, t+256, ... and the 256 sums are added
+// by a fixed tree.
+__global__ __launch_bounds__(256) void coef_bwd_reduce(int32_t W, int nb, const float* __restrict__ part,
+                                                       float* __restrict__ d_a_s, float* __restrict__ d_a_t) {
+    __shared__ float sm[256];
+    const int x = blockIdx.x;
+    const int which = x / W, y = x % W;
+    if (which == 1 && !d_a_t) return;
+    float a = 0.f;
+    for (int b = threadIdx.x; b < nb; b += 256) a += part[((int64_t)b * 2 + which) * W + y];
+    sm[threadIdx.x] = a;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if ((int)threadIdx.x < off) sm[threadIdx.x] += sm[threadIdx.x + off];
+        __syncthreads();
     }
+    if (threadIdx.x == 0) (which == 0 ? d_a_s : d_a_t)[y] = sm[0];
 }
 
 // out[n, c] = (1/H) sum_h in[n, h, c] (heads averaged, in head order)
@@ -207,13 +240,14 @@ extern "C" int gga_gat_coef_fwd(int32_t n, int32_t heads, int32_t head_dim, cons
     if (n == 0) return GGA_OK;
     if (!hf || !a_s || !s_src || (a_t != nullptr) != (s_dst != nullptr)) return GGA_EINVAL;
     const int64_t nh = (int64_t)n * heads;
-    coef_fwd<<<grid_for(nh, 256), 256, 0, as_stream(stream)>>>(nh, heads, head_dim, hf, a_s, a_t, s_src, s_dst);
+    const int vec = head_dim % 4 == 0 && aligned16(hf);
+    coef_fwd<<<grid_for(nh, 256), 256, 0, as_stream(stream)>>>(nh, heads, head_dim, hf, a_s, a_t, s_src, s_dst, vec);
     return launch_status();
 }
 
 extern "C" size_t gga_gat_coef_bwd_workspace(int32_t n, int32_t heads, int32_t head_dim) {
     if (n < 0 || heads < 1 || head_dim < 1) return 0;
-    return align_up((size_t)kCoefBlocks * 2 * heads * head_dim * sizeof(float), 256);
+    return align_up((size_t)coef_blocks(n) * 2 * heads * head_dim * sizeof(float), 256);
 }
 
 extern "C" int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, const float* hf, const float* a_s,
@@ -229,9 +263,10 @@ extern "C" int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, cons
     hipStream_t s = as_stream(stream);
     const int W = heads * head_dim;
     float* part = static_cast<float*>(ws);
-    coef_bwd_partial<<<kCoefBlocks, 256, 0, s>>>(n, heads, head_dim, hf, a_s, a_t, d_hf_attn, d_s_src, d_s_dst, d_hf,
+    const int nb = coef_blocks(n);
+    coef_bwd_partial<<<nb, 256, 0, s>>>(n, heads, head_dim, hf, a_s, a_t, d_hf_attn, d_s_src, d_s_dst, d_hf,
                                                  part);
-    coef_bwd_reduce<<<grid_for(2 * W, 256), 256, 0, s>>>(W, part, d_a_s, d_a_t);
+    coef_bwd_reduce<<<(unsigned)(2 * W), 256, 0, s>>>(W, nb, part, d_a_s, d_a_t);
     return launch_status();
 }
 

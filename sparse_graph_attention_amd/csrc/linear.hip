@@ -211,10 +211,132 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ 
     }
 }
 
+// ---- skinny shapes, where a 128-row MFMA tile would mostly compute padding
+
+// element (r, kk) of op(a) and (kk, j) of op(b)
+__device__ __forceinline__ float op_a(const GemmArgs& g, int64_t r, int64_t kk) {
+    return g.trans_a ? g.a[kk * g.M + r] : g.a[r * g.K + kk];
+}
+__device__ __forceinline__ float op_b(const GemmArgs& g, int64_t kk, int64_t j) {
+    return g.trans_b ? g.b[j * g.K + kk] : g.b[kk * g.N + j];
+}
+
+// Few outputs of a transposed-A product (c = a^T b, a stored [K][M], b [K][N]; M, N <= 32)
+// over a long k: workgroup z sums its k range into part[z][M][N].  Rows of a and b come
+// through LDS 128 at a time (coalesced), the next tile's loads issued before the current
+// one is used; with M*N < 256 each output's rows are split into interleaved streams added
+// in stream order.
+__global__ __launch_bounds__(256) void gemm_small_out(GemmArgs g, float* __restrict__ part) {
+    constexpr int TR = 128, PER = TR * 32 / 256;
+    __shared__ float as[TR * 32], bs[TR * 32];
+    __shared__ float sm[256];
+    const int t = threadIdx.x;
+    const int M = g.M, N = g.N, mn = M * N;
+    const int64_t kb = (int64_t)blockIdx.x * g.kchunk;
+    const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+    const int reps = mn < 256 ? 256 / mn : 1;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float ra[PER], rb[PER];
+    auto fetch = [&](int64_t r0) {
+        const int rows = (int)(ke - r0 < TR ? ke - r0 : TR);
+#pragma unroll
+        for (int q = 0; q < PER; q++) {
+            const int x = t + 256 * q;
+            ra[q] = x < rows * M ? g.a[r0 * M + x] : 0.f;
+            rb[q] = x < rows * N ? g.b[r0 * N + x] : 0.f;
+        }
+    };
+    if (kb < ke) fetch(kb);
+    for (int64_t r0 = kb; r0 < ke; r0 += TR) {
+        const int rows = (int)(ke - r0 < TR ? ke - r0 : TR);
+#pragma unroll
+        for (int q = 0; q < PER; q++) {
+            as[t + 256 * q] = ra[q];
+            bs[t + 256 * q] = rb[q];
+        }
+        __syncthreads();
+        if (r0 + TR < ke) fetch(r0 + TR);
+        if (mn < 256) {
+            if (t < reps * mn) {
+                const int o = t % mn, rs = t / mn;
+                const int i = o / N, j = o % N;
+                for (int r = rs; r < rows; r += reps) acc[0] = fmaf(as[r * M + i], bs[r * N + j], acc[0]);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int o = t + 256 * q;
+                if (o < mn) {
+                    const int i = o / N, j = o % N;
+                    for (int r = 0; r < rows; r++) acc[q] = fmaf(as[r * M + i], bs[r * N + j], acc[q]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    float* out = part + (int64_t)blockIdx.x * mn;
+    if (mn < 256) {
+        sm[t] = acc[0];
+        __syncthreads();
+        if (t < mn) {
+            float s = 0.f;
+            for (int r = 0; r < reps; r++) s += sm[r * mn + t];
+            out[t] = s;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+            if (t + 256 * q < mn) out[t + 256 * q] = acc[q];
+    }
+}
+
+// Narrow contraction (K, N <= 64): a workgroup owns 64 output rows; their op(a) rows and
+// op(b) are staged in LDS with coalesced loads, and thread t computes outputs t, t+256, ...
+// of the 64 x N block (so stores are coalesced), summing k in order.
+__global__ __launch_bounds__(256) void gemm_narrow(GemmArgs g) {
+    __shared__ float as[64 * 65], bs[64 * 64];
+    const int K = g.K, N = g.N;
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int rows = (int)(g.M - r0 < 64 ? g.M - r0 : 64);
+    for (int x = threadIdx.x; x < K * N; x += 256) bs[x] = op_b(g, x / N, x % N);
+    if (g.trans_a) {  // a stored [K][M]: rows of the tile are columns, k-major
+        for (int x = threadIdx.x; x < K * 64; x += 256) {
+            const int kk = x / 64, rr = x % 64;
+            if (rr < rows) as[rr * 65 + kk] = g.a[(int64_t)kk * g.M + r0 + rr];
+        }
+    } else {  // the tile is one contiguous block of rows * K floats
+        for (int x = threadIdx.x; x < rows * K; x += 256) as[(x / K) * 65 + x % K] = g.a[r0 * K + x];
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < rows * N; o += 256) {
+        const int rr = o / N, j = o % N;
+        float acc = 0.f;
+        for (int kk = 0; kk < K; kk++) acc = fmaf(as[rr * 65 + kk], bs[kk * N + j], acc);
+        const int64_t ci = (r0 + rr) * N + j;
+        const float prev = g.accumulate ? g.c[ci] : 0.f;
+        g.c[ci] = prev + (acc + (g.bias ? g.bias[j] : 0.f));
+    }
+}
+
 struct Split {
     int splits;
     int32_t kchunk;
 };
+
+// Few outputs and a long k: the small-output kernel over fixed k ranges of at least 1024
+// (at most 2048 ranges); a transposed a, plain b.
+bool small_out_shape(int32_t m, int32_t k, int32_t n) { return m <= 32 && n <= 32 && k > 4096; }
+
+Split small_out_split(int32_t k) {
+    int64_t kc = ((int64_t)k + 2047) / 2048;
+    if (kc < 1024) kc = 1024;
+    Split s;
+    s.kchunk = (int32_t)kc;
+    s.splits = (int)(((int64_t)k + kc - 1) / kc);
+    return s;
+}
+
+bool narrow(int32_t k, int32_t n) { return k <= 64 && n <= 64; }
 
 int pick_bn(int32_t n) { return n <= 64 ? 64 : 128; }
 
@@ -248,8 +370,12 @@ using namespace gga;
 extern "C" size_t gga_linear_workspace(int32_t m, int32_t k, int32_t n) {
     if (m < 0 || k < 0 || n < 0) return 0;
     const Split s = pick_split(m, k, n);
-    if (s.splits <= 1) return 0;
-    return align_up((size_t)s.splits * m * n * sizeof(float), 256);
+    size_t need = s.splits <= 1 ? 0 : align_up((size_t)s.splits * m * n * sizeof(float), 256);
+    if (small_out_shape(m, k, n)) {  // (the choice also depends on the transposes)
+        const size_t so = align_up((size_t)small_out_split(k).splits * m * n * sizeof(float), 256);
+        need = so > need ? so : need;
+    }
+    return need;
 }
 
 namespace {
@@ -261,9 +387,36 @@ int linear_impl(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_
     if (!c || (k > 0 && (!a || !b))) return GGA_EINVAL;
     if ((int64_t)m * n >= ((int64_t)1 << 40)) return GGA_ERANGE;
     hipStream_t s = as_stream(stream);
-    const Split sp = pick_split(m, k, n);
     const size_t need = gga_linear_workspace(m, k, n);
     if (ws_bytes < need || (need > 0 && !ws)) return GGA_EWORKSPACE;
+    const bool so_path = small_out_shape(m, k, n) && trans_a && !trans_b;
+    if (so_path || narrow(k, n)) {
+        GemmArgs g{};
+        g.a = a;
+        g.b = b;
+        g.bias = bias;
+        g.c = c;
+        g.M = m;
+        g.K = k;
+        g.N = n;
+        g.trans_a = trans_a != 0;
+        g.trans_b = trans_b != 0;
+        g.accumulate = accumulate;
+        if (so_path) {
+            const Split so = small_out_split(k);
+            g.kchunk = so.kchunk;
+            gemm_small_out<<<(unsigned)so.splits, 256, 0, s>>>(g, static_cast<float*>(ws));
+            const int64_t mn = (int64_t)m * n;
+            splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(static_cast<const float*>(ws), so.splits, mn, n,
+                                                                    bias, accumulate, c);
+        } else {
+            const int64_t blocks = ((int64_t)m + 63) / 64;
+            if (blocks >= ((int64_t)1 << 31)) return GGA_ERANGE;
+            gemm_narrow<<<(unsigned)blocks, 256, 0, s>>>(g);
+        }
+        return launch_status();
+    }
+    const Split sp = pick_split(m, k, n);
     GemmArgs g{};
     g.a = a;
     g.b = b;

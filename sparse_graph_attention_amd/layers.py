@@ -34,15 +34,18 @@ def gat_forward(x: torch.Tensor, w: torch.Tensor, a_s: torch.Tensor, a_t: torch.
     hf = gga_linear(x, w).view(n, heads, c)
     s_src, s_dst = gga_gat_coef_fwd(hf, a_s, a_t)
     desc = make_desc(n, topo.e, heads, c, GGA_SCORE_ADDITIVE, GGA_F32, 1.0, negative_slope)
-    he = s_edge = None
+    g_e = s_edge = None
     if edge is None:
         out, lse = gga_local_attn_fwd(desc, s_dst, s_src, hf, topo.row_ptr, topo.col, topo.plan)
     else:
-        he = gga_linear(edge["f"], edge["w_e"]).view(topo.e, heads, c)
-        s_edge, _ = gga_gat_coef_fwd(he, edge["a_e"], None)
+        # s_edge[e,k] = a_e[k] . (F W_e)[e,k] = F[e] . G[:,k] with G[f,k] = a_e[k] . W_e[f,k]:
+        # the [E, K*C] edge state is never formed
+        fe = edge["f"].shape[1]
+        g_e, _ = gga_gat_coef_fwd(edge["w_e"].view(fe, heads, c), edge["a_e"], None)
+        s_edge = gga_linear(edge["f"], g_e)
         out, lse = gga_local_attn_fwd_edge(desc, s_dst, s_src, hf, s_edge, topo)
     res = out.view(n, heads * c) if concat else gga_head_mean(out)
-    return dict(out=res, hf=hf, s_src=s_src, s_dst=s_dst, lse=lse, desc=desc, out3=out, he=he, s_edge=s_edge)
+    return dict(out=res, hf=hf, s_src=s_src, s_dst=s_dst, lse=lse, desc=desc, out3=out, g_e=g_e, s_edge=s_edge)
 
 
 def gat_backward(x, w, a_s, a_t, d_out: torch.Tensor, fwd: dict, topo: Topology, concat: bool = True,
@@ -60,10 +63,13 @@ def gat_backward(x, w, a_s, a_t, d_out: torch.Tensor, fwd: dict, topo: Topology,
     else:
         d_sdst, d_ssrc, d_hf_attn, d_se = gga_local_attn_bwd_edge(fwd["desc"], fwd["s_dst"], fwd["s_src"], fwd["hf"],
                                                                   fwd["s_edge"], fwd["out3"], fwd["lse"], d3, topo)
-        d_he, d_a_e, _ = gga_gat_coef_bwd(fwd["he"], edge["a_e"], None, None, d_se, None)
-        dhe = d_he.view(topo.e, heads * c)
-        res.update(d_s_edge=d_se, d_a_e=d_a_e, d_w_e=gga_linear(edge["f"], dhe, trans_a=True),
-                   d_f=gga_linear(dhe, edge["w_e"], trans_b=True))
+        # dG = F^T d s_edge, dF = d s_edge G^T; through G[f,k] = a_e[k] . W_e[f,k]:
+        # dW_e[f,k,:] = dG[f,k] a_e[k] and da_e[k,:] = sum_f dG[f,k] W_e[f,k,:]
+        fe = edge["f"].shape[1]
+        d_g = gga_linear(edge["f"], d_se, trans_a=True)
+        d_w_e, d_a_e, _ = gga_gat_coef_bwd(edge["w_e"].view(fe, heads, c), edge["a_e"], None, None, d_g, None)
+        res.update(d_s_edge=d_se, d_a_e=d_a_e, d_w_e=d_w_e.view(fe, heads * c),
+                   d_f=gga_linear(d_se, fwd["g_e"], trans_b=True))
     d_hf, d_a_s, d_a_t = gga_gat_coef_bwd(fwd["hf"], a_s, a_t, d_hf_attn, d_ssrc, d_sdst)
     dh = d_hf.view(n, heads * c)
     d_w = gga_linear(x, dh, trans_a=True)
