@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
         L.orc_edge_values_bwd.restype = None
         L.orc_batch_edges.argtypes = [i32, P, P, P, P, P, P]
         L.orc_batch_edges.restype = i64
+        L.orc_relation_fwd.argtypes = [ctypes.c_int, i32, i32, i32, P, P, P, P, P, P, P, f64, P, i64, P, P]
+        L.orc_relation_fwd.restype = None
+        L.orc_relation_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, P, P, P]
+        L.orc_relation_bwd.restype = None
         L.orc_threads.argtypes = []
         L.orc_threads.restype = ctypes.c_int
         _lib = L
@@ -315,6 +319,139 @@ def gat_backward(x, w, a_s, a_t, d_out, g: Graph, slope: float = SLOPE, concat: 
         d_se = r["d_s_edge"]
         d_he = (d_se[..., None] * a_e[None]).reshape(f.shape[0], hh * c)
         res.update(d_s_edge=d_se, d_a_e=(d_se[..., None] * he).sum(0), d_w_e=f.T @ d_he, d_f=d_he @ w_e.T)
+    return res
+
+
+# --------------------------------------------------------------------------- relation-typed edges
+
+REL_SOFTMAX = 0  # softmax weighting of scaled q_v . k_{u,r} (GiGL "edge_type_attention")
+REL_MEAN = 1  # every in-edge weighs 1/deg(v) (GiGL "edge_type_linear")
+
+
+def relation_of_segments(e: int, segments, n_rel: int):
+    """Relation of each packed edge row from host-side (relation, start, end) segments
+    (GiGL pull request "Support relation message modes on the packed
+    GraphTransformerEncoder path", section "Approach": relation edges travel as packed
+    rows with per-relation segments).  Segments are taken in order; each starts where the
+    previous one ended (the first at 0, the last ends at e), may be empty, and names a
+    relation in [0, n_rel).  Anything else raises ValueError.  Pinned by a brute-force
+    membership loop."""
+    rel = np.empty(int(e), np.int32)
+    pos = 0
+    for r, start, end in segments:
+        r, start, end = int(r), int(start), int(end)
+        if start != pos or end < start or end > e or not 0 <= r < n_rel:
+            raise ValueError(f"bad relation segment ({r}, {start}, {end})")
+        rel[start:end] = r
+        pos = end
+    if pos != e:
+        raise ValueError("relation segments do not cover the edge list")
+    return rel
+
+
+def relation_rows(src, rel, n: int, n_rel: int):
+    """Row of the stacked per-relation projection that edge e reads: a projection of all
+    nodes by the R relation transforms side by side is [N, R*W], which viewed as
+    [N*R, W] holds x_u W^r in row u*R + r.  A source outside [0, n) gives -1 and is
+    counted.  This is a layout convention, not a formula of the pages; pinned by indexing
+    the stacked projection (library matmul) against the per-relation products."""
+    src, rel = _i32(src), _i32(rel)
+    ok = (src >= 0) & (src < n)
+    out = np.where(ok, src.astype(np.int64) * n_rel + rel, -1).astype(np.int32)
+    return out, int((~ok).sum())
+
+
+def relation_projections(x, w_q, w_k, w_v, heads: int):
+    """q = X W_Q [N,H,C] (None when w_q is None) and the per-relation key and message
+    transforms key[r] = X W_K^r, val[r] = X W_V^r, each [R,N,H,C] (GiGL "Approach":
+    per-relation transforms).  w_k, w_v are [R, d, H*C]; w_k may be None."""
+    x = _f64(x)
+    n = x.shape[0]
+    w_v = _f64(w_v)
+    n_rel, _, width = w_v.shape
+    c = width // heads
+    val = np.stack([x @ w_v[r] for r in range(n_rel)]).reshape(n_rel, n, heads, c)
+    q = None if w_q is None else (x @ _f64(w_q)).reshape(n, heads, c)
+    key = None if w_k is None else np.stack([x @ _f64(w_k)[r] for r in range(n_rel)]).reshape(n_rel, n, heads, c)
+    return q, key, val
+
+
+def relation_attention(q, key, val, src, dst, rel, mode: int, scale=None, rows=None):
+    """Relation-typed message aggregation (GiGL "Approach": per-relation transforms, mean
+    or softmax weighting, scatter-add).  Edge e: u -> v of relation r carries val[r, u];
+    in softmax mode its head-h score is scale * q[v,h] . key[r,u,h] and the weights of
+    v's in-edges (all relations together) are their softmax; in mean mode each weighs
+    1/deg(v).  Returns out [R',H,C] and lse [R',H] for rows (all N by default); a row
+    with no in-edges gets 0 and -inf.  Pinned by autograd through a dense masked
+    formulation (library), the one-relation reduction to plain dot attention, a
+    scatter-mean (library) and relabelling invariance."""
+    val = _f64(val)
+    n_rel, n, hh, c = val.shape
+    if scale is None:
+        scale = c ** -0.5
+    row_ptr, col, eid = coo_to_csr(n, dst, src)
+    rel = _i32(rel)
+    r, nr = _rows(rows)
+    nr = n if r is None else nr
+    out = np.empty((nr, hh, c), np.float64)
+    lse = np.empty((nr, hh), np.float64)
+    qd = None if mode == REL_MEAN else _f64(q)
+    kd = None if mode == REL_MEAN else _f64(key)
+    lib().orc_relation_fwd(mode, n, hh, c, _p(qd), _p(kd), _p(val), _p(row_ptr), _p(col), _p(rel), _p(eid),
+                           float(scale), _p(r), nr, _p(out), _p(lse))
+    return out, lse
+
+
+def relation_attention_bwd(q, key, val, d_out, src, dst, rel, mode: int, scale=None):
+    """Gradients of sum(out * d_out) for relation_attention: d_q [N,H,C] and d_key,
+    d_val [R,N,H,C] (d_q, d_key are None in mean mode, whose weights are constants)."""
+    val = _f64(val)
+    n_rel, n, hh, c = val.shape
+    if scale is None:
+        scale = c ** -0.5
+    row_ptr, col, eid = coo_to_csr(n, dst, src)
+    rel = _i32(rel)
+    d_val = np.empty_like(val)
+    d_q = d_key = qd = kd = None
+    if mode == REL_SOFTMAX:
+        qd, kd = _f64(q), _f64(key)
+        d_q, d_key = np.empty_like(qd), np.empty_like(kd)
+    lib().orc_relation_bwd(mode, n, n_rel, hh, c, _p(qd), _p(kd), _p(val), _p(_f64(d_out)), _p(row_ptr), _p(col),
+                           _p(rel), _p(eid), float(scale), _p(d_q), _p(d_key), _p(d_val))
+    return dict(d_q=d_q, d_key=d_key, d_val=d_val)
+
+
+def relation_forward(x, w_q, w_k, w_v, src, dst, rel, heads: int, mode: int, rows=None):
+    """Relation message layer: the projections then relation_attention.  Returns out
+    [N, H*C] (rows only, when given) with the intermediates."""
+    q, key, val = relation_projections(x, w_q if mode == REL_SOFTMAX else None,
+                                       w_k if mode == REL_SOFTMAX else None, w_v, heads)
+    out, lse = relation_attention(q, key, val, src, dst, rel, mode, rows=rows)
+    return dict(out=out.reshape(out.shape[0], -1), lse=lse, q=q, key=key, val=val)
+
+
+def relation_backward(x, w_q, w_k, w_v, src, dst, rel, heads: int, mode: int, d_out):
+    """dX, dW_Q, dW_K, dW_V of sum(out * d_out): the attention gradients, then for each
+    transform dW = X^T dY and dX = sum of dY W^T (dW_Q, dW_K are None in mean mode)."""
+    x = _f64(x)
+    n = x.shape[0]
+    soft = mode == REL_SOFTMAX
+    q, key, val = relation_projections(x, w_q if soft else None, w_k if soft else None, w_v, heads)
+    n_rel, _, hh, c = val.shape
+    g = relation_attention_bwd(q, key, val, _f64(d_out).reshape(n, hh, c), src, dst, rel, mode)
+    w_v = _f64(w_v)
+    dv = g["d_val"].reshape(n_rel, n, hh * c)
+    d_w_v = np.stack([x.T @ dv[r] for r in range(n_rel)])
+    d_x = sum(dv[r] @ w_v[r].T for r in range(n_rel))
+    res = dict(d_w_v=d_w_v, d_w_q=None, d_w_k=None, d_q=g["d_q"], d_key=g["d_key"], d_val=g["d_val"])
+    if soft:
+        w_q, w_k = _f64(w_q), _f64(w_k)
+        dq = g["d_q"].reshape(n, hh * c)
+        dk = g["d_key"].reshape(n_rel, n, hh * c)
+        res["d_w_q"] = x.T @ dq
+        res["d_w_k"] = np.stack([x.T @ dk[r] for r in range(n_rel)])
+        d_x = d_x + dq @ w_q.T + sum(dk[r] @ w_k[r].T for r in range(n_rel))
+    res["d_x"] = d_x
     return res
 
 

@@ -326,6 +326,150 @@ int64_t orc_batch_edges(int32_t b, const int32_t *node_ptr, const int32_t *edge_
     return bad;
 }
 
+/*
+ * Relation-typed messages (GiGL pull request "Support relation message modes on the
+ * packed GraphTransformerEncoder path", section "Approach": per-relation transforms,
+ * mean or softmax weighting, scatter-add into the targets).  Edge e: u -> v of relation
+ * r carries the message val_r[u] = x_u W_V^r; in softmax mode its score for head h is
+ * scale * q[v,h] . key_r[u,h] with key_r[u] = x_u W_K^r.  The weights of v's in-edges
+ * (all relations together) are the target softmax of those scores (softmax mode) or
+ * 1/deg(v) each (mean mode); out[v] = sum of weight * message.
+ *
+ * Per-relation tensors are [R, N, H, C]; rel is the relation of each COO edge and eid
+ * the COO index of each CSR position, so the relation of CSR position p is rel[eid[p]].
+ * mode 0: softmax (q, key needed); mode 1: mean (q, key unused, may be NULL).
+ * lse[v,h] is the log of the softmax normaliser (log deg(v) in mean mode); a row with
+ * no in-edges gets out = 0 and lse = -inf.
+ */
+static const double *rel_row(const double *t, int32_t n, int32_t hh, int32_t c, int32_t r, int64_t u, int h) {
+    return t + ((((size_t)r * n + (size_t)u) * hh + h) * c);
+}
+
+static void relation_weights(int mode, int32_t n, int32_t hh, int32_t c, const double *q, const double *key,
+                             int64_t v, int h, const int32_t *row_ptr, const int32_t *col, const int32_t *rel,
+                             const int32_t *eid, double scale, double *s, double *a, double *lse) {
+    const int64_t b = row_ptr[v], deg = row_ptr[v + 1] - b;
+    if (deg == 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    if (mode == 1) {
+        for (int64_t j = 0; j < deg; j++) a[j] = 1.0 / (double)deg;
+        *lse = log((double)deg);
+        return;
+    }
+    const double *qv = q + ((size_t)v * hh + h) * c;
+    for (int64_t j = 0; j < deg; j++) {
+        const double *k = rel_row(key, n, hh, c, rel[eid[b + j]], col[b + j], h);
+        double d = 0.0;
+        for (int i = 0; i < c; i++) d += qv[i] * k[i];
+        s[j] = d * scale;
+    }
+    *lse = row_softmax(s, deg, a);
+}
+
+void orc_relation_fwd(int mode, int32_t n, int32_t hh, int32_t c, const double *q, const double *key,
+                      const double *val, const int32_t *row_ptr, const int32_t *col, const int32_t *rel,
+                      const int32_t *eid, double scale, const int32_t *rows, int64_t n_rows, double *out,
+                      double *lse) {
+    int64_t maxdeg = 0;
+    for (int64_t v = 0; v < n; v++)
+        if (row_ptr[v + 1] - row_ptr[v] > maxdeg) maxdeg = row_ptr[v + 1] - row_ptr[v];
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(maxdeg + 1));
+        double *a = (double *)malloc(sizeof(double) * (size_t)(maxdeg + 1));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t i = 0; i < n_rows; i++) {
+            const int64_t v = ROW(rows, i);
+            const int64_t b = row_ptr[v], deg = row_ptr[v + 1] - b;
+            for (int h = 0; h < hh; h++) {
+                double *o = out + ((size_t)i * hh + h) * c;
+                for (int x = 0; x < c; x++) o[x] = 0.0;
+                relation_weights(mode, n, hh, c, q, key, v, h, row_ptr, col, rel, eid, scale, s, a,
+                                 &lse[(size_t)i * hh + h]);
+                for (int64_t j = 0; j < deg; j++) {
+                    const double *m = rel_row(val, n, hh, c, rel[eid[b + j]], col[b + j], h);
+                    for (int x = 0; x < c; x++) o[x] += a[j] * m[x];
+                }
+            }
+        }
+        free(s);
+        free(a);
+    }
+}
+
+/*
+ * First-order gradients of sum(out * d_out) for orc_relation_fwd over all rows.  Per edge
+ * e (target v, source u, relation r) and head h, with weight a_e, da_e = d_out[v] . val_r[u]
+ * and D_v = d_out[v] . out[v]:
+ *   d_val_r[u]  += a_e d_out[v]
+ *   softmax mode, ds_e = a_e (da_e - D_v):  d_q[v] += scale ds_e key_r[u],
+ *                                            d_key_r[u] += scale ds_e q[v]
+ * The mean weights do not depend on the inputs.  Rows are visited in order and each
+ * head's sums touch that head's slice only, so the result does not depend on the thread
+ * count.  d_q and d_key may be NULL in mean mode.
+ */
+void orc_relation_bwd(int mode, int32_t n, int32_t n_rel, int32_t hh, int32_t c, const double *q,
+                      const double *key, const double *val, const double *d_out, const int32_t *row_ptr,
+                      const int32_t *col, const int32_t *rel, const int32_t *eid, double scale, double *d_q,
+                      double *d_key, double *d_val) {
+    const size_t rel_size = (size_t)n_rel * n * hh * c;
+    memset(d_val, 0, sizeof(double) * rel_size);
+    if (mode == 0) {
+        memset(d_key, 0, sizeof(double) * rel_size);
+        memset(d_q, 0, sizeof(double) * (size_t)n * hh * c);
+    }
+    int64_t maxdeg = 0;
+    for (int64_t v = 0; v < n; v++)
+        if (row_ptr[v + 1] - row_ptr[v] > maxdeg) maxdeg = row_ptr[v + 1] - row_ptr[v];
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(maxdeg + 1));
+        double *a = (double *)malloc(sizeof(double) * (size_t)(maxdeg + 1));
+        double *o = (double *)malloc(sizeof(double) * (size_t)c);
+#pragma omp for schedule(static, 1)
+        for (int h = 0; h < hh; h++) {
+            for (int64_t v = 0; v < n; v++) {
+                const int64_t b = row_ptr[v], deg = row_ptr[v + 1] - b;
+                if (deg == 0) continue;
+                double lse;
+                relation_weights(mode, n, hh, c, q, key, v, h, row_ptr, col, rel, eid, scale, s, a, &lse);
+                const double *g = d_out + ((size_t)v * hh + h) * c;
+                for (int x = 0; x < c; x++) o[x] = 0.0;
+                for (int64_t j = 0; j < deg; j++) {
+                    const double *m = rel_row(val, n, hh, c, rel[eid[b + j]], col[b + j], h);
+                    for (int x = 0; x < c; x++) o[x] += a[j] * m[x];
+                }
+                double dd = 0.0;
+                for (int x = 0; x < c; x++) dd += g[x] * o[x];
+                const double *qv = mode == 0 ? q + ((size_t)v * hh + h) * c : NULL;
+                double *dq = mode == 0 ? d_q + ((size_t)v * hh + h) * c : NULL;
+                for (int64_t j = 0; j < deg; j++) {
+                    const int32_t r = rel[eid[b + j]];
+                    const int64_t u = col[b + j];
+                    const double *m = rel_row(val, n, hh, c, r, u, h);
+                    double *dm = d_val + (rel_row(val, n, hh, c, r, u, h) - val);
+                    for (int x = 0; x < c; x++) dm[x] += a[j] * g[x];
+                    if (mode != 0) continue;
+                    double da = 0.0;
+                    for (int x = 0; x < c; x++) da += g[x] * m[x];
+                    const double ds = a[j] * (da - dd) * scale;
+                    const double *k = rel_row(key, n, hh, c, r, u, h);
+                    double *dk = d_key + (k - key);
+                    for (int x = 0; x < c; x++) {
+                        dq[x] += ds * k[x];
+                        dk[x] += ds * qv[x];
+                    }
+                }
+            }
+        }
+        free(s);
+        free(a);
+        free(o);
+    }
+}
+
 int orc_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);
