@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GGA_ABI_VERSION 1
+#define GGA_ABI_VERSION 2
 
 /* status codes */
 #define GGA_OK 0
@@ -60,6 +60,7 @@ extern "C" {
 /* score of edge u -> v */
 #define GGA_SCORE_DOT 0      /* scale * q[v,h,:] . k[u,h,:] */
 #define GGA_SCORE_ADDITIVE 1 /* LeakyReLU(s_src[u,h] + s_dst[v,h]) */
+#define GGA_SCORE_MEAN 2     /* no score: every in-edge of v weighs 1/deg(v) */
 
 int gga_abi_version(void);
 const char *gga_status_string(int status);
@@ -106,11 +107,11 @@ typedef struct gga_local_desc {
     int32_t heads;        /* H */
     int64_t e;            /* edges (length of col) */
     int32_t head_dim;     /* C (r): per-head width */
-    int32_t score;        /* GGA_SCORE_DOT or GGA_SCORE_ADDITIVE */
+    int32_t score;        /* GGA_SCORE_DOT, GGA_SCORE_ADDITIVE or GGA_SCORE_MEAN */
     int32_t dtype;        /* storage type of q, k, v (dot) or of v (additive) */
     float scale;          /* dot: multiplier of q.k, usually 1/sqrt(C) */
     float negative_slope; /* additive: LeakyReLU slope, usually 0.2 */
-    int32_t reserved;     /* must be 0 */
+    int32_t n_src;        /* rows of the source-side tensors (ks, v); 0 means n */
 } gga_local_desc;
 
 /*
@@ -122,12 +123,18 @@ typedef struct gga_local_desc {
  *   dot:      s_e = scale * q[v,h,:] . k[u,h,:]      (qs = q, ks = k: [n,H,C])
  *   additive: s_e = LeakyReLU(s_src[u,h] + s_dst[v,h]) (qs = s_dst, ks = s_src:
  *             fp32 [n,H])
+ *   mean:     s_e = 0, so alpha_e = 1/deg(v)         (qs, ks unused, may be NULL;
+ *             GiGL pull request "Support relation message modes on the packed
+ *             GraphTransformerEncoder path", section "Approach": mean weighting)
  *   alpha_e = exp(s_e - max) / sum exp(s - max)       (per v, h)
  *   out[v,h,:] = sum_e alpha_e v[u,h,:]               (fp32 [n,H,C])
  *   lse[v,h] = log sum_e exp(s_e)                     (fp32 [n,H]; may be NULL)
  * A row with no in-edges gets out = 0 and lse = -inf.  Heads are normalised
  * independently and concatenated.  `plan` comes from gga_plan_build on the same
  * row_ptr.  Deterministic: the same inputs give bit-identical outputs.
+ * Sources and targets may index different row sets: with d->n_src > 0 the
+ * source-side tensors (k or s_src, and v) have n_src rows and col holds ids in
+ * [0, n_src), e.g. one row per (node, relation) pair (gga_relation_sources).
  */
 size_t gga_local_attn_fwd_workspace(const gga_local_desc *d);
 int gga_local_attn_fwd(const gga_local_desc *d, const void *qs, const void *ks, const void *v,
@@ -143,17 +150,42 @@ int gga_local_attn_fwd(const gga_local_desc *d, const void *qs, const void *ks, 
  *             d_ks = dk[u] = sum_{e out of u} ds_e scale q[v]        fp32 [n,H,C]
  *   additive: d_qs = d s_dst[v] = sum_{e into v} ds_e LeakyReLU'(z_e) fp32 [n,H]
  *             d_ks = d s_src[u] = sum_{e out of u} ds_e LeakyReLU'(z_e)
- *   both:     d_v[u] = sum_{e out of u} alpha_e d_out[v]              fp32 [n,H,C]
+ *   all:      d_v[u] = sum_{e out of u} alpha_e d_out[v]              fp32 [n,H,C]
  * Sums over the edges out of u walk the CSR by source (row_ptr_s, col_s with
  * plan_s), grouping edge gradients by the selected endpoint (section "Endpoint
  * projection", backward), so no floating-point atomics are used and results are
  * deterministic.  `out` and `lse` are the forward's outputs.
+ * Mean mode has constant weights 1/deg(v) (taken from row_ptr): only d_v is
+ * written; qs, ks, out, lse, d_qs and d_ks are unused and may be NULL.
+ * With d->n_src > 0, d_ks and d_v have n_src rows and the CSR by source (row_ptr_s
+ * with n_src + 1 entries, plan_s built for n_src rows) is keyed by source ids in
+ * [0, n_src).
  */
 size_t gga_local_attn_bwd_workspace(const gga_local_desc *d);
 int gga_local_attn_bwd(const gga_local_desc *d, const void *qs, const void *ks, const void *v, const float *out,
                        const float *lse, const float *d_out, const int32_t *row_ptr, const int32_t *col,
                        const void *plan, const int32_t *row_ptr_s, const int32_t *col_s, const void *plan_s,
                        float *d_qs, float *d_ks, float *d_v, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Relation-typed edges (GiGL pull request "Support relation message modes on the
+ * packed GraphTransformerEncoder path", section "Approach": relation edges travel as
+ * packed rows (target, source, relation) with host-side (relation, start, end)
+ * segments, and messages go through per-relation transforms).  Maps each edge to the
+ * row of a per-relation node tensor: projecting all n nodes by the R transforms side
+ * by side gives [n, R*W], which viewed as [n*R, W] holds node u under relation r in
+ * row u*R + r.  So
+ *   src_rel[i] = src[i] * R + r   for the segment (r, start, end) with start <= i < end
+ * and the local attention calls run with d->n_src = n*R over (src_rel, dst).
+ * seg is HOST memory: n_seg triples (relation, start, end) of int32, in order, each
+ * starting where the previous ended (the first at 0, the last ending at e), possibly
+ * empty, with relation in [0, R); anything else returns GGA_EINVAL.  A src outside
+ * [0, n) is written as -1 and a dst outside [0, n) is left as it is; both are counted
+ * in the device int *d_bad (cleared first): run no compute call on a nonzero count.
+ * n * R must be < 2^31 (GGA_ERANGE).  Bit-exact.
+ */
+int gga_relation_sources(int32_t n, int32_t relations, int64_t e, const int32_t *src, const int32_t *dst,
+                         int32_t n_seg, const int32_t *seg, int32_t *src_rel, int32_t *d_bad, void *stream);
 
 /*
  * Endpoint projection (Tinymesh "Sparse attention experiment", section

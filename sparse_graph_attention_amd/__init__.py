@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libgga.so")
 
 GGA_OK, GGA_EINVAL, GGA_ERANGE, GGA_EUNSUPPORTED, GGA_EWORKSPACE, GGA_EHIP = range(6)
 GGA_F32, GGA_BF16 = 0, 1
-GGA_SCORE_DOT, GGA_SCORE_ADDITIVE = 0, 1
+GGA_SCORE_DOT, GGA_SCORE_ADDITIVE, GGA_SCORE_MEAN = 0, 1, 2
 
 
 class GGAError(RuntimeError):
@@ -39,7 +39,7 @@ class gga_local_desc(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("negative_slope", ctypes.c_float),
-        ("reserved", ctypes.c_int32),
+        ("n_src", ctypes.c_int32),
     ]
 
 
@@ -81,6 +81,7 @@ def _load() -> ctypes.CDLL:
         "gga_global_linear_bwd_workspace": ([i32, i32, i32], sz),
         "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_batch_edges": ([i32, P, P, i64, P, P, P, P, P, P], ctypes.c_int),
+        "gga_relation_sources": ([i32, i32, i64, P, P, i32, P, P, P, P], ctypes.c_int),
         "gga_local_attn_fwd_edge_workspace": ([D], sz),
         "gga_local_attn_fwd_edge": ([D, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_local_attn_bwd_edge_workspace": ([D], sz),
@@ -196,10 +197,13 @@ def gga_plan_build(n: int, e: int, row_ptr: torch.Tensor, plan=None, ws=None, st
 class Topology:
     """A fixed graph on the device: the CSR by destination with its plan and, when
     ``backward`` is set, the CSR by source with its plan (built by the entry points
-    above; this class only keeps the tensors together)."""
+    above; this class only keeps the tensors together).  Sources index n_src rows
+    (default n), e.g. the (node, relation) rows of gga_relation_sources."""
 
-    def __init__(self, n: int, src: torch.Tensor, dst: torch.Tensor, backward: bool = False, stream=None):
+    def __init__(self, n: int, src: torch.Tensor, dst: torch.Tensor, backward: bool = False, stream=None,
+                 n_src: int | None = None):
         self.n = int(n)
+        self.n_src = self.n if n_src is None else int(n_src)
         self.e = int(src.numel())
         self.src, self.dst = src, dst
         self.row_ptr, self.col, self.eid = gga_coo_to_csr(n, dst, src, stream=stream)
@@ -209,17 +213,17 @@ class Topology:
             self.build_source_csr(stream)
 
     def build_source_csr(self, stream=None):
-        self.row_ptr_s, self.col_s, self.eid_s = gga_coo_to_csr(self.n, self.src, self.dst, stream=stream)
-        self.plan_s = gga_plan_build(self.n, self.e, self.row_ptr_s, stream=stream)
+        self.row_ptr_s, self.col_s, self.eid_s = gga_coo_to_csr(self.n_src, self.src, self.dst, stream=stream)
+        self.plan_s = gga_plan_build(self.n_src, self.e, self.row_ptr_s, stream=stream)
 
 
 # --------------------------------------------------------------------------- local attention
 
 
-def make_desc(n, e, heads, head_dim, score, dtype, scale=None, negative_slope=0.2) -> gga_local_desc:
+def make_desc(n, e, heads, head_dim, score, dtype, scale=None, negative_slope=0.2, n_src=0) -> gga_local_desc:
     if scale is None:
         scale = head_dim ** -0.5 if head_dim > 0 else 1.0
-    return gga_local_desc(n, heads, e, head_dim, score, dtype, scale, negative_slope, 0)
+    return gga_local_desc(n, heads, e, head_dim, score, dtype, scale, negative_slope, n_src)
 
 
 def gga_local_attn_fwd(desc: gga_local_desc, qs, ks, v, row_ptr, col, plan, out=None, lse=None, want_lse=True,
@@ -239,11 +243,13 @@ def gga_local_attn_fwd(desc: gga_local_desc, qs, ks, v, row_ptr, col, plan, out=
 
 def gga_local_attn_bwd(desc: gga_local_desc, qs, ks, v, out, lse, d_out, topo: Topology, d_qs=None, d_ks=None,
                        d_v=None, ws=None, stream=None):
-    dev = v.device
-    qs_shape = (desc.n, desc.heads, desc.head_dim) if desc.score == GGA_SCORE_DOT else (desc.n, desc.heads)
-    d_qs = torch.empty(qs_shape, dtype=torch.float32, device=dev) if d_qs is None else d_qs
-    d_ks = torch.empty(qs_shape, dtype=torch.float32, device=dev) if d_ks is None else d_ks
-    d_v = torch.empty(desc.n, desc.heads, desc.head_dim, dtype=torch.float32, device=dev) if d_v is None else d_v
+    dev = d_out.device
+    ns = desc.n_src if desc.n_src > 0 else desc.n
+    if desc.score != GGA_SCORE_MEAN:
+        tail = (desc.heads, desc.head_dim) if desc.score == GGA_SCORE_DOT else (desc.heads,)
+        d_qs = torch.empty((desc.n,) + tail, dtype=torch.float32, device=dev) if d_qs is None else d_qs
+        d_ks = torch.empty((ns,) + tail, dtype=torch.float32, device=dev) if d_ks is None else d_ks
+    d_v = torch.empty(ns, desc.heads, desc.head_dim, dtype=torch.float32, device=dev) if d_v is None else d_v
     nb = lib.gga_local_attn_bwd_workspace(ctypes.byref(desc))
     ws = _workspace(nb, dev, ws)
     _check("gga_local_attn_bwd", lib.gga_local_attn_bwd(
@@ -427,6 +433,20 @@ def gga_batch_edges(node_ptr: torch.Tensor, edge_ptr: torch.Tensor, src_local: t
     return src, dst, d_bad
 
 
+def gga_relation_sources(n: int, relations: int, src: torch.Tensor, dst: torch.Tensor, segments, src_rel=None,
+                         d_bad=None, stream=None):
+    """Source rows of relation-typed edges; ``segments`` is host data: (relation, start,
+    end) triples.  Returns (src_rel, d_bad)."""
+    e = src.numel()
+    dev = src.device
+    seg = (ctypes.c_int32 * max(1, 3 * len(segments)))(*[int(x) for t in segments for x in t])
+    src_rel = torch.empty(e, dtype=torch.int32, device=dev) if src_rel is None else src_rel
+    d_bad = torch.empty(1, dtype=torch.int32, device=dev) if d_bad is None else d_bad
+    _check("gga_relation_sources", lib.gga_relation_sources(n, relations, e, _ptr(src), _ptr(dst), len(segments),
+                                                            seg, _ptr(src_rel), _ptr(d_bad), _stream(stream)))
+    return src_rel, d_bad
+
+
 def gga_global_linear_batch_fwd(node_ptr, q, k, v, eps=1e-6, s_out=None, z_out=None, g_out=None, ws=None,
                                 stream=None):
     n, heads, r = q.shape
@@ -478,9 +498,10 @@ def gga_local_attn_bwd_edge(desc: gga_local_desc, s_dst, s_src, hf, s_edge, out,
     """Returns d s_dst, d s_src, d hf (aggregation part) and d s_edge (COO order)."""
     dev = hf.device
     n, heads, c = desc.n, desc.heads, desc.head_dim
+    ns = desc.n_src if desc.n_src > 0 else n
     d_s_dst = torch.empty(n, heads, dtype=torch.float32, device=dev) if d_s_dst is None else d_s_dst
-    d_s_src = torch.empty(n, heads, dtype=torch.float32, device=dev) if d_s_src is None else d_s_src
-    d_hf = torch.empty(n, heads, c, dtype=torch.float32, device=dev) if d_hf is None else d_hf
+    d_s_src = torch.empty(ns, heads, dtype=torch.float32, device=dev) if d_s_src is None else d_s_src
+    d_hf = torch.empty(ns, heads, c, dtype=torch.float32, device=dev) if d_hf is None else d_hf
     d_s_edge = torch.empty(desc.e, heads, dtype=torch.float32, device=dev) if d_s_edge is None else d_s_edge
     nb = lib.gga_local_attn_bwd_edge_workspace(ctypes.byref(desc))
     ws = _workspace(nb, dev, ws)

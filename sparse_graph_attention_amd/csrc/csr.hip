@@ -176,6 +176,34 @@ __global__ void batch_edges_kernel(int32_t batch, const int32_t* __restrict__ no
     if (local) atomicAdd(bad, local);
 }
 
+// Relation-typed edges: a launch covers up to kRelSegs consecutive host-side segments,
+// passed by value; edge i takes the relation of the last segment starting at or before i
+// (segments are contiguous and ordered, so that is the one holding i).
+constexpr int kRelSegs = 32;
+
+struct RelSegs {
+    int32_t rel[kRelSegs];
+    int32_t start[kRelSegs];
+    int32_t count;
+};
+
+__global__ void relation_sources_kernel(int32_t n, int32_t n_rel, int64_t lo, int64_t hi, RelSegs sg,
+                                        const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
+                                        int32_t* __restrict__ out, int32_t* __restrict__ bad) {
+    int local = 0;
+    for (int64_t i = lo + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < hi;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        int32_t r = sg.rel[0];
+        for (int k = 1; k < sg.count; k++)
+            if ((int64_t)sg.start[k] <= i) r = sg.rel[k];
+        const int32_t u = src[i];
+        const bool ok = (uint32_t)u < (uint32_t)n;
+        out[i] = ok ? u * n_rel + r : -1;
+        local += !ok + ((uint32_t)dst[i] >= (uint32_t)n);
+    }
+    if (local) atomicAdd(bad, local);
+}
+
 int key_bits(int32_t n) {
     if (n <= 1) return 0;
     uint32_t m = (uint32_t)(n - 1);
@@ -284,5 +312,36 @@ extern "C" int gga_batch_edges(int32_t batch, const int32_t* node_ptr, const int
     fill_i32(d_bad, 1, 0, s);
     if (e > 0) batch_edges_kernel<<<grid_for(e), 256, 0, s>>>(batch, node_ptr, edge_ptr, e, src_local, dst_local, src,
                                                               dst, d_bad);
+    return launch_status();
+}
+
+extern "C" int gga_relation_sources(int32_t n, int32_t relations, int64_t e, const int32_t* src, const int32_t* dst,
+                                    int32_t n_seg, const int32_t* seg, int32_t* src_rel, int32_t* d_bad,
+                                    void* stream) {
+    if (n < 0 || relations < 1 || e < 0 || n_seg < 0 || !d_bad) return GGA_EINVAL;
+    if (e >= (int64_t)INT32_MAX || (int64_t)n * relations >= (int64_t)INT32_MAX) return GGA_ERANGE;
+    if (e > 0 && (!src || !dst || !src_rel)) return GGA_EINVAL;
+    if (n_seg > 0 && !seg) return GGA_EINVAL;
+    int64_t pos = 0;
+    for (int32_t k = 0; k < n_seg; k++) {
+        const int32_t r = seg[3 * k], start = seg[3 * k + 1], end = seg[3 * k + 2];
+        if (r < 0 || r >= relations || start != pos || end < start || end > e) return GGA_EINVAL;
+        pos = end;
+    }
+    if (pos != e) return GGA_EINVAL;
+    hipStream_t s = as_stream(stream);
+    fill_i32(d_bad, 1, 0, s);
+    for (int32_t k0 = 0; k0 < n_seg; k0 += kRelSegs) {
+        RelSegs sg{};
+        sg.count = n_seg - k0 < kRelSegs ? n_seg - k0 : kRelSegs;
+        for (int k = 0; k < sg.count; k++) {
+            sg.rel[k] = seg[3 * (k0 + k)];
+            sg.start[k] = seg[3 * (k0 + k) + 1];
+        }
+        const int64_t lo = sg.start[0], hi = seg[3 * (k0 + sg.count - 1) + 2];
+        if (hi > lo)
+            relation_sources_kernel<<<grid_for(hi - lo), 256, 0, s>>>(n, relations, lo, hi, sg, src, dst, src_rel,
+                                                                      d_bad);
+    }
     return launch_status();
 }

@@ -13,10 +13,17 @@ struct BwdWs {
     size_t bytes;
 };
 
+// Width of the score-side gradients: q/k rows (dot), one value per head (additive),
+// none (mean).
+int64_t score_width(const gga_local_desc* d) {
+    const int64_t W = (int64_t)d->heads * d->head_dim;
+    return d->score == GGA_SCORE_DOT ? W : d->score == GGA_SCORE_MEAN ? 0 : d->heads;
+}
+
 BwdWs carve_bwd(void* ws, const gga_local_desc* d) {
     const PlanBounds b = plan_bounds(d->e);
     const int64_t W = (int64_t)d->heads * d->head_dim;
-    const int64_t wk = d->score == GGA_SCORE_DOT ? W : d->heads;
+    const int64_t wk = score_width(d);
     BwdWs w;
     w.stride_a = (int32_t)align_up((size_t)wk, 8);
     w.stride_b = (int32_t)(align_up((size_t)wk, 8) + align_up((size_t)W, 8));
@@ -49,13 +56,24 @@ size_t edge_ws_bytes(const gga_local_desc* d) {
     return c.bytes();
 }
 
+// No targets: every source-side gradient is zero.
+int zero_source_grads(const gga_local_desc* d, float* d_ks, float* d_v, hipStream_t s) {
+    const int64_t ns = source_rows(d), wk = score_width(d);
+    if (ns == 0) return GGA_OK;
+    if (!d_v || (wk > 0 && !d_ks)) return GGA_EINVAL;
+    if (wk > 0) fill_f32(d_ks, ns * wk, 0.f, s);
+    fill_f32(d_v, ns * (int64_t)d->heads * d->head_dim, 0.f, s);
+    return launch_status();
+}
+
 int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void* v, const float* out,
              const float* lse, const float* d_out, const int32_t* row_ptr, const int32_t* col, const void* plan,
              const int32_t* row_ptr_s, const int32_t* col_s, const void* plan_s, float* d_qs, float* d_ks,
              float* d_v, const EdgeWs* ew, void* ws, size_t ws_bytes, hipStream_t s) {
-    if (!qs || !out || !lse || !d_out || !row_ptr || !plan || !row_ptr_s || !plan_s || !d_qs || !d_ks || !d_v)
-        return GGA_EINVAL;
-    if (d->e > 0 && (!ks || !v || !col || !col_s)) return GGA_EINVAL;
+    const bool mean = d->score == GGA_SCORE_MEAN;
+    if (!d_out || !row_ptr || !plan || !row_ptr_s || !plan_s || !d_v) return GGA_EINVAL;
+    if (!mean && (!qs || !out || !lse || !d_qs || !d_ks)) return GGA_EINVAL;
+    if (d->e > 0 && (!col || !col_s || (!mean && (!ks || !v)))) return GGA_EINVAL;
     for (const void* p : {qs, ks, v, (const void*)out, (const void*)d_out, (const void*)d_qs, (const void*)d_ks,
                           (const void*)d_v})
         if (p && !aligned16(p)) return GGA_EINVAL;
@@ -63,18 +81,21 @@ int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
     if (ws_bytes < need.bytes || !ws) return GGA_EWORKSPACE;
     const BwdWs w = carve_bwd(ws, d);
     const int64_t W = (int64_t)d->heads * d->head_dim;
-    const int64_t wk = d->score == GGA_SCORE_DOT ? W : d->heads;
+    const int64_t wk = score_width(d);
+    const int32_t ns = source_rows(d);
     if (d->e == 0) {
-        fill_f32(d_qs, (int64_t)d->n * wk, 0.f, s);
-        fill_f32(d_ks, (int64_t)d->n * wk, 0.f, s);
-        fill_f32(d_v, (int64_t)d->n * W, 0.f, s);
+        if (wk > 0) {
+            fill_f32(d_qs, (int64_t)d->n * wk, 0.f, s);
+            fill_f32(d_ks, (int64_t)ns * wk, 0.f, s);
+        }
+        fill_f32(d_v, (int64_t)ns * W, 0.f, s);
         return launch_status();
     }
     Shape sh;
     pick_shape(d->heads, d->head_dim, d->dtype, &sh);
     const PlanBounds b = plan_bounds(d->e);
     const PlanView pa = plan_view(const_cast<void*>(plan), d->n, d->e);
-    const PlanView pb = plan_view(const_cast<void*>(plan_s), d->n, d->e);
+    const PlanView pb = plan_view(const_cast<void*>(plan_s), ns, d->e);
     const int64_t cb = b.max_chunks < 2048 ? b.max_chunks : 2048;
     BwdParams p{};
     p.qs = qs;
@@ -106,8 +127,9 @@ int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
         p.dz_a = ew->dz_a;
         mode = kScoreAddEdge;
     }
-    const int64_t light_blocks = ((int64_t)d->n + kBwdWaves - 1) / kBwdWaves;
-    const int64_t ga = p.a.chunk_blocks + light_blocks, gb = p.b.chunk_blocks + light_blocks;
+    const int64_t light_a = ((int64_t)d->n + kBwdWaves - 1) / kBwdWaves;
+    const int64_t light_b = ((int64_t)ns + kBwdWaves - 1) / kBwdWaves;
+    const int64_t ga = p.a.chunk_blocks + light_a, gb = p.b.chunk_blocks + light_b;
     if (ga >= ((int64_t)1 << 31) || gb >= ((int64_t)1 << 31)) return GGA_ERANGE;
     const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;
     const bool ok = d->dtype == GGA_BF16
@@ -134,7 +156,7 @@ extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const
                                   void* ws, size_t ws_bytes, void* stream) {
     int st = check_desc(d);
     if (st != GGA_OK) return st;
-    if (d->n == 0) return GGA_OK;
+    if (d->n == 0) return zero_source_grads(d, d_ks, d_v, as_stream(stream));
     return bwd_impl(d, qs, ks, v, out, lse, d_out, row_ptr, col, plan, row_ptr_s, col_s, plan_s, d_qs, d_ks, d_v,
                     nullptr, ws, ws_bytes, as_stream(stream));
 }
@@ -154,7 +176,7 @@ extern "C" int gga_local_attn_bwd_edge(const gga_local_desc* d, const float* s_d
     int st = check_desc(d);
     if (st != GGA_OK) return st;
     if (d->score != GGA_SCORE_ADDITIVE || d->dtype != GGA_F32) return GGA_EUNSUPPORTED;
-    if (d->n == 0) return GGA_OK;
+    if (d->n == 0) return zero_source_grads(d, d_s_src, d_hf, as_stream(stream));
     if (d->e > 0 && (!s_edge || !eid || !eid_s || !d_s_edge)) return GGA_EINVAL;
     if (ws_bytes < gga_local_attn_bwd_edge_workspace(d) || !ws) return GGA_EWORKSPACE;
     hipStream_t s = as_stream(stream);

@@ -7,6 +7,7 @@
 // Pass A walks the CSR by destination: dq[v] (dot) or d s_dst[v] (additive), and D.
 // Pass B walks the CSR by source, grouping the edge gradients by their source
 // (Tinymesh "Endpoint projection", backward): dk[u] or d s_src[u], and dv[u].
+// Mean weighting (alpha_e = 1/deg(v), constant) needs pass B alone, for dv.
 // Long rows of either CSR are cut into chunks whose partial sums are added in slot order.
 #pragma once
 
@@ -262,14 +263,16 @@ struct PassB {
 #pragma unroll
         for (int s = 0; s < NS; s++) {
             const size_t ro = (size_t)u * p.W + geo.off[s];
-            raw_t r{};
-            if (geo.ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.v) + ro);
-            V::widen(r, vf[s]);
+            if constexpr (MODE != GGA_SCORE_MEAN) {
+                raw_t r{};
+                if (geo.ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.v) + ro);
+                V::widen(r, vf[s]);
+            }
             if constexpr (MODE == GGA_SCORE_DOT) {
                 raw_t kr{};
                 if (geo.ok[s]) kr = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.ks) + ro);
                 V::widen(kr, kf[s]);
-            } else {
+            } else if constexpr (MODE != GGA_SCORE_MEAN) {
                 ssv[s] = geo.ok[s] ? static_cast<const float*>(p.ks)[(size_t)u * p.H + geo.head[s]] : 0.f;
             }
 #pragma unroll
@@ -314,14 +317,18 @@ struct PassB {
                         const size_t hi = (size_t)t[j] * p.H + geo.head[s];
                         if constexpr (MODE == GGA_SCORE_DOT) {
                             qr[j][s] = *reinterpret_cast<const raw_t*>(qp + ro);
-                        } else {
+                        } else if constexpr (MODE != GGA_SCORE_MEAN) {
                             sj[j][s] = sdst[hi];
                             if constexpr (MODE == kScoreAddEdge)
                                 sj[j][s] += p.se_b[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]];
                         }
                         load_f32<EPL>(p.dout + ro, gr[j][s]);
-                        lj[j][s] = p.lse[hi];
-                        dj[j][s] = p.D[hi];
+                        if constexpr (MODE == GGA_SCORE_MEAN) {  // the weight itself: 1/deg(t)
+                            lj[j][s] = 1.f / (float)(p.a.row_ptr[t[j] + 1] - p.a.row_ptr[t[j]]);
+                        } else {
+                            lj[j][s] = p.lse[hi];
+                            dj[j][s] = p.D[hi];
+                        }
                     }
                 }
             }
@@ -330,6 +337,12 @@ struct PassB {
                 if (j >= U) continue;
 #pragma unroll
                 for (int s = 0; s < NS; s++) {
+                    if constexpr (MODE == GGA_SCORE_MEAN) {
+                        const float al = ev[j] ? lj[j][s] : 0.f;
+#pragma unroll
+                        for (int i = 0; i < EPL; i++) dv[s][i] = fmaf(al, gr[j][s][i], dv[s][i]);
+                        continue;
+                    }
                     float da = 0.f;
 #pragma unroll
                     for (int i = 0; i < EPL; i++) da = fmaf(gr[j][s][i], vf[s][i], da);
@@ -371,7 +384,7 @@ struct PassB {
     }
 
     __device__ __forceinline__ int dk_width(const BwdParams& p) const {
-        return MODE == GGA_SCORE_DOT ? p.W : p.H;
+        return MODE == GGA_SCORE_DOT ? p.W : MODE == GGA_SCORE_MEAN ? 0 : p.H;
     }
 
     __device__ __forceinline__ void write_to(const BwdParams& p, float* dkp, float* dvp) {
@@ -381,7 +394,7 @@ struct PassB {
             if (!geo.ok[s]) continue;
             if constexpr (MODE == GGA_SCORE_DOT)
                 store_f32<EPL>(dkp + geo.off[s], dk[s]);
-            else if (geo.lead[s])
+            else if (MODE != GGA_SCORE_MEAN && geo.lead[s])
                 dkp[geo.head[s]] = dk[s][0];
             store_f32<EPL>(dvp + geo.off[s], dv[s]);
         }
@@ -391,13 +404,13 @@ struct PassB {
         if (geo.exact) {  // all lanes take part (the row store exchanges chunks)
             if constexpr (MODE == GGA_SCORE_DOT) {
                 store_row_nt<EPL>(p.d_ks + (size_t)u * p.W, dk[0], geo.lpr, geo.lane, geo.g);
-            } else {
+            } else if constexpr (MODE != GGA_SCORE_MEAN) {
                 if (geo.g == 0 && geo.lead[0]) p.d_ks[(size_t)u * p.H + geo.head[0]] = dk[0][0];
             }
             store_row_nt<EPL>(p.d_v + (size_t)u * p.W, dv[0], geo.lpr, geo.lane, geo.g);
             return;
         }
-        write_to(p, p.d_ks + (size_t)u * dk_width(p), p.d_v + (size_t)u * p.W);
+        write_to(p, MODE == GGA_SCORE_MEAN ? nullptr : p.d_ks + (size_t)u * dk_width(p), p.d_v + (size_t)u * p.W);
     }
 
     __device__ __forceinline__ void write_partial(const BwdParams& p, int32_t slot) {
@@ -544,11 +557,13 @@ static __global__ __launch_bounds__(kBwdThreads) void bwd_merge(BwdCsr c, int wi
 
 template <typename T, int EPL, int HDP, int NS, int MODE>
 void launch_bwd_t(const BwdParams& p, unsigned grid_a, unsigned grid_b, int64_t max_heavy, hipStream_t s) {
-    const int wk = MODE == GGA_SCORE_DOT ? p.W : p.H;
+    const int wk = MODE == GGA_SCORE_DOT ? p.W : MODE == GGA_SCORE_MEAN ? 0 : p.H;
     int64_t mb = (max_heavy + kBwdWaves - 1) / kBwdWaves;
     const unsigned mg = (unsigned)(mb < 1024 ? (mb < 1 ? 1 : mb) : 1024);
-    bwd_dst_kernel<T, EPL, HDP, NS, MODE><<<grid_a, kBwdThreads, 0, s>>>(p);
-    if (max_heavy > 0) bwd_merge<<<mg, kBwdThreads, 0, s>>>(p.a, wk, p.d_qs, 0, nullptr);
+    if constexpr (MODE != GGA_SCORE_MEAN) {
+        bwd_dst_kernel<T, EPL, HDP, NS, MODE><<<grid_a, kBwdThreads, 0, s>>>(p);
+        if (max_heavy > 0) bwd_merge<<<mg, kBwdThreads, 0, s>>>(p.a, wk, p.d_qs, 0, nullptr);
+    }
     bwd_src_kernel<T, EPL, HDP, NS, MODE><<<grid_b, kBwdThreads, 0, s>>>(p);
     if (max_heavy > 0) bwd_merge<<<mg, kBwdThreads, 0, s>>>(p.b, wk, p.d_ks, p.W, p.d_v);
 }
@@ -584,6 +599,10 @@ bool launch_bwd_dtype(const BwdParams& p, int epl, int hdp, int ns, int mode, un
     if (mode == GGA_SCORE_DOT) {
         if (epl == VEC) return launch_bwd_hdp<T, VEC, GGA_SCORE_DOT>(p, hdp, ns, ga, gb, mh, s);
         return launch_bwd_hdp<T, 1, GGA_SCORE_DOT>(p, hdp, ns, ga, gb, mh, s);
+    }
+    if (mode == GGA_SCORE_MEAN) {
+        if (epl == VEC) return launch_bwd_hdp<T, VEC, GGA_SCORE_MEAN>(p, hdp, ns, ga, gb, mh, s);
+        return launch_bwd_hdp<T, 1, GGA_SCORE_MEAN>(p, hdp, ns, ga, gb, mh, s);
     }
     if (mode == kScoreAddEdge) {  // fp32 node tensors only
         if constexpr (std::is_same<T, float>::value) {

@@ -92,7 +92,7 @@ struct FwdRow {
                 raw_t r{};
                 if (ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.qs) + (size_t)v * p.W + off[s]);
                 V::widen(r, qf[s]);
-            } else {
+            } else if constexpr (MODE != GGA_SCORE_MEAN) {
                 sd[s] = ok[s] ? static_cast<const float*>(p.qs)[(size_t)v * p.H + head[s]] : 0.f;
             }
         }
@@ -132,7 +132,7 @@ struct FwdRow {
                         const size_t ro = (size_t)u[j] * p.W + off[s];
                         if constexpr (MODE == GGA_SCORE_DOT) {
                             kr[j][s] = *reinterpret_cast<const raw_t*>(kp + ro);
-                        } else {
+                        } else if constexpr (MODE != GGA_SCORE_MEAN) {
                             ss[j][s] = ssrc[(size_t)u[j] * p.H + head[s]];
                             if constexpr (MODE == kScoreAddEdge)
                                 ss[j][s] += p.se[(size_t)(base + g + G * j) * p.H + head[s]];
@@ -148,7 +148,9 @@ struct FwdRow {
                 for (int s = 0; s < NS; s++) {
                     if (j < U) {
                         float t;
-                        if constexpr (MODE == GGA_SCORE_DOT) {
+                        if constexpr (MODE == GGA_SCORE_MEAN) {
+                            t = 0.f;
+                        } else if constexpr (MODE == GGA_SCORE_DOT) {
                             float f[EPL];
                             V::widen(kr[j][s], f);
                             float d = 0.f;
@@ -409,8 +411,9 @@ size_t fwd_part_bytes(const gga_local_desc* d) {
 int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void* v, const int32_t* row_ptr,
              const int32_t* col, const void* plan, float* out, float* lse, const float* se, void* ws,
              size_t ws_bytes, hipStream_t s) {
-    if (!row_ptr || !plan || !out || !qs) return GGA_EINVAL;
-    if (d->e > 0 && (!col || !ks || !v)) return GGA_EINVAL;
+    const bool mean = d->score == GGA_SCORE_MEAN;
+    if (!row_ptr || !plan || !out || (!qs && !mean)) return GGA_EINVAL;
+    if (d->e > 0 && (!col || (!ks && !mean) || !v)) return GGA_EINVAL;
     if (!aligned16(out) || !aligned16(qs) || (ks && !aligned16(ks)) || (v && !aligned16(v))) return GGA_EINVAL;
     const size_t need = fwd_part_bytes(d);
     if (ws_bytes < need || (need > 0 && !ws)) return GGA_EWORKSPACE;
@@ -453,6 +456,8 @@ int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
         ok = dispatch_edge(d->dtype, sh, p, (unsigned)grid, mh, s);
     else if (d->score == GGA_SCORE_DOT)
         ok = dispatch<GGA_SCORE_DOT>(d->dtype, sh, p, (unsigned)grid, mh, s);
+    else if (mean)
+        ok = dispatch<GGA_SCORE_MEAN>(d->dtype, sh, p, (unsigned)grid, mh, s);
     else
         ok = dispatch<GGA_SCORE_ADDITIVE>(d->dtype, sh, p, (unsigned)grid, mh, s);
     if (!ok) return GGA_EUNSUPPORTED;

@@ -15,7 +15,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // Internal score mode: the additive logit plus a per-edge term read in CSR order.
-constexpr int kScoreAddEdge = 2;
+constexpr int kScoreAddEdge = 3;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -42,12 +42,17 @@ inline bool pick_shape(int H, int C, int dtype, Shape* sh) {
     return true;
 }
 
+// Rows of the source-side tensors (keys or source scores, values).
+inline int32_t source_rows(const gga_local_desc* d) { return d->n_src > 0 ? d->n_src : d->n; }
+
 inline int check_desc(const gga_local_desc* d) {
     if (!d) return GGA_EINVAL;
-    if (d->n < 0 || d->e < 0 || d->heads < 1 || d->head_dim < 1 || d->reserved != 0) return GGA_EINVAL;
+    if (d->n < 0 || d->e < 0 || d->heads < 1 || d->head_dim < 1 || d->n_src < 0) return GGA_EINVAL;
     if (d->e >= (int64_t)INT32_MAX) return GGA_ERANGE;
-    if ((int64_t)d->n * d->heads * d->head_dim >= ((int64_t)1 << 40)) return GGA_ERANGE;
-    if (d->score != GGA_SCORE_DOT && d->score != GGA_SCORE_ADDITIVE) return GGA_EUNSUPPORTED;
+    const int64_t rows = d->n > source_rows(d) ? d->n : source_rows(d);
+    if (rows * d->heads * d->head_dim >= ((int64_t)1 << 40)) return GGA_ERANGE;
+    if (d->score != GGA_SCORE_DOT && d->score != GGA_SCORE_ADDITIVE && d->score != GGA_SCORE_MEAN)
+        return GGA_EUNSUPPORTED;
     if (d->dtype != GGA_F32 && d->dtype != GGA_BF16) return GGA_EUNSUPPORTED;
     Shape sh;
     if (!pick_shape(d->heads, d->head_dim, d->dtype, &sh)) return GGA_EUNSUPPORTED;

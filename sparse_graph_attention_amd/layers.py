@@ -9,18 +9,22 @@ tensors from one to the next.
 - Gated local-global layer ("Gated Local-Global Graph Attention", Implementation notes
   item 2): Q, K, V projections, local masked softmax, phi = elu+1 global branch, node
   gate, W_o, residual LayerNorm.
+- Relation-typed messages (GiGL pull request "Support relation message modes on the
+  packed GraphTransformerEncoder path", section "Approach"): per-relation key and message
+  transforms of every node, relation edges mapped to (node, relation) rows, then softmax
+  or mean weighting over each target's in-edges and the weighted sum.
 """
 
 from __future__ import annotations
 
 import torch
 
-from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, Topology, gga_add_layernorm,
+from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, GGA_SCORE_MEAN, Topology, gga_add_layernorm,
                gga_add_layernorm_bwd, gga_gat_coef_bwd, gga_gat_coef_fwd, gga_gated_combine, gga_gated_combine_bwd,
                gga_head_mean, gga_head_mean_bwd, gga_local_attn_bwd_edge, gga_local_attn_fwd_edge,
                gga_global_linear_batch_bwd, gga_global_linear_batch_fwd, gga_global_linear_bwd,
                gga_global_linear_fwd, gga_linear, gga_linear_accumulate, gga_local_attn_bwd, gga_local_attn_fwd,
-               make_desc)
+               gga_relation_sources, make_desc)
 
 
 def gat_forward(x: torch.Tensor, w: torch.Tensor, a_s: torch.Tensor, a_t: torch.Tensor, topo: Topology,
@@ -133,4 +137,65 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
     return grads
 
 
-__all__ = ["gat_forward", "gat_backward", "gated_layer_forward", "gated_layer_backward", "GGA_BF16"]
+def relation_topology(n: int, n_rel: int, src: torch.Tensor, dst: torch.Tensor, segments, backward: bool = False):
+    """Relation edges as packed rows (src, dst) grouped by relation, with host-side
+    (relation, start, end) segments: each source becomes its (node, relation) row
+    u * R + r and the topology is built over n targets and n * R source rows.  Returns
+    (topology, d_bad); d_bad (device int32) counts endpoints outside [0, n), and no
+    attention call may run on the topology unless it is 0."""
+    src_rel, bad = gga_relation_sources(n, n_rel, src, dst, segments)
+    return Topology(n, src_rel, dst, backward=backward, n_src=n * n_rel), bad
+
+
+def relation_forward(x: torch.Tensor, w_q, w_k, w_v: torch.Tensor, topo: Topology, heads: int, n_rel: int,
+                     mean: bool):
+    """Relation-typed messages.  x [N, d]; w_k, w_v [d, R*W] hold the R relation transforms
+    side by side (columns r*W .. r*W+W-1 are W^r), so that X w_v viewed as [N*R, W] has the
+    message of node u under relation r in row u*R + r; w_q [d, W].  Softmax mode: per head,
+    softmax over v's in-edges of q_v . k_{u,r} / sqrt(C); mean mode (w_q, w_k unused): each
+    in-edge weighs 1/deg(v).  topo from relation_topology.  Returns out [N, W] and the
+    intermediates the backward needs."""
+    n = x.shape[0]
+    width = w_v.shape[1] // n_rel
+    c = width // heads
+    v = gga_linear(x, w_v).view(n * n_rel, heads, c)
+    if mean:
+        desc = make_desc(n, topo.e, heads, c, GGA_SCORE_MEAN, GGA_F32, 1.0, n_src=n * n_rel)
+        q = k = None
+    else:
+        desc = make_desc(n, topo.e, heads, c, GGA_SCORE_DOT, GGA_F32, c ** -0.5, n_src=n * n_rel)
+        q = gga_linear(x, w_q).view(n, heads, c)
+        k = gga_linear(x, w_k).view(n * n_rel, heads, c)
+    out, lse = gga_local_attn_fwd(desc, q, k, v, topo.row_ptr, topo.col, topo.plan, want_lse=not mean)
+    return dict(out=out.view(n, width), out3=out, lse=lse, q=q, k=k, v=v, desc=desc)
+
+
+def relation_backward(x: torch.Tensor, w_q, w_k, w_v: torch.Tensor, d_out: torch.Tensor, fwd: dict, topo: Topology,
+                      heads: int, n_rel: int, mean: bool):
+    """dX, dW_V (and in softmax mode dW_Q, dW_K) of sum(out * d_out), in the layouts of
+    relation_forward.  topo must hold the CSR by source (relation_topology(...,
+    backward=True))."""
+    n = x.shape[0]
+    width = w_v.shape[1] // n_rel
+    c = width // heads
+    d3 = d_out.reshape(n, heads, c)
+    if mean:
+        _, _, d_v = gga_local_attn_bwd(fwd["desc"], None, None, None, None, None, d3, topo)
+    else:
+        d_q, d_k, d_v = gga_local_attn_bwd(fwd["desc"], fwd["q"], fwd["k"], fwd["v"], fwd["out3"], fwd["lse"], d3,
+                                           topo)
+    dv2 = d_v.view(n, n_rel * width)
+    res = dict(d_w_v=gga_linear(x, dv2, trans_a=True), d_w_q=None, d_w_k=None)
+    d_x = gga_linear(dv2, w_v, trans_b=True)
+    if not mean:
+        dq2, dk2 = d_q.view(n, width), d_k.view(n, n_rel * width)
+        res["d_w_q"] = gga_linear(x, dq2, trans_a=True)
+        res["d_w_k"] = gga_linear(x, dk2, trans_a=True)
+        gga_linear_accumulate(dq2, w_q, d_x, trans_b=True)
+        gga_linear_accumulate(dk2, w_k, d_x, trans_b=True)
+    res["d_x"] = d_x
+    return res
+
+
+__all__ = ["gat_forward", "gat_backward", "gated_layer_forward", "gated_layer_backward", "relation_topology",
+           "relation_forward", "relation_backward", "GGA_BF16"]

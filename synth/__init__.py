@@ -176,6 +176,7 @@ class Workload:
     fin: int = 0  # GAT input width
     d_model: int = 0  # gated layer model width
     batch: int = 1  # graphs packed along the node axis (n nodes in all)
+    relations: int = 0  # relation types of the edges (relation-typed messages)
 
 
 WORKLOADS = {
@@ -186,6 +187,10 @@ WORKLOADS = {
     5: Workload(5, "dot-zipf1.8-n2m-h8-c32-bf16", 1 << 21, 8, 32, "bf16", "dot"),
     6: Workload(6, "gated-layer-batch64-n4096-d256-h4", 1 << 18, 4, 64, "f32", "dot", d_model=256, batch=64),
     7: Workload(7, "gat-edgefeat-mean-powerlaw-n170k", 170_000, 8, 8, "f32", "additive", fin=128),
+    8: Workload(8, "relation-mean-packed-512x256-d512-h8-r3", 512 * 256, 8, 64, "f32", "mean", d_model=512,
+                batch=512, relations=3),
+    9: Workload(9, "relation-softmax-packed-512x256-d512-h8-r3", 512 * 256, 8, 64, "f32", "dot", d_model=512,
+                batch=512, relations=3),
 }
 
 
@@ -229,6 +234,46 @@ def workload_batch(ident: int):
     """The per-graph COO lists of a batched workload (equal graph sizes n / batch)."""
     w = WORKLOADS[ident]
     return batch_of_graphs([w.n // w.batch] * w.batch, 32, _rng(ident, TOPOLOGY))
+
+
+def relation_edges(sizes, degree: int, n_rel: int, rng: np.random.Generator):
+    """Packed relation-typed edges over a batch of sequences (GiGL pull request "Support
+    relation message modes on the packed GraphTransformerEncoder path": packed tokens,
+    relation edges as rows (target, source, relation) with host-side (relation, start,
+    end) segments).  Sequence b holds sizes[b] tokens; its edges are degree * n_b uniform
+    (source, target) pairs over its own tokens plus one self-loop per token, each with a
+    uniform relation in [0, n_rel).  The rows are grouped by relation (stable).  Returns
+    n, src, dst (global packed ids, int32), rel and the segments [(r, start, end)]."""
+    node_ptr, edge_ptr, sl, dl = batch_of_graphs(sizes, degree, rng)
+    owner = np.repeat(np.arange(len(sizes)), np.diff(edge_ptr))
+    src = (sl + node_ptr[owner]).astype(np.int32)
+    dst = (dl + node_ptr[owner]).astype(np.int32)
+    rel = rng.integers(0, n_rel, src.size).astype(np.int32)
+    order = np.argsort(rel, kind="stable")
+    src, dst, rel = src[order], dst[order], rel[order]
+    bounds = np.searchsorted(rel, np.arange(n_rel + 1))
+    segments = [(r, int(bounds[r]), int(bounds[r + 1])) for r in range(n_rel)]
+    return int(node_ptr[-1]), src, dst, rel, segments
+
+
+def workload_relation_edges(ident: int):
+    """Relation workloads: sequences of n / batch tokens, 8 uniform in-edges per token plus
+    a self-loop, uniform relations."""
+    w = WORKLOADS[ident]
+    return relation_edges([w.n // w.batch] * w.batch, 8, w.relations, _rng(8, TOPOLOGY))
+
+
+def relation_inputs(n: int, d: int, heads: int, ch: int, n_rel: int, ident: int = 8):
+    """X ~ N(0,1) [n,d]; W_Q [d, H*C] and the per-relation W_K, W_V [R, d, H*C] ~ N(0, 1/d),
+    so that projected rows have unit scale; upstream gradient ~ N(0,1) [n, H*C]."""
+    w = heads * ch
+    x = node_tensor(ident, 0, (n, d))
+    std = d ** -0.5
+    w_q = normal_f32(d * w, ident, WEIGHTS, 0, std=std).reshape(d, w)
+    w_k = normal_f32(n_rel * d * w, ident, WEIGHTS, 1, std=std).reshape(n_rel, d, w)
+    w_v = normal_f32(n_rel * d * w, ident, WEIGHTS, 2, std=std).reshape(n_rel, d, w)
+    d_out = node_tensor(ident, 0, (n, w), stream=GRADS)
+    return dict(x=x, w_q=w_q, w_k=w_k, w_v=w_v, d_out=d_out)
 
 
 def ragged_batch(seed: int, sizes=(1, 0, 17, 300, 4096, 2, 1000, 0, 2500, 63)):

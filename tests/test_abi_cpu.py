@@ -57,7 +57,7 @@ def test_binding_names_match_header():
 def test_version_and_status(lib):
     lib.gga_abi_version.restype = ctypes.c_int
     lib.gga_status_string.restype = ctypes.c_char_p
-    assert lib.gga_abi_version() == 1
+    assert lib.gga_abi_version() == 2
     assert lib.gga_status_string(0) == b"ok"
     assert lib.gga_status_string(4).startswith(b"workspace")
 
@@ -81,6 +81,55 @@ def test_fwd_rejects_bad_desc(bad, status):
     fake = ctypes.c_void_p(256)
     rc = g.lib.gga_local_attn_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None, None, 0, None)
     assert rc == status
+
+
+def test_desc_rejects_negative_source_rows():
+    import sparse_graph_attention_amd as g
+
+    d = _desc()
+    d.n_src = -3
+    fake = ctypes.c_void_p(256)
+    assert g.lib.gga_local_attn_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None, None, 0,
+                                    None) == 1
+    assert g.lib.gga_local_attn_bwd_workspace(ctypes.byref(d)) == 0
+
+
+def test_mean_mode_needs_no_query_or_key():
+    """Mean weighting reads neither q nor k: NULL passes the pointer checks (the call then
+    stops at the workspace check, before any launch)."""
+    import sparse_graph_attention_amd as g
+
+    d = _desc(e=5000, score=g.GGA_SCORE_MEAN)
+    a = ctypes.c_void_p(4096)
+    need = g.lib.gga_local_attn_fwd_workspace(ctypes.byref(d))
+    assert need > 0
+    assert g.lib.gga_local_attn_fwd(ctypes.byref(d), None, None, a, a, a, a, a, None, a, need - 1, None) == 4
+    dd = _desc(e=5000, score=g.GGA_SCORE_DOT)
+    assert g.lib.gga_local_attn_fwd(ctypes.byref(dd), None, None, a, a, a, a, a, None, a, 1 << 40, None) == 1
+    nb = g.lib.gga_local_attn_bwd_workspace(ctypes.byref(d))
+    assert nb > 0
+    assert g.lib.gga_local_attn_bwd(ctypes.byref(d), None, None, None, None, None, a, a, a, a, a, a, a, None, None,
+                                    a, a, nb - 1, None) == 4
+    assert g.lib.gga_local_attn_bwd(ctypes.byref(d), None, None, None, None, None, a, a, a, a, a, a, a, None, None,
+                                    None, a, nb, None) == 1
+
+
+@pytest.mark.parametrize("segs,n,rels,e,status", [
+    ([(0, 0, 5), (1, 5, 9)], 4, 2, 10, 1),    # does not reach e
+    ([(0, 0, 5), (1, 6, 10)], 4, 2, 10, 1),   # gap
+    ([(0, 0, 6), (1, 5, 10)], 4, 2, 10, 1),   # overlap
+    ([(2, 0, 10)], 4, 2, 10, 1),              # relation out of range
+    ([(-1, 0, 10)], 4, 2, 10, 1),
+    ([(0, 0, 11)], 4, 2, 10, 1),              # beyond e
+    ([(0, 0, 10)], 4, 0, 10, 1),              # no relations
+    ([(0, 0, 10)], 1 << 29, 8, 10, 2),        # n * R beyond int32
+])
+def test_relation_sources_rejects(segs, n, rels, e, status):
+    import sparse_graph_attention_amd as g
+
+    a = ctypes.c_void_p(4096)
+    flat = (ctypes.c_int32 * (3 * len(segs)))(*[x for t in segs for x in t])
+    assert g.lib.gga_relation_sources(n, rels, e, a, a, len(segs), flat, a, a, None) == status
 
 
 def test_fwd_rejects_null_and_misaligned_and_small_workspace():
