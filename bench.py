@@ -19,6 +19,9 @@ Other workloads (``--workload``), each printed as its own line when asked for:
      (block-diagonal edges, per-graph global statistics): forward + gradients
   7  the 170k-node GAT layer with 16 learned features per edge in the score and the
      heads averaged: forward + first-order gradients
+  8  relation-typed messages over 512 packed sequences of 256 tokens, d = 512, 8 heads of
+     64, 3 relations, mean weighting: forward + gradients of the input and transforms
+  9  the same with softmax weighting (shared query, per-relation keys and messages)
   1  tiny 1024-node dot-product graph, H = 1, r = 16, fp32: forward
 
 Prints one JSON line: throughput in GEdges/s, the roofline of the dominant kernel call
@@ -29,6 +32,7 @@ launch stream) and the CPU oracle timed on this host over the same work.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -410,12 +414,113 @@ def bench_layer(args, g, torch, synth, ident):
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
 
 
+def bench_relation(args, g, torch, synth, ident):
+    """Relation-typed messages (per-relation key and message transforms of every node,
+    mean or softmax weighting over each target's in-edges), forward + gradients of the
+    input and every transform, over a packed batch of token sequences."""
+    from sparse_graph_attention_amd import layers
+
+    w = synth.WORKLOADS[ident]
+    n, heads, c, d, n_rel = w.n, w.heads, w.head_dim, w.d_model, w.relations
+    mean = w.score == "mean"
+    width = heads * c
+    dev = torch.device("cuda:0")
+    _, src, dst, rel, segs = synth.workload_relation_edges(ident)
+    e = int(src.size)
+    log(f"workload {w.name}: n={n} e={e} relations={n_rel} mode={'mean' if mean else 'softmax'}")
+    p = synth.relation_inputs(n, d, heads, c, n_rel, ident=8)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)  # noqa: E731
+    xd, wqd = t(p["x"]), t(p["w_q"])
+    wkd, wvd = t(np.concatenate(list(p["w_k"]), 1)), t(np.concatenate(list(p["w_v"]), 1))
+    dod = t(p["d_out"])
+    src_d, dst_d = torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev)
+    layers.relation_topology(n, n_rel, src_d, dst_d, segs, backward=True)  # untimed warm-up build
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    topo, bad = layers.relation_topology(n, n_rel, src_d, dst_d, segs, backward=True)
+    e1.record()
+    torch.cuda.synchronize()
+    if int(bad.item()) != 0:
+        raise RuntimeError("relation edges with endpoints outside the batch")
+    tt = {"relation_rows_csrs_and_plans_ms": e0.elapsed_time(e1)}
+
+    def step(tm):
+        _mark(tm, "f0")
+        f = layers.relation_forward(xd, wqd, wkd, wvd, topo, heads, n_rel, mean)
+        _mark(tm, "f1")
+        layers.relation_backward(xd, wqd, wkd, wvd, dod, f, topo, heads, n_rel, mean)
+        _mark(tm, "b1")
+
+    tm = Timer(torch, torch.cuda.current_stream())
+    ms = tm.run(step, args.steps, args.warmup)
+    fms, bms = tm.phase_ms("f0", "f1"), tm.phase_ms("f1", "b1")
+    # the attention kernels alone, on the layer's own tensors
+    f = layers.relation_forward(xd, wqd, wkd, wvd, topo, heads, n_rel, mean)
+    desc = f["desc"]
+    fws = torch.empty(g.lib.gga_local_attn_fwd_workspace(ctypes.byref(desc)) + 1, dtype=torch.uint8, device=dev)
+    bws = torch.empty(g.lib.gga_local_attn_bwd_workspace(ctypes.byref(desc)) + 1, dtype=torch.uint8, device=dev)
+    d3 = dod.view(n, heads, c)
+    grads = [None, None, torch.empty_like(f["v"], dtype=torch.float32)]
+    if not mean:
+        grads[0], grads[1] = torch.empty_like(f["q"]), torch.empty_like(f["k"])
+
+    def attn(tm):
+        _mark(tm, "a0")
+        g.gga_local_attn_fwd(desc, f["q"], f["k"], f["v"], topo.row_ptr, topo.col, topo.plan, out=f["out3"],
+                             lse=f["lse"], want_lse=not mean, ws=fws)
+        _mark(tm, "a1")
+        g.gga_local_attn_bwd(desc, f["q"], f["k"], f["v"], f["out3"], f["lse"], d3, topo, *grads, ws=bws)
+        _mark(tm, "a2")
+
+    ta = Timer(torch, torch.cuda.current_stream())
+    ta.run(attn, args.steps, args.warmup)
+    afms, abms = ta.phase_ms("a0", "a1"), ta.phase_ms("a1", "a2")
+    ns = n * n_rel
+    if mean:
+        # forward: a message row and col per edge, row_ptr, out; backward (CSR by source): per
+        # edge a dO row, col and the target's two row_ptr entries; row_ptr_s; d_v written
+        fa = e * (4 * width + 4) + 4 * (n + 1) + 4 * n * width
+        ba = e * (4 * width + 4 + 8) + 4 * (ns + 1) + 4 * ns * width
+    else:
+        fa = fwd_bytes(n, e, heads, c, 4)
+        ba = (e * (2 * 4 * width + 4) + n * (4 * width + 8 * width + 4 * heads + 4) + n * (4 * width + 4 * heads)
+              + e * (4 * width + 4 * width + 8 * heads + 4) + ns * (2 * 4 * width + 4) + ns * 8 * width)
+    # every transform's product appears three times (forward, its weight gradient, dX)
+    flops = 3 * 2.0 * n * d * (n_rel * width + (0 if mean else width + n_rel * width))
+    log(f"step {ms:.3f} ms: fwd {fms:.3f} ms, bwd {bms:.3f} ms ({flops / ms / 1e9:.1f} TFLOP/s over the "
+        f"projections); attention alone fwd {afms:.3f} ms ({fa / afms / 1e6:.0f} GB/s), bwd {abms:.3f} ms "
+        f"({ba / abms / 1e6:.0f} GB/s); {tt}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        omode = oracle.REL_MEAN if mean else oracle.REL_SOFTMAX
+        t1 = time.perf_counter()
+        oracle.relation_forward(p["x"], p["w_q"], p["w_k"], p["w_v"], src, dst, rel, heads, omode)
+        oracle.relation_backward(p["x"], p["w_q"], p["w_k"], p["w_v"], src, dst, rel, heads, omode, p["d_out"])
+        dt = time.perf_counter() - t1
+        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the whole step (forward + first-order gradients), fp64 (numpy matmuls for the "
+                         f"projections), {dt:.1f} s"}
+    roof = roofline("mfma", flops / (ms * 1e-3) / 1e12, MFMA_F32_PEAK_TFLOPS, "TFLOP/s", None,
+                    kernel="whole step (fp32 projections dominate)", flops_per_step=flops, launch_ms=ms,
+                    attention_fwd={"ms": afms, "alg_bytes": fa, "GB_s": fa / afms / 1e6,
+                                   "hbm_frac": fa / afms / 1e6 / HBM_PEAK_GBS},
+                    attention_bwd={"ms": abms, "alg_bytes": ba, "GB_s": ba / abms / 1e6,
+                                   "hbm_frac": ba / abms / 1e6 / HBM_PEAK_GBS})
+    cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "d_model": d, "relations": n_rel,
+           "weighting": "mean" if mean else "softmax", "sequences": w.batch, "seq_len": n // w.batch,
+           "storage": "fp32", "step": "forward + first-order gradients"}
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6, 7, 8, 9])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
@@ -436,6 +541,8 @@ def main() -> int:
         rec = bench_heavy_tail(args, g, torch, synth)
     elif args.workload in (2, 7):
         rec = bench_gat(args, g, torch, synth, args.workload)
+    elif args.workload in (8, 9):
+        rec = bench_relation(args, g, torch, synth, args.workload)
     else:
         rec = bench_layer(args, g, torch, synth, args.workload)
     if args.copy_calibration:
