@@ -10,6 +10,18 @@ namespace gga {
 
 constexpr int kWave = 64;
 
+// MI355X hands the workgroups of a launch to its 8 XCDs round-robin by linear id, and each
+// XCD has its own L2.  xcd_order maps a linear id so that each XCD receives one contiguous
+// range of the logical order: workgroups that share operands then share an L2.  A
+// bijection on [0, total) for any total.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_order(uint32_t lin, uint32_t total) {
+    const uint32_t xcd = lin % kXcds, j = lin / kXcds;
+    const uint32_t q = total / kXcds, r = total % kXcds;
+    return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + j;
+}
+
 // ---------------------------------------------------------------- host helpers
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? GGA_OK : GGA_EHIP; }

@@ -131,8 +131,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_mfma(GemmArgs g) {
     __shared__ float Bs[2][BN * LDS_ROW];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 2, wn = wave & 3;
-    const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-    const int64_t kb = (int64_t)blockIdx.z * g.kchunk;
+    // tiles in (split, row tile, column tile) order, each XCD taking a contiguous range, so
+    // the column tiles of one row tile share an L2
+    const uint32_t gxy = gridDim.x * gridDim.y;
+    const uint32_t t = xcd_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gxy * gridDim.z);
+    const uint32_t bz = t / gxy, by = (t % gxy) / gridDim.x, bx = t % gridDim.x;
+    const int64_t m0 = (int64_t)by * BM, n0 = (int64_t)bx * BN;
+    const int64_t kb = (int64_t)bz * g.kchunk;
     const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
     const bool a_km = g.trans_a != 0;   // a stored [K][M]
     const bool b_km = g.trans_b == 0;   // b stored [K][N]
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_mfma(GemmArgs g) {
         __syncthreads();
     }
 
-    float* cbase = g.c + (int64_t)blockIdx.z * g.M * g.N;
+    float* cbase = g.c + (int64_t)bz * g.M * g.N;
     const bool add_bias = g.bias != nullptr && gridDim.z == 1;
 #pragma unroll
     for (int j = 0; j < TJ; j++) {
@@ -184,6 +189,247 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_mfma(GemmArgs g) {
                 if (row >= g.M) continue;
                 const float prev = (g.accumulate && gridDim.z == 1) ? cbase[row * g.N + col] : 0.f;
                 cbase[row * g.N + col] = prev + (acc[i][j][r] + bv);
+            }
+        }
+    }
+}
+
+// ---- the main tile kernel for n > 64: 128 x 128 outputs per workgroup of four wavefronts,
+// each owning 64 x 64 (a 4 x 4 grid of 16x16 MFMA tiles); k staged through LDS 32 at a time,
+// double-buffered, the next stage's global loads in flight during the current MFMAs.  An
+// operand whose rows run along k (a plain, b transposed) is staged as [row][k], one whose
+// rows run along m or n (a transposed, b plain) as [k][row]: both are 16-byte copies, with
+// no transposition on the way into LDS.  Both layouts are free of bank conflicts for the
+// stores and the MFMA operand reads: a [row][k] tile (rows of 32 floats, no padding) is
+// read 16 bytes per lane (four k at once, the contraction index permuted inside the stage as
+// in gemm_f32_mfma), with the eight 16-byte chunks of row r stored in the order
+// c ^ swz(r), so that 16 consecutive rows reading the same chunk hit different banks; a
+// [k][row] tile is read one float per lane, its pitch putting the four lane groups' k rows
+// 16 banks apart.
+constexpr int kBigThreads = 256;
+constexpr int TT = 128;                     // tile rows and columns
+constexpr int TK2 = 32;                     // k per stage
+constexpr int PITCH_RK = TK2;               // [row][k]
+constexpr int PITCH_KR = TT + 4;            // [k][row]
+constexpr int kStageFloats = TK2 * PITCH_KR;  // >= TT * PITCH_RK
+
+// chunk order of a [row][k] row: a different permutation for each of 8 consecutive rows
+// and for each parity among 16
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// This thread's four 16-byte pieces of one operand stage: rows row0 + 32q of a [row][k]
+// tile (eight threads per 32-float row), or k rows kr0 + 8q of a [k][row] tile (32 threads
+// per 128-float row).
+template <bool KM>
+__device__ __forceinline__ void big_fetch(const float* src, int64_t ld, int64_t o0, int64_t olim, int64_t k0,
+                                          int64_t klim, bool fast, bool vec, v4f (&r)[4]) {
+    const int t = threadIdx.x;
+    if constexpr (!KM) {
+        const int row = t >> 3, k4 = (t & 7) * 4;
+        if (fast) {
+            const float* p = src + (o0 + row) * ld + k0 + k4;
+#pragma unroll
+            for (int q = 0; q < 4; q++) r[q] = *reinterpret_cast<const v4f*>(p + (int64_t)(32 * q) * ld);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int64_t o = o0 + row + 32 * q;
+                const float4 x = o < olim ? load4(src + o * ld, k0 + k4, klim, vec) : make_float4(0.f, 0.f, 0.f, 0.f);
+                r[q] = v4f{x.x, x.y, x.z, x.w};
+            }
+        }
+    } else {
+        const int kr = t >> 5, c4 = (t & 31) * 4;
+        if (fast) {
+            const float* p = src + (k0 + kr) * ld + o0 + c4;
+#pragma unroll
+            for (int q = 0; q < 4; q++) r[q] = *reinterpret_cast<const v4f*>(p + (int64_t)(8 * q) * ld);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int64_t k = k0 + kr + 8 * q;
+                const float4 x = k < klim ? load4(src + k * ld, o0 + c4, olim, vec) : make_float4(0.f, 0.f, 0.f, 0.f);
+                r[q] = v4f{x.x, x.y, x.z, x.w};
+            }
+        }
+    }
+}
+
+template <bool KM>
+__device__ __forceinline__ void big_stash(float* lds, const v4f (&r)[4]) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const int row = (t >> 3) + 32 * q;
+        float* d = KM ? lds + ((t >> 5) + 8 * q) * PITCH_KR + (t & 31) * 4
+                      : lds + row * PITCH_RK + 4 * ((t & 7) ^ swz(row));
+        *reinterpret_cast<v4f*>(d) = r[q];
+    }
+}
+
+// Operand values of one 16-wide tile (rows base .. base+15) for the four MFMA steps of a
+// 16-deep half stage h: step t takes k = 16h + 4g + t in lane group g = lane / 16.
+template <bool KM>
+__device__ __forceinline__ void big_operand(const float* lds, int base, int h, int lane, float (&v)[4]) {
+    const int r = lane & 15, kq = h * 16 + (lane >> 4) * 4;
+    if constexpr (!KM) {
+        const int row = base + r;
+        const v4f x = *reinterpret_cast<const v4f*>(lds + row * PITCH_RK + 4 * ((kq >> 2) ^ swz(row)));
+        v[0] = x[0];
+        v[1] = x[1];
+        v[2] = x[2];
+        v[3] = x[3];
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; t++) v[t] = lds[(kq + t) * PITCH_KR + base + r];
+    }
+}
+
+// Pointers to this thread's four 16-byte pieces of an operand stage (see big_fetch) when
+// the whole tile and k range are inside the matrix, and the distance to the next stage.
+template <bool KM>
+__device__ __forceinline__ int64_t fast_rows(const float* src, int64_t ld, int64_t o0, int64_t k0,
+                                             const float* (&p)[4]) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+        p[q] = KM ? src + (k0 + (t >> 5) + 8 * q) * ld + o0 + (t & 31) * 4
+                  : src + (o0 + (t >> 3) + 32 * q) * ld + k0 + (t & 7) * 4;
+    return KM ? (int64_t)TK2 * ld : TK2;
+}
+
+__device__ __forceinline__ void fast_fetch(const float* (&p)[4], int64_t step, v4f (&r)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        r[q] = *reinterpret_cast<const v4f*>(p[q]);
+        p[q] += step;
+    }
+}
+
+// The k loop of one tile: nk stages from kb, double-buffered through LDS.  FAST: the tile
+// and every stage lie inside the matrices, and rows are 16-byte aligned.
+template <bool AKM, bool BKM, bool FAST>
+__device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kStageFloats], int64_t m0, int64_t n0,
+                                         int64_t kb, int64_t ke, bool a_vec, bool b_vec, v4f (&acc)[4][4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nk = (int)((ke - kb + TK2 - 1) / TK2);
+    v4f ra[4], rb[4];
+    const float* pa[4];
+    const float* pb[4];
+    const int64_t sa = fast_rows<AKM>(g.a, g.lda, m0, kb, pa);
+    const int64_t sb = fast_rows<BKM>(g.b, g.ldb, n0, kb, pb);
+#define GGA_BIG_FETCH(k0)                                                      \
+    if constexpr (FAST) {                                                      \
+        fast_fetch(pa, sa, ra);                                                \
+        fast_fetch(pb, sb, rb);                                                \
+    } else {                                                                   \
+        big_fetch<AKM>(g.a, g.lda, m0, g.M, (k0), ke, false, a_vec, ra);       \
+        big_fetch<BKM>(g.b, g.ldb, n0, g.N, (k0), ke, false, b_vec, rb);       \
+    }
+    if (nk > 0) {
+        GGA_BIG_FETCH(kb)
+        big_stash<AKM>(lds[0][0], ra);
+        big_stash<BKM>(lds[0][1], rb);
+    }
+    __syncthreads();
+    for (int t = 0; t < nk; t++) {
+        const int cur = t & 1;
+        if (t + 1 < nk) {
+            GGA_BIG_FETCH(kb + (int64_t)(t + 1) * TK2)
+        }
+        const float* as = lds[cur][0];
+        const float* bs = lds[cur][1];
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            float af[4][4], bf[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) big_operand<AKM>(as, wm * 64 + i * 16, h, lane, af[i]);
+#pragma unroll
+            for (int j = 0; j < 4; j++) big_operand<BKM>(bs, wn * 64 + j * 16, h, lane, bf[j]);
+#pragma unroll
+            for (int st = 0; st < 4; st++)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][st], bf[j][st], acc[i][j], 0, 0, 0);
+        }
+        if (t + 1 < nk) {
+            big_stash<AKM>(lds[cur ^ 1][0], ra);
+            big_stash<BKM>(lds[cur ^ 1][1], rb);
+        }
+        __syncthreads();
+    }
+#undef GGA_BIG_FETCH
+}
+
+template <bool AKM, bool BKM>
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_big(GemmArgs g) {
+    __shared__ float lds[2][2][kStageFloats];  // [buffer][operand]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t gxy = gridDim.x * gridDim.y;
+    const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gxy * gridDim.z);
+    const uint32_t bz = tl / gxy, by = (tl % gxy) / gridDim.x, bx = tl % gridDim.x;
+    const int64_t m0 = (int64_t)by * TT, n0 = (int64_t)bx * TT;
+    const int64_t kb = (int64_t)bz * g.kchunk;
+    const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+    const bool a_vec = (g.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
+    const bool b_vec = (g.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(g.b) & 15) == 0;
+    const bool fast = a_vec && b_vec && m0 + TT <= g.M && n0 + TT <= g.N && (ke - kb) % TK2 == 0;
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (fast)
+        big_loop<AKM, BKM, true>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
+    else
+        big_loop<AKM, BKM, false>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
+
+    // Epilogue through LDS, 32 rows of the wavefront's 64 x 64 block at a time: the
+    // accumulators go to a private [32][68] region, then each row leaves as 16-byte stores,
+    // 16 lanes covering 64 consecutive columns.
+    float* cbase = g.c + (int64_t)bz * g.M * g.N;
+    const bool add_bias = g.bias != nullptr && gridDim.z == 1;
+    const bool acc_in = g.accumulate && gridDim.z == 1;
+    const bool c_vec = (g.N % 4) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0 &&
+                       (!add_bias || (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0);
+    constexpr int EP = 68;
+    float* ep = &lds[0][0][0] + wave * 32 * EP;
+    const int g4 = (lane >> 4) * 4, cl = lane & 15;
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+        __syncthreads();
+#pragma unroll
+        for (int ii = 0; ii < 2; ii++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) ep[(ii * 16 + g4 + r) * EP + j * 16 + cl] = acc[2 * hh + ii][j][r];
+        __syncthreads();
+        const int64_t col = n0 + wn * 64 + cl * 4;
+#pragma unroll
+        for (int it = 0; it < 8; it++) {
+            const int rl = it * 4 + (lane >> 4);
+            const int64_t row = m0 + wm * 64 + hh * 32 + rl;
+            if (row >= g.M) continue;
+            const v4f v = *reinterpret_cast<const v4f*>(ep + rl * EP + cl * 4);
+            float* dst = cbase + row * g.N + col;
+            if (c_vec && col + 3 < g.N) {
+                v4f o = v;
+                if (add_bias) o += *reinterpret_cast<const v4f*>(g.bias + col);
+                if (acc_in) o = *reinterpret_cast<const v4f*>(dst) + o;
+                *reinterpret_cast<v4f*>(dst) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    if (col + e >= g.N) continue;
+                    const float o = v[e] + (add_bias ? g.bias[col + e] : 0.f);
+                    dst[e] = acc_in ? dst[e] + o : o;
+                }
             }
         }
     }
@@ -353,7 +599,7 @@ Split pick_split(int32_t m, int32_t k, int32_t n) {
         if (sp > 1024) sp = 1024;
         if (sp > 1) {
             int64_t kc = (k + sp - 1) / sp;
-            kc = (kc + KT - 1) / KT * KT;
+            kc = (kc + 31) / 32 * 32;  // whole stages of either tile kernel
             s.kchunk = (int32_t)kc;
             s.splits = (int)((k + kc - 1) / kc);
         }
@@ -437,8 +683,14 @@ int linear_impl(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_
     const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)sp.splits);
     if (bn == 64)
         gemm_f32_mfma<64><<<grid, kGemmThreads, 0, s>>>(g);
+    else if (!g.trans_a && g.trans_b)
+        gemm_f32_big<false, false><<<grid, kBigThreads, 0, s>>>(g);
+    else if (!g.trans_a)
+        gemm_f32_big<false, true><<<grid, kBigThreads, 0, s>>>(g);
+    else if (g.trans_b)
+        gemm_f32_big<true, false><<<grid, kBigThreads, 0, s>>>(g);
     else
-        gemm_f32_mfma<128><<<grid, kGemmThreads, 0, s>>>(g);
+        gemm_f32_big<true, true><<<grid, kBigThreads, 0, s>>>(g);
     if (sp.splits > 1) {
         const int64_t mn = (int64_t)m * n;
         splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(static_cast<const float*>(ws), sp.splits, mn, n,
