@@ -121,7 +121,7 @@ def per_topology(g, torch, n, src_d, dst_d, backward=False):
     plan = g.gga_plan_build(n, int(src_d.numel()), row_ptr)
     ev[2].record()
     topo = g.Topology.__new__(g.Topology)
-    topo.n, topo.e, topo.src, topo.dst = n, int(src_d.numel()), src_d, dst_d
+    topo.n, topo.n_src, topo.e, topo.src, topo.dst = n, n, int(src_d.numel()), src_d, dst_d
     topo.row_ptr, topo.col, topo.eid, topo.plan = row_ptr, col, eid, plan
     topo.row_ptr_s = topo.col_s = topo.eid_s = topo.plan_s = None
     torch.cuda.synchronize()
