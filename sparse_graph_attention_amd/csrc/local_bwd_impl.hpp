@@ -67,11 +67,13 @@ bool launch_bwd_bf16(const BwdParams& p, int epl, int hdp, int ns, int mode, uns
 
 // ------------------------------------------------------------------------ pass A
 
-template <typename T, int EPL, int HDP, int NS, int MODE>
+// UMAX: edge slots per lane and iteration over the NS row slots (8 for rows that fill the
+// wavefront, 4 for narrower rows, leaving registers for more resident wavefronts).
+template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 struct PassA {
     using V = Vec<T, EPL>;
     using raw_t = typename V::raw_t;
-    static constexpr int kUMax = 8 / NS;
+    static constexpr int kUMax = UMAX / NS;
     static constexpr int kAcc = MODE == GGA_SCORE_DOT ? EPL : 1;
 
     RowGeo<EPL, HDP, NS> geo;
@@ -81,7 +83,7 @@ struct PassA {
 
     __device__ __forceinline__ void init(const BwdParams& p) {
         geo.init(p.lpr_log2, p.H, p.C);
-        U = geo.G >= kUMax ? 1 : kUMax / geo.G;
+        U = geo.G * kUMax <= 64 ? kUMax : 64 / geo.G;  // all slots, at most 64 edges per wave
         EIT = geo.G * U;
     }
 
@@ -255,7 +257,7 @@ struct PassB {
 
     __device__ __forceinline__ void init(const BwdParams& p) {
         geo.init(p.lpr_log2, p.H, p.C);
-        U = geo.G >= kUMax ? 1 : kUMax / geo.G;
+        U = geo.G * kUMax <= 64 ? kUMax : 64 / geo.G;  // all slots, at most 64 edges per wave
         EIT = geo.G * U;
     }
 
@@ -438,9 +440,9 @@ __device__ __forceinline__ void lds_sum_waves(float (&x)[N], float (*sm)[64][N],
     }
 }
 
-template <typename T, int EPL, int HDP, int NS, int MODE>
+template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dst_kernel(BwdParams p) {
-    using Row = PassA<T, EPL, HDP, NS, MODE>;
+    using Row = PassA<T, EPL, HDP, NS, MODE, UMAX>;
     constexpr int kA = Row::kAcc;
     Row r;
     r.init(p);
@@ -555,13 +557,13 @@ static __global__ __launch_bounds__(kBwdThreads) void bwd_merge(BwdCsr c, int wi
     }
 }
 
-template <typename T, int EPL, int HDP, int NS, int MODE>
+template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 void launch_bwd_t(const BwdParams& p, unsigned grid_a, unsigned grid_b, int64_t max_heavy, hipStream_t s) {
     const int wk = MODE == GGA_SCORE_DOT ? p.W : MODE == GGA_SCORE_MEAN ? 0 : p.H;
     int64_t mb = (max_heavy + kBwdWaves - 1) / kBwdWaves;
     const unsigned mg = (unsigned)(mb < 1024 ? (mb < 1 ? 1 : mb) : 1024);
     if constexpr (MODE != GGA_SCORE_MEAN) {
-        bwd_dst_kernel<T, EPL, HDP, NS, MODE><<<grid_a, kBwdThreads, 0, s>>>(p);
+        bwd_dst_kernel<T, EPL, HDP, NS, MODE, UMAX><<<grid_a, kBwdThreads, 0, s>>>(p);
         if (max_heavy > 0) bwd_merge<<<mg, kBwdThreads, 0, s>>>(p.a, wk, p.d_qs, 0, nullptr);
     }
     bwd_src_kernel<T, EPL, HDP, NS, MODE><<<grid_b, kBwdThreads, 0, s>>>(p);
@@ -570,12 +572,14 @@ void launch_bwd_t(const BwdParams& p, unsigned grid_a, unsigned grid_b, int64_t 
 
 template <typename T, int EPL, int MODE>
 bool launch_bwd_hdp(const BwdParams& p, int hdp, int ns, unsigned ga, unsigned gb, int64_t mh, hipStream_t s) {
-#define GGA_BCASE(HD)                                               \
-    case HD:                                                        \
-        if (ns == 1)                                                \
-            launch_bwd_t<T, EPL, HD, 1, MODE>(p, ga, gb, mh, s);    \
-        else if constexpr (EPL > 1)                                 \
-            launch_bwd_t<T, EPL, HD, 2, MODE>(p, ga, gb, mh, s);    \
+#define GGA_BCASE(HD)                                                 \
+    case HD:                                                          \
+        if (ns == 1 && p.lpr_log2 == 6)                               \
+            launch_bwd_t<T, EPL, HD, 1, MODE, 8>(p, ga, gb, mh, s);   \
+        else if (ns == 1)                                             \
+            launch_bwd_t<T, EPL, HD, 1, MODE, 4>(p, ga, gb, mh, s);   \
+        else if constexpr (EPL > 1)                                   \
+            launch_bwd_t<T, EPL, HD, 2, MODE, 8>(p, ga, gb, mh, s);   \
         else                                                        \
             return false;                                           \
         return true;

@@ -42,11 +42,14 @@ struct FwdParams {
     const float* se;  // kScoreAddEdge: edge term of the logit, CSR order [E, H]
 };
 
-template <typename T, int EPL, int HDP, int NS, int MODE>
+// UMAX: edge slots per lane and iteration over the NS row slots.  A row that fills the
+// wavefront keeps 8 edges in flight per lane; a row narrower than the wavefront (several
+// edge groups per wavefront) keeps 4, which leaves registers for more resident wavefronts.
+template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 struct FwdRow {
     using V = Vec<T, EPL>;
     using raw_t = typename V::raw_t;
-    static constexpr int kUMax = 8 / NS;
+    static constexpr int kUMax = UMAX / NS;
 
     RowGeo<EPL, HDP, NS> geo;
     int lane, g, G, U, EIT, lpr;
@@ -64,7 +67,7 @@ struct FwdRow {
         lpr = geo.lpr;
         G = geo.G;
         g = geo.g;
-        U = G >= kUMax ? 1 : kUMax / G;
+        U = G * kUMax <= 64 ? kUMax : 64 / G;  // edges per group per iteration: all slots, at most 64 per wave
         EIT = G * U;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
@@ -263,9 +266,9 @@ struct FwdRow {
     }
 };
 
-template <typename T, int EPL, int HDP, int NS, int MODE>
+template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
-    using Row = FwdRow<T, EPL, HDP, NS, MODE>;
+    using Row = FwdRow<T, EPL, HDP, NS, MODE, UMAX>;
     Row r;
     r.geometry(p);
     const int wave = threadIdx.x >> 6;
@@ -350,9 +353,9 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_merge(FwdParams p) {
 
 size_t part_stride(int H, int C) { return align_up((size_t)H * C + 2 * (size_t)H, 8); }
 
-template <typename T, int EPL, int HDP, int NS, int MODE>
+template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 void launch(const FwdParams& p, unsigned grid, int64_t max_heavy, hipStream_t s) {
-    local_fwd_kernel<T, EPL, HDP, NS, MODE><<<grid, kFwdThreads, 0, s>>>(p);
+    local_fwd_kernel<T, EPL, HDP, NS, MODE, UMAX><<<grid, kFwdThreads, 0, s>>>(p);
     if (max_heavy > 0) {
         int64_t mb = (max_heavy + kFwdWaves - 1) / kFwdWaves;
         unsigned mg = (unsigned)(mb < 1024 ? mb : 1024);
@@ -364,10 +367,12 @@ template <typename T, int EPL, int MODE>
 bool dispatch_hdp(const Shape& sh, const FwdParams& p, unsigned grid, int64_t mh, hipStream_t s) {
 #define GGA_CASE(HD)                                                              \
     case HD:                                                                      \
-        if (sh.ns == 1)                                                           \
-            launch<T, EPL, HD, 1, MODE>(p, grid, mh, s);                          \
+        if (sh.ns == 1 && sh.lpr_log2 == 6)                                       \
+            launch<T, EPL, HD, 1, MODE, 8>(p, grid, mh, s);                       \
+        else if (sh.ns == 1)                                                      \
+            launch<T, EPL, HD, 1, MODE, 4>(p, grid, mh, s);                       \
         else if constexpr (EPL > 1)                                               \
-            launch<T, EPL, HD, 2, MODE>(p, grid, mh, s);                          \
+            launch<T, EPL, HD, 2, MODE, 8>(p, grid, mh, s);                       \
         else                                                                      \
             return false;                                                         \
         return true;
