@@ -105,7 +105,7 @@ int gga_plan_build(int32_t n, int64_t e, const int32_t *row_ptr, void *plan, siz
 typedef struct gga_local_desc {
     int32_t n;            /* nodes */
     int32_t heads;        /* H */
-    int64_t e;            /* edges (length of col) */
+    int64_t e;            /* edges (length of col), at most 2^31 - 4097 (GGA_ERANGE) */
     int32_t head_dim;     /* C (r): per-head width */
     int32_t score;        /* GGA_SCORE_DOT, GGA_SCORE_ADDITIVE or GGA_SCORE_MEAN */
     int32_t dtype;        /* storage type of q, k, v (dot) or of v (additive) */

@@ -122,8 +122,12 @@ struct PassA {
         const T* __restrict__ kp = static_cast<const T*>(p.ks);
         const T* __restrict__ vp = static_cast<const T*>(p.v);
         const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
-        for (int32_t base = beg + start; base < end; base += stride) {
-            const int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.a.col[base + geo.lane] : 0;
+        int32_t base = beg + start;
+        int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.a.col[base + geo.lane] : 0;
+        for (; base < end; base += stride) {
+            // the next iteration's sources, in flight while this iteration's rows are gathered
+            const int32_t nxt = base + stride;
+            const int32_t coln = (geo.lane < EIT && nxt + geo.lane < end) ? p.a.col[nxt + geo.lane] : 0;
             int32_t u[kUMax];
             bool ev[kUMax];
 #pragma unroll
@@ -195,6 +199,7 @@ struct PassA {
                     }
                 }
             }
+            colv = coln;
         }
     }
 
@@ -288,8 +293,12 @@ struct PassB {
                                         int32_t stride) {
         const T* __restrict__ qp = static_cast<const T*>(p.qs);
         const float* __restrict__ sdst = static_cast<const float*>(p.qs);
-        for (int32_t base = beg + start; base < end; base += stride) {
-            const int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.b.col[base + geo.lane] : 0;
+        int32_t base = beg + start;
+        int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.b.col[base + geo.lane] : 0;
+        for (; base < end; base += stride) {
+            // the next iteration's sources, in flight while this iteration's rows are gathered
+            const int32_t nxt = base + stride;
+            const int32_t coln = (geo.lane < EIT && nxt + geo.lane < end) ? p.b.col[nxt + geo.lane] : 0;
             int32_t t[kUMax];
             bool ev[kUMax];
 #pragma unroll
@@ -372,6 +381,7 @@ struct PassB {
                     for (int i = 0; i < EPL; i++) dv[s][i] = fmaf(al, gr[j][s][i], dv[s][i]);
                 }
             }
+            colv = coln;
         }
     }
 

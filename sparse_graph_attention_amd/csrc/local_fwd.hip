@@ -107,8 +107,12 @@ struct FwdRow {
         const T* __restrict__ kp = static_cast<const T*>(p.ks);
         const T* __restrict__ vp = static_cast<const T*>(p.v);
         const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
-        for (int32_t base = beg + start; base < end; base += stride) {
-            const int32_t colv = (lane < EIT && base + lane < end) ? p.col[base + lane] : 0;
+        int32_t base = beg + start;
+        int32_t colv = (lane < EIT && base + lane < end) ? p.col[base + lane] : 0;
+        for (; base < end; base += stride) {
+            // the next iteration's sources, in flight while this iteration's rows are gathered
+            const int32_t nxt = base + stride;
+            const int32_t coln = (lane < EIT && nxt + lane < end) ? p.col[nxt + lane] : 0;
             int32_t u[kUMax];
             bool ev[kUMax];
 #pragma unroll
@@ -196,6 +200,7 @@ struct FwdRow {
                     m[s] = mn;
                 }
             }
+            colv = coln;
         }
     }
 

@@ -48,7 +48,7 @@ inline int32_t source_rows(const gga_local_desc* d) { return d->n_src > 0 ? d->n
 inline int check_desc(const gga_local_desc* d) {
     if (!d) return GGA_EINVAL;
     if (d->n < 0 || d->e < 0 || d->heads < 1 || d->head_dim < 1 || d->n_src < 0) return GGA_EINVAL;
-    if (d->e >= (int64_t)INT32_MAX) return GGA_ERANGE;
+    if (d->e > (int64_t)INT32_MAX - 4096) return GGA_ERANGE;  // edge positions plus a loop stride fit int32
     const int64_t rows = d->n > source_rows(d) ? d->n : source_rows(d);
     if (rows * d->heads * d->head_dim >= ((int64_t)1 << 40)) return GGA_ERANGE;
     if (d->score != GGA_SCORE_DOT && d->score != GGA_SCORE_ADDITIVE && d->score != GGA_SCORE_MEAN)

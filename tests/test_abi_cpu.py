@@ -72,7 +72,7 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("bad,status", [
     (dict(n=-1), 1), (dict(heads=0), 1), (dict(head_dim=0), 1), (dict(e=-5), 1),
-    (dict(e=1 << 31), 2), (dict(score=7), 3), (dict(dtype=9), 3), (dict(heads=1, head_dim=1000), 3),
+    (dict(e=1 << 31), 2), (dict(e=(1 << 31) - 4000), 2), (dict(score=7), 3), (dict(dtype=9), 3), (dict(heads=1, head_dim=1000), 3),
 ])
 def test_fwd_rejects_bad_desc(bad, status):
     import sparse_graph_attention_amd as g
