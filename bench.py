@@ -49,7 +49,10 @@ MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 # HBM bytes per forward launch on the default workload counted by rocprofv3 (FETCH_SIZE x 2.00
 # + WRITE_SIZE x 1.00, factors from a plain 1 GiB copy), for the kernel as of the summary in
 # profiles/local_fwd_dot_n1m_h8_r64_bf16.md; None once the kernel changes.
-COUNTED_TRAFFIC_GB = 39.93
+COUNTED_TRAFFIC_GB = 39.91
+# The same for one backward call (pass A + pass B + merges) of the heavy-tailed workload,
+# profiles/local_fwd_bwd_dot_n2m_zipf_h8_c32_bf16.md.
+COUNTED_TRAFFIC_W5_BWD_GB = 157.71
 
 METRIC = "GEdges/s (x heads) for local graph-attention fwd; achieved HBM GB/s vs peak"
 
@@ -279,9 +282,10 @@ def bench_heavy_tail(args, g, torch, synth):
         cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
                "sample": f"the whole step (forward + backward, {e} edges), fp64, {dt:.1f} s"}
         log(f"cpu oracle: {dt:.2f} s")
-    roof = roofline("hbm", ba / (bms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", None,
+    traffic = COUNTED_TRAFFIC_W5_BWD_GB
+    roof = roofline("hbm", ba / (bms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", traffic,
                     kernel="bwd_dst_kernel + bwd_src_kernel (+ merges), one call", alg_bytes_per_launch=ba,
-                    launch_ms=bms)
+                    launch_ms=bms, counted_frac=traffic / (bms * 1e-3) / HBM_PEAK_GBS if traffic else None)
     cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "storage": "bf16 q/k/v, fp32 grads",
            "step": "forward + backward", "seq_len": n}
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "bf16", cfg, roof, cpu,
