@@ -107,6 +107,37 @@ class Timer:
     def phase_ms(self, a, b):
         return float(np.mean([x.elapsed_time(y) for x, y in zip(self.events[a], self.events[b])]))
 
+    def phase_median_ms(self, a, b):
+        return float(np.median([x.elapsed_time(y) for x, y in zip(self.events[a], self.events[b])]))
+
+
+def mall_cold_ms(torch, launch, reps, dev):
+    """Launch times (HIP events around the launch) with a 1 GiB fill kernel run before each,
+    so that the 256 MB MALL holds none of the inputs when the launch starts."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    out = []
+    for _ in range(reps):
+        scratch.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    del scratch
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 
 def _mark(tm, name):
     if tm is not None:
@@ -222,9 +253,23 @@ def bench_dot_forward(args, g, torch, synth, ident):
         t1 = time.perf_counter()
         oracle.local_fwd_dot(h64[0], h64[1], h64[2], og, 1.0 / np.sqrt(c))
         dt = time.perf_counter() - t1
-        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the whole forward of this workload ({e} edges, all {n} rows), fp64, {dt:.1f} s"}
-        log(f"cpu oracle: {dt:.2f} s with {oracle.threads()} threads")
+        cores = oracle.threads()
+        cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": cores, "kind": "oracle",
+               "sample": f"the whole forward of this workload ({e} edges, all {n} rows), fp64, {dt:.1f} s",
+               "model": cpu_model()}
+        # one thread on every 16th target row
+        rows = np.arange(0, n, 16, dtype=np.int32)
+        e1 = int((og.row_ptr[rows + 1] - og.row_ptr[rows]).sum())
+        oracle.set_threads(1)
+        t1 = time.perf_counter()
+        oracle.local_fwd_dot(h64[0], h64[1], h64[2], og, 1.0 / np.sqrt(c), rows=rows)
+        dt1 = time.perf_counter() - t1
+        oracle.set_threads(cores)
+        cpu["one_thread"] = {"value": e1 / dt1 / 1e9, "unit": "GEdges/s", "cores": 1,
+                             "sample": f"every 16th target row ({rows.size} rows, {e1} edges), {dt1:.1f} s"}
+        log(f"cpu oracle: {dt:.2f} s with {cores} threads; one thread {e1 / dt1 / 1e9:.5f} GEdges/s")
+    cold = mall_cold_ms(torch, lambda: step(None), max(5, min(args.steps, 20)), dev)
+    log(f"launch with the MALL flushed before each (median of {len(cold)}): {float(np.median(cold)):.3f} ms")
     traffic = COUNTED_TRAFFIC_GB if ident == 3 else None
     roof = roofline("hbm", ach, HBM_PEAK_GBS, "GB/s", traffic, kernel="local_fwd_kernel (+ heavy-row merge launch)",
                     alg_bytes_per_launch=alg, launch_ms=kms)
@@ -232,7 +277,8 @@ def bench_dot_forward(args, g, torch, synth, ident):
            "seq_len": n}
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, w.dtype, cfg, roof, cpu,
                   dict(tt, gedge_heads_per_s=e * heads / (ms * 1e-3) / 1e9, hbm_gbs_algorithmic=ach,
-                       graph_replay_ms_per_step=graph_ms))
+                       graph_replay_ms_per_step=graph_ms, launch_ms_median=tm.phase_median_ms("f0", "f1"),
+                       launch_ms_mall_flushed_median=float(np.median(cold))))
 
 
 def bench_heavy_tail(args, g, torch, synth):

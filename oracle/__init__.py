@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.orc_relation_fwd.restype = None
         L.orc_relation_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, P, P, P]
         L.orc_relation_bwd.restype = None
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_set_threads.restype = None
         L.orc_threads.argtypes = []
         L.orc_threads.restype = ctypes.c_int
         _lib = L
@@ -74,6 +76,11 @@ def lib() -> ctypes.CDLL:
 
 def threads() -> int:
     return int(lib().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the C loops (OpenMP); results do not depend on it."""
+    lib().orc_set_threads(int(n))
 
 
 def _p(a: np.ndarray | None):

@@ -470,6 +470,16 @@ void orc_relation_bwd(int mode, int32_t n, int32_t n_rel, int32_t hh, int32_t c,
     }
 }
 
+/* Thread count of the OpenMP loops (benchmark baselines time one thread and all). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 int orc_threads(void) {
 #ifdef _OPENMP
     extern int omp_get_max_threads(void);
