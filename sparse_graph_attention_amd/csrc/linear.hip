@@ -1,12 +1,16 @@
 // Dense fp32 product on the matrix cores (v_mfma_f32_16x16x4_f32): c = op(a) op(b) (+ bias),
 // or c += op(a) op(b).
 //
-// Workgroup tile 128 x BN (BN = 128, or 64 when n <= 64), eight wavefronts each owning
-// 64 x BN/4 (MFMA tiles of 16x16), K staged through LDS 16 at a time with double buffering.
-// LDS holds both operands as [row][k]; with the contraction index permuted inside a tile,
-// each lane reads its operands for four MFMA steps with one 16-byte LDS read.  When the
-// output has few tiles and K is long, K is split into a fixed number of ranges whose partial products are added in a fixed order by a second
-// kernel, so results do not depend on scheduling.
+// Kernels by shape:
+// - n > 64: gemm_f32_big, 128 x 128 tiles of four wavefronts, each operand staged in LDS in
+//   the layout its memory order gives (see its comment);
+// - n <= 64: gemm_f32_mfma<64>, 128 x 64 tiles of eight wavefronts, both operands staged as
+//   [row][k];
+// - k, n <= 64: gemm_narrow; a transposed a with at most 32 x 32 outputs over a long k:
+//   gemm_small_out.
+// When the output has few tiles and k is long, k is split into a fixed number of ranges whose
+// partial products are added in a fixed order by a second kernel, so results do not depend on
+// scheduling.
 #include "common.hpp"
 
 namespace gga {
