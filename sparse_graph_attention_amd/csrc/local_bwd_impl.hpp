@@ -25,7 +25,7 @@ struct BwdCsr {
     const int32_t* row_ptr;
     const int32_t* col;
     const PlanHeader* hdr;
-    const int32_t* light;
+    const int4* light;
     const int4* chunks;
     const int4* heavy;
     float* part;
@@ -487,9 +487,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dst_kernel(BwdParams p) {
     }
     const int li = (blockIdx.x - p.a.chunk_blocks) * kBwdWaves + wave;
     if (li >= p.a.hdr->n_light) return;
-    const int32_t v = p.a.light[li];
+    const int4 lr = p.a.light[li];
+    const int32_t v = lr.x;
     r.load_target(p, v);
-    r.run(p, p.a.row_ptr[v], p.a.row_ptr[v + 1], 0, r.EIT);
+    r.run(p, lr.y, lr.z, 0, r.EIT);
     r.reduce_groups();
     r.write_final(p, v);
 }
@@ -538,9 +539,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_src_kernel(BwdParams p) {
     }
     const int li = (blockIdx.x - p.b.chunk_blocks) * kBwdWaves + wave;
     if (li >= p.b.hdr->n_light) return;
-    const int32_t u = p.b.light[li];
+    const int4 lr = p.b.light[li];
+    const int32_t u = lr.x;
     r.load_source(p, u);
-    r.run(p, p.b.row_ptr[u], p.b.row_ptr[u + 1], 0, r.EIT);
+    r.run(p, lr.y, lr.z, 0, r.EIT);
     r.reduce_groups();
     r.write_final(p, u);
 }

@@ -27,7 +27,7 @@ struct FwdParams {
     const int32_t* row_ptr;
     const int32_t* col;
     const PlanHeader* hdr;
-    const int32_t* light;
+    const int4* light;
     const int4* chunks;
     const int4* heavy;
     float* out;
@@ -319,10 +319,11 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
     }
     const int li = (blockIdx.x - p.chunk_blocks) * kFwdWaves + wave;
     if (li >= p.hdr->n_light) return;
-    const int32_t v = p.light[li];
+    const int4 lr = p.light[li];
+    const int32_t v = lr.x;
     r.reset();
     r.load_target(p, v);
-    r.run(p, p.row_ptr[v], p.row_ptr[v + 1], 0, r.EIT);
+    r.run(p, lr.y, lr.z, 0, r.EIT);
     r.merge_groups();
     r.write_final(p, v);
 }

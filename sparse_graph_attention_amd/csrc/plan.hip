@@ -47,7 +47,7 @@ __global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, const 
         const int32_t beg = row_ptr[v], end = row_ptr[v + 1];
         const int32_t deg = end - beg;
         if (deg <= kLightEdges) {
-            pv.light[a[v]] = (int32_t)v;
+            pv.light[a[v]] = make_int4((int32_t)v, beg, end, 0);
             continue;
         }
         const int32_t chunks = (deg + kChunkEdges - 1) / kChunkEdges;

@@ -40,7 +40,7 @@ inline PlanBounds plan_bounds(int64_t e) {
 // Device views into a plan buffer.
 struct PlanView {
     PlanHeader* hdr;
-    int32_t* light;  // [n]
+    int4* light;     // [n]: row, begin, end, 0 (the row's edge range read with its id)
     int4* chunks;    // [max_chunks]: row, begin, end, slot (-1: chunk is the whole row)
     int4* heavy;     // [max_heavy]: row, first slot, slot count, 0
     size_t bytes;
@@ -51,7 +51,7 @@ inline PlanView plan_view(void* plan, int32_t n, int64_t e) {
     Carver c(plan);
     PlanView v;
     v.hdr = c.take<PlanHeader>(1);
-    v.light = c.take<int32_t>((size_t)n);
+    v.light = c.take<int4>((size_t)n);
     v.chunks = c.take<int4>((size_t)b.max_chunks);
     v.heavy = c.take<int4>((size_t)b.max_heavy);
     v.bytes = c.bytes();
