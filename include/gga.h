@@ -108,7 +108,7 @@ typedef struct gga_local_desc {
     int64_t e;            /* edges (length of col), at most 2^31 - 4097 (GGA_ERANGE) */
     int32_t head_dim;     /* C (r): per-head width */
     int32_t score;        /* GGA_SCORE_DOT, GGA_SCORE_ADDITIVE or GGA_SCORE_MEAN */
-    int32_t dtype;        /* storage type of q, k, v (dot) or of v (additive) */
+    int32_t dtype;        /* storage type of q, k, v (dot) or of v (additive, mean) */
     float scale;          /* dot: multiplier of q.k, usually 1/sqrt(C) */
     float negative_slope; /* additive: LeakyReLU slope, usually 0.2 */
     int32_t n_src;        /* rows of the source-side tensors (ks, v); 0 means n */
