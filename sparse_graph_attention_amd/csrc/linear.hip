@@ -6,8 +6,9 @@
 //   the layout its memory order gives (see its comment);
 // - n <= 64: gemm_f32_mfma<64>, 128 x 64 tiles of eight wavefronts, both operands staged as
 //   [row][k];
-// - k, n <= 64: gemm_narrow; a transposed a with at most 32 x 32 outputs over a long k:
-//   gemm_small_out.
+// - k, n <= 32: gemm_rows (a thread per output row); k, n <= 64: gemm_narrow;
+// - a transposed a with few outputs over a long k: gemm_outer (m, n <= 16, one MFMA tile)
+//   or gemm_small_out (m, n <= 32).
 // When the output has few tiles and k is long, k is split into a fixed number of ranges whose
 // partial products are added in a fixed order by a second kernel, so results do not depend on
 // scheduling.
@@ -543,6 +544,98 @@ __global__ __launch_bounds__(256) void gemm_small_out(GemmArgs g, float* __restr
 // Narrow contraction (K, N <= 64): a workgroup owns 64 output rows; their op(a) rows and
 // op(b) are staged in LDS with coalesced loads, and thread t computes outputs t, t+256, ...
 // of the 64 x N block (so stores are coalesced), summing k in order.
+// Short rows (k, n <= 32): one thread per output row, op(b) in LDS (read by broadcast), the
+// row of op(a) in registers (16-byte loads when rows are 16-byte aligned), n outputs written
+// as 16-byte stores when possible.  Each output sums over k in order, as gemm_narrow does.
+template <int KP, int NP>
+__global__ __launch_bounds__(256) void gemm_rows(GemmArgs g) {
+    __shared__ float bs[KP * NP];
+    const int K = g.K, N = g.N;
+    for (int x = threadIdx.x; x < K * N; x += 256) bs[x] = op_b(g, x / N, x % N);
+    __syncthreads();
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= g.M) return;
+    float a[KP];
+    const bool a_vec = !g.trans_a && K % 4 == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
+    if (a_vec) {
+#pragma unroll
+        for (int q = 0; q < KP / 4; q++) {
+            const v4f x = q * 4 < K ? *reinterpret_cast<const v4f*>(g.a + r * K + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
+            a[4 * q] = x[0];
+            a[4 * q + 1] = x[1];
+            a[4 * q + 2] = x[2];
+            a[4 * q + 3] = x[3];
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < KP; kk++) a[kk] = kk < K ? op_a(g, r, kk) : 0.f;
+    }
+    float o[NP];
+#pragma unroll
+    for (int j = 0; j < NP; j++) {
+        float acc = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KP; kk++)
+            if (kk < K && j < N) acc = fmaf(a[kk], bs[kk * N + j], acc);
+        o[j] = acc + (g.bias && j < N ? g.bias[j] : 0.f);
+    }
+    float* c = g.c + r * N;
+    if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < NP / 4; q++) {
+            if (q * 4 >= N) continue;
+            v4f x = v4f{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+            if (g.accumulate) x = *reinterpret_cast<const v4f*>(c + 4 * q) + x;
+            *reinterpret_cast<v4f*>(c + 4 * q) = x;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NP; j++)
+            if (j < N) c[j] = (g.accumulate ? c[j] : 0.f) + o[j];
+    }
+}
+
+// Few outputs (m, n <= 16) of a transposed-a product c = a^T b over a long k (a stored
+// [K][M], b [K][N]) on the matrix cores: one 16 x 16 tile, each MFMA taking four rows of k
+// (lane l holds a[r + l/16][l%16] and b[r + l/16][l%16]: a wave-wide load of four
+// consecutive rows each).  Workgroup z covers its fixed k range; wavefront w takes rows
+// kb + 16 (4 i + w) .. + 15 in four independent accumulation chains (chain u: rows
+// +4u .. +4u+3), added in chain order, and the four wavefronts in wavefront order into
+// part[z][M][N].
+__global__ __launch_bounds__(256) void gemm_outer(GemmArgs g, float* __restrict__ part) {
+    __shared__ float sm[4][256];
+    const int M = g.M, N = g.N;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, kq = lane >> 4;
+    const int64_t kb = (int64_t)blockIdx.x * g.kchunk;
+    const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+    v4f acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int64_t r0 = kb + 16 * wave; r0 < ke; r0 += 64) {
+        float av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t r = r0 + 4 * u + kq;
+            const bool ok = r < ke;
+            av[u] = ok && col < M ? g.a[r * M + col] : 0.f;
+            bv[u] = ok && col < N ? g.b[r * N + col] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc[u], 0, 0, 0);
+    }
+    const v4f t = ((acc[0] + acc[1]) + acc[2]) + acc[3];
+    // acc element e of lane l is c[4 (l / 16) + e][l % 16]
+#pragma unroll
+    for (int e = 0; e < 4; e++) sm[wave][(4 * kq + e) * 16 + col] = t[e];
+    __syncthreads();
+    float* out = part + (int64_t)blockIdx.x * M * N;
+    for (int x = threadIdx.x; x < M * N; x += 256) {
+        const int i = x / N, j = x % N;
+        out[x] = ((sm[0][i * 16 + j] + sm[1][i * 16 + j]) + sm[2][i * 16 + j]) + sm[3][i * 16 + j];
+    }
+}
+
 __global__ __launch_bounds__(256) void gemm_narrow(GemmArgs g) {
     __shared__ float as[64 * 65], bs[64 * 64];
     const int K = g.K, N = g.N;
@@ -587,6 +680,27 @@ Split small_out_split(int32_t k) {
 }
 
 bool narrow(int32_t k, int32_t n) { return k <= 64 && n <= 64; }
+
+// The register-row paths: short rows, or few outputs.
+bool short_rows(int32_t k, int32_t n) { return k <= 32 && n <= 32; }
+bool outer_shape(int32_t m, int32_t n) { return m <= 16 && n <= 16; }
+
+// k ranges of the outer-product path: at least 4096 rows each, at most 1024 ranges (never
+// more ranges than small_out_split gives, so the same workspace holds the partials).
+Split outer_split(int32_t k) {
+    int64_t kc = ((int64_t)k + 1023) / 1024;
+    if (kc < 4096) kc = 4096;
+    Split s;
+    s.kchunk = (int32_t)kc;
+    s.splits = (int)(((int64_t)k + kc - 1) / kc);
+    return s;
+}
+
+int pow2_at_least4(int x) {
+    int p = 4;
+    while (p < x) p <<= 1;
+    return p;
+}
 
 int pick_bn(int32_t n) { return n <= 64 ? 64 : 128; }
 
@@ -653,12 +767,27 @@ int linear_impl(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_
         g.trans_b = trans_b != 0;
         g.accumulate = accumulate;
         if (so_path) {
-            const Split so = small_out_split(k);
+            const bool outer = outer_shape(m, n);
+            const Split so = outer ? outer_split(k) : small_out_split(k);
             g.kchunk = so.kchunk;
-            gemm_small_out<<<(unsigned)so.splits, 256, 0, s>>>(g, static_cast<float*>(ws));
+            float* part = static_cast<float*>(ws);
+            if (!outer) {
+                gemm_small_out<<<(unsigned)so.splits, 256, 0, s>>>(g, part);
+            } else {
+                gemm_outer<<<(unsigned)so.splits, 256, 0, s>>>(g, part);
+            }
             const int64_t mn = (int64_t)m * n;
-            splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(static_cast<const float*>(ws), so.splits, mn, n,
-                                                                    bias, accumulate, c);
+            splitk_reduce<<<(unsigned)((mn + 63) / 64), 1024, 0, s>>>(part, so.splits, mn, n, bias, accumulate, c);
+        } else if (short_rows(k, n)) {
+            const int64_t blocks = ((int64_t)m + 255) / 256;
+            if (blocks >= ((int64_t)1 << 31)) return GGA_ERANGE;
+            const int kp = pow2_at_least4(k), np = pow2_at_least4(n);
+#define GGA_ROWS(KP_, NP_) \
+    if (kp == KP_ && np == NP_) gemm_rows<KP_, NP_><<<(unsigned)blocks, 256, 0, s>>>(g);
+            GGA_ROWS(4, 4) GGA_ROWS(4, 8) GGA_ROWS(4, 16) GGA_ROWS(4, 32) GGA_ROWS(8, 4) GGA_ROWS(8, 8)
+            GGA_ROWS(8, 16) GGA_ROWS(8, 32) GGA_ROWS(16, 4) GGA_ROWS(16, 8) GGA_ROWS(16, 16) GGA_ROWS(16, 32)
+            GGA_ROWS(32, 4) GGA_ROWS(32, 8) GGA_ROWS(32, 16) GGA_ROWS(32, 32)
+#undef GGA_ROWS
         } else {
             const int64_t blocks = ((int64_t)m + 63) / 64;
             if (blocks >= ((int64_t)1 << 31)) return GGA_ERANGE;
