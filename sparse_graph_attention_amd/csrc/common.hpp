@@ -142,11 +142,6 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 void fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
 void fill_f32(float* p, int64_t n, float value, hipStream_t s);
 
-// out[i, :] = in[idx[i], :] (gather) and out[idx[i], :] = in[i, :] (scatter; idx must be a
-// permutation) for rows of `width` floats, i < rows.
-void gather_rows_f32(const float* in, const int32_t* idx, int64_t rows, int32_t width, float* out, hipStream_t s);
-void scatter_rows_f32(const float* in, const int32_t* idx, int64_t rows, int32_t width, float* out, hipStream_t s);
-
 // Exclusive prefix sum of in[0..n) into out[0..n); if total != nullptr, *total (device) = sum.
 // out may alias in.  Needs scan_workspace_elems(n) int32 of scratch.
 size_t scan_workspace_elems(int64_t n);

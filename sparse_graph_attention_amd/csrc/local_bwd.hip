@@ -35,26 +35,14 @@ BwdWs carve_bwd(void* ws, const gga_local_desc* d) {
     return w;
 }
 
-struct EdgeWs {
-    float* se_a;  // edge term in the order of the CSR by destination
-    float* se_b;  // ... by source
-    float* dz_a;  // dz_e in the order of the CSR by destination
+// The per-edge logit term (COO order) and the CSRs' COO indices through which the passes
+// read it; pass A writes dz_e for every edge, in COO order, through the same indices.
+struct EdgeTerms {
+    const float* se;
+    float* dz;
+    const int32_t* eid_a;
+    const int32_t* eid_b;
 };
-
-EdgeWs carve_edge(void* base, const gga_local_desc* d) {
-    Carver c(base);
-    EdgeWs w;
-    w.se_a = c.take<float>((size_t)d->e * d->heads);
-    w.se_b = c.take<float>((size_t)d->e * d->heads);
-    w.dz_a = c.take<float>((size_t)d->e * d->heads);
-    return w;
-}
-
-size_t edge_ws_bytes(const gga_local_desc* d) {
-    Carver c(nullptr);
-    for (int i = 0; i < 3; i++) c.take<float>((size_t)d->e * d->heads);
-    return c.bytes();
-}
 
 // No targets: every source-side gradient is zero.
 int zero_source_grads(const gga_local_desc* d, float* d_ks, float* d_v, hipStream_t s) {
@@ -69,7 +57,7 @@ int zero_source_grads(const gga_local_desc* d, float* d_ks, float* d_v, hipStrea
 int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void* v, const float* out,
              const float* lse, const float* d_out, const int32_t* row_ptr, const int32_t* col, const void* plan,
              const int32_t* row_ptr_s, const int32_t* col_s, const void* plan_s, float* d_qs, float* d_ks,
-             float* d_v, const EdgeWs* ew, void* ws, size_t ws_bytes, hipStream_t s) {
+             float* d_v, const EdgeTerms* et, void* ws, size_t ws_bytes, hipStream_t s) {
     const bool mean = d->score == GGA_SCORE_MEAN;
     if (!d_out || !row_ptr || !plan || !row_ptr_s || !plan_s || !d_v) return GGA_EINVAL;
     if (!mean && (!qs || !out || !lse || !d_qs || !d_ks)) return GGA_EINVAL;
@@ -121,10 +109,11 @@ int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
     p.score_mul = d->score == GGA_SCORE_DOT ? d->scale * kLog2e : kLog2e;
     p.slope = d->negative_slope;
     int mode = d->score;
-    if (ew) {
-        p.se_a = ew->se_a;
-        p.se_b = ew->se_b;
-        p.dz_a = ew->dz_a;
+    if (et) {
+        p.se = et->se;
+        p.dz = et->dz;
+        p.eid_a = et->eid_a;
+        p.eid_b = et->eid_b;
         mode = kScoreAddEdge;
     }
     const int64_t light_a = ((int64_t)d->n + kBwdWaves - 1) / kBwdWaves;
@@ -163,7 +152,7 @@ extern "C" int gga_local_attn_bwd(const gga_local_desc* d, const void* qs, const
 
 extern "C" size_t gga_local_attn_bwd_edge_workspace(const gga_local_desc* d) {
     if (check_desc(d) != GGA_OK) return 0;
-    return carve_bwd(nullptr, d).bytes + edge_ws_bytes(d);
+    return carve_bwd(nullptr, d).bytes;
 }
 
 extern "C" int gga_local_attn_bwd_edge(const gga_local_desc* d, const float* s_dst, const float* s_src,
@@ -178,17 +167,9 @@ extern "C" int gga_local_attn_bwd_edge(const gga_local_desc* d, const float* s_d
     if (d->score != GGA_SCORE_ADDITIVE || d->dtype != GGA_F32) return GGA_EUNSUPPORTED;
     if (d->n == 0) return zero_source_grads(d, d_s_src, d_hf, as_stream(stream));
     if (d->e > 0 && (!s_edge || !eid || !eid_s || !d_s_edge)) return GGA_EINVAL;
-    if (ws_bytes < gga_local_attn_bwd_edge_workspace(d) || !ws) return GGA_EWORKSPACE;
-    hipStream_t s = as_stream(stream);
-    const size_t main_bytes = carve_bwd(nullptr, d).bytes;
-    const EdgeWs ew = carve_edge(static_cast<char*>(ws) + main_bytes, d);
-    if (d->e > 0) {
-        gather_rows_f32(s_edge, eid, d->e, d->heads, ew.se_a, s);
-        gather_rows_f32(s_edge, eid_s, d->e, d->heads, ew.se_b, s);
-    }
-    st = bwd_impl(d, s_dst, s_src, hf, out, lse, d_out, row_ptr, col, plan, row_ptr_s, col_s, plan_s, d_s_dst,
-                  d_s_src, d_hf, d->e > 0 ? &ew : nullptr, ws, main_bytes, s);
-    if (st != GGA_OK) return st;
-    if (d->e > 0) scatter_rows_f32(ew.dz_a, eid, d->e, d->heads, d_s_edge, s);  // CSR order -> COO order
-    return launch_status();
+    // both passes read the edge term in COO order through the CSRs' eid; pass A writes dz_e
+    // straight to d_s_edge in COO order
+    const EdgeTerms et{s_edge, d_s_edge, eid, eid_s};
+    return bwd_impl(d, s_dst, s_src, hf, out, lse, d_out, row_ptr, col, plan, row_ptr_s, col_s, plan_s, d_s_dst,
+                    d_s_src, d_hf, d->e > 0 ? &et : nullptr, ws, ws_bytes, as_stream(stream));
 }

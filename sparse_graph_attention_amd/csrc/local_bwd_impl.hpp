@@ -50,11 +50,13 @@ struct BwdParams {
     float scale;      // dot: score scale
     float score_mul;  // multiplier taking a raw score to log2 units
     float slope;
-    // kScoreAddEdge: the edge term of the logit in the order of each CSR, and dz_e out in
-    // the order of the CSR by destination
-    const float* se_a;
-    const float* se_b;
-    float* dz_a;
+    // kScoreAddEdge: the edge term of the logit and dz_e out, both in COO order [E, H],
+    // reached through the COO index of each position of the CSR by destination (eid_a) and
+    // by source (eid_b)
+    const float* se;
+    float* dz;
+    const int32_t* eid_a;
+    const int32_t* eid_b;
 };
 
 // Launchers, one per storage type (instantiated in local_bwd_f32.hip / local_bwd_bf16.hip).
@@ -124,20 +126,28 @@ struct PassA {
         const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
         int32_t base = beg + start;
         int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.a.col[base + geo.lane] : 0;
+        int32_t eidv = 0;  // edge terms: the COO index of each position, loaded like col
+        if constexpr (MODE == kScoreAddEdge)
+            eidv = (geo.lane < EIT && base + geo.lane < end) ? p.eid_a[base + geo.lane] : 0;
         for (; base < end; base += stride) {
             // the next iteration's sources, in flight while this iteration's rows are gathered
             const int32_t nxt = base + stride;
             const int32_t coln = (geo.lane < EIT && nxt + geo.lane < end) ? p.a.col[nxt + geo.lane] : 0;
-            int32_t u[kUMax];
+            int32_t eidn = 0;
+            if constexpr (MODE == kScoreAddEdge)
+                eidn = (geo.lane < EIT && nxt + geo.lane < end) ? p.eid_a[nxt + geo.lane] : 0;
+            int32_t u[kUMax], ej[kUMax];
             bool ev[kUMax];
 #pragma unroll
             for (int j = 0; j < kUMax; j++) {
                 if (j < U) {
                     const int idx = geo.g + geo.G * j;
                     u[j] = __shfl(colv, idx, 64);
+                    ej[j] = MODE == kScoreAddEdge ? __shfl(eidv, idx, 64) : 0;
                     ev[j] = base + idx < end;
                 } else {
                     u[j] = 0;
+                    ej[j] = 0;
                     ev[j] = false;
                 }
             }
@@ -157,7 +167,7 @@ struct PassA {
                         } else {
                             ss[j][s] = ssrc[(size_t)u[j] * p.H + geo.head[s]];
                             if constexpr (MODE == kScoreAddEdge)
-                                ss[j][s] += p.se_a[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]];
+                                ss[j][s] += p.se[(size_t)ej[j] * p.H + geo.head[s]];
                         }
                         vr[j][s] = *reinterpret_cast<const raw_t*>(vp + ro);
                     }
@@ -193,13 +203,14 @@ struct PassA {
                         acc[s][0] = fmaf(ds, z > 0.f ? 1.f : p.slope, acc[s][0]);
                         if constexpr (MODE == kScoreAddEdge) {
                             if (ev[j] && geo.ok[s] && geo.lead[s])
-                                p.dz_a[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]] =
+                                p.dz[(size_t)ej[j] * p.H + geo.head[s]] =
                                     ds * (z > 0.f ? 1.f : p.slope);
                         }
                     }
                 }
             }
             colv = coln;
+            if constexpr (MODE == kScoreAddEdge) eidv = eidn;
         }
     }
 
@@ -295,20 +306,28 @@ struct PassB {
         const float* __restrict__ sdst = static_cast<const float*>(p.qs);
         int32_t base = beg + start;
         int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.b.col[base + geo.lane] : 0;
+        int32_t eidv = 0;  // edge terms: the COO index of each position, loaded like col
+        if constexpr (MODE == kScoreAddEdge)
+            eidv = (geo.lane < EIT && base + geo.lane < end) ? p.eid_b[base + geo.lane] : 0;
         for (; base < end; base += stride) {
             // the next iteration's sources, in flight while this iteration's rows are gathered
             const int32_t nxt = base + stride;
             const int32_t coln = (geo.lane < EIT && nxt + geo.lane < end) ? p.b.col[nxt + geo.lane] : 0;
-            int32_t t[kUMax];
+            int32_t eidn = 0;
+            if constexpr (MODE == kScoreAddEdge)
+                eidn = (geo.lane < EIT && nxt + geo.lane < end) ? p.eid_b[nxt + geo.lane] : 0;
+            int32_t t[kUMax], ej[kUMax];
             bool ev[kUMax];
 #pragma unroll
             for (int j = 0; j < kUMax; j++) {
                 if (j < U) {
                     const int idx = geo.g + geo.G * j;
                     t[j] = __shfl(colv, idx, 64);
+                    ej[j] = MODE == kScoreAddEdge ? __shfl(eidv, idx, 64) : 0;
                     ev[j] = base + idx < end;
                 } else {
                     t[j] = 0;
+                    ej[j] = 0;
                     ev[j] = false;
                 }
             }
@@ -331,7 +350,7 @@ struct PassB {
                         } else if constexpr (MODE != GGA_SCORE_MEAN) {
                             sj[j][s] = sdst[hi];
                             if constexpr (MODE == kScoreAddEdge)
-                                sj[j][s] += p.se_b[(size_t)(base + geo.g + geo.G * j) * p.H + geo.head[s]];
+                                sj[j][s] += p.se[(size_t)ej[j] * p.H + geo.head[s]];
                         }
                         load_f32<EPL>(p.dout + ro, gr[j][s]);
                         if constexpr (MODE == GGA_SCORE_MEAN) {  // the weight itself: 1/deg(t)
@@ -382,6 +401,7 @@ struct PassB {
                 }
             }
             colv = coln;
+            if constexpr (MODE == kScoreAddEdge) eidv = eidn;
         }
     }
 

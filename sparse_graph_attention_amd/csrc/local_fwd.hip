@@ -39,7 +39,8 @@ struct FwdParams {
     float score_mul;
     float slope;
     int32_t chunk_blocks;
-    const float* se;  // kScoreAddEdge: edge term of the logit, CSR order [E, H]
+    const float* se;     // kScoreAddEdge: edge term of the logit, COO order [E, H]
+    const int32_t* eid;  // kScoreAddEdge: COO index of each CSR position
 };
 
 // UMAX: edge slots per lane and iteration over the NS row slots.  A row that fills the
@@ -109,20 +110,26 @@ struct FwdRow {
         const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
         int32_t base = beg + start;
         int32_t colv = (lane < EIT && base + lane < end) ? p.col[base + lane] : 0;
+        int32_t eidv = 0;  // edge terms: the COO index of each position, loaded like col
+        if constexpr (MODE == kScoreAddEdge) eidv = (lane < EIT && base + lane < end) ? p.eid[base + lane] : 0;
         for (; base < end; base += stride) {
             // the next iteration's sources, in flight while this iteration's rows are gathered
             const int32_t nxt = base + stride;
             const int32_t coln = (lane < EIT && nxt + lane < end) ? p.col[nxt + lane] : 0;
-            int32_t u[kUMax];
+            int32_t eidn = 0;
+            if constexpr (MODE == kScoreAddEdge) eidn = (lane < EIT && nxt + lane < end) ? p.eid[nxt + lane] : 0;
+            int32_t u[kUMax], ej[kUMax];
             bool ev[kUMax];
 #pragma unroll
             for (int j = 0; j < kUMax; j++) {
                 if (j < U) {
                     const int idx = g + G * j;
                     u[j] = __shfl(colv, idx, 64);
+                    ej[j] = MODE == kScoreAddEdge ? __shfl(eidv, idx, 64) : 0;
                     ev[j] = base + idx < end;
                 } else {
                     u[j] = 0;
+                    ej[j] = 0;
                     ev[j] = false;
                 }
             }
@@ -141,8 +148,7 @@ struct FwdRow {
                             kr[j][s] = *reinterpret_cast<const raw_t*>(kp + ro);
                         } else if constexpr (MODE != GGA_SCORE_MEAN) {
                             ss[j][s] = ssrc[(size_t)u[j] * p.H + head[s]];
-                            if constexpr (MODE == kScoreAddEdge)
-                                ss[j][s] += p.se[(size_t)(base + g + G * j) * p.H + head[s]];
+                            if constexpr (MODE == kScoreAddEdge) ss[j][s] += p.se[(size_t)ej[j] * p.H + head[s]];
                         }
                         vr[j][s] = *reinterpret_cast<const raw_t*>(vp + ro);
                     }
@@ -201,6 +207,7 @@ struct FwdRow {
                 }
             }
             colv = coln;
+            if constexpr (MODE == kScoreAddEdge) eidv = eidn;
         }
     }
 
@@ -420,7 +427,7 @@ size_t fwd_part_bytes(const gga_local_desc* d) {
 
 // The forward with an optional edge term `se` (CSR order); ws holds the split-row partials.
 int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void* v, const int32_t* row_ptr,
-             const int32_t* col, const void* plan, float* out, float* lse, const float* se, void* ws,
+             const int32_t* col, const void* plan, float* out, float* lse, const float* se, const int32_t* eid, void* ws,
              size_t ws_bytes, hipStream_t s) {
     const bool mean = d->score == GGA_SCORE_MEAN;
     if (!row_ptr || !plan || !out || (!qs && !mean)) return GGA_EINVAL;
@@ -447,6 +454,7 @@ int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
     p.lse = lse;
     p.part = static_cast<float*>(ws);
     p.se = se;
+    p.eid = eid;
     p.n = d->n;
     p.H = d->heads;
     p.C = d->head_dim;
@@ -492,12 +500,12 @@ extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const
     int st = check_desc(d);
     if (st != GGA_OK) return st;
     if (d->n == 0) return GGA_OK;
-    return fwd_impl(d, qs, ks, v, row_ptr, col, plan, out, lse, nullptr, ws, ws_bytes, as_stream(stream));
+    return fwd_impl(d, qs, ks, v, row_ptr, col, plan, out, lse, nullptr, nullptr, ws, ws_bytes, as_stream(stream));
 }
 
 extern "C" size_t gga_local_attn_fwd_edge_workspace(const gga_local_desc* d) {
     if (check_desc(d) != GGA_OK) return 0;
-    return fwd_part_bytes(d) + align_up((size_t)d->e * d->heads * sizeof(float), 256);
+    return fwd_part_bytes(d);
 }
 
 extern "C" int gga_local_attn_fwd_edge(const gga_local_desc* d, const float* s_dst, const float* s_src,
@@ -509,10 +517,7 @@ extern "C" int gga_local_attn_fwd_edge(const gga_local_desc* d, const float* s_d
     if (d->score != GGA_SCORE_ADDITIVE || d->dtype != GGA_F32) return GGA_EUNSUPPORTED;
     if (d->n == 0) return GGA_OK;
     if (d->e > 0 && (!s_edge || !eid)) return GGA_EINVAL;
-    const size_t part = fwd_part_bytes(d);
-    if (ws_bytes < gga_local_attn_fwd_edge_workspace(d) || !ws) return GGA_EWORKSPACE;
-    hipStream_t s = as_stream(stream);
-    float* se = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
-    gather_rows_f32(s_edge, eid, d->e, d->heads, se, s);  // COO order -> CSR order
-    return fwd_impl(d, s_dst, s_src, hf, row_ptr, col, plan, out, lse, d->e > 0 ? se : nullptr, ws, part, s);
+    // the kernel reads each edge's term in COO order through eid
+    return fwd_impl(d, s_dst, s_src, hf, row_ptr, col, plan, out, lse, d->e > 0 ? s_edge : nullptr, eid, ws,
+                    ws_bytes, as_stream(stream));
 }

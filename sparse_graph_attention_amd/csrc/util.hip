@@ -119,37 +119,7 @@ int grid_for(int64_t n, int threads) {
     return (int)b;
 }
 
-
-__global__ void gather_rows_kernel(const float* __restrict__ in, const int32_t* __restrict__ idx, int64_t rows,
-                                   int32_t width, float* __restrict__ out) {
-    const int64_t total = rows * width;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / width;
-        out[i] = in[(int64_t)idx[r] * width + (i - r * width)];
-    }
-}
-
-__global__ void scatter_rows_kernel(const float* __restrict__ in, const int32_t* __restrict__ idx, int64_t rows,
-                                    int32_t width, float* __restrict__ out) {
-    const int64_t total = rows * width;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / width;
-        out[(int64_t)idx[r] * width + (i - r * width)] = in[i];
-    }
-}
-
 }  // namespace
-
-void gather_rows_f32(const float* in, const int32_t* idx, int64_t rows, int32_t width, float* out, hipStream_t s) {
-    if (rows <= 0 || width <= 0) return;
-    gather_rows_kernel<<<grid_for(rows * width, 256), 256, 0, s>>>(in, idx, rows, width, out);
-}
-
-void scatter_rows_f32(const float* in, const int32_t* idx, int64_t rows, int32_t width, float* out, hipStream_t s) {
-    if (rows <= 0 || width <= 0) return;
-    scatter_rows_kernel<<<grid_for(rows * width, 256), 256, 0, s>>>(in, idx, rows, width, out);
-}
-
 
 void fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s) {
     if (n <= 0) return;
