@@ -545,22 +545,44 @@ __global__ __launch_bounds__(256) void gemm_small_out(GemmArgs g, float* __restr
 // op(b) are staged in LDS with coalesced loads, and thread t computes outputs t, t+256, ...
 // of the 64 x N block (so stores are coalesced), summing k in order.
 // Short rows (k, n <= 32): one thread per output row, op(b) in LDS (read by broadcast), the
-// row of op(a) in registers (16-byte loads when rows are 16-byte aligned), n outputs written
-// as 16-byte stores when possible.  Each output sums over k in order, as gemm_narrow does.
+// row of op(a) in registers; each output sums over k in order, as gemm_narrow does.  When a
+// wavefront's 64 rows lie inside the matrices with 16-byte rows (plain a), the rows move
+// through a wavefront-private LDS block both ways, so every global access is a contiguous
+// 16-byte-per-lane run (measured faster than per-thread rows on either side alone for
+// k = 16, n = 8 and k = 8, n = 16); otherwise each thread reads and writes its own row.
 template <int KP, int NP>
 __global__ __launch_bounds__(256) void gemm_rows(GemmArgs g) {
+    constexpr int PA = KP + 4, PC = NP + 4;  // padded rows: 16-byte reads of 8 lanes hit distinct banks
     __shared__ float bs[KP * NP];
+    __shared__ float stage[4][64 * (PA > PC ? PA : PC)];
     const int K = g.K, N = g.N;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int x = threadIdx.x; x < K * N; x += 256) bs[x] = op_b(g, x / N, x % N);
-    __syncthreads();
-    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= g.M) return;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
+    const int64_t r = r0 + lane;
+    const bool tile = !g.trans_a && K % 4 == 0 && N % 4 == 0 && r0 + 64 <= g.M &&
+                      (reinterpret_cast<uintptr_t>(g.a) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    float* st = stage[wave];
     float a[KP];
-    const bool a_vec = !g.trans_a && K % 4 == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
-    if (a_vec) {
+    __syncthreads();  // bs complete; from here on each wavefront works alone
+    if (r >= g.M) return;
+    if (tile) {
+        const float* src = g.a + r0 * K;
+        v4f v[KP / 4];  // 64 rows of K floats, 4 at a time: all loads in flight together
 #pragma unroll
         for (int q = 0; q < KP / 4; q++) {
-            const v4f x = q * 4 < K ? *reinterpret_cast<const v4f*>(g.a + r * K + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
+            const int x = lane + 64 * q;
+            v[q] = x < 16 * K ? *reinterpret_cast<const v4f*>(src + 4 * x) : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < KP / 4; q++) {
+            const int x = lane + 64 * q;
+            if (x < 16 * K) *reinterpret_cast<v4f*>(st + (4 * x / K) * PA + (4 * x) % K) = v[q];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < KP / 4; q++) {
+            const v4f x = q * 4 < K ? *reinterpret_cast<const v4f*>(st + lane * PA + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
             a[4 * q] = x[0];
             a[4 * q + 1] = x[1];
             a[4 * q + 2] = x[2];
@@ -579,28 +601,36 @@ __global__ __launch_bounds__(256) void gemm_rows(GemmArgs g) {
             if (kk < K && j < N) acc = fmaf(a[kk], bs[kk * N + j], acc);
         o[j] = acc + (g.bias && j < N ? g.bias[j] : 0.f);
     }
-    float* c = g.c + r * N;
-    if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0) {
+    if (tile) {
+        // the wavefront's rows leave through LDS (its A rows were all read above)
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = 0; q < NP / 4; q++)
+            if (q * 4 < N) *reinterpret_cast<v4f*>(st + lane * PC + 4 * q) = v4f{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+        __builtin_amdgcn_wave_barrier();
+        float* dst = g.c + r0 * N;
 #pragma unroll
         for (int q = 0; q < NP / 4; q++) {
-            if (q * 4 >= N) continue;
-            v4f x = v4f{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-            if (g.accumulate) x = *reinterpret_cast<const v4f*>(c + 4 * q) + x;
-            *reinterpret_cast<v4f*>(c + 4 * q) = x;
+            const int x = lane + 64 * q;
+            if (x >= 16 * N) continue;
+            v4f v = *reinterpret_cast<const v4f*>(st + (4 * x / N) * PC + (4 * x) % N);
+            if (g.accumulate) v = *reinterpret_cast<const v4f*>(dst + 4 * x) + v;
+            *reinterpret_cast<v4f*>(dst + 4 * x) = v;
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < NP; j++)
-            if (j < N) c[j] = (g.accumulate ? c[j] : 0.f) + o[j];
+        return;
     }
+    float* c = g.c + r * N;
+#pragma unroll
+    for (int j = 0; j < NP; j++)
+        if (j < N) c[j] = (g.accumulate ? c[j] : 0.f) + o[j];
 }
 
 // Few outputs (m, n <= 16) of a transposed-a product c = a^T b over a long k (a stored
 // [K][M], b [K][N]) on the matrix cores: one 16 x 16 tile, each MFMA taking four rows of k
 // (lane l holds a[r + l/16][l%16] and b[r + l/16][l%16]: a wave-wide load of four
-// consecutive rows each).  Workgroup z covers its fixed k range; wavefront w takes rows
-// kb + 16 (4 i + w) .. + 15 in four independent accumulation chains (chain u: rows
-// +4u .. +4u+3), added in chain order, and the four wavefronts in wavefront order into
+// consecutive rows each).  Workgroup z covers its fixed k range; wavefront w takes the
+// 64-row blocks kb + 64 (4 i + w), block row 4u + kq going to accumulation chain u % 4; the
+// four chains are added in chain order, and the four wavefronts in wavefront order into
 // part[z][M][N].
 __global__ __launch_bounds__(256) void gemm_outer(GemmArgs g, float* __restrict__ part) {
     __shared__ float sm[4][256];
@@ -612,17 +642,18 @@ __global__ __launch_bounds__(256) void gemm_outer(GemmArgs g, float* __restrict_
     v4f acc[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int64_t r0 = kb + 16 * wave; r0 < ke; r0 += 64) {
-        float av[4], bv[4];
+    for (int64_t r0 = kb + 64 * wave; r0 < ke; r0 += 256) {
+        float av[16], bv[16];  // 64 rows in flight per wavefront
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
+        for (int u = 0; u < 16; u++) {
             const int64_t r = r0 + 4 * u + kq;
             const bool ok = r < ke;
             av[u] = ok && col < M ? g.a[r * M + col] : 0.f;
             bv[u] = ok && col < N ? g.b[r * N + col] : 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc[u], 0, 0, 0);
+        for (int u = 0; u < 16; u++)
+            acc[u & 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], bv[u], acc[u & 3], 0, 0, 0);
     }
     const v4f t = ((acc[0] + acc[1]) + acc[2]) + acc[3];
     // acc element e of lane l is c[4 (l / 16) + e][l % 16]
