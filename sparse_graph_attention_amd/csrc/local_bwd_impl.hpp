@@ -580,7 +580,14 @@ static __global__ __launch_bounds__(kBwdThreads) void bwd_merge(BwdCsr c, int wi
         for (int x = lane; x < width + width_b; x += 64) {
             const int col = x < width ? x : off_b + (x - width);
             float a = 0.f;
-            for (int i = 0; i < hv.z; i++) a += c.part[(size_t)(hv.y + i) * c.part_stride + col];
+            for (int i0 = 0; i0 < hv.z; i0 += 8) {  // eight slots' loads in flight, added in slot order
+                float t[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) t[j] = i0 + j < hv.z ? c.part[(size_t)(hv.y + i0 + j) * c.part_stride + col] : 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; j++)
+                    if (i0 + j < hv.z) a += t[j];
+            }
             if (x < width)
                 out_a[(size_t)hv.x * width + x] = a;
             else

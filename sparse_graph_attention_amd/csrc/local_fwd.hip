@@ -335,29 +335,68 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
     r.write_final(p, v);
 }
 
-// Folds the partial states of each heavy row in slot order.
+// Folds the partial states of each heavy row in slot order.  A lane holds kMergeCols
+// columns (lane + 64 c) of the row at once, and the loads of kMergeBatch slots are issued
+// before their folds, so a row of S slots takes about S / kMergeBatch memory round trips
+// per 64 * kMergeCols columns.
+constexpr int kMergeBatch = 8, kMergeCols = 4;
+
 __global__ __launch_bounds__(kFwdThreads) void local_fwd_merge(FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int nh = p.hdr->n_heavy;
     for (int hr = blockIdx.x * kFwdWaves + (threadIdx.x >> 6); hr < nh; hr += gridDim.x * kFwdWaves) {
         const int4 hv = p.heavy[hr];
-        for (int x = lane; x < p.W; x += 64) {
-            const int h = x / p.C;
-            float m = kNegInf, l = 0.f, a = 0.f;
-            for (int i = 0; i < hv.z; i++) {
-                const float* sp = p.part + (size_t)(hv.y + i) * p.part_stride;
-                const float mi = sp[p.W + h], li = sp[p.W + p.H + h], ai = sp[x];
-                const float mn = fmaxf(m, mi);
-                if (mn > kNegInf) {
-                    const float ca = fexp2(m - mn), cb = fexp2(mi - mn);
-                    l = l * ca + li * cb;
-                    a = a * ca + ai * cb;
-                    m = mn;
+        for (int x0 = 0; x0 < p.W; x0 += 64 * kMergeCols) {
+            int h[kMergeCols];
+            bool in[kMergeCols];
+            float m[kMergeCols], l[kMergeCols], a[kMergeCols];
+#pragma unroll
+            for (int c = 0; c < kMergeCols; c++) {
+                const int x = x0 + lane + 64 * c;
+                in[c] = x < p.W;
+                h[c] = in[c] ? x / p.C : 0;
+                m[c] = kNegInf;
+                l[c] = a[c] = 0.f;
+            }
+            for (int i0 = 0; i0 < hv.z; i0 += kMergeBatch) {
+                float mi[kMergeBatch][kMergeCols], li[kMergeBatch][kMergeCols], ai[kMergeBatch][kMergeCols];
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; j++) {
+                    const float* sp = p.part + (size_t)(hv.y + i0 + j) * p.part_stride;
+#pragma unroll
+                    for (int c = 0; c < kMergeCols; c++) {
+                        mi[j][c] = kNegInf;
+                        li[j][c] = ai[j][c] = 0.f;
+                        if (i0 + j < hv.z && in[c]) {
+                            mi[j][c] = sp[p.W + h[c]];
+                            li[j][c] = sp[p.W + p.H + h[c]];
+                            ai[j][c] = sp[x0 + lane + 64 * c];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; j++) {
+                    if (i0 + j >= hv.z) break;
+#pragma unroll
+                    for (int c = 0; c < kMergeCols; c++) {
+                        const float mn = fmaxf(m[c], mi[j][c]);
+                        if (mn > kNegInf) {
+                            const float ca = fexp2(m[c] - mn), cb = fexp2(mi[j][c] - mn);
+                            l[c] = l[c] * ca + li[j][c] * cb;
+                            a[c] = a[c] * ca + ai[j][c] * cb;
+                            m[c] = mn;
+                        }
+                    }
                 }
             }
-            p.out[(size_t)hv.x * p.W + x] = l > 0.f ? a * (1.0f / l) : 0.f;
-            if (p.lse && x - h * p.C == 0)
-                p.lse[(size_t)hv.x * p.H + h] = l > 0.f ? (m + __log2f(l)) * kLn2 : kNegInf;
+#pragma unroll
+            for (int c = 0; c < kMergeCols; c++) {
+                if (!in[c]) continue;
+                const int x = x0 + lane + 64 * c;
+                p.out[(size_t)hv.x * p.W + x] = l[c] > 0.f ? a[c] * (1.0f / l[c]) : 0.f;
+                if (p.lse && x - h[c] * p.C == 0)
+                    p.lse[(size_t)hv.x * p.H + h[c]] = l[c] > 0.f ? (m[c] + __log2f(l[c])) * kLn2 : kNegInf;
+            }
         }
     }
 }
