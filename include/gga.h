@@ -115,6 +115,16 @@ typedef struct gga_local_desc {
 } gga_local_desc;
 
 /*
+ * Shapes the local kernels handle (others give GGA_EUNSUPPORTED before any
+ * launch).  A head's C values are read E at a time, E = 8 for bf16 with C a
+ * multiple of 8, 4 for fp32 with C a multiple of 4, else 1; a head takes
+ * P = next power of two >= C / E lanes, and P <= 64.  With E > 1 the H heads
+ * take at most two wavefront slots (H * P <= 128: bf16 up to C = 512 for one
+ * head or H * C <= 1024; fp32 up to C = 256 or H * C <= 512); with E = 1 they
+ * take one (H * P <= 64).
+ */
+
+/*
  * Local attention forward ("Gated Local-Global Graph Attention", Key formulas,
  * local branch L_i; Tinymesh "Sparse attention experiment", sections
  * "Composition", "Multiple heads are composition" and "Target softmax").

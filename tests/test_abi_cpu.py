@@ -83,6 +83,28 @@ def test_fwd_rejects_bad_desc(bad, status):
     assert rc == status
 
 
+@pytest.mark.parametrize("heads,c,dtype,ok", [
+    (1, 512, 1, True), (1, 1024, 1, False),   # bf16: at most 64 lanes of 8 per head
+    (1, 256, 0, True), (1, 512, 0, False),    # fp32: 64 lanes of 4
+    (16, 64, 1, True), (24, 64, 1, False),    # at most two 64-lane slots
+    (8, 64, 0, True), (12, 64, 0, False),
+    (64, 1, 0, True), (65, 1, 0, False),      # scalar elements: one slot
+    (1, 64, 0, True), (1, 65, 0, False),      # scalar path: 65 lanes for one head
+])
+def test_shape_limits(heads, c, dtype, ok):
+    """The lane layouts cover heads x head_dim up to the limits the header states; one
+    step past each is rejected as unsupported before any launch."""
+    import sparse_graph_attention_amd as g
+
+    d = _desc(heads=heads, head_dim=c, dtype=dtype)
+    assert (g.lib.gga_local_attn_fwd_workspace(ctypes.byref(d)) > 0) == ok
+    assert (g.lib.gga_local_attn_bwd_workspace(ctypes.byref(d)) > 0) == ok
+    if not ok:
+        fake = ctypes.c_void_p(256)
+        assert g.lib.gga_local_attn_fwd(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None, None, 0,
+                                        None) == 3
+
+
 def test_desc_rejects_negative_source_rows():
     import sparse_graph_attention_amd as g
 

@@ -67,6 +67,9 @@ SHAPES = [
     (1, 16, "f32", 0), (8, 64, "bf16", 0), (8, 32, "bf16", 0), (4, 64, "f32", 0), (8, 8, "f32", 1),
     (1, 1, "f32", 1), (2, 3, "f32", 0), (3, 5, "bf16", 0), (16, 64, "bf16", 0), (12, 32, "f32", 0),
     (8, 16, "bf16", 1), (2, 6, "f32", 1),
+    # the widest layouts: 32 and 64 lanes per head, two full fp32 slots, additive with two slots
+    (2, 256, "bf16", 0), (1, 256, "f32", 0), (1, 512, "bf16", 0), (8, 64, "f32", 0), (16, 32, "f32", 1),
+    (64, 1, "f32", 0),
 ]
 
 

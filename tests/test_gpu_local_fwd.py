@@ -68,6 +68,10 @@ SHAPES = [
     (2, 256, "bf16", 0), # 32 lanes per head
     (1, 256, "f32", 0),  # 64 lanes per head
     (8, 16, "bf16", 1),  # additive with bf16 values
+    (1, 512, "bf16", 0), # widest head: 64 lanes of 8 bf16
+    (8, 64, "f32", 0),   # two full slots of fp32
+    (16, 32, "f32", 1),  # additive, two slots
+    (64, 1, "f32", 0),   # 64 one-element heads
 ]
 
 
