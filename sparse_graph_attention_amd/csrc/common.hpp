@@ -22,6 +22,16 @@ __device__ __forceinline__ uint32_t xcd_order(uint32_t lin, uint32_t total) {
     return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + j;
 }
 
+// Orders a wavefront's LDS writes before later LDS reads of the same locations by other
+// lanes of that wavefront.  The hardware completes one wavefront's LDS operations in
+// order, so nothing waits; the wavefront-scope fences keep the compiler from moving
+// memory operations across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------- host helpers
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? GGA_OK : GGA_EHIP; }

@@ -652,11 +652,13 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
 // wavefronts take the piece's 16-row tiles in turn:
 //   dphi(K)^T = dS V^T: A = dS^T rows, B = the lane's own v;
 //   dV^T = dS^T phi(K)^T: A = dS rows, B = the lane's own phi(k).
+// The next tile's k, v and the current tile's dk, dv (which it adds to) are loaded before
+// the current tile's products; registers are held to two wavefronts per SIMD so that one
+// wavefront's loads overlap the other's products.
 template <int TR>
-__global__ __launch_bounds__(256) void dkv_mfma(Seg sg, int32_t H, const float* __restrict__ k,
-                                                const float* __restrict__ v, const float* __restrict__ ds,
-                                                const float* __restrict__ dz, float* __restrict__ dk,
-                                                float* __restrict__ dv) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dkv_mfma(
+    Seg sg, int32_t H, const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ ds,
+    const float* __restrict__ dz, float* __restrict__ dk, float* __restrict__ dv) {
     constexpr int R = TR * 16, KQ = R / 4;
     __shared__ float sl[R * R], st[R * R];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -671,25 +673,45 @@ __global__ __launch_bounds__(256) void dkv_mfma(Seg sg, int32_t H, const float* 
 #pragma unroll
         for (int t = 0; t < KQ; t++) zreg[t] = dz[bh * R + gq * KQ + t];
         __syncthreads();
-        for (int64_t row0 = r0 + wave * 16; row0 < r1; row0 += 64) {
+        // the next tile's k and v, loaded during the current tile's products
+        v4f kx[KQ / 4], vx[KQ / 4];
+        auto fetch = [&](int64_t row0) {
+            const int64_t row = row0 + li;
+            const int64_t off = row * W + h * R + gq * KQ;
+#pragma unroll
+            for (int c = 0; c < KQ / 4; c++) {
+                kx[c] = vx[c] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (row < r1) {
+                    kx[c] = *reinterpret_cast<const v4f*>(k + off + 4 * c);
+                    vx[c] = *reinterpret_cast<const v4f*>(v + off + 4 * c);
+                }
+            }
+        };
+        int64_t row0 = r0 + wave * 16;
+        if (row0 < r1) fetch(row0);
+        for (; row0 < r1; row0 += 64) {
             const int64_t row = row0 + li;
             const bool valid = row < r1;
             const int64_t off = row * W + h * R + gq * KQ;
-            float kr[KQ], pk[KQ], vv[KQ];
-            if (valid) {
+            float pk[KQ], vv[KQ];
+            uint32_t pos = 0;              // bit t: k feature t > 0, where dphi = 1
+            v4f odk[KQ / 4], odv[KQ / 4];  // the dk, dv this tile adds to, also in flight during the products
 #pragma unroll
-                for (int c = 0; c < KQ / 4; c++) {
-                    const float4 k4 = *reinterpret_cast<const float4*>(k + off + 4 * c);
-                    const float4 v4 = *reinterpret_cast<const float4*>(v + off + 4 * c);
-                    kr[4 * c + 0] = k4.x; kr[4 * c + 1] = k4.y; kr[4 * c + 2] = k4.z; kr[4 * c + 3] = k4.w;
-                    vv[4 * c + 0] = v4.x; vv[4 * c + 1] = v4.y; vv[4 * c + 2] = v4.z; vv[4 * c + 3] = v4.w;
+            for (int c = 0; c < KQ / 4; c++) {
+                odk[c] = odv[c] = v4f{0.f, 0.f, 0.f, 0.f};
+                if (valid) {
+                    odk[c] = *reinterpret_cast<const v4f*>(dk + off + 4 * c);
+                    odv[c] = *reinterpret_cast<const v4f*>(dv + off + 4 * c);
                 }
 #pragma unroll
-                for (int t = 0; t < KQ; t++) pk[t] = phi(kr[t]);
-            } else {
-#pragma unroll
-                for (int t = 0; t < KQ; t++) kr[t] = pk[t] = vv[t] = 0.f;
+                for (int e = 0; e < 4; e++) {
+                    const float x = kx[c][e];
+                    pk[4 * c + e] = valid ? phi(x) : 0.f;
+                    pos |= (x > 0.f ? 1u : 0u) << (4 * c + e);
+                    vv[4 * c + e] = vx[c][e];
+                }
             }
+            if (row0 + 64 < r1) fetch(row0 + 64);
             v4f ak[TR], av[TR];
 #pragma unroll
             for (int j = 0; j < TR; j++) ak[j] = av[j] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -703,25 +725,22 @@ __global__ __launch_bounds__(256) void dkv_mfma(Seg sg, int32_t H, const float* 
                     ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], vv[t], ak[j], 0, 0, 0);
                     av[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sb[j], pk[t], av[j], 0, 0, 0);
                 }
+                if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // at most four steps' dS loads live
             }
             // ak[ct][q4] = (dS v)[row li][gq*KQ + q4*TR + ct]; av likewise for dS^T phi(k)
             if (valid) {
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
-                    float4* pk4 = reinterpret_cast<float4*>(dk + off + 4 * c);
-                    float4* pv4 = reinterpret_cast<float4*>(dv + off + 4 * c);
-                    float4 ok = *pk4, ov = *pv4;
-                    float uk[4], uv[4];
+                    v4f ok, ov;
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int idx = 4 * c + e;
-                        uk[e] = (ak[idx % TR][idx / TR] + zreg[idx]) * dphi(kr[idx], pk[idx]);
-                        uv[e] = av[idx % TR][idx / TR];
+                        const float dp = (pos >> idx) & 1u ? 1.f : pk[idx];  // dphi
+                        ok[e] = odk[c][e] + (ak[idx % TR][idx / TR] + zreg[idx]) * dp;
+                        ov[e] = odv[c][e] + av[idx % TR][idx / TR];
                     }
-                    ok.x += uk[0]; ok.y += uk[1]; ok.z += uk[2]; ok.w += uk[3];
-                    ov.x += uv[0]; ov.y += uv[1]; ov.z += uv[2]; ov.w += uv[3];
-                    *pk4 = ok;
-                    *pv4 = ov;
+                    *reinterpret_cast<v4f*>(dk + off + 4 * c) = ok;
+                    *reinterpret_cast<v4f*>(dv + off + 4 * c) = ov;
                 }
             }
         }

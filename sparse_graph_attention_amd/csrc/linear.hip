@@ -579,7 +579,7 @@ __global__ __launch_bounds__(256) void gemm_rows(GemmArgs g) {
             const int x = lane + 64 * q;
             if (x < 16 * K) *reinterpret_cast<v4f*>(st + (4 * x / K) * PA + (4 * x) % K) = v[q];
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
 #pragma unroll
         for (int q = 0; q < KP / 4; q++) {
             const v4f x = q * 4 < K ? *reinterpret_cast<const v4f*>(st + lane * PA + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
@@ -603,11 +603,11 @@ __global__ __launch_bounds__(256) void gemm_rows(GemmArgs g) {
     }
     if (tile) {
         // the wavefront's rows leave through LDS (its A rows were all read above)
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
 #pragma unroll
         for (int q = 0; q < NP / 4; q++)
             if (q * 4 < N) *reinterpret_cast<v4f*>(st + lane * PC + 4 * q) = v4f{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
         float* dst = g.c + r0 * N;
 #pragma unroll
         for (int q = 0; q < NP / 4; q++) {
