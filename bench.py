@@ -576,7 +576,7 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures a single GPU; runs on more than one GPU are not part of this build",
+        print("bench.py measures a single GPU; --gpus above 1 is not supported",
               file=sys.stderr)
         return 2
 

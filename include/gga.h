@@ -30,8 +30,7 @@
  *   index ranges are not checked by the compute calls (they would need a device
  *   read): run gga_validate_coo on untrusted input first.  A HIP launch error is
  *   returned as GGA_EHIP.  n == 0 or E == 0 are valid and return GGA_OK.
- * Threads.  Calls are re-entrant; there is no mutable global state beyond a
- *   per-device cache of device properties.
+ * Threads.  Calls are re-entrant; the library keeps no mutable global state.
  */
 #ifndef GGA_H
 #define GGA_H
@@ -49,7 +48,7 @@ extern "C" {
 #define GGA_OK 0
 #define GGA_EINVAL 1       /* null pointer with a nonzero size, negative size, misalignment */
 #define GGA_ERANGE 2       /* a size beyond what int32 indexing supports */
-#define GGA_EUNSUPPORTED 3 /* dtype, score mode or shape this build does not handle */
+#define GGA_EUNSUPPORTED 3 /* dtype, score mode or shape the library does not handle */
 #define GGA_EWORKSPACE 4   /* workspace or plan buffer smaller than its query says */
 #define GGA_EHIP 5         /* a HIP runtime call or kernel launch failed */
 

@@ -21,7 +21,7 @@ inline int ilog2(int x) {
     return r;
 }
 
-// Picks the lane layout; returns false for shapes this build does not handle.
+// Picks the lane layout; returns false for shapes the kernels do not handle.
 // Vector path: 16-byte element vectors when C is a multiple of 8 (bf16) or 4 (fp32);
 // otherwise one element per lane.  At most two slots per lane on the vector path.
 inline bool pick_shape(int H, int C, int dtype, Shape* sh) {

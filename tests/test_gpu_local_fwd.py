@@ -3,7 +3,7 @@
 Small cases span every lane layout (16-byte and scalar element paths, one and two
 slots per lane, 1..64 lanes per head), both score modes, and every degree bucket
 (light rows, workgroup rows, rows split into merged chunks, isolated rows), with the
-the benchmark spec tolerances (fp32: 1e-5 abs + 1e-4 rel; bf16 inputs: 2e-2 rel).  The full
+stated tolerances (fp32: 1e-5 abs + 1e-4 rel; bf16 inputs: 2e-2 rel).  The full
 workloads run in the launch configuration the benchmark times and are compared on
 sampled rows (random rows, the longest rows, empty rows)."""
 
