@@ -39,6 +39,7 @@ struct FwdParams {
     float score_mul;
     float slope;
     int32_t chunk_blocks;
+    int32_t own_rows;    // light rows: each edge group of a wavefront takes a row of its own
     const float* se;     // kScoreAddEdge: edge term of the logit, COO order [E, H]
     const int32_t* eid;  // kScoreAddEdge: COO index of each CSR position
 };
@@ -102,31 +103,39 @@ struct FwdRow {
         }
     }
 
-    // Edges at positions beg + start + k*stride + (g + G*j), j < U, for k = 0, 1, ...
-    __device__ __forceinline__ void run(const FwdParams& p, int32_t beg, int32_t end, int32_t start,
-                                        int32_t stride) {
+    // Shared row (OWN false): the groups take the edges at positions
+    // beg + start + k*stride + (g + G*j), j < U, for k = 0, 1, ... while inside [beg, end).
+    // Own rows (OWN true): group g alone takes the edges of its own row [beg, end) (beg and
+    // end differ by group), beg + k*U + j, for k < iters (the same for the wavefront).
+    template <bool OWN>
+    __device__ __forceinline__ void run_t(const FwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                          int32_t stride, int32_t iters) {
         const T* __restrict__ kp = static_cast<const T*>(p.ks);
         const T* __restrict__ vp = static_cast<const T*>(p.v);
         const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
+        // lane `ll` loads the id of the iteration's edge `ll` (of the wavefront, or of its group)
+        const int ll = OWN ? (lane & (lpr - 1)) : lane;
+        const int lim = OWN ? U : EIT;
+        const int g0 = OWN ? g * lpr : 0;
         int32_t base = beg + start;
-        int32_t colv = (lane < EIT && base + lane < end) ? p.col[base + lane] : 0;
+        int32_t colv = (ll < lim && base + ll < end) ? p.col[base + ll] : 0;
         int32_t eidv = 0;  // edge terms: the COO index of each position, loaded like col
-        if constexpr (MODE == kScoreAddEdge) eidv = (lane < EIT && base + lane < end) ? p.eid[base + lane] : 0;
-        for (; base < end; base += stride) {
+        if constexpr (MODE == kScoreAddEdge) eidv = (ll < lim && base + ll < end) ? p.eid[base + ll] : 0;
+        for (int32_t k = 0; OWN ? k < iters : base < end; k++, base += stride) {
             // the next iteration's sources, in flight while this iteration's rows are gathered
             const int32_t nxt = base + stride;
-            const int32_t coln = (lane < EIT && nxt + lane < end) ? p.col[nxt + lane] : 0;
+            const int32_t coln = (ll < lim && nxt + ll < end) ? p.col[nxt + ll] : 0;
             int32_t eidn = 0;
-            if constexpr (MODE == kScoreAddEdge) eidn = (lane < EIT && nxt + lane < end) ? p.eid[nxt + lane] : 0;
+            if constexpr (MODE == kScoreAddEdge) eidn = (ll < lim && nxt + ll < end) ? p.eid[nxt + ll] : 0;
             int32_t u[kUMax], ej[kUMax];
             bool ev[kUMax];
 #pragma unroll
             for (int j = 0; j < kUMax; j++) {
                 if (j < U) {
-                    const int idx = g + G * j;
+                    const int idx = OWN ? g0 + j : g + G * j;
                     u[j] = __shfl(colv, idx, 64);
                     ej[j] = MODE == kScoreAddEdge ? __shfl(eidv, idx, 64) : 0;
-                    ev[j] = base + idx < end;
+                    ev[j] = base + (OWN ? j : idx) < end;
                 } else {
                     u[j] = 0;
                     ej[j] = 0;
@@ -211,6 +220,11 @@ struct FwdRow {
         }
     }
 
+    __device__ __forceinline__ void run(const FwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                        int32_t stride) {
+        run_t<false>(p, beg, end, start, stride, 0);
+    }
+
     __device__ __forceinline__ void fold(float mo, float lo, const float* ao, int s) {
         const float mn = fmaxf(m[s], mo);
         if (mn > kNegInf) {
@@ -261,6 +275,24 @@ struct FwdRow {
             if (lead[s] && p.lse)
                 p.lse[(size_t)v * p.H + head[s]] = l[s] > 0.f ? (m[s] + __log2f(l[s])) * kLn2 : kNegInf;
         }
+    }
+
+    // Own rows: every group writes its own row v (one slot); `valid` false for a group
+    // without a row.  All 64 lanes must call it (the exact layout exchanges values
+    // within each group so that a store covers consecutive 16-byte chunks of a row).
+    __device__ __forceinline__ void write_own(const FwdParams& p, int32_t v, bool valid) {
+        const float inv = l[0] > 0.f ? 1.0f / l[0] : 0.f;
+        float o[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; i++) o[i] = acc[0][i] * inv;
+        float* row = p.out + (size_t)v * p.W;
+        if (geo.exact) {
+            store_group_row_nt<EPL>(row, o, lpr, lane, valid);
+        } else if (valid && ok[0]) {
+            store_f32<EPL>(row + off[0], o);
+        }
+        if (valid && lead[0] && ok[0] && p.lse)
+            p.lse[(size_t)v * p.H + head[0]] = l[0] > 0.f ? (m[0] + __log2f(l[0])) * kLn2 : kNegInf;
     }
 
     __device__ __forceinline__ void write_partial(const FwdParams& p, int32_t slot) {
@@ -324,8 +356,24 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
         }
         return;
     }
+    const int nl = p.hdr->n_light;
+    if (p.own_rows) {
+        // each of the G groups takes a light row of its own
+        const int li0 = ((blockIdx.x - p.chunk_blocks) * kFwdWaves + wave) * r.G;
+        if (li0 >= nl) return;
+        const int li = li0 + r.g;
+        const bool valid = li < nl;
+        const int4 lr = valid ? p.light[li] : make_int4(0, 0, 0, 0);
+        int32_t iters = (lr.z - lr.y + r.U - 1) / r.U;
+        for (int o = r.lpr; o < 64; o <<= 1) iters = max(iters, __shfl_xor(iters, o, 64));
+        r.reset();
+        r.load_target(p, lr.x);
+        r.template run_t<true>(p, lr.y, lr.z, 0, r.U, iters);
+        r.write_own(p, lr.x, valid);
+        return;
+    }
     const int li = (blockIdx.x - p.chunk_blocks) * kFwdWaves + wave;
-    if (li >= p.hdr->n_light) return;
+    if (li >= nl) return;
     const int4 lr = p.light[li];
     const int32_t v = lr.x;
     r.reset();
@@ -505,7 +553,10 @@ int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
     p.slope = d->negative_slope;
     const int64_t cb = b.max_chunks < 2048 ? b.max_chunks : 2048;
     p.chunk_blocks = d->e > kLightEdges ? (int32_t)cb : 0;
-    const int64_t light_blocks = ((int64_t)d->n + kFwdWaves - 1) / kFwdWaves;
+    // rows narrower than a wavefront: its edge groups take light rows of their own
+    p.own_rows = sh.ns == 1 && sh.lpr_log2 < 6;
+    const int64_t rows_per_block = (int64_t)kFwdWaves << (p.own_rows ? 6 - sh.lpr_log2 : 0);
+    const int64_t light_blocks = ((int64_t)d->n + rows_per_block - 1) / rows_per_block;
     const int64_t grid = p.chunk_blocks + light_blocks;
     if (grid >= ((int64_t)1 << 31)) return GGA_ERANGE;
     const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;

@@ -110,6 +110,38 @@ __device__ __forceinline__ void store_row_nt(float* row, const float* vals, int 
     }
 }
 
+// Stores, for every group of lpr lanes, the output row that group holds (lane l of the
+// group holds elements [l*EPL, (l+1)*EPL) of a row of lpr*EPL floats at `row`, which
+// differs by group) with non-temporal stores covering consecutive 16-byte chunks; with 8
+// floats per lane the chunks are exchanged within the group first.  All 64 lanes must
+// call it; a group with `valid` false stores nothing.
+template <int EPL>
+__device__ __forceinline__ void store_group_row_nt(float* row, const float* vals, int lpr, int lane, bool valid) {
+    const int gl = lane & (lpr - 1), g0 = lane - gl;
+    if constexpr (EPL == 8) {
+#pragma unroll
+        for (int k = 0; k < 2; k++) {
+            const int c = k * lpr + gl;
+            const int srcl = g0 + (c >> 1);
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                a[i] = __shfl(vals[i], srcl, 64);
+                b[i] = __shfl(vals[4 + i], srcl, 64);
+            }
+            const f32x4 val = (c & 1) ? f32x4{b[0], b[1], b[2], b[3]} : f32x4{a[0], a[1], a[2], a[3]};
+            if (valid) __builtin_nontemporal_store(val, reinterpret_cast<f32x4*>(row) + c);
+        }
+    } else if constexpr (EPL == 4) {
+        if (valid)
+            __builtin_nontemporal_store(f32x4{vals[0], vals[1], vals[2], vals[3]}, reinterpret_cast<f32x4*>(row) + gl);
+    } else {
+        if (valid)
+#pragma unroll
+            for (int i = 0; i < EPL; i++) __builtin_nontemporal_store(vals[i], row + gl * EPL + i);
+    }
+}
+
 // Sum of a value over the G edge groups of a wavefront (butterfly from LPR up to 32).
 __device__ __forceinline__ float sum_groups(float x, int lpr) {
     for (int o = lpr; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
