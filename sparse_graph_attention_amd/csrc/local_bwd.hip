@@ -116,8 +116,11 @@ int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
         p.eid_b = et->eid_b;
         mode = kScoreAddEdge;
     }
-    const int64_t light_a = ((int64_t)d->n + kBwdWaves - 1) / kBwdWaves;
-    const int64_t light_b = ((int64_t)ns + kBwdWaves - 1) / kBwdWaves;
+    // rows narrower than a wavefront: its edge groups take light rows of their own
+    p.own_rows = sh.ns == 1 && sh.lpr_log2 < 6;
+    const int64_t rows_per_block = (int64_t)kBwdWaves << (p.own_rows ? 6 - sh.lpr_log2 : 0);
+    const int64_t light_a = ((int64_t)d->n + rows_per_block - 1) / rows_per_block;
+    const int64_t light_b = ((int64_t)ns + rows_per_block - 1) / rows_per_block;
     const int64_t ga = p.a.chunk_blocks + light_a, gb = p.b.chunk_blocks + light_b;
     if (ga >= ((int64_t)1 << 31) || gb >= ((int64_t)1 << 31)) return GGA_ERANGE;
     const int64_t mh = d->e > kChunkEdges ? b.max_heavy : 0;

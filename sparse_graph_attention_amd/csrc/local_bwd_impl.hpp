@@ -47,6 +47,7 @@ struct BwdParams {
     BwdCsr a;  // by destination
     BwdCsr b;  // by source
     int32_t n, H, C, W, lpr_log2;
+    int32_t own_rows;  // light rows: each edge group of a wavefront takes a row of its own
     float scale;      // dot: score scale
     float score_mul;  // multiplier taking a raw score to log2 units
     float slope;
@@ -119,32 +120,36 @@ struct PassA {
         }
     }
 
-    __device__ __forceinline__ void run(const BwdParams& p, int32_t beg, int32_t end, int32_t start,
-                                        int32_t stride) {
+    // Shared row (OWN false): the groups take the edges beg + start + k*stride + (g + G*j).
+    // Own rows (OWN true): group g alone takes beg + k*U + j of its own row, k < iters.
+    template <bool OWN>
+    __device__ __forceinline__ void run_t(const BwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                          int32_t stride, int32_t iters) {
         const T* __restrict__ kp = static_cast<const T*>(p.ks);
         const T* __restrict__ vp = static_cast<const T*>(p.v);
         const float* __restrict__ ssrc = static_cast<const float*>(p.ks);
+        const int ll = OWN ? (geo.lane & (geo.lpr - 1)) : geo.lane;
+        const int lim = OWN ? U : EIT;
+        const int g0 = OWN ? geo.g * geo.lpr : 0;
         int32_t base = beg + start;
-        int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.a.col[base + geo.lane] : 0;
+        int32_t colv = (ll < lim && base + ll < end) ? p.a.col[base + ll] : 0;
         int32_t eidv = 0;  // edge terms: the COO index of each position, loaded like col
-        if constexpr (MODE == kScoreAddEdge)
-            eidv = (geo.lane < EIT && base + geo.lane < end) ? p.eid_a[base + geo.lane] : 0;
-        for (; base < end; base += stride) {
+        if constexpr (MODE == kScoreAddEdge) eidv = (ll < lim && base + ll < end) ? p.eid_a[base + ll] : 0;
+        for (int32_t k = 0; OWN ? k < iters : base < end; k++, base += stride) {
             // the next iteration's sources, in flight while this iteration's rows are gathered
             const int32_t nxt = base + stride;
-            const int32_t coln = (geo.lane < EIT && nxt + geo.lane < end) ? p.a.col[nxt + geo.lane] : 0;
+            const int32_t coln = (ll < lim && nxt + ll < end) ? p.a.col[nxt + ll] : 0;
             int32_t eidn = 0;
-            if constexpr (MODE == kScoreAddEdge)
-                eidn = (geo.lane < EIT && nxt + geo.lane < end) ? p.eid_a[nxt + geo.lane] : 0;
+            if constexpr (MODE == kScoreAddEdge) eidn = (ll < lim && nxt + ll < end) ? p.eid_a[nxt + ll] : 0;
             int32_t u[kUMax], ej[kUMax];
             bool ev[kUMax];
 #pragma unroll
             for (int j = 0; j < kUMax; j++) {
                 if (j < U) {
-                    const int idx = geo.g + geo.G * j;
+                    const int idx = OWN ? g0 + j : geo.g + geo.G * j;
                     u[j] = __shfl(colv, idx, 64);
                     ej[j] = MODE == kScoreAddEdge ? __shfl(eidv, idx, 64) : 0;
-                    ev[j] = base + idx < end;
+                    ev[j] = base + (OWN ? j : idx) < end;
                 } else {
                     u[j] = 0;
                     ej[j] = 0;
@@ -214,11 +219,31 @@ struct PassA {
         }
     }
 
+    __device__ __forceinline__ void run(const BwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                        int32_t stride) {
+        run_t<false>(p, beg, end, start, stride, 0);
+    }
+
     __device__ __forceinline__ void reduce_groups() {
 #pragma unroll
         for (int s = 0; s < NS; s++)
 #pragma unroll
             for (int i = 0; i < kAcc; i++) acc[s][i] = sum_groups(acc[s][i], geo.lpr);
+    }
+
+    // Own rows: every group writes its own row v (one slot); nothing for `valid` false.
+    // All 64 lanes must call it.
+    __device__ __forceinline__ void write_own(const BwdParams& p, int32_t v, bool valid) {
+        const size_t hi = (size_t)v * p.H + geo.head[0];
+        if constexpr (MODE == GGA_SCORE_DOT) {
+            if (geo.exact)
+                store_group_row_nt<EPL>(p.d_qs + (size_t)v * p.W, acc[0], geo.lpr, geo.lane, valid);
+            else if (valid && geo.ok[0])
+                store_f32<EPL>(p.d_qs + (size_t)v * p.W + geo.off[0], acc[0]);
+        } else {
+            if (valid && geo.ok[0] && geo.lead[0]) p.d_qs[hi] = acc[0][0];
+        }
+        if (valid && geo.ok[0] && geo.lead[0]) p.D[hi] = Dh[0];
     }
 
     __device__ __forceinline__ void write_final(const BwdParams& p, int32_t v) {
@@ -300,31 +325,34 @@ struct PassB {
         }
     }
 
-    __device__ __forceinline__ void run(const BwdParams& p, int32_t beg, int32_t end, int32_t start,
-                                        int32_t stride) {
+    // Shared row or own rows, as in pass A.
+    template <bool OWN>
+    __device__ __forceinline__ void run_t(const BwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                          int32_t stride, int32_t iters) {
         const T* __restrict__ qp = static_cast<const T*>(p.qs);
         const float* __restrict__ sdst = static_cast<const float*>(p.qs);
+        const int ll = OWN ? (geo.lane & (geo.lpr - 1)) : geo.lane;
+        const int lim = OWN ? U : EIT;
+        const int g0 = OWN ? geo.g * geo.lpr : 0;
         int32_t base = beg + start;
-        int32_t colv = (geo.lane < EIT && base + geo.lane < end) ? p.b.col[base + geo.lane] : 0;
+        int32_t colv = (ll < lim && base + ll < end) ? p.b.col[base + ll] : 0;
         int32_t eidv = 0;  // edge terms: the COO index of each position, loaded like col
-        if constexpr (MODE == kScoreAddEdge)
-            eidv = (geo.lane < EIT && base + geo.lane < end) ? p.eid_b[base + geo.lane] : 0;
-        for (; base < end; base += stride) {
+        if constexpr (MODE == kScoreAddEdge) eidv = (ll < lim && base + ll < end) ? p.eid_b[base + ll] : 0;
+        for (int32_t k = 0; OWN ? k < iters : base < end; k++, base += stride) {
             // the next iteration's sources, in flight while this iteration's rows are gathered
             const int32_t nxt = base + stride;
-            const int32_t coln = (geo.lane < EIT && nxt + geo.lane < end) ? p.b.col[nxt + geo.lane] : 0;
+            const int32_t coln = (ll < lim && nxt + ll < end) ? p.b.col[nxt + ll] : 0;
             int32_t eidn = 0;
-            if constexpr (MODE == kScoreAddEdge)
-                eidn = (geo.lane < EIT && nxt + geo.lane < end) ? p.eid_b[nxt + geo.lane] : 0;
+            if constexpr (MODE == kScoreAddEdge) eidn = (ll < lim && nxt + ll < end) ? p.eid_b[nxt + ll] : 0;
             int32_t t[kUMax], ej[kUMax];
             bool ev[kUMax];
 #pragma unroll
             for (int j = 0; j < kUMax; j++) {
                 if (j < U) {
-                    const int idx = geo.g + geo.G * j;
+                    const int idx = OWN ? g0 + j : geo.g + geo.G * j;
                     t[j] = __shfl(colv, idx, 64);
                     ej[j] = MODE == kScoreAddEdge ? __shfl(eidv, idx, 64) : 0;
-                    ev[j] = base + idx < end;
+                    ev[j] = base + (OWN ? j : idx) < end;
                 } else {
                     t[j] = 0;
                     ej[j] = 0;
@@ -405,6 +433,30 @@ struct PassB {
         }
     }
 
+    __device__ __forceinline__ void run(const BwdParams& p, int32_t beg, int32_t end, int32_t start,
+                                        int32_t stride) {
+        run_t<false>(p, beg, end, start, stride, 0);
+    }
+
+    // Own rows: every group writes its own row u (one slot); nothing for `valid` false.
+    // All 64 lanes must call it.
+    __device__ __forceinline__ void write_own(const BwdParams& p, int32_t u, bool valid) {
+        if (geo.exact) {
+            if constexpr (MODE == GGA_SCORE_DOT)
+                store_group_row_nt<EPL>(p.d_ks + (size_t)u * p.W, dk[0], geo.lpr, geo.lane, valid);
+            else if constexpr (MODE != GGA_SCORE_MEAN)
+                if (valid && geo.lead[0]) p.d_ks[(size_t)u * p.H + geo.head[0]] = dk[0][0];
+            store_group_row_nt<EPL>(p.d_v + (size_t)u * p.W, dv[0], geo.lpr, geo.lane, valid);
+            return;
+        }
+        if (!valid || !geo.ok[0]) return;
+        if constexpr (MODE == GGA_SCORE_DOT)
+            store_f32<EPL>(p.d_ks + (size_t)u * p.W + geo.off[0], dk[0]);
+        else if constexpr (MODE != GGA_SCORE_MEAN)
+            if (geo.lead[0]) p.d_ks[(size_t)u * p.H + geo.head[0]] = dk[0][0];
+        store_f32<EPL>(p.d_v + (size_t)u * p.W + geo.off[0], dv[0]);
+    }
+
     __device__ __forceinline__ void reduce_groups() {
 #pragma unroll
         for (int s = 0; s < NS; s++) {
@@ -454,6 +506,14 @@ struct PassB {
 };
 
 // ------------------------------------------------------------------------ kernels
+
+// Iterations of U edges that the longest of a wavefront's own rows needs (deg: this
+// group's row length; the result is the same in every lane).
+__device__ __forceinline__ int32_t own_iters(int32_t deg, int U, int lpr) {
+    int32_t it = (deg + U - 1) / U;
+    for (int o = lpr; o < 64; o <<= 1) it = max(it, __shfl_xor(it, o, 64));
+    return it;
+}
 
 // Adds the per-wave partial arrays of a workgroup through LDS in wave order.
 template <int N>
@@ -505,8 +565,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dst_kernel(BwdParams p) {
         }
         return;
     }
+    const int nl = p.a.hdr->n_light;
+    if (p.own_rows) {  // the wavefront owns G consecutive light rows
+        const int li0 = ((blockIdx.x - p.a.chunk_blocks) * kBwdWaves + wave) * r.geo.G;
+        if (li0 >= nl) return;
+        if ((int64_t)p.a.hdr->light_sum > (int64_t)nl * r.EIT) {  // long rows: one after another
+            const int lend = min(li0 + r.geo.G, nl);
+            for (int li = li0; li < lend; li++) {
+                const int4 lr = p.a.light[li];
+                r.load_target(p, lr.x);
+                r.run(p, lr.y, lr.z, 0, r.EIT);
+                r.reduce_groups();
+                r.write_final(p, lr.x);
+            }
+            return;
+        }
+        const int li = li0 + r.geo.g;  // short rows: each group takes one
+        const bool valid = li < nl;
+        const int4 lr = valid ? p.a.light[li] : make_int4(0, 0, 0, 0);
+        const int32_t iters = own_iters(lr.z - lr.y, r.U, r.geo.lpr);
+        r.load_target(p, lr.x);
+        r.template run_t<true>(p, lr.y, lr.z, 0, r.U, iters);
+        r.write_own(p, lr.x, valid);
+        return;
+    }
     const int li = (blockIdx.x - p.a.chunk_blocks) * kBwdWaves + wave;
-    if (li >= p.a.hdr->n_light) return;
+    if (li >= nl) return;
     const int4 lr = p.a.light[li];
     const int32_t v = lr.x;
     r.load_target(p, v);
@@ -557,8 +641,32 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_src_kernel(BwdParams p) {
         }
         return;
     }
+    const int nl = p.b.hdr->n_light;
+    if (p.own_rows) {  // the wavefront owns G consecutive light rows
+        const int li0 = ((blockIdx.x - p.b.chunk_blocks) * kBwdWaves + wave) * r.geo.G;
+        if (li0 >= nl) return;
+        if ((int64_t)p.b.hdr->light_sum > (int64_t)nl * r.EIT) {  // long rows: one after another
+            const int lend = min(li0 + r.geo.G, nl);
+            for (int li = li0; li < lend; li++) {
+                const int4 lr = p.b.light[li];
+                r.load_source(p, lr.x);
+                r.run(p, lr.y, lr.z, 0, r.EIT);
+                r.reduce_groups();
+                r.write_final(p, lr.x);
+            }
+            return;
+        }
+        const int li = li0 + r.geo.g;  // short rows: each group takes one
+        const bool valid = li < nl;
+        const int4 lr = valid ? p.b.light[li] : make_int4(0, 0, 0, 0);
+        const int32_t iters = own_iters(lr.z - lr.y, r.U, r.geo.lpr);
+        r.load_source(p, lr.x);
+        r.template run_t<true>(p, lr.y, lr.z, 0, r.U, iters);
+        r.write_own(p, lr.x, valid);
+        return;
+    }
     const int li = (blockIdx.x - p.b.chunk_blocks) * kBwdWaves + wave;
-    if (li >= p.b.hdr->n_light) return;
+    if (li >= nl) return;
     const int4 lr = p.b.light[li];
     const int32_t u = lr.x;
     r.load_source(p, u);

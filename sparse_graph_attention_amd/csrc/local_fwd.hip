@@ -358,9 +358,24 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
     }
     const int nl = p.hdr->n_light;
     if (p.own_rows) {
-        // each of the G groups takes a light row of its own
+        // the wavefront owns G consecutive light rows
         const int li0 = ((blockIdx.x - p.chunk_blocks) * kFwdWaves + wave) * r.G;
         if (li0 >= nl) return;
+        if ((int64_t)p.hdr->light_sum > (int64_t)nl * r.EIT) {
+            // light rows longer than one iteration on average: one after another, every
+            // group on each
+            const int lend = min(li0 + r.G, nl);
+            for (int li = li0; li < lend; li++) {
+                const int4 lr = p.light[li];
+                r.reset();
+                r.load_target(p, lr.x);
+                r.run(p, lr.y, lr.z, 0, r.EIT);
+                r.merge_groups();
+                r.write_final(p, lr.x);
+            }
+            return;
+        }
+        // short rows: each group takes one of them
         const int li = li0 + r.g;
         const bool valid = li < nl;
         const int4 lr = valid ? p.light[li] : make_int4(0, 0, 0, 0);

@@ -12,6 +12,7 @@ struct PlanWs {
     int32_t* b;  // chunk count -> first chunk
     int32_t* c;  // slot count -> first slot
     int32_t* d;  // heavy flag -> heavy position
+    int32_t* e;  // degree of a light row (0 otherwise), summed into the header
     int32_t* scan;
     size_t bytes;
 };
@@ -23,13 +24,14 @@ PlanWs carve_ws(void* ws, int32_t n) {
     w.b = c.take<int32_t>((size_t)n);
     w.c = c.take<int32_t>((size_t)n);
     w.d = c.take<int32_t>((size_t)n);
+    w.e = c.take<int32_t>((size_t)n);
     w.scan = c.take<int32_t>(scan_workspace_elems(n));
     w.bytes = c.bytes();
     return w;
 }
 
 __global__ void plan_classify(const int32_t* __restrict__ row_ptr, int32_t n, int32_t* a, int32_t* b, int32_t* c,
-                              int32_t* d) {
+                              int32_t* d, int32_t* e) {
     for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < n; v += (int64_t)gridDim.x * blockDim.x) {
         const int32_t deg = row_ptr[v + 1] - row_ptr[v];
         const bool light = deg <= kLightEdges;
@@ -38,6 +40,7 @@ __global__ void plan_classify(const int32_t* __restrict__ row_ptr, int32_t n, in
         b[v] = chunks;
         c[v] = chunks > 1 ? chunks : 0;
         d[v] = chunks > 1;
+        e[v] = light ? deg : 0;
     }
 }
 
@@ -108,11 +111,12 @@ extern "C" int gga_plan_build(int32_t n, int64_t e, const int32_t* row_ptr, void
     fill_i32(hdr_i, sizeof(PlanHeader) / 4, 0, s);
     plan_header<<<1, 1, 0, s>>>(pv.hdr, n);
     if (n == 0) return launch_status();
-    plan_classify<<<grid_for(n), 256, 0, s>>>(row_ptr, n, w.a, w.b, w.c, w.d);
+    plan_classify<<<grid_for(n), 256, 0, s>>>(row_ptr, n, w.a, w.b, w.c, w.d, w.e);
     exclusive_scan_i32(w.a, w.a, n, &pv.hdr->n_light, w.scan, s);
     exclusive_scan_i32(w.b, w.b, n, &pv.hdr->n_chunks, w.scan, s);
     exclusive_scan_i32(w.c, w.c, n, &pv.hdr->n_slots, w.scan, s);
     exclusive_scan_i32(w.d, w.d, n, &pv.hdr->n_heavy, w.scan, s);
+    exclusive_scan_i32(w.e, w.e, n, &pv.hdr->light_sum, w.scan, s);
     plan_fill<<<grid_for(n), 256, 0, s>>>(row_ptr, n, w.a, w.b, w.c, w.d, pv);
     return launch_status();
 }

@@ -21,6 +21,7 @@ struct PlanHeader {
     int32_t light_edges;
     int32_t chunk_edges;
     int32_t magic;
+    int32_t light_sum;  // edges of the light rows together (their mean length picks a lane layout)
 };
 
 constexpr int32_t kPlanMagic = 0x67676150;

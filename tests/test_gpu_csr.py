@@ -75,7 +75,7 @@ def test_plan_counts(g):
     n = 6000
     src, dst = synth.mixed_degree_graph(n, 2, hubs=(50000, 4097, 1025, 1024, 700, 65, 64))
     t = g.Topology(n, i32(src), i32(dst))
-    hdr = t.plan[:32].view(torch.int32).cpu().numpy()
+    hdr = t.plan[:36].view(torch.int32).cpu().numpy()
     deg = np.bincount(dst, minlength=n)
     light = (deg <= 64).sum()
     chunks = np.where(deg > 64, (deg + 1023) // 1024, 0)
@@ -83,3 +83,4 @@ def test_plan_counts(g):
     assert hdr[1] == chunks.sum()
     assert hdr[2] == (chunks > 1).sum()
     assert hdr[3] == chunks[chunks > 1].sum()
+    assert hdr[8] == deg[deg <= 64].sum()  # edges of the light rows
