@@ -49,7 +49,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix
 # HBM bytes per forward launch on the default workload counted by rocprofv3 (FETCH_SIZE x 2.00
 # + WRITE_SIZE x 1.00, factors from a plain 1 GiB copy), for the kernel as of the summary in
 # profiles/local_fwd_dot_n1m_h8_r64_bf16.md; None once the kernel changes.
-COUNTED_TRAFFIC_GB = 39.91
+COUNTED_TRAFFIC_GB = 39.86
 # The same for one backward call (pass A + pass B + merges) of the heavy-tailed workload,
 # profiles/local_fwd_bwd_dot_n2m_zipf_h8_c32_bf16.md.
 COUNTED_TRAFFIC_W5_BWD_GB = 157.61
