@@ -79,12 +79,13 @@ __global__ void coef_fwd(int64_t nh, int32_t heads, int32_t c, const float* __re
     }
 }
 
-// Fixed split of the row axis for the coefficient gradients: ranges of about 512 rows, at
-// least 1 and at most 4096 of them (a function of n, so the order of the sums is too).
+// Fixed split of the row axis for the coefficient gradients: ranges of about 64 rows (enough
+// workgroups to keep every CU's loads in flight), at least 1 and at most 16384 of them (a
+// function of n, so the order of the sums is too).
 inline int coef_blocks(int64_t n) {
-    int64_t b = (n + 511) / 512;
+    int64_t b = (n + 63) / 64;
     if (b < 1) b = 1;
-    if (b > 4096) b = 4096;
+    if (b > 16384) b = 16384;
     return (int)b;
 }
 

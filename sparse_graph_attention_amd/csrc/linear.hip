@@ -462,6 +462,104 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ 
     }
 }
 
+// ---- tall products with all of op(b) in LDS (k, n <= 128, multiples of 16, k*n <= 8192,
+// plain a): each workgroup stages op(b) once as [n][k] (rows padded by 4 floats, so the
+// 16-byte reads of 16 consecutive n rows hit distinct banks) and its eight wavefronts walk
+// two 16-row tiles of a each (measured best of 1-8 tiles and 4 or 8 wavefronts).  In 16-deep chunk h, lane (r = lane%16, g = lane/16) holds
+// a[row r][16h + 4g .. +3] (one 16-byte load) and b[16h + 4g .. +3][16j + r] (one LDS
+// read), MFMA step t taking k = 16h + 4g + t; lane l ends with c[4g + i][16j + r].  The next
+// tile's a rows are loaded during the current tile's MFMAs.
+constexpr int kStreamTiles = 2;  // 16-row tiles per wavefront
+constexpr int kStreamWaves = 8;  // wavefronts per workgroup (sharing one staged op(b))
+constexpr int kStreamThreads = 64 * kStreamWaves;
+
+template <int KC, int NT>
+__global__ __launch_bounds__(kStreamThreads) void gemm_stream(GemmArgs g) {
+    constexpr int K = KC * 16, N = NT * 16, PB = K + 4;
+    __shared__ float bt[N * PB];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, gq = lane >> 4;
+    {
+        // op(b) in its memory order, 16 bytes per load, every load issued before the stores
+        constexpr int NV = K * N / 4, PER = (NV + kStreamThreads - 1) / kStreamThreads;
+        v4f sv[PER];
+#pragma unroll
+        for (int q = 0; q < PER; q++) {
+            const int x = threadIdx.x + kStreamThreads * q;
+            if (x < NV) sv[q] = *reinterpret_cast<const v4f*>(g.b + 4 * x);
+        }
+#pragma unroll
+        for (int q = 0; q < PER; q++) {
+            const int x = threadIdx.x + kStreamThreads * q;
+            if (x >= NV) continue;
+            if (g.trans_b) {  // b [N][K]: four consecutive k of row j
+                const int j = 4 * x / K, kk = 4 * x % K;
+                *reinterpret_cast<v4f*>(bt + j * PB + kk) = sv[q];
+            } else {  // b [K][N]: four consecutive n of row kk
+                const int kk = 4 * x / N, j0 = 4 * x % N;
+#pragma unroll
+                for (int e = 0; e < 4; e++) bt[(j0 + e) * PB + kk] = sv[q][e];
+            }
+        }
+    }
+    __syncthreads();
+    const int64_t t0 = ((int64_t)blockIdx.x * kStreamWaves + wave) * kStreamTiles;
+    v4f an[KC];
+    // rows past the end re-read the last row (never stored), so no load is conditional
+    auto fetch = [&](int64_t tile) {
+        const int64_t row = min(tile * 16 + r, (int64_t)g.M - 1);
+#pragma unroll
+        for (int h = 0; h < KC; h++) an[h] = *reinterpret_cast<const v4f*>(g.a + row * K + 16 * h + 4 * gq);
+    };
+    fetch(t0);
+    for (int tt = 0; tt < kStreamTiles; tt++) {
+        const int64_t tile = t0 + tt;
+        if (tile * 16 >= g.M) break;
+        v4f a[KC];
+#pragma unroll
+        for (int h = 0; h < KC; h++) a[h] = an[h];
+        if (tt + 1 < kStreamTiles) fetch(tile + 1);
+        v4f acc[NT];
+#pragma unroll
+        for (int j = 0; j < NT; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < KC; h++) {
+            v4f b[NT];
+#pragma unroll
+            for (int j = 0; j < NT; j++) b[j] = *reinterpret_cast<const v4f*>(bt + (16 * j + r) * PB + 16 * h + 4 * gq);
+            // consecutive MFMAs go to different accumulators
+#pragma unroll
+            for (int t = 0; t < 4; t++)
+#pragma unroll
+                for (int j = 0; j < NT; j++)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[h][t], b[j][t], acc[j], 0, 0, 0);
+        }
+        if (g.bias) {
+#pragma unroll
+            for (int j = 0; j < NT; j++) acc[j] += g.bias[16 * j + r];
+        }
+        if (g.accumulate) {  // every read of c before any write
+            v4f old[NT];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int64_t row = min(tile * 16 + 4 * gq + i, (int64_t)g.M - 1);
+#pragma unroll
+                for (int j = 0; j < NT; j++) old[j][i] = g.c[row * N + 16 * j + r];
+            }
+#pragma unroll
+            for (int j = 0; j < NT; j++) acc[j] = old[j] + acc[j];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t row = tile * 16 + 4 * gq + i;
+            if (row >= g.M) continue;
+            float* dst = g.c + row * N + r;
+#pragma unroll
+            for (int j = 0; j < NT; j++) dst[16 * j] = acc[j][i];
+        }
+    }
+}
+
 // ---- skinny shapes, where a 128-row MFMA tile would mostly compute padding
 
 // element (r, kk) of op(a) and (kk, j) of op(b)
@@ -712,6 +810,11 @@ Split small_out_split(int32_t k) {
 
 bool narrow(int32_t k, int32_t n) { return k <= 64 && n <= 64; }
 
+// Tall products whose whole op(b) fits the streaming kernel's LDS block.
+bool stream_shape(int32_t m, int32_t k, int32_t n) {
+    return m >= 1024 && k % 16 == 0 && n % 16 == 0 && k <= 128 && n <= 128 && k * n <= 8192 && !narrow(k, n);
+}
+
 // The register-row paths: short rows, or few outputs.
 bool short_rows(int32_t k, int32_t n) { return k <= 32 && n <= 32; }
 bool outer_shape(int32_t m, int32_t n) { return m <= 16 && n <= 16; }
@@ -824,6 +927,36 @@ int linear_impl(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_
             if (blocks >= ((int64_t)1 << 31)) return GGA_ERANGE;
             gemm_narrow<<<(unsigned)blocks, 256, 0, s>>>(g);
         }
+        return launch_status();
+    }
+    if (!trans_a && stream_shape(m, k, n) && (reinterpret_cast<uintptr_t>(a) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(b) & 15) == 0) {
+        GemmArgs g{};
+        g.a = a;
+        g.b = b;
+        g.bias = bias;
+        g.c = c;
+        g.M = m;
+        g.K = k;
+        g.N = n;
+        g.trans_b = trans_b != 0;
+        g.accumulate = accumulate;
+        const int64_t tiles = ((int64_t)m + 15) / 16;
+        const int64_t blocks = (tiles + kStreamWaves * kStreamTiles - 1) / (kStreamWaves * kStreamTiles);
+        const int kc = k / 16, nt = n / 16;
+#define GGA_STREAM(KC_, NT_) \
+    else if (kc == KC_ && nt == NT_) gemm_stream<KC_, NT_><<<(unsigned)blocks, kStreamThreads, 0, s>>>(g);
+        if (false) {
+        }
+        GGA_STREAM(1, 5) GGA_STREAM(1, 6) GGA_STREAM(1, 7) GGA_STREAM(1, 8)
+        GGA_STREAM(2, 5) GGA_STREAM(2, 6) GGA_STREAM(2, 7) GGA_STREAM(2, 8)
+        GGA_STREAM(3, 5) GGA_STREAM(3, 6) GGA_STREAM(3, 7) GGA_STREAM(3, 8)
+        GGA_STREAM(4, 5) GGA_STREAM(4, 6) GGA_STREAM(4, 7) GGA_STREAM(4, 8)
+        GGA_STREAM(5, 1) GGA_STREAM(5, 2) GGA_STREAM(5, 3) GGA_STREAM(5, 4) GGA_STREAM(5, 5) GGA_STREAM(5, 6)
+        GGA_STREAM(6, 1) GGA_STREAM(6, 2) GGA_STREAM(6, 3) GGA_STREAM(6, 4) GGA_STREAM(6, 5)
+        GGA_STREAM(7, 1) GGA_STREAM(7, 2) GGA_STREAM(7, 3) GGA_STREAM(7, 4)
+        GGA_STREAM(8, 1) GGA_STREAM(8, 2) GGA_STREAM(8, 3) GGA_STREAM(8, 4)
+#undef GGA_STREAM
         return launch_status();
     }
     const Split sp = pick_split(m, k, n);
