@@ -114,7 +114,8 @@ def test_global_linear_bwd(g, n, heads, r):
 @pytest.mark.parametrize("m,k,n,ta,tb", [(300, 200, 150, False, True), (256, 5000, 64, True, False),
                                          (512, 256, 256, False, False), (512, 256, 384, False, True),
                                          (64, 262144 // 16, 256, True, False), (1, 7, 3, False, False),
-                                         (5003, 64, 128, False, True), (2049, 128, 64, False, False)])
+                                         (5003, 64, 128, False, True), (2049, 128, 64, False, False),
+                                         (128, 40000, 128, True, False)])
 def test_linear_accumulate(g, m, k, n, ta, tb):
     a = _rand((k, m) if ta else (m, k), 40)
     b = _rand((n, k) if tb else (k, n), 41)
