@@ -566,7 +566,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dst_kernel(BwdParams p) {
         return;
     }
     const int nl = p.a.hdr->n_light;
-    if (p.own_rows) {  // the wavefront owns G consecutive light rows
+    if (NS == 1 && UMAX == 4 && p.own_rows) {  // the wavefront owns G consecutive light rows
         const int li0 = ((blockIdx.x - p.a.chunk_blocks) * kBwdWaves + wave) * r.geo.G;
         if (li0 >= nl) return;
         if ((int64_t)p.a.hdr->light_sum > (int64_t)nl * r.EIT) {  // long rows: one after another
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_src_kernel(BwdParams p) {
         return;
     }
     const int nl = p.b.hdr->n_light;
-    if (p.own_rows) {  // the wavefront owns G consecutive light rows
+    if (NS == 1 && p.own_rows) {  // the wavefront owns G consecutive light rows
         const int li0 = ((blockIdx.x - p.b.chunk_blocks) * kBwdWaves + wave) * r.geo.G;
         if (li0 >= nl) return;
         if ((int64_t)p.b.hdr->light_sum > (int64_t)nl * r.EIT) {  // long rows: one after another

@@ -357,7 +357,8 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
         return;
     }
     const int nl = p.hdr->n_light;
-    if (p.own_rows) {
+    // (light rows narrower than a wavefront: one slot, four edge slots per lane)
+    if (NS == 1 && UMAX == 4 && p.own_rows) {
         // the wavefront owns G consecutive light rows
         const int li0 = ((blockIdx.x - p.chunk_blocks) * kFwdWaves + wave) * r.G;
         if (li0 >= nl) return;
