@@ -812,7 +812,8 @@ bool narrow(int32_t k, int32_t n) { return k <= 64 && n <= 64; }
 
 // Tall products whose whole op(b) fits the streaming kernel's LDS block.
 bool stream_shape(int32_t m, int32_t k, int32_t n) {
-    return m >= 1024 && k % 16 == 0 && n % 16 == 0 && k <= 128 && n <= 128 && k * n <= 8192 && !narrow(k, n);
+    return m >= 1024 && k >= 16 && k % 16 == 0 && n % 16 == 0 && k <= 128 && n <= 128 && k * n <= 8192 &&
+           !narrow(k, n);
 }
 
 // The register-row paths: short rows, or few outputs.

@@ -40,6 +40,7 @@ def _t(a):
     (70001, 7, 5, 0, 0, True), (4099, 32, 32, 0, 1, True), (5, 50001, 3, 1, 0, True), (16, 9000, 16, 1, 0, False),
     # op(b) held in LDS, 16-row tiles streamed (k, n <= 128): the GAT X W, ragged rows, both b layouts
     (170000, 128, 64, 0, 0, False), (4099, 96, 80, 0, 1, True), (1030, 16, 128, 0, 0, True), (2055, 128, 16, 0, 1, False),
+    (2000, 0, 80, 0, 0, True),  # empty contraction beside the streaming shapes: c is the bias
     # transposed a over a long k (split-k), ragged k, with bias
     (128, 170001, 64, 1, 0, True), (48, 20000, 64, 1, 0, False), (64, 16384, 112, 1, 0, True),
 ])
