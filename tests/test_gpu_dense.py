@@ -113,3 +113,32 @@ def test_add_layernorm(g, n, d):
     out = g.gga_add_layernorm(_t(x), _t(y), _t(gm), _t(bt), 1e-5)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), oracle.layer_norm(x.astype(np.float64) + y, gm, bt), "f32", "ln")
+
+
+def test_linear_shape_sweep(g):
+    """Every product path, chosen by shape and transposes (short rows, narrow, LDS-resident
+    b, the tile kernels, split k), at the boundaries of the conditions that pick it: k and n
+    around 16, 32, 64 and 128, an empty contraction, m below and above the streaming
+    threshold, with bias and accumulation."""
+    edges = (0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 80, 127, 128, 129)
+    rng = np.random.default_rng(11)
+    checked = 0
+    for m in (37, 1030):
+        for k in edges:
+            for n in edges[1:]:
+                for ta, tb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+                    a = rng.standard_normal((k, m) if ta else (m, k)).astype(np.float32)
+                    b = rng.standard_normal((n, k) if tb else (k, n)).astype(np.float32)
+                    bv = rng.standard_normal(n).astype(np.float32)
+                    c0 = rng.standard_normal((m, n)).astype(np.float32)
+                    ref = (a.T if ta else a).astype(np.float64) @ (b.T if tb else b).astype(np.float64)
+                    c = g.gga_linear(_t(a), _t(b), _t(bv), trans_a=bool(ta), trans_b=bool(tb))
+                    acc = _t(c0)
+                    g.gga_linear_accumulate(_t(a), _t(b), acc, trans_a=bool(ta), trans_b=bool(tb))
+                    torch.cuda.synchronize()
+                    what = f"m={m} k={k} n={n} ta={ta} tb={tb}"
+                    assert_close(c.cpu().numpy(), ref + bv, "f32", "c " + what, atol=1e-5 * max(1.0, np.sqrt(k)))
+                    assert_close(acc.cpu().numpy(), ref + c0, "f32", "c+= " + what,
+                                 atol=1e-5 * max(1.0, np.sqrt(k)))
+                    checked += 1
+    assert checked == 2 * 15 * 14 * 4
