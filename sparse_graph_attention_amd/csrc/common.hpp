@@ -32,6 +32,23 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A row piece of 16, 8 or 4 bytes loaded with the non-temporal hint: for rows a kernel reads
+// once (the row it owns), so that they displace fewer of the rows it gathers again.
+template <typename R>
+__device__ __forceinline__ R load_once(const R* p) {
+    if constexpr (sizeof(R) == 16) {
+        typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+        return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p)));
+    } else if constexpr (sizeof(R) == 8) {
+        typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const u2v*>(p)));
+    } else if constexpr (sizeof(R) == 4) {
+        return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p)));
+    } else {
+        return *p;
+    }
+}
+
 // ---------------------------------------------------------------- host helpers
 
 inline int launch_status() { return hipGetLastError() == hipSuccess ? GGA_OK : GGA_EHIP; }

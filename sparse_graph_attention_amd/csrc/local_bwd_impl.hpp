@@ -96,8 +96,8 @@ struct PassA {
             const size_t ro = (size_t)v * p.W + geo.off[s];
             float o[EPL];
             if (geo.ok[s]) {
-                load_f32<EPL>(p.dout + ro, go[s]);
-                load_f32<EPL>(p.out + ro, o);
+                load_f32_once<EPL>(p.dout + ro, go[s]);
+                load_f32_once<EPL>(p.out + ro, o);
             } else {
 #pragma unroll
                 for (int i = 0; i < EPL; i++) go[s][i] = o[i] = 0.f;
@@ -110,7 +110,7 @@ struct PassA {
             l2[s] = geo.ok[s] ? p.lse[hi] * kLog2e : 0.f;
             if constexpr (MODE == GGA_SCORE_DOT) {
                 raw_t r{};
-                if (geo.ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.qs) + ro);
+                if (geo.ok[s]) r = load_once(reinterpret_cast<const raw_t*>(static_cast<const T*>(p.qs) + ro));
                 V::widen(r, qf[s]);
             } else {
                 sd[s] = geo.ok[s] ? static_cast<const float*>(p.qs)[hi] : 0.f;
@@ -308,12 +308,12 @@ struct PassB {
             const size_t ro = (size_t)u * p.W + geo.off[s];
             if constexpr (MODE != GGA_SCORE_MEAN) {
                 raw_t r{};
-                if (geo.ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.v) + ro);
+                if (geo.ok[s]) r = load_once(reinterpret_cast<const raw_t*>(static_cast<const T*>(p.v) + ro));
                 V::widen(r, vf[s]);
             }
             if constexpr (MODE == GGA_SCORE_DOT) {
                 raw_t kr{};
-                if (geo.ok[s]) kr = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.ks) + ro);
+                if (geo.ok[s]) kr = load_once(reinterpret_cast<const raw_t*>(static_cast<const T*>(p.ks) + ro));
                 V::widen(kr, kf[s]);
             } else if constexpr (MODE != GGA_SCORE_MEAN) {
                 ssv[s] = geo.ok[s] ? static_cast<const float*>(p.ks)[(size_t)u * p.H + geo.head[s]] : 0.f;

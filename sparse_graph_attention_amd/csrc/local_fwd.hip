@@ -95,7 +95,7 @@ struct FwdRow {
         for (int s = 0; s < NS; s++) {
             if constexpr (MODE == GGA_SCORE_DOT) {
                 raw_t r{};
-                if (ok[s]) r = *reinterpret_cast<const raw_t*>(static_cast<const T*>(p.qs) + (size_t)v * p.W + off[s]);
+                if (ok[s]) r = load_once(reinterpret_cast<const raw_t*>(static_cast<const T*>(p.qs) + (size_t)v * p.W + off[s]));
                 V::widen(r, qf[s]);
             } else if constexpr (MODE != GGA_SCORE_MEAN) {
                 sd[s] = ok[s] ? static_cast<const float*>(p.qs)[(size_t)v * p.H + head[s]] : 0.f;

@@ -47,6 +47,21 @@ __device__ __forceinline__ void load_f32(const float* src, float* f) {
     }
 }
 
+// load_f32 for a row the kernel reads once (non-temporal hint).
+template <int EPL>
+__device__ __forceinline__ void load_f32_once(const float* src, float* f) {
+    if constexpr (EPL == 8 || EPL == 4) {
+#pragma unroll
+        for (int h = 0; h < EPL / 4; h++) {
+            const float4 a = load_once(reinterpret_cast<const float4*>(src) + h);
+            f[4 * h] = a.x; f[4 * h + 1] = a.y; f[4 * h + 2] = a.z; f[4 * h + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPL; i++) f[i] = load_once(src + i);
+    }
+}
+
 template <int EPL, int HDP, int NS>
 struct RowGeo {
     int lane, g, G, lpr;
