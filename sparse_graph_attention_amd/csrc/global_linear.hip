@@ -192,22 +192,31 @@ __global__ __launch_bounds__(512) void stats_mfma(Seg sg, int32_t H, const float
 #pragma unroll
                 for (int j = 0; j < TR; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
             }
+            // the next 16 rows are loaded during the current rows' MFMAs; rows past the piece
+            // read its last row and are zeroed by a select, so no load is conditional
+            float kn[4][TR], vn[4][TR];
+            auto fetch = [&](int64_t base) {
+#pragma unroll
+                for (int st = 0; st < 4; st++) {
+                    const int64_t row = base + st * 4 + (lane >> 4);
+                    const int64_t o = (row < r1 ? row : r1 - 1) * W + h * R + TR * (lane & 15);
+                    load_n<TR>(k + o, kn[st]);
+                    load_n<TR>(v + o, vn[st]);
+                }
+            };
+            if (r0 < r1) fetch(r0);
             for (int64_t base = r0; base < r1; base += 16) {
                 float a[4][TR], bv[4][TR];
 #pragma unroll
                 for (int st = 0; st < 4; st++) {
-                    const int64_t row = base + st * 4 + (lane >> 4);
-                    if (row < r1) {
-                        const int64_t o = row * W + h * R + TR * (lane & 15);
-                        load_n<TR>(k + o, a[st]);
-                        load_n<TR>(v + o, bv[st]);
+                    const bool ok = base + st * 4 + (lane >> 4) < r1;
 #pragma unroll
-                        for (int u = 0; u < TR; u++) a[st][u] = phi(a[st][u]);
-                    } else {
-#pragma unroll
-                        for (int u = 0; u < TR; u++) a[st][u] = bv[st][u] = 0.f;
+                    for (int u = 0; u < TR; u++) {
+                        a[st][u] = ok ? phi(kn[st][u]) : 0.f;
+                        bv[st][u] = ok ? vn[st][u] : 0.f;
                     }
                 }
+                if (base + 16 < r1) fetch(base + 16);
 #pragma unroll
                 for (int st = 0; st < 4; st++) {
 #pragma unroll
