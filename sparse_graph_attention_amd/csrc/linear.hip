@@ -464,12 +464,12 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ 
 
 // ---- tall products with all of op(b) in LDS (k, n <= 128, multiples of 16, k*n <= 8192,
 // plain a): each workgroup stages op(b) once as [n][k] (rows padded by 4 floats, so the
-// 16-byte reads of 16 consecutive n rows hit distinct banks) and its eight wavefronts walk
-// two 16-row tiles of a each (measured best of 1-8 tiles and 4 or 8 wavefronts).  In 16-deep chunk h, lane (r = lane%16, g = lane/16) holds
+// 16-byte reads of 16 consecutive n rows hit distinct banks) and its eight wavefronts take
+// one 16-row tile of a each (measured best of 1-8 tiles and 4 or 8 wavefronts).  In 16-deep chunk h, lane (r = lane%16, g = lane/16) holds
 // a[row r][16h + 4g .. +3] (one 16-byte load) and b[16h + 4g .. +3][16j + r] (one LDS
 // read), MFMA step t taking k = 16h + 4g + t; lane l ends with c[4g + i][16j + r].  The next
 // tile's a rows are loaded during the current tile's MFMAs.
-constexpr int kStreamTiles = 2;  // 16-row tiles per wavefront
+constexpr int kStreamTiles = 1;  // 16-row tiles per wavefront
 constexpr int kStreamWaves = 8;  // wavefronts per workgroup (sharing one staged op(b))
 constexpr int kStreamThreads = 64 * kStreamWaves;
 
@@ -479,46 +479,44 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream(GemmArgs g) {
     __shared__ float bt[N * PB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r = lane & 15, gq = lane >> 4;
-    {
-        // op(b) in its memory order, 16 bytes per load, every load issued before the stores
-        constexpr int NV = K * N / 4, PER = (NV + kStreamThreads - 1) / kStreamThreads;
-        v4f sv[PER];
+    const int64_t t0 = ((int64_t)blockIdx.x * kStreamWaves + wave) * kStreamTiles;
+    // op(b) in its memory order, 16 bytes per load, requested first (the staging stores wait
+    // for these loads only, not for the a rows requested after them)
+    constexpr int NV = K * N / 4, PER = (NV + kStreamThreads - 1) / kStreamThreads;
+    v4f sv[PER];
 #pragma unroll
-        for (int q = 0; q < PER; q++) {
-            const int x = threadIdx.x + kStreamThreads * q;
-            if (x < NV) sv[q] = *reinterpret_cast<const v4f*>(g.b + 4 * x);
-        }
+    for (int q = 0; q < PER; q++) {
+        const int x = threadIdx.x + kStreamThreads * q;
+        if (x < NV) sv[q] = *reinterpret_cast<const v4f*>(g.b + 4 * x);
+    }
+    // every tile's a rows are requested before any tile is multiplied, so the loads of the
+    // later tiles arrive while the earlier ones are multiplied; rows past the end re-read
+    // the last row (never stored), so no load is conditional
+    v4f at[kStreamTiles][KC];
 #pragma unroll
-        for (int q = 0; q < PER; q++) {
-            const int x = threadIdx.x + kStreamThreads * q;
-            if (x >= NV) continue;
-            if (g.trans_b) {  // b [N][K]: four consecutive k of row j
-                const int j = 4 * x / K, kk = 4 * x % K;
-                *reinterpret_cast<v4f*>(bt + j * PB + kk) = sv[q];
-            } else {  // b [K][N]: four consecutive n of row kk
-                const int kk = 4 * x / N, j0 = 4 * x % N;
+    for (int tt = 0; tt < kStreamTiles; tt++) {
+        const int64_t row = min((t0 + tt) * 16 + r, (int64_t)g.M - 1);
 #pragma unroll
-                for (int e = 0; e < 4; e++) bt[(j0 + e) * PB + kk] = sv[q][e];
-            }
+        for (int h = 0; h < KC; h++) at[tt][h] = *reinterpret_cast<const v4f*>(g.a + row * K + 16 * h + 4 * gq);
+    }
+#pragma unroll
+    for (int q = 0; q < PER; q++) {
+        const int x = threadIdx.x + kStreamThreads * q;
+        if (x >= NV) continue;
+        if (g.trans_b) {  // b [N][K]: four consecutive k of row j
+            const int j = 4 * x / K, kk = 4 * x % K;
+            *reinterpret_cast<v4f*>(bt + j * PB + kk) = sv[q];
+        } else {  // b [K][N]: four consecutive n of row kk
+            const int kk = 4 * x / N, j0 = 4 * x % N;
+#pragma unroll
+            for (int e = 0; e < 4; e++) bt[(j0 + e) * PB + kk] = sv[q][e];
         }
     }
     __syncthreads();
-    const int64_t t0 = ((int64_t)blockIdx.x * kStreamWaves + wave) * kStreamTiles;
-    v4f an[KC];
-    // rows past the end re-read the last row (never stored), so no load is conditional
-    auto fetch = [&](int64_t tile) {
-        const int64_t row = min(tile * 16 + r, (int64_t)g.M - 1);
 #pragma unroll
-        for (int h = 0; h < KC; h++) an[h] = *reinterpret_cast<const v4f*>(g.a + row * K + 16 * h + 4 * gq);
-    };
-    fetch(t0);
     for (int tt = 0; tt < kStreamTiles; tt++) {
         const int64_t tile = t0 + tt;
         if (tile * 16 >= g.M) break;
-        v4f a[KC];
-#pragma unroll
-        for (int h = 0; h < KC; h++) a[h] = an[h];
-        if (tt + 1 < kStreamTiles) fetch(tile + 1);
         v4f acc[NT];
 #pragma unroll
         for (int j = 0; j < NT; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -532,7 +530,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemm_stream(GemmArgs g) {
             for (int t = 0; t < 4; t++)
 #pragma unroll
                 for (int j = 0; j < NT; j++)
-                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[h][t], b[j][t], acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(at[tt][h][t], b[j][t], acc[j], 0, 0, 0);
         }
         if (g.bias) {
 #pragma unroll
