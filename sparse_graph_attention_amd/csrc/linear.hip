@@ -653,23 +653,28 @@ __global__ __launch_bounds__(256) void gemm_rows(GemmArgs g) {
     __shared__ float stage[4][64 * (PA > PC ? PA : PC)];
     const int K = g.K, N = g.N;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int x = threadIdx.x; x < K * N; x += 256) bs[x] = op_b(g, x / N, x % N);
     const int64_t r0 = ((int64_t)blockIdx.x * 4 + wave) * 64;
     const int64_t r = r0 + lane;
-    const bool tile = !g.trans_a && K % 4 == 0 && N % 4 == 0 && r0 + 64 <= g.M &&
+    // (K > 0: an empty a has no first element for the clamped loads below to re-read)
+    const bool tile = !g.trans_a && K > 0 && K % 4 == 0 && N % 4 == 0 && r0 + 64 <= g.M &&
                       (reinterpret_cast<uintptr_t>(g.a) & 15) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0;
+    // the wavefront's 64 rows of K floats are requested first, 4 at a time, all in flight
+    // together and during the op(b) staging (positions past 16 K re-read the first one)
+    v4f v[KP / 4];
+    if (tile) {
+        const float* src = g.a + r0 * K;
+#pragma unroll
+        for (int q = 0; q < KP / 4; q++) {
+            const int x = lane + 64 * q;
+            v[q] = *reinterpret_cast<const v4f*>(src + 4 * (x < 16 * K ? x : 0));
+        }
+    }
+    for (int x = threadIdx.x; x < K * N; x += 256) bs[x] = op_b(g, x / N, x % N);
     float* st = stage[wave];
     float a[KP];
     __syncthreads();  // bs complete; from here on each wavefront works alone
     if (r >= g.M) return;
     if (tile) {
-        const float* src = g.a + r0 * K;
-        v4f v[KP / 4];  // 64 rows of K floats, 4 at a time: all loads in flight together
-#pragma unroll
-        for (int q = 0; q < KP / 4; q++) {
-            const int x = lane + 64 * q;
-            v[q] = x < 16 * K ? *reinterpret_cast<const v4f*>(src + 4 * x) : v4f{0.f, 0.f, 0.f, 0.f};
-        }
 #pragma unroll
         for (int q = 0; q < KP / 4; q++) {
             const int x = lane + 64 * q;
