@@ -321,26 +321,7 @@ __global__ __launch_bounds__(NW * 64) void seg_reduce(Seg sg, int32_t H, int32_t
 // R/4 consecutive elements of its row (16-byte loads), and its B operands S[k][j] are held in
 // registers for the whole piece.  Output columns are permuted too (MFMA tile j, position
 // li <-> column TR*li + j), so each lane ends with TR consecutive outputs of a row.  The
-// next tile's q is loaded before the current one is multiplied.
-template <int TR>
-__device__ __forceinline__ void load_phi_row(const float* __restrict__ q, int64_t off, bool ok, float (&a)[TR * 4]) {
-    constexpr int KQ = TR * 4;
-    if (ok) {
-        const float4* qp = reinterpret_cast<const float4*>(q + off);
-#pragma unroll
-        for (int c = 0; c < KQ / 4; c++) {
-            const float4 t4 = qp[c];
-            a[4 * c + 0] = phi(t4.x);
-            a[4 * c + 1] = phi(t4.y);
-            a[4 * c + 2] = phi(t4.z);
-            a[4 * c + 3] = phi(t4.w);
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < KQ; t++) a[t] = 0.f;
-    }
-}
-
+// next tile's q is loaded (and kept raw until used) before the current one is multiplied.
 template <int TR>
 __global__ __launch_bounds__(512) void apply_mfma(Seg sg, int32_t H, float eps, const float* __restrict__ q,
                                                    const float* __restrict__ s, const float* __restrict__ z,
@@ -367,13 +348,25 @@ __global__ __launch_bounds__(512) void apply_mfma(Seg sg, int32_t H, float eps, 
                 for (int j = 0; j < TR; j++) sreg[t][j] = sh[kk * R + TR * li + j];
             }
             const int64_t col = h * R + gq * KQ;
-            float a[KQ];
+            // the next tile's q rows stay raw until used, so their loads overlap this tile's
+            // MFMAs; rows past the piece read its last row and are zeroed by a select
+            v4f qn[KQ / 4];
+            auto fetch = [&](int64_t rowt) {
+                const int64_t row = rowt + li < r1 ? rowt + li : r1 - 1;
+#pragma unroll
+                for (int c = 0; c < KQ / 4; c++) qn[c] = *reinterpret_cast<const v4f*>(q + row * W + col + 4 * c);
+            };
             int64_t row0 = r0 + 16 * p0;
-            load_phi_row<TR>(q, (row0 + li) * W + col, row0 + li < r1, a);
+            if (row0 < r1) fetch(row0);
             for (; row0 < r1; row0 += 16 * P) {
-                float an[KQ];
+                float a[KQ];
+                const bool ok = row0 + li < r1;
+#pragma unroll
+                for (int c = 0; c < KQ / 4; c++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) a[4 * c + e] = ok ? phi(qn[c][e]) : 0.f;
                 const int64_t nxt = row0 + 16 * P;
-                load_phi_row<TR>(q, (nxt + li) * W + col, nxt + li < r1, an);
+                if (nxt < r1) fetch(nxt);
                 float d = 0.f;
 #pragma unroll
                 for (int t = 0; t < KQ; t++) d = fmaf(a[t], zreg[t], d);
@@ -399,8 +392,6 @@ __global__ __launch_bounds__(512) void apply_mfma(Seg sg, int32_t H, float eps, 
                         store_n<TR>(g + orow * W + h * R + TR * li, o);
                     }
                 }
-#pragma unroll
-                for (int t = 0; t < KQ; t++) a[t] = an[t];
             }
         }
     });
