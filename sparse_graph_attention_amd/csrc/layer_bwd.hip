@@ -28,8 +28,9 @@ struct RowSplit {
     int wpb;         // wavefronts per workgroup
 };
 
-// Ranges of at least 64 rows, at most 1024 of them; up to 4 wavefronts per workgroup, fewer
-// when their accumulator rows (ncols floats each) would pass 64 KiB.
+// Ranges of at least 64 rows, at most 1024 of them; up to 16 wavefronts per workgroup (each
+// walks its rows one after another, so more of them keep more rows in flight), fewer when
+// their accumulator rows (ncols floats each) would pass 64 KiB.
 RowSplit row_split(int32_t n, int ncols) {
     RowSplit r;
     int64_t nb = ((int64_t)n + 63) / 64;
@@ -38,7 +39,7 @@ RowSplit row_split(int32_t n, int ncols) {
     r.nb = (int)nb;
     r.per = (int32_t)(((int64_t)n + nb - 1) / nb);
     int w = kLdsLimitFloats / acc_stride(ncols > 0 ? ncols : 1);
-    r.wpb = w > 4 ? 4 : w;
+    r.wpb = w > 16 ? 16 : w;
     return r;
 }
 
@@ -61,7 +62,7 @@ __device__ __forceinline__ void flush_acc(const float* acc, int ncols, int nw, f
 // ---- LayerNorm backward, row held in registers (d % 4 == 0, d <= 256 * NV, aligned).
 // Lane owns float4 columns lane + 64 k.  acc row: [0, d) d_gamma, [d, 2d) d_beta.
 template <int NV>
-__global__ __launch_bounds__(256) void ln_bwd_vec(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
+__global__ __launch_bounds__(1024) void ln_bwd_vec(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
                                                    const float* __restrict__ y, const float* __restrict__ gamma,
                                                    float eps, const float* __restrict__ d_out,
                                                    float* __restrict__ d_pre, float* __restrict__ part) {
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void ln_bwd_vec(int32_t n, int32_t d, int32_t 
 }
 
 // ---- LayerNorm backward, any width: passes re-read the row (from cache).
-__global__ __launch_bounds__(256) void ln_bwd_generic(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
+__global__ __launch_bounds__(1024) void ln_bwd_generic(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
                                                        const float* __restrict__ y, const float* __restrict__ gamma,
                                                        float eps, const float* __restrict__ d_out,
                                                        float* __restrict__ d_pre, float* __restrict__ part) {
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(256) void ln_bwd_generic(int32_t n, int32_t d, int3
 }
 
 // ---- gate and combination backward.  acc row: [0, d) d_w_g, [d] d_b_g.
-__global__ __launch_bounds__(256) void combine_bwd_kernel(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
+__global__ __launch_bounds__(1024) void combine_bwd_kernel(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
                                                            const float* __restrict__ w_g, float b_g, int32_t width,
                                                            const float* __restrict__ l, const float* __restrict__ gg,
                                                            const float* __restrict__ d_y, float* __restrict__ d_l,
