@@ -200,8 +200,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_mfma(GemmArgs g) {
 }
 
 // ---- the main tile kernel for n > 64: 128 x 128 outputs per workgroup of four wavefronts,
-// each owning 64 x 64 (a 4 x 4 grid of 16x16 MFMA tiles); k staged through LDS 32 at a time,
-// double-buffered, the next stage's global loads in flight during the current MFMAs.  An
+// each owning 64 x 64 (a 4 x 4 grid of 16x16 MFMA tiles); k staged through LDS 32 at a time
+// (one or two buffers, BigCfg), the next stage's global loads in flight during the current MFMAs.  An
 // operand whose rows run along k (a plain, b transposed) is staged as [row][k], one whose
 // rows run along m or n (a transposed, b plain) as [k][row]: both are 16-byte copies, with
 // no transposition on the way into LDS.  Both layouts are free of bank conflicts for the
@@ -217,6 +217,20 @@ constexpr int TK2 = 32;                     // k per stage
 constexpr int PITCH_RK = TK2;               // [row][k]
 constexpr int PITCH_KR = TT + 4;            // [k][row]
 constexpr int kStageFloats = TK2 * PITCH_KR;  // >= TT * PITCH_RK
+constexpr int kEpPitch = 68;                   // epilogue rows: 64 columns + 4
+constexpr int kEpFloats = 4 * 32 * kEpPitch;   // four wavefronts' 32-row epilogue blocks
+
+// Stage buffers and workgroups per CU of one instance.  One buffer (two barriers per stage)
+// lets three workgroups share a CU, so one's barriers, prologue and epilogue are covered by
+// the others' MFMAs: 3-5% faster than two double-buffered workgroups.  Only a b^T, whose
+// loop needs more than the 168 registers three workgroups allow (it spilled and lost 7%),
+// keeps two buffers and two workgroups.
+template <bool AKM, bool BKM>
+struct BigCfg {
+    static constexpr int buffers = (AKM || BKM) ? 1 : 2;
+    static constexpr int per_cu = 4 - buffers;
+    static constexpr int lds_floats = 2 * buffers * kStageFloats > kEpFloats ? 2 * buffers * kStageFloats : kEpFloats;
+};
 
 // chunk order of a [row][k] row: a different permutation for each of 8 consecutive rows
 // and for each parity among 16
@@ -311,9 +325,10 @@ __device__ __forceinline__ void fast_fetch(const float* (&p)[4], int64_t step, v
     }
 }
 
-// The k loop of one tile: nk stages from kb, double-buffered through LDS.  FAST: the tile
-// and every stage lie inside the matrices, and rows are 16-byte aligned.
-template <bool AKM, bool BKM, bool FAST>
+// The k loop of one tile: nk stages from kb through NB LDS buffers (with one, the stores of
+// the next stage wait at a barrier for every wavefront's reads of the current one).  FAST:
+// the tile and every stage lie inside the matrices, and rows are 16-byte aligned.
+template <bool AKM, bool BKM, bool FAST, int NB>
 __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kStageFloats], int64_t m0, int64_t n0,
                                          int64_t kb, int64_t ke, bool a_vec, bool b_vec, v4f (&acc)[4][4]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -339,7 +354,7 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
     }
     __syncthreads();
     for (int t = 0; t < nk; t++) {
-        const int cur = t & 1;
+        const int cur = NB == 2 ? (t & 1) : 0;
         if (t + 1 < nk) {
             GGA_BIG_FETCH(kb + (int64_t)(t + 1) * TK2)
         }
@@ -361,8 +376,9 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][st], bf[j][st], acc[i][j], 0, 0, 0);
         }
         if (t + 1 < nk) {
-            big_stash<AKM>(lds[cur ^ 1][0], ra);
-            big_stash<BKM>(lds[cur ^ 1][1], rb);
+            if constexpr (NB == 1) __syncthreads();
+            big_stash<AKM>(lds[NB == 2 ? cur ^ 1 : 0][0], ra);
+            big_stash<BKM>(lds[NB == 2 ? cur ^ 1 : 0][1], rb);
         }
         __syncthreads();
     }
@@ -370,8 +386,11 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
 }
 
 template <bool AKM, bool BKM>
-__global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_big(GemmArgs g) {
-    __shared__ float lds[2][2][kStageFloats];  // [buffer][operand]
+__global__ __launch_bounds__(kBigThreads, (BigCfg<AKM, BKM>::per_cu)) void gemm_f32_big(GemmArgs g) {
+    using Cfg = BigCfg<AKM, BKM>;
+    __shared__ float lds_raw[Cfg::lds_floats];
+    // [buffer][operand]; the epilogue reuses the same memory
+    float(*lds)[2][kStageFloats] = reinterpret_cast<float(*)[2][kStageFloats]>(lds_raw);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const uint32_t gxy = gridDim.x * gridDim.y;
@@ -390,9 +409,9 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_big(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
     if (fast)
-        big_loop<AKM, BKM, true>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
+        big_loop<AKM, BKM, true, Cfg::buffers>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
     else
-        big_loop<AKM, BKM, false>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
+        big_loop<AKM, BKM, false, Cfg::buffers>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
 
     // Epilogue through LDS, 32 rows of the wavefront's 64 x 64 block at a time: the
     // accumulators go to a private [32][68] region, then each row leaves as 16-byte stores,
@@ -402,8 +421,8 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_big(GemmArgs g) {
     const bool acc_in = g.accumulate && gridDim.z == 1;
     const bool c_vec = (g.N % 4) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0 &&
                        (!add_bias || (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0);
-    constexpr int EP = 68;
-    float* ep = &lds[0][0][0] + wave * 32 * EP;
+    constexpr int EP = kEpPitch;
+    float* ep = lds_raw + wave * 32 * EP;
     const int g4 = (lane >> 4) * 4, cl = lane & 15;
 #pragma unroll
     for (int hh = 0; hh < 2; hh++) {
