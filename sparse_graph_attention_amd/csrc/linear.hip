@@ -222,9 +222,9 @@ constexpr int kEpFloats = 4 * 32 * kEpPitch;   // four wavefronts' 32-row epilog
 
 // Stage buffers and workgroups per CU of one instance.  One buffer (two barriers per stage)
 // lets three workgroups share a CU, so one's barriers, prologue and epilogue are covered by
-// the others' MFMAs: 3-5% faster than two double-buffered workgroups.  Only a b^T, whose
-// loop needs more than the 168 registers three workgroups allow (it spilled and lost 7%),
-// keeps two buffers and two workgroups.
+// the others' MFMAs: 3-5% faster than two double-buffered workgroups.  Only a b^T keeps two
+// buffers and two workgroups: three of its workgroups ran 6-7% slower, also in a build whose
+// loop fitted the 168 registers without spilling.  (A fourth workgroup for a^T b gained 1%.)
 template <bool AKM, bool BKM>
 struct BigCfg {
     static constexpr int buffers = (AKM || BKM) ? 1 : 2;
