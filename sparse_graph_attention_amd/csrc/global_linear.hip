@@ -7,7 +7,7 @@
 // input of the page's Implementation notes (one adjacency list per graph).
 //
 // Work is cut into tiles of `rs` consecutive node rows (rs a multiple of 16, at least 256,
-// fixed by n, so at most 1024 tiles).  A graph of at most rs rows is handled whole by the
+// fixed by n and the head count, so at most 1024 / heads tiles and 1024 tiles x heads).  A graph of at most rs rows is handled whole by the
 // tile holding its first row; a longer graph is cut at tile boundaries and each piece gives
 // a partial sum in one of two slots of its tile (slot 0: the graph holding the tile's first
 // row; slot 1: a long graph starting inside the tile), which a second kernel adds in tile
@@ -499,20 +499,30 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             const int64_t row = r0 + tl * 16 + li;
             const bool valid = tl < ntile && row < r1;
             const int64_t off = row * W + h * R + gq * KQ;
-            float qr[KQ], a[KQ], dgl[KQ];
+            // q, dG and the dq being accumulated into are requested together, so the dq
+            // values arrive during the products instead of after them; q itself is kept only
+            // as phi(q) and a sign mask (phi'(q) is 1 where q > 0 and phi(q) elsewhere).
+            float a[KQ], dgl[KQ], dqo[KQ];
+            uint32_t pos = 0;
             if (valid) {
+                float qr[KQ];
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
                     const float4 t4 = *reinterpret_cast<const float4*>(q + off + 4 * c);
                     const float4 g4 = *reinterpret_cast<const float4*>(dg + off + 4 * c);
+                    const float4 o4 = *reinterpret_cast<const float4*>(dq + off + 4 * c);
                     qr[4 * c + 0] = t4.x; qr[4 * c + 1] = t4.y; qr[4 * c + 2] = t4.z; qr[4 * c + 3] = t4.w;
                     dgl[4 * c + 0] = g4.x; dgl[4 * c + 1] = g4.y; dgl[4 * c + 2] = g4.z; dgl[4 * c + 3] = g4.w;
+                    dqo[4 * c + 0] = o4.x; dqo[4 * c + 1] = o4.y; dqo[4 * c + 2] = o4.z; dqo[4 * c + 3] = o4.w;
                 }
 #pragma unroll
-                for (int t = 0; t < KQ; t++) a[t] = phi(qr[t]);
+                for (int t = 0; t < KQ; t++) {
+                    a[t] = phi(qr[t]);
+                    pos |= (qr[t] > 0.f ? 1u : 0u) << t;
+                }
             } else {
 #pragma unroll
-                for (int t = 0; t < KQ; t++) qr[t] = a[t] = dgl[t] = 0.f;
+                for (int t = 0; t < KQ; t++) a[t] = dgl[t] = dqo[t] = 0.f;
             }
             float d = 0.f;
 #pragma unroll
@@ -562,17 +572,14 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             if (valid) {
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
-                    float4* p = reinterpret_cast<float4*>(dq + off + 4 * c);
-                    float4 o = *p;
                     float u[4];
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int idx = 4 * c + e;
                         const float gv = acc2[idx % TR][idx / TR] + zreg[idx] * dden;
-                        u[e] = gv * dphi(qr[idx], a[idx]);
+                        u[e] = dqo[idx] + gv * ((pos >> idx) & 1u ? 1.f : a[idx]);
                     }
-                    o.x += u[0]; o.y += u[1]; o.z += u[2]; o.w += u[3];
-                    *p = o;
+                    *reinterpret_cast<float4*>(dq + off + 4 * c) = make_float4(u[0], u[1], u[2], u[3]);
                 }
             }
 #pragma unroll
@@ -845,14 +852,20 @@ __global__ __launch_bounds__(256) void dkv_scalar(Seg sg, int32_t H, int32_t R, 
 
 // ---------------------------------------------------------------- host side
 
-// Rows per tile: a multiple of 16, at least 256, and large enough for at most 1024 tiles.
-int32_t tile_rows(int32_t n) {
-    int64_t per = ((int64_t)n + 1023) / 1024;
+// Rows per tile: a multiple of 16, at least 256, and large enough for at most 1024 / heads
+// tiles.  Every kernel here runs a workgroup per (tile, head), and each workgroup stages S
+// (and its transpose) and writes a partial of r x r + r sums besides its rows: about 1024
+// workgroups fill the chip, and longer tiles spread that fixed cost over more rows (at 4
+// heads of 64 and 2^18 rows, 256 tiles against 1024: forward 297 -> 248 us, backward
+// 780 -> 703 us; 128 tiles, 512 workgroups, left CUs idle: forward 404 us).
+int32_t tile_rows(int32_t n, int32_t heads) {
+    const int64_t cap = heads < 1024 ? 1024 / heads : 1;
+    int64_t per = ((int64_t)n + cap - 1) / cap;
     per = (per + 15) / 16 * 16;
     return (int32_t)(per < 256 ? 256 : per);
 }
 
-int64_t tile_count(int32_t n) { return n > 0 ? ((int64_t)n + tile_rows(n) - 1) / tile_rows(n) : 0; }
+int64_t tile_count(int32_t n, int32_t rs) { return n > 0 ? ((int64_t)n + rs - 1) / rs : 0; }
 
 struct GlWs {
     float* part;    // [2 * tiles][H][R*R + R] pieces of long graphs
@@ -864,7 +877,7 @@ struct GlWs {
 };
 
 GlWs carve_gl(void* ws, int32_t n, int32_t batch, int32_t H, int32_t R) {
-    const int64_t tiles = tile_count(n);
+    const int64_t tiles = tile_count(n, tile_rows(n, H));
     Carver c(ws);
     GlWs w;
     w.part = c.take<float>((size_t)(tiles > 0 ? 2 * tiles : 1) * H * (R * R + R));
@@ -877,7 +890,7 @@ GlWs carve_gl(void* ws, int32_t n, int32_t batch, int32_t H, int32_t R) {
 }
 
 void launch_list_and_reduce(const Seg& sg, int32_t H, int32_t R, const GlWs& w, float* s, float* z, hipStream_t st) {
-    const int64_t tiles = tile_count(sg.n);
+    const int64_t tiles = tile_count(sg.n, sg.rs);
     list_long<<<1, 1024, 0, st>>>(sg, tiles, w.list, w.count);
     const int64_t longest = tiles < sg.batch ? tiles : sg.batch;  // long graphs: at most one per tile
     const int64_t tot = (int64_t)H * (R * R + R);
@@ -907,7 +920,7 @@ int gl_fwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
         fill_f32(z, (int64_t)sg.batch * heads * r, 0.f, st);
     }
     if (sg.n == 0) return launch_status();
-    const int64_t tiles = tile_count(sg.n);
+    const int64_t tiles = tile_count(sg.n, sg.rs);
     const bool mfma = mfma_ok(r) && aligned16(q) && aligned16(k) && aligned16(v) && aligned16(g_out) &&
                       aligned16(s) && aligned16(z);
     const int wpb = heads < 8 ? heads : 8;  // wavefronts (heads) per workgroup
@@ -952,7 +965,7 @@ int gl_bwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
         fill_f32(w.s, (int64_t)sg.batch * heads * r * r, 0.f, st);
         fill_f32(w.z, (int64_t)sg.batch * heads * r, 0.f, st);
     }
-    const int64_t tiles = tile_count(sg.n);
+    const int64_t tiles = tile_count(sg.n, sg.rs);
     const bool mfma = mfma_ok(r) && aligned16(q) && aligned16(k) && aligned16(v) && aligned16(d_g) &&
                       aligned16(d_q) && aligned16(d_k) && aligned16(d_v);
     const dim3 ga((unsigned)tiles, (unsigned)heads);
@@ -982,7 +995,7 @@ int gl_bwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
     return launch_status();
 }
 
-Seg one_graph(int32_t n) { return Seg{nullptr, 1, n, tile_rows(n)}; }
+Seg one_graph(int32_t n, int32_t heads) { return Seg{nullptr, 1, n, tile_rows(n, heads)}; }
 
 }  // namespace
 }  // namespace gga
@@ -1001,7 +1014,7 @@ extern "C" int gga_global_linear_fwd(int32_t n, int32_t heads, int32_t r, const 
     if (r > 1024) return GGA_EUNSUPPORTED;
     if (heads > 65535) return GGA_ERANGE;
     if (n > 0 && (!q || !k || !v || !g_out)) return GGA_EINVAL;
-    return gl_fwd(one_graph(n), heads, r, q, k, v, eps, s_out, z_out, g_out, ws, ws_bytes, as_stream(stream));
+    return gl_fwd(one_graph(n, heads), heads, r, q, k, v, eps, s_out, z_out, g_out, ws, ws_bytes, as_stream(stream));
 }
 
 extern "C" size_t gga_global_linear_bwd_workspace(int32_t n, int32_t heads, int32_t r) {
@@ -1017,7 +1030,7 @@ extern "C" int gga_global_linear_bwd(int32_t n, int32_t heads, int32_t r, const 
     if (heads > 65535) return GGA_ERANGE;
     if (n == 0) return GGA_OK;
     if (!q || !k || !v || !s_in || !z_in || !d_g || !d_q || !d_k || !d_v) return GGA_EINVAL;
-    return gl_bwd(one_graph(n), heads, r, q, k, v, eps, s_in, z_in, d_g, d_q, d_k, d_v, ws, ws_bytes,
+    return gl_bwd(one_graph(n, heads), heads, r, q, k, v, eps, s_in, z_in, d_g, d_q, d_k, d_v, ws, ws_bytes,
                   as_stream(stream));
 }
 
@@ -1034,7 +1047,7 @@ extern "C" int gga_global_linear_batch_fwd(int32_t n, int32_t batch, const int32
     if (r > 1024) return GGA_EUNSUPPORTED;
     if (heads > 65535) return GGA_ERANGE;
     if (!node_ptr || (n > 0 && (!q || !k || !v || !g_out))) return GGA_EINVAL;
-    const Seg sg{node_ptr, batch, n, tile_rows(n)};
+    const Seg sg{node_ptr, batch, n, tile_rows(n, heads)};
     return gl_fwd(sg, heads, r, q, k, v, eps, s_out, z_out, g_out, ws, ws_bytes, as_stream(stream));
 }
 
@@ -1047,6 +1060,6 @@ extern "C" int gga_global_linear_batch_bwd(int32_t n, int32_t batch, const int32
     if (heads > 65535) return GGA_ERANGE;
     if (n == 0) return GGA_OK;
     if (!node_ptr || !q || !k || !v || !s_in || !z_in || !d_g || !d_q || !d_k || !d_v) return GGA_EINVAL;
-    const Seg sg{node_ptr, batch, n, tile_rows(n)};
+    const Seg sg{node_ptr, batch, n, tile_rows(n, heads)};
     return gl_bwd(sg, heads, r, q, k, v, eps, s_in, z_in, d_g, d_q, d_k, d_v, ws, ws_bytes, as_stream(stream));
 }

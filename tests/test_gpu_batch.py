@@ -39,6 +39,9 @@ BATCHES = {
     "ragged": (1, 0, 17, 300, 4096, 2, 1000, 0, 2500, 63),
     "tiny": tuple((np.arange(700) % 5 + 1).tolist()),  # 700 graphs of 1-5 nodes
     "long": (5000, 3, 7000, 256, 257, 512),  # tile-boundary sizes for 256-row tiles
+    # 104,779 rows: tiles longer than 256 rows (416 at 4 heads, 320 at 3), graphs longer than
+    # one tile starting inside tiles
+    "long_tiles": (40000, 593, 1, 30000, 1185, 0, 33000),
     "one": (3000,),
     "empty_tail": (40, 0, 0),
 }

@@ -71,7 +71,9 @@ def test_linear_deterministic(g):
 
 
 @pytest.mark.parametrize("n,h,r", [(1, 1, 16), (1000, 2, 16), (5000, 4, 64), (3001, 3, 32), (777, 2, 48),
-                                   (500, 2, 5), (20000, 1, 8)])
+                                   (500, 2, 5), (20000, 1, 8),
+                                   # tiles longer than 256 rows: 592 at 4 heads, 272 at one head
+                                   (150001, 4, 64), (270001, 1, 16)])
 def test_global_linear(g, n, h, r):
     print(f"global n={n} h={h} r={r}", flush=True)
     rng = np.random.default_rng(n + r)

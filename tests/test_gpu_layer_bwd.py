@@ -86,7 +86,8 @@ def test_gated_combine_bwd_in_place(g):
 
 
 @pytest.mark.parametrize("n,heads,r", [(1000, 4, 64), (997, 2, 48), (500, 8, 32), (77, 3, 16), (1, 1, 64),
-                                       (600, 2, 24), (40, 5, 8), (300, 1, 64 - 1)])
+                                       (600, 2, 24), (40, 5, 8), (300, 1, 64 - 1),
+                                       (150001, 4, 64)])  # 592-row tiles, a ragged last one
 def test_global_linear_bwd(g, n, heads, r):
     q, k, v = _rand((n, heads, r), 20), _rand((n, heads, r), 21), _rand((n, heads, r), 22)
     d_g = _rand((n, heads, r), 23)
