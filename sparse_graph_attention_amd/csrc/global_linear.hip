@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
         for (int t = 0; t < KQ; t++) dzacc[t] = 0.f;
 
         const int64_t ntile = (r1 - r0 + 15) / 16;
-        const int64_t iters = (ntile + 3) / 4;  // the same for every wavefront (block barriers below)
+        const int64_t iters = (ntile + 3) / 4;
         for (int64_t it = 0; it < iters; it++) {
             const int64_t tl = it * 4 + wave;
             const int64_t row = r0 + tl * 16 + li;
@@ -594,7 +594,7 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
                 *reinterpret_cast<float4*>(dw + li * R + gq * KQ + 4 * c) =
                     make_float4(dn[4 * c], dn[4 * c + 1], dn[4 * c + 2], dn[4 * c + 3]);
             }
-            __syncthreads();
+            wave_lds_sync();  // pq[wave], dn_l[wave] belong to this wavefront alone
 #pragma unroll
             for (int u = 0; u < 4; u++) {
                 float pa[TR], pb[TR];
@@ -606,8 +606,9 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
                     for (int j = 0; j < TR; j++)
                         dsacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[i], pb[j], dsacc[i][j], 0, 0, 0);
             }
-            __syncthreads();
+            wave_lds_sync();  // read before the next tile overwrites them
         }
+        __syncthreads();  // every wavefront is done reading sl, st before they take the sums
         // dz over the 16 rows of the lane group
 #pragma unroll
         for (int t = 0; t < KQ; t++) {
