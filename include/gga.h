@@ -246,6 +246,9 @@ int gga_gat_coef_bwd(int32_t n, int32_t heads, int32_t head_dim, const float *hf
  * Mathematical statement; Tinymesh "Composition").  bias may be NULL.  When
  * the output is small and k long, k is split into a fixed number of ranges
  * whose partial products (in `ws`) are added in range order: deterministic.
+ * For a tall a times a small b stored [n,k] (trans_b), b is first transposed
+ * into `ws` (same results).  gga_linear_workspace does not know the transposes
+ * and returns enough for either use.
  */
 size_t gga_linear_workspace(int32_t m, int32_t k, int32_t n);
 int gga_linear(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float *a, const float *b,

@@ -459,6 +459,24 @@ __global__ __launch_bounds__(kBigThreads, (BigCfg<AKM, BKM>::per_cu)) void gemm_
     }
 }
 
+// dst[c][r] = src[r][c] for a rows x cols matrix, through a 32 x 32 LDS tile padded by one
+// column (the column reads of the second half then hit distinct banks).
+__global__ __launch_bounds__(256) void transpose_f32(const float* __restrict__ src, int32_t rows, int32_t cols,
+                                                     float* __restrict__ dst) {
+    __shared__ float t[32][33];
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const int64_t c0 = (int64_t)blockIdx.x * 32, r0 = (int64_t)blockIdx.y * 32;
+    for (int i = ty; i < 32; i += 8) {
+        const int64_t r = r0 + i, c = c0 + tx;
+        if (r < rows && c < cols) t[i][tx] = src[r * cols + c];
+    }
+    __syncthreads();
+    for (int i = ty; i < 32; i += 8) {
+        const int64_t c = c0 + i, r = r0 + tx;
+        if (c < cols && r < rows) dst[c * rows + r] = t[tx][i];
+    }
+}
+
 // c = (c if accumulating) + (sum over the splits of the partial products (in split order) + bias).  A workgroup of
 // 16 wavefronts owns 64 consecutive outputs: wavefront w adds splits w, w+16, ... and the
 // 16 running sums are then added in wavefront order.
@@ -883,6 +901,15 @@ Split pick_split(int32_t m, int32_t k, int32_t n) {
     return s;
 }
 
+// a b^T with a tall a and a small b (a layer's weight): b is first transposed into the
+// workspace and the product runs as a b, whose tile kernel keeps three workgroups on a CU
+// where a b^T's keeps two.  Both feed the matrix cores the same k order, so the results
+// are the same bits.
+bool tall_abt(int32_t m, int32_t k, int32_t n) {
+    return m >= 4096 && n > 64 && k >= 32 && (int64_t)k * n <= ((int64_t)1 << 22) && !narrow(k, n) &&
+           !stream_shape(m, k, n) && pick_split(m, k, n).splits == 1;
+}
+
 }  // namespace
 }  // namespace gga
 
@@ -895,6 +922,10 @@ extern "C" size_t gga_linear_workspace(int32_t m, int32_t k, int32_t n) {
     if (small_out_shape(m, k, n)) {  // (the choice also depends on the transposes)
         const size_t so = align_up((size_t)small_out_split(k).splits * m * n * sizeof(float), 256);
         need = so > need ? so : need;
+    }
+    if (tall_abt(m, k, n)) {  // (used only when b is transposed; the query does not know)
+        const size_t bt = align_up((size_t)k * n * sizeof(float), 256);
+        need = bt > need ? bt : need;
     }
     return need;
 }
@@ -983,6 +1014,12 @@ int linear_impl(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_
         return launch_status();
     }
     const Split sp = pick_split(m, k, n);
+    if (!trans_a && trans_b && tall_abt(m, k, n)) {
+        float* bt = static_cast<float*>(ws);  // b^T, [k][n]
+        transpose_f32<<<dim3((unsigned)((k + 31) / 32), (unsigned)((n + 31) / 32)), 256, 0, s>>>(b, n, k, bt);
+        b = bt;
+        trans_b = 0;
+    }
     GemmArgs g{};
     g.a = a;
     g.b = b;

@@ -34,6 +34,8 @@ def _t(a):
     (384, 96, 256, 0, 1, True), (129, 33, 132, 0, 0, True), (256, 70000, 192, 1, 0, True),
     # whole k stages with ragged m and n: the fast kernel takes the inner tiles, the guarded one the edges
     (1000, 256, 300, 0, 0, True), (1000, 256, 300, 0, 1, False), (1000, 256, 300, 1, 0, True), (1000, 256, 300, 1, 1, False),
+    # tall a times a small b stored [n, k]: b transposed into the workspace first
+    (5000, 256, 300, 0, 1, True), (4096, 300, 257, 0, 1, False), (8192, 512, 512, 0, 1, True),
     # skinny shapes: narrow contractions (k, n <= 64) and few outputs over a long k
     (100000, 16, 8, 0, 0, True), (50000, 8, 16, 0, 1, False), (3000, 64, 64, 1, 0, True), (5, 1, 1, 0, 0, False),
     (16, 300000, 8, 1, 0, False), (32, 20000, 32, 1, 1, True), (3, 5000, 2, 0, 0, False),

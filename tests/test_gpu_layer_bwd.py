@@ -116,6 +116,7 @@ def test_global_linear_bwd(g, n, heads, r):
                                          (512, 256, 256, False, False), (512, 256, 384, False, True),
                                          (64, 262144 // 16, 256, True, False), (1, 7, 3, False, False),
                                          (5003, 64, 128, False, True), (2049, 128, 64, False, False),
+                                         (5000, 256, 300, False, True), (4096, 300, 257, False, True),
                                          (128, 40000, 128, True, False)])
 def test_linear_accumulate(g, m, k, n, ta, tb):
     a = _rand((k, m) if ta else (m, k), 40)
