@@ -28,17 +28,6 @@ def i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
 
 
-def sample_rows(row_ptr: np.ndarray, k: int, seed: int):
-    """k random rows plus the 8 longest rows and up to 4 empty rows."""
-    n = row_ptr.shape[0] - 1
-    deg = np.diff(row_ptr)
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(n, size=min(k, n), replace=False).tolist())
-    rows.update(np.argsort(deg)[-8:].tolist())
-    rows.update(np.nonzero(deg == 0)[0][:4].tolist())
-    return np.array(sorted(rows), np.int32)
-
-
 def assert_close(got, want, dtype: str, what: str, atol=None, rtol=None):
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)

@@ -8,9 +8,11 @@ import torch
 
 import oracle
 import synth
-from gpu_util import assert_close, i32
+from gpu_util import TOL, assert_close, i32
 
 pytestmark = pytest.mark.gpu
+
+TOL_F32_ATOL = TOL["f32"]["atol"]
 
 
 @pytest.fixture(scope="module")
@@ -141,33 +143,36 @@ def test_gat_workload_full(g, layers):
     # LeakyReLU has a kink at z = 0: where an edge logit z = s_src[u] + s_dst[v] lies within
     # the fp32 rounding of the GPU's logits (|z| < 1e-5; the coefficients are fp32 sums of
     # 128- and 8-term products of magnitude < 2), fp32 and fp64 may take different one-sided
-    # derivatives (1 or 0.2), both valid.  Such edges change ds_e and with it the gradient
-    # rows of their two endpoints; every other row must match at the standard tolerance,
-    # and any row outside it must be such an endpoint.
+    # derivatives (1 or 0.2), both valid.  The largest possible effect of that choice follows
+    # from oracle quantities alone: at a kink edge e (u -> v, head h) the two derivatives
+    # differ by 0.8 * |ds_e| in d s_src[u,h] and in d s_dst[v,h]; these enter dH[u] through
+    # a_s, dH[v] through a_t, then dX = dH W^T and dW = X^T dH, and da_s / da_t through
+    # hf[u] / hf[v].  That bound is added to the standard tolerance of the elements it can
+    # reach; every element of every output is compared.
     z = rf["s_src"][src] + rf["s_dst"][dst]
-    amb = np.nonzero((np.abs(z) < 1e-5).any(axis=1))[0]
-    kink_nodes = np.unique(np.concatenate([src[amb], dst[amb]]))
-    print(f"edges at the kink: {amb.size}, endpoint rows excused: {kink_nodes.size}", flush=True)
-    # expected about E * H * 2e-5 * density(z = 0) ~ 4e2 edges: a small fraction of the rows
-    assert kink_nodes.size < n * 1e-2
-    dx = b["d_x"].cpu().numpy()
-    keep = np.ones(n, bool)
-    keep[kink_nodes] = False
-    assert_close(dx[keep], rb["d_x"][keep], "f32", "d_x")
-    # dW, da_s, da_t sum over every node, so they also carry the kink edges' one-sided
-    # choice.  Its largest possible effect follows from oracle quantities: at a kink edge e
-    # (u -> v, head h) the two derivatives differ by 0.8 * |ds_e| in d s_src[u,h] and in
-    # d s_dst[v,h]; these enter dH[u] through a_s, dH[v] through a_t, then X^T dH, and
-    # da_s / da_t through hf[u] / hf[v].  That bound is added to the tolerance.
     heads, c = a_s.shape
     eh, hh = np.nonzero(np.abs(z) < 1e-5)
     u, v = src[eh], dst[eh]
     zz = z[eh, hh]
+    print(f"(edge, head) pairs at the kink: {eh.size}, endpoint rows: {np.unique(np.concatenate([u, v])).size}",
+          flush=True)
+    # expected about E * H * 2e-5 * density(z = 0) ~ 4e2 pairs: a small fraction of the rows
+    assert eh.size < n * 1e-2
     d3 = d_out.reshape(n, heads, c).astype(np.float64)
     dd = oracle.local_bwd_add(rf["s_src"], rf["s_dst"], rf["hf"], d3, og)["D"]
     alpha = np.exp(np.where(zz > 0, zz, 0.2 * zz) - rf["lse"][v, hh])
     ds = alpha * ((d3[v, hh] * rf["hf"][u, hh]).sum(-1) - dd[v, hh])
     delta = 0.8 * np.abs(ds)
+    w3 = np.abs(wt.astype(np.float64)).reshape(x.shape[1], heads, c)
+    # |W[:, h, :]| |a_s[h]| and |W[:, h, :]| |a_t[h]|: [fin, heads]
+    wa_s = np.einsum("ihc,hc->ih", w3, np.abs(a_s.astype(np.float64)))
+    wa_t = np.einsum("ihc,hc->ih", w3, np.abs(a_t.astype(np.float64)))
+    kb_x = np.zeros((n, x.shape[1]))
+    np.add.at(kb_x, u, delta[:, None] * wa_s[:, hh].T)
+    np.add.at(kb_x, v, delta[:, None] * wa_t[:, hh].T)
+    tol_x = TOL_F32_ATOL + kb_x
+    print(f"dX elements with a kink allowance: {(kb_x > 0).sum()} of {kb_x.size}", flush=True)
+    assert_close(b["d_x"].cpu().numpy(), rb["d_x"], "f32", "d_x", atol=tol_x)
     kb_w = np.zeros((x.shape[1], heads, c))
     kb_as = np.zeros((heads, c))
     kb_at = np.zeros((heads, c))

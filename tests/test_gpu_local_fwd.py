@@ -5,7 +5,7 @@ slots per lane, 1..64 lanes per head), both score modes, and every degree bucket
 (light rows, workgroup rows, rows split into merged chunks, isolated rows), with the
 stated tolerances (fp32: 1e-5 abs + 1e-4 rel; bf16 inputs: 2e-2 rel).  The full
 workloads run in the launch configuration the benchmark times and are compared on
-sampled rows (random rows, the longest rows, empty rows)."""
+every row."""
 
 import numpy as np
 import pytest
@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import assert_close, i32, node_pair, sample_rows
+from gpu_util import assert_close, i32, node_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,7 @@ def test_fwd_deterministic(g):
 # --------------------------------------------------------------------------- full workloads
 
 
-def _workload_dot(g, ident, k_rows):
+def _workload_dot(g, ident):
     w = synth.WORKLOADS[ident]
     n, heads, c = w.n, w.heads, w.head_dim
     src, dst = synth.workload_graph(ident)
@@ -138,22 +138,19 @@ def _workload_dot(g, ident, k_rows):
     out, lse = g.gga_local_attn_fwd(desc, qd, kd, vd, topo.row_ptr, topo.col, topo.plan)
     torch.cuda.synchronize()
     og = oracle.Graph(n, src, dst)
-    rows = sample_rows(og.row_ptr, k_rows, ident) if k_rows else None
-    ref_out, ref_lse = oracle.local_fwd_dot(qh, kh, vh, og, c ** -0.5, rows=rows)
+    ref_out, ref_lse = oracle.local_fwd_dot(qh, kh, vh, og, c ** -0.5)
     out, lse = out.cpu().numpy(), lse.cpu().numpy()
-    if rows is not None:
-        out, lse = out[rows], lse[rows]
     assert_close(out, ref_out, w.dtype, "out")
     assert_close(lse, ref_lse, w.dtype, "lse")
 
 
 def test_workload_tiny_full(g):
-    _workload_dot(g, 1, 0)
+    _workload_dot(g, 1)
 
 
-def test_workload_1m_sampled(g):
-    _workload_dot(g, 3, 3000)
+def test_workload_1m_full(g):
+    _workload_dot(g, 3)
 
 
-def test_workload_heavy_tail_sampled(g):
-    _workload_dot(g, 5, 2000)
+def test_workload_heavy_tail_full(g):
+    _workload_dot(g, 5)
