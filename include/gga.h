@@ -100,6 +100,19 @@ size_t gga_plan_workspace(int32_t n, int64_t e);
 int gga_plan_build(int32_t n, int64_t e, const int32_t *row_ptr, void *plan, size_t plan_bytes, void *ws,
                    size_t ws_bytes, void *stream);
 
+/*
+ * The plan records the n and e it was built for.  No topology is changed behind
+ * the caller's back (Tinymesh "Sparse attention experiment", section "Reference
+ * contract"): a row of row_ptr outside [0, e] (or rows that together overflow the
+ * tables sized for e edges) marks the plan invalid at build time, and a kernel
+ * handed a plan built for another n or e, or an invalid one, processes no row and
+ * writes nothing (its outputs keep their contents) and marks the plan as misused.
+ * gga_plan_status writes to the device int *d_status, in stream order: GGA_OK,
+ * GGA_ERANGE (row_ptr inconsistent with e) or GGA_EINVAL (not a plan for this n
+ * and e, or misused by an earlier call).  The caller reads it when it chooses.
+ */
+int gga_plan_status(const void *plan, int32_t n, int64_t e, int32_t *d_status, void *stream);
+
 /* Shape and mode of a local attention call. */
 typedef struct gga_local_desc {
     int32_t n;            /* nodes */

@@ -58,6 +58,7 @@ def _load() -> ctypes.CDLL:
         "gga_plan_bytes": ([i32, i64], sz),
         "gga_plan_workspace": ([i32, i64], sz),
         "gga_plan_build": ([i32, i64, P, P, sz, P, sz, P], ctypes.c_int),
+        "gga_plan_status": ([P, i32, i64, P, P], ctypes.c_int),
         "gga_local_attn_fwd_workspace": ([D], sz),
         "gga_local_attn_fwd": ([D, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_local_attn_bwd_workspace": ([D], sz),
@@ -192,6 +193,13 @@ def gga_plan_build(n: int, e: int, row_ptr: torch.Tensor, plan=None, ws=None, st
     _check("gga_plan_build", lib.gga_plan_build(n, e, _ptr(row_ptr), _ptr(plan), plan.numel(), _ptr(ws), wb,
                                                 _stream(stream)))
     return plan
+
+
+def gga_plan_status(plan: torch.Tensor, n: int, e: int, stream=None) -> torch.Tensor:
+    """Device int32 [1]: the plan's status for (n, e) (GGA_OK, GGA_ERANGE or GGA_EINVAL)."""
+    st = torch.empty(1, dtype=torch.int32, device=plan.device)
+    _check("gga_plan_status", lib.gga_plan_status(_ptr(plan), n, e, _ptr(st), _stream(stream)))
+    return st
 
 
 class Topology:

@@ -97,9 +97,9 @@ int bwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
     p.d_v = d_v;
     p.D = w.D;
     p.a = BwdCsr{row_ptr, col, pa.hdr, pa.light, pa.chunks, pa.heavy, w.part_a, w.stride_a,
-                 d->e > kLightEdges ? (int32_t)cb : 0};
+                 d->e > kLightEdges ? (int32_t)cb : 0, d->n, (int32_t)d->e};
     p.b = BwdCsr{row_ptr_s, col_s, pb.hdr, pb.light, pb.chunks, pb.heavy, w.part_b, w.stride_b,
-                 d->e > kLightEdges ? (int32_t)cb : 0};
+                 d->e > kLightEdges ? (int32_t)cb : 0, ns, (int32_t)d->e};
     p.n = d->n;
     p.H = d->heads;
     p.C = d->head_dim;

@@ -31,6 +31,7 @@ struct BwdCsr {
     float* part;
     int32_t part_stride;
     int32_t chunk_blocks;
+    int32_t rows, edges;  // sizes the plan must have been built for
 };
 
 struct BwdParams {
@@ -534,6 +535,7 @@ template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dst_kernel(BwdParams p) {
     using Row = PassA<T, EPL, HDP, NS, MODE, UMAX>;
     constexpr int kA = Row::kAcc;
+    if (!plan_usable(p.a.hdr, p.a.rows, p.a.edges)) return;
     Row r;
     r.init(p);
     const int wave = threadIdx.x >> 6;
@@ -604,6 +606,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_src_kernel(BwdParams p) {
     using Row = PassB<T, EPL, HDP, NS, MODE>;
     constexpr int kA = Row::kAcc;
     constexpr int kF = NS * (kA + EPL);
+    if (!plan_usable(p.b.hdr, p.b.rows, p.b.edges)) return;
     Row r;
     r.init(p);
     const int wave = threadIdx.x >> 6;
@@ -680,6 +683,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_src_kernel(BwdParams p) {
 // the 8-aligned offset) go to out_b.
 static __global__ __launch_bounds__(kBwdThreads) void bwd_merge(BwdCsr c, int width, float* out_a, int width_b,
                                                          float* out_b) {
+    if (!plan_usable(c.hdr, c.rows, c.edges)) return;
     const int lane = threadIdx.x & 63;
     const int nh = c.hdr->n_heavy;
     const int off_b = (width + 7) & ~7;

@@ -34,6 +34,7 @@ struct FwdParams {
     float* lse;
     float* part;
     int32_t n, H, C, W;
+    int32_t e;  // edges the plan must have been built for
     int32_t lpr_log2;
     int32_t part_stride;
     float score_mul;
@@ -313,6 +314,7 @@ struct FwdRow {
 template <typename T, int EPL, int HDP, int NS, int MODE, int UMAX>
 __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
     using Row = FwdRow<T, EPL, HDP, NS, MODE, UMAX>;
+    if (!plan_usable(p.hdr, p.n, p.e)) return;
     Row r;
     r.geometry(p);
     const int wave = threadIdx.x >> 6;
@@ -406,6 +408,7 @@ __global__ __launch_bounds__(kFwdThreads) void local_fwd_kernel(FwdParams p) {
 constexpr int kMergeBatch = 8, kMergeCols = 4;
 
 __global__ __launch_bounds__(kFwdThreads) void local_fwd_merge(FwdParams p) {
+    if (!plan_usable(p.hdr, p.n, p.e)) return;
     const int lane = threadIdx.x & 63;
     const int nh = p.hdr->n_heavy;
     for (int hr = blockIdx.x * kFwdWaves + (threadIdx.x >> 6); hr < nh; hr += gridDim.x * kFwdWaves) {
@@ -559,6 +562,7 @@ int fwd_impl(const gga_local_desc* d, const void* qs, const void* ks, const void
     p.se = se;
     p.eid = eid;
     p.n = d->n;
+    p.e = (int32_t)d->e;
     p.H = d->heads;
     p.C = d->head_dim;
     p.W = d->heads * d->head_dim;

@@ -44,10 +44,17 @@ __global__ void plan_classify(const int32_t* __restrict__ row_ptr, int32_t n, in
     }
 }
 
-__global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, const int32_t* a, const int32_t* b,
-                          const int32_t* c, const int32_t* d, PlanView pv) {
+// Writes each row's entries.  A row outside [0, e], or entries past the tables sized for e
+// edges (rows that overlap add up to more than e), are not written: the plan's status
+// becomes GGA_ERANGE and every kernel then reads it as empty.
+__global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, int64_t e, PlanBounds bnd, const int32_t* a,
+                          const int32_t* b, const int32_t* c, const int32_t* d, PlanView pv) {
     for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < n; v += (int64_t)gridDim.x * blockDim.x) {
         const int32_t beg = row_ptr[v], end = row_ptr[v + 1];
+        if (beg < 0 || end < beg || (int64_t)end > e) {
+            pv.hdr->status = GGA_ERANGE;
+            continue;
+        }
         const int32_t deg = end - beg;
         if (deg <= kLightEdges) {
             pv.light[a[v]] = make_int4((int32_t)v, beg, end, 0);
@@ -55,6 +62,11 @@ __global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, const 
         }
         const int32_t chunks = (deg + kChunkEdges - 1) / kChunkEdges;
         const bool heavy = chunks > 1;
+        if ((int64_t)b[v] + chunks > bnd.max_chunks ||
+            (heavy && ((int64_t)d[v] >= bnd.max_heavy || (int64_t)c[v] + chunks > bnd.max_slots))) {
+            pv.hdr->status = GGA_ERANGE;
+            continue;
+        }
         for (int32_t k = 0; k < chunks; k++) {
             const int32_t cb = beg + k * kChunkEdges;
             const int32_t ce = (end - cb) < kChunkEdges ? end : cb + kChunkEdges;
@@ -64,8 +76,9 @@ __global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, const 
     }
 }
 
-__global__ void plan_header(PlanHeader* hdr, int32_t n) {
+__global__ void plan_header(PlanHeader* hdr, int32_t n, int64_t e) {
     hdr->n = n;
+    hdr->e = (int32_t)e;
     hdr->light_edges = kLightEdges;
     hdr->chunk_edges = kChunkEdges;
     hdr->magic = kPlanMagic;
@@ -109,7 +122,7 @@ extern "C" int gga_plan_build(int32_t n, int64_t e, const int32_t* row_ptr, void
     hipStream_t s = as_stream(stream);
     int32_t* hdr_i = reinterpret_cast<int32_t*>(pv.hdr);
     fill_i32(hdr_i, sizeof(PlanHeader) / 4, 0, s);
-    plan_header<<<1, 1, 0, s>>>(pv.hdr, n);
+    plan_header<<<1, 1, 0, s>>>(pv.hdr, n, e);
     if (n == 0) return launch_status();
     plan_classify<<<grid_for(n), 256, 0, s>>>(row_ptr, n, w.a, w.b, w.c, w.d, w.e);
     exclusive_scan_i32(w.a, w.a, n, &pv.hdr->n_light, w.scan, s);
@@ -117,6 +130,30 @@ extern "C" int gga_plan_build(int32_t n, int64_t e, const int32_t* row_ptr, void
     exclusive_scan_i32(w.c, w.c, n, &pv.hdr->n_slots, w.scan, s);
     exclusive_scan_i32(w.d, w.d, n, &pv.hdr->n_heavy, w.scan, s);
     exclusive_scan_i32(w.e, w.e, n, &pv.hdr->light_sum, w.scan, s);
-    plan_fill<<<grid_for(n), 256, 0, s>>>(row_ptr, n, w.a, w.b, w.c, w.d, pv);
+    plan_fill<<<grid_for(n), 256, 0, s>>>(row_ptr, n, e, plan_bounds(e), w.a, w.b, w.c, w.d, pv);
+    return launch_status();
+}
+
+namespace gga {
+namespace {
+
+__global__ void plan_status_kernel(const PlanHeader* hdr, int32_t n, int64_t e, int32_t* out) {
+    int32_t st = GGA_OK;
+    if (hdr->magic != kPlanMagic || hdr->n != n || (int64_t)hdr->e != e)
+        st = GGA_EINVAL;
+    else if (hdr->status != 0)
+        st = hdr->status;
+    else if (hdr->misuse != 0)
+        st = GGA_EINVAL;
+    *out = st;
+}
+
+}  // namespace
+}  // namespace gga
+
+extern "C" int gga_plan_status(const void* plan, int32_t n, int64_t e, int32_t* d_status, void* stream) {
+    if (!plan || !d_status || n < 0 || e < 0) return GGA_EINVAL;
+    if (e >= (int64_t)INT32_MAX) return GGA_ERANGE;
+    plan_status_kernel<<<1, 1, 0, as_stream(stream)>>>(static_cast<const PlanHeader*>(plan), n, e, d_status);
     return launch_status();
 }

@@ -22,6 +22,9 @@ struct PlanHeader {
     int32_t chunk_edges;
     int32_t magic;
     int32_t light_sum;  // edges of the light rows together (their mean length picks a lane layout)
+    int32_t e;          // edges the plan was built for
+    int32_t status;     // 0, or GGA_ERANGE when a row of row_ptr lies outside [0, e] or the rows overflow e
+    int32_t misuse;     // set by a kernel handed this plan with other sizes than it was built for
 };
 
 constexpr int32_t kPlanMagic = 0x67676150;
@@ -46,6 +49,17 @@ struct PlanView {
     int4* heavy;     // [max_heavy]: row, first slot, slot count, 0
     size_t bytes;
 };
+
+// A kernel over `rows` rows and `edges` edges uses a plan only when it is a plan, built for
+// those sizes, from a row_ptr whose rows lie within [0, edges].  Any other plan reads as
+// empty: the kernel processes no row and writes nothing, so no table or column index is
+// read out of bounds; the first thread of the grid records the misuse in the plan.
+__device__ __forceinline__ bool plan_usable(const PlanHeader* h, int32_t rows, int64_t edges) {
+    const bool ok = h->magic == kPlanMagic && h->status == 0 && h->n == rows && (int64_t)h->e == edges;
+    if (!ok && blockIdx.x == 0 && threadIdx.x == 0 && h->magic == kPlanMagic)
+        const_cast<PlanHeader*>(h)->misuse = 1;
+    return ok;
+}
 
 inline PlanView plan_view(void* plan, int32_t n, int64_t e) {
     PlanBounds b = plan_bounds(e);

@@ -181,6 +181,10 @@ def test_csr_and_plan_checks():
     assert L.gga_coo_to_csr(100, 1000, a, a, a, a, a, a, need - 1, None) == 4
     pb = L.gga_plan_bytes(100, 1000)
     assert L.gga_plan_build(100, 1000, a, a, pb - 1, a, 1 << 30, None) == 4
+    assert L.gga_plan_status(None, 100, 1000, a, None) == 1
+    assert L.gga_plan_status(a, 100, 1000, None, None) == 1
+    assert L.gga_plan_status(a, -1, 1000, a, None) == 1
+    assert L.gga_plan_status(a, 100, 1 << 31, a, None) == 2
     assert L.gga_validate_coo(3, 4, None, a, a, None) == 1
 
 

@@ -84,3 +84,48 @@ def test_plan_counts(g):
     assert hdr[2] == (chunks > 1).sum()
     assert hdr[3] == chunks[chunks > 1].sum()
     assert hdr[8] == deg[deg <= 64].sum()  # edges of the light rows
+
+
+def test_plan_guard(g):
+    """A plan is used only for the n and e it was built for, from a row_ptr consistent with
+    e: otherwise the attention kernels process no row and write nothing (their outputs keep
+    what they held) and gga_plan_status reports it; a correct call afterwards still works."""
+    n, heads, c = 3000, 2, 16
+    src, dst = synth.mixed_degree_graph(n, 3, hubs=(5000, 1500, 100))
+    e = src.size
+    topo = g.Topology(n, i32(src), i32(dst), backward=True)
+    assert int(g.gga_plan_status(topo.plan, n, e).item()) == g.GGA_OK
+    assert int(g.gga_plan_status(topo.plan, n, e - 1).item()) == g.GGA_EINVAL
+    assert int(g.gga_plan_status(topo.plan, n + 1, e).item()) == g.GGA_EINVAL
+    rng = np.random.default_rng(4)
+    q, k, v = (torch.from_numpy(rng.standard_normal((n, heads, c)).astype(np.float32)).cuda() for _ in range(3))
+    good = g.make_desc(n, e, heads, c, g.GGA_SCORE_DOT, g.GGA_F32)
+    ref, ref_lse = g.gga_local_attn_fwd(good, q, k, v, topo.row_ptr, topo.col, topo.plan)
+    torch.cuda.synchronize()
+    # a plan built for e edges, handed a call over e - 7
+    wrong = g.make_desc(n, e - 7, heads, c, g.GGA_SCORE_DOT, g.GGA_F32)
+    out = torch.full((n, heads, c), 7.0, device="cuda")
+    lse = torch.full((n, heads), 7.0, device="cuda")
+    g.gga_local_attn_fwd(wrong, q, k, v, topo.row_ptr, topo.col, topo.plan, out=out, lse=lse)
+    d_out = torch.ones_like(out)
+    dq, dk, dv = (torch.full((n, heads, c), 7.0, device="cuda") for _ in range(3))
+    g.gga_local_attn_bwd(wrong, q, k, v, ref, ref_lse, d_out, topo, d_qs=dq, d_ks=dk, d_v=dv)
+    torch.cuda.synchronize()
+    for t in (out, lse, dq, dk, dv):
+        assert bool((t == 7.0).all())
+    assert int(g.gga_plan_status(topo.plan, n, e).item()) == g.GGA_EINVAL  # misuse recorded
+    again, again_lse = g.gga_local_attn_fwd(good, q, k, v, topo.row_ptr, topo.col, topo.plan)
+    torch.cuda.synchronize()
+    assert torch.equal(again, ref) and torch.equal(again_lse, ref_lse)
+    # a row_ptr whose rows run past e: the plan is marked invalid at build time
+    short = e - 100
+    bad_plan = g.gga_plan_build(n, short, topo.row_ptr)
+    assert int(g.gga_plan_status(bad_plan, n, short).item()) == g.GGA_ERANGE
+    d_short = g.make_desc(n, short, heads, c, g.GGA_SCORE_DOT, g.GGA_F32)
+    out.fill_(7.0)
+    g.gga_local_attn_fwd(d_short, q, k, v, topo.row_ptr, topo.col, bad_plan, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    # rows that overlap (row_ptr not monotone)
+    rp = i32(np.array([0, 100, 50, 150], np.int32))
+    assert int(g.gga_plan_status(g.gga_plan_build(3, 150, rp), 3, 150).item()) == g.GGA_ERANGE
