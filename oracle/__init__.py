@@ -24,27 +24,35 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "_oracle.so")
+# ORACLE_LIB names another build of oracle.c to load (the sanitizer test uses it)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "_oracle.so")
 _lib = None
+
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
 
 SLOPE = 0.2  # LeakyReLU negative slope of the GAT score
 LN_EPS = 1e-5
 GLOBAL_EPS = 1e-6
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc into _oracle.so."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+def build(force: bool = True, path: str | None = None, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc into _oracle.so (or `path`); with sanitize=True the host
+    code is built with AddressSanitizer and UndefinedBehaviorSanitizer."""
+    path = path or _LIB_PATH
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp"
+        opt = SANITIZE_FLAGS if sanitize else ["-O2"]
+        subprocess.check_call(["gcc", *opt, "-std=c11", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, path)
+    return path
 
 
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        stale = not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+        if stale and "ORACLE_LIB" not in os.environ:
             build()
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
