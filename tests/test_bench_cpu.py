@@ -51,3 +51,31 @@ def test_roofline_record():
     r = bench.roofline("hbm", 5000.0, 8000.0, "GB/s", traffic=39.86, kernel="k")
     assert r == {"bound": "hbm", "achieved": 5000.0, "peak": 8000.0, "unit": "GB/s", "frac": 0.625,
                  "traffic": 39.86, "kernel": "k"}
+
+
+def test_roofline_never_above_peak():
+    import pytest
+
+    import bench
+
+    with pytest.raises(ValueError):
+        bench.roofline("hbm", 8100.0, 8000.0, "GB/s")
+
+
+def test_counted_traffic_is_tied_to_its_profile_and_sources():
+    """Every counted figure names a committed profile summary that states it and the digest of
+    the kernel sources it was taken with; a changed kernel reports no counted figure."""
+    import bench
+
+    for key, c in bench.COUNTED.items():
+        if c["gb"] is None:
+            assert bench.counted_traffic(key) is None
+            continue
+        txt = open(os.path.join(ROOT, c["profile"])).read()
+        assert f"{c['gb']:.2f} GB" in txt, (key, c["profile"])
+        assert c["digest"] in txt, (key, c["profile"])
+        assert len(c["digest"]) == 16
+        if c["digest"] == bench.sources_digest(c["sources"]):
+            assert bench.counted_traffic(key) == c["gb"]
+        else:
+            assert bench.counted_traffic(key) is None
