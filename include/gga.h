@@ -30,7 +30,8 @@
  *   index ranges are not checked by the compute calls (they would need a device
  *   read): run gga_validate_coo on untrusted input first.  A HIP launch error is
  *   returned as GGA_EHIP.  n == 0 or E == 0 are valid and return GGA_OK.
- * Threads.  Calls are re-entrant; the library keeps no mutable global state.
+ * Threads.  Calls are re-entrant; the library keeps no mutable global state,
+ *   except the fixed scratch array of gga_local_attn_fwd_noalloc (see there).
  */
 #ifndef GGA_H
 #define GGA_H
@@ -51,6 +52,7 @@ extern "C" {
 #define GGA_EUNSUPPORTED 3 /* dtype, score mode or shape the library does not handle */
 #define GGA_EWORKSPACE 4   /* workspace or plan buffer smaller than its query says */
 #define GGA_EHIP 5         /* a HIP runtime call or kernel launch failed */
+#define GGA_ESCRATCH 6     /* gga_local_attn_fwd_noalloc: the input needs more than its fixed scratch */
 
 /* storage type of node tensors */
 #define GGA_F32 0
@@ -162,6 +164,24 @@ size_t gga_local_attn_fwd_workspace(const gga_local_desc *d);
 int gga_local_attn_fwd(const gga_local_desc *d, const void *qs, const void *ks, const void *v,
                        const int32_t *row_ptr, const int32_t *col, const void *plan, float *out, float *lse,
                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Allocation-free local attention forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and bits as gga_local_attn_fwd, with the
+ * partial softmax states of split rows kept in a fixed device array of 96 MiB that the
+ * library holds on each device it runs on until the process ends, instead of a caller
+ * workspace.  Nothing is allocated or freed; the caller passes inputs and outputs.
+ * Inputs whose gga_local_attn_fwd_workspace(d) exceeds 96 MiB are rejected with
+ * GGA_ESCRATCH before anything is enqueued (with rows of H*C = 512 values that allows
+ * about 24M edges, with 256 values about 47M).  The stream must belong to the current
+ * device.  Every call on a device shares that device's array, and nothing in it needs
+ * to start cleared: calls that overlap in time on one device (different streams, or
+ * different host threads) race on it and must be serialised by the caller.
+ */
+int gga_local_attn_fwd_noalloc(const gga_local_desc *d, const void *qs, const void *ks, const void *v,
+                               const int32_t *row_ptr, const int32_t *col, const void *plan, float *out,
+                               float *lse, void *stream);
 
 /*
  * Local attention backward: first-order gradients of sum(out * d_out), with the

@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgga.so")
 
-GGA_OK, GGA_EINVAL, GGA_ERANGE, GGA_EUNSUPPORTED, GGA_EWORKSPACE, GGA_EHIP = range(6)
+GGA_OK, GGA_EINVAL, GGA_ERANGE, GGA_EUNSUPPORTED, GGA_EWORKSPACE, GGA_EHIP, GGA_ESCRATCH = range(7)
 GGA_F32, GGA_BF16 = 0, 1
 GGA_SCORE_DOT, GGA_SCORE_ADDITIVE, GGA_SCORE_MEAN = 0, 1, 2
 
@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "gga_plan_status": ([P, i32, i64, P, P], ctypes.c_int),
         "gga_local_attn_fwd_workspace": ([D], sz),
         "gga_local_attn_fwd": ([D, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_local_attn_fwd_noalloc": ([D, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "gga_local_attn_bwd_workspace": ([D], sz),
         "gga_local_attn_bwd": ([D, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_edge_values": ([i32, i32, i32, P, i64, P, P, P], ctypes.c_int),
@@ -246,6 +247,15 @@ def gga_local_attn_fwd(desc: gga_local_desc, qs, ks, v, row_ptr, col, plan, out=
     _check("gga_local_attn_fwd", lib.gga_local_attn_fwd(ctypes.byref(desc), _ptr(qs), _ptr(ks), _ptr(v),
                                                         _ptr(row_ptr), _ptr(col), _ptr(plan), _ptr(out), _ptr(lse),
                                                         _ptr(ws), nb, _stream(stream)))
+    return out, lse
+
+
+def gga_local_attn_fwd_noalloc(desc: gga_local_desc, qs, ks, v, row_ptr, col, plan, out, lse=None, stream=None):
+    """The allocation-free forward: the caller passes out (and lse, or None); nothing is
+    allocated here or in the library (split-row partials use the library's fixed array)."""
+    _check("gga_local_attn_fwd_noalloc", lib.gga_local_attn_fwd_noalloc(
+        ctypes.byref(desc), _ptr(qs), _ptr(ks), _ptr(v), _ptr(row_ptr), _ptr(col), _ptr(plan), _ptr(out), _ptr(lse),
+        _stream(stream)))
     return out, lse
 
 

@@ -11,6 +11,7 @@ extern "C" const char* gga_status_string(int status) {
         case GGA_EUNSUPPORTED: return "unsupported dtype, mode or shape";
         case GGA_EWORKSPACE: return "workspace or plan buffer too small";
         case GGA_EHIP: return "HIP runtime error";
+        case GGA_ESCRATCH: return "input needs more scratch than the allocation-free entry point's fixed array";
         default: return "unknown status";
     }
 }

@@ -9,6 +9,9 @@
 // wavefront take different edges of the same row; their states are merged at the end.
 // Scores are kept in log2 units (the score multiplier includes log2(e)), so the
 // softmax uses exp2.  No floating-point atomics: every sum has a fixed order.
+#include <atomic>
+#include <mutex>
+
 #include "plan.hpp"
 #include "rowgeo.hpp"
 #include "shape.hpp"
@@ -611,6 +614,63 @@ extern "C" int gga_local_attn_fwd(const gga_local_desc* d, const void* qs, const
     if (st != GGA_OK) return st;
     if (d->n == 0) return GGA_OK;
     return fwd_impl(d, qs, ks, v, row_ptr, col, plan, out, lse, nullptr, nullptr, ws, ws_bytes, as_stream(stream));
+}
+
+// ---------------------------------------------------------------- allocation-free forward
+//
+// gga_local_attn_fwd_noalloc keeps the split-row partial states in `scratch`, a fixed
+// array of device memory that each device holds for the life of the process, instead of
+// a caller workspace.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the first call on a device looks up that device's
+// address of the array once, with the device current, and every later call on the device
+// uses the address it keeps.
+
+namespace gga {
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(96) << 20;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return GGA_EHIP;
+    if (dev < 0 || dev >= kMaxDevices) return GGA_EUNSUPPORTED;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GGA_EHIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return GGA_OK;
+}
+
+}  // namespace
+}  // namespace gga
+
+extern "C" int gga_local_attn_fwd_noalloc(const gga_local_desc* d, const void* qs, const void* ks, const void* v,
+                                          const int32_t* row_ptr, const int32_t* col, const void* plan, float* out,
+                                          float* lse, void* stream) {
+    int st = check_desc(d);
+    if (st != GGA_OK) return st;
+    // the partial states of every row split into chunks must fit the fixed array
+    const size_t need = fwd_part_bytes(d);
+    if (need > kNoAllocScratchBytes) return GGA_ESCRATCH;
+    if (d->n == 0) return GGA_OK;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != GGA_OK) return st;
+    return fwd_impl(d, qs, ks, v, row_ptr, col, plan, out, lse, nullptr, nullptr, ws, kNoAllocScratchBytes,
+                    as_stream(stream));
 }
 
 extern "C" size_t gga_local_attn_fwd_edge_workspace(const gga_local_desc* d) {

@@ -198,3 +198,15 @@ def test_workspaces_are_linear_not_quadratic():
         assert L.gga_plan_bytes(n, e) < 64 * (n + e)
         d = _desc(n=n, e=e, heads=8, head_dim=64, dtype=1)
         assert L.gga_local_attn_fwd_workspace(ctypes.byref(d)) < 8 * e * 8 * 64
+
+
+def test_noalloc_forward_refuses_inputs_beyond_its_scratch():
+    """The allocation-free forward checks its fixed scratch size on the host, before any
+    device work: a graph whose split-row partials would need more is refused."""
+    import sparse_graph_attention_amd as g
+
+    a = ctypes.c_void_p(4096)
+    d = _desc(n=1000, e=1 << 30, heads=8, head_dim=64, dtype=1)
+    assert g.lib.gga_local_attn_fwd_workspace(ctypes.byref(d)) > 96 << 20
+    assert g.lib.gga_local_attn_fwd_noalloc(ctypes.byref(d), a, a, a, a, a, a, a, a, None) == g.GGA_ESCRATCH
+    assert g.lib.gga_status_string(g.GGA_ESCRATCH) != g.lib.gga_status_string(99)
