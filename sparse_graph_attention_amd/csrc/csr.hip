@@ -1,25 +1,33 @@
-// COO -> CSR by key: a stable least-significant-digit radix sort of (key, COO index).
+// COO -> CSR by key: a stable least-significant-digit radix sort of (key, COO index,
+// other endpoint).
 //
-// Each pass sorts by 8 bits of the key.  A pass is stable by construction: a tile's
-// items are ranked in their original order (wave ballots give the rank among equal
-// digits inside a wave, per-wave counts in LDS order the waves, a running per-digit
-// count orders the rounds) and tiles are ordered by a digit-major exclusive scan of
-// per-tile histograms.  The result therefore equals a stable sort, independent of
-// scheduling: within a row the COO indices ascend, bit-exact across runs and devices.
-// Each tile's items are staged in LDS in digit order before they are written, so the
-// scatter writes contiguous runs.  row_ptr comes from the segment boundaries of the
-// sorted keys; no atomics take part in the build.
+// A build takes ceil(bits / 8) passes over the key bits (three for n <= 2^24), each sorting
+// by one digit of at most 8 bits.  A pass is stable by construction: each wavefront of a
+// tile ranks its own contiguous run of items in their original order (64 at a time, the
+// lanes with equal digits found by ballots, a per-digit running count in LDS carrying over
+// from one 64-item round to the next), the wavefronts' runs are placed in wavefront order
+// (per-digit counts of each wavefront, scanned in LDS), and tiles are ordered by a
+// digit-major exclusive scan of per-tile histograms.  The result therefore equals a stable
+// sort, independent of scheduling: within a row the COO indices ascend, bit-exact across
+// runs and devices.  The other endpoint travels with each item, so the last pass writes
+// col directly.  Each tile is staged in LDS in digit order before it is written, so the
+// scatter writes contiguous runs.  row_ptr comes from the segment boundaries of the sorted
+// keys; no atomics decide any position.
 #include "common.hpp"
 
 namespace gga {
 
 namespace {
 
-constexpr int kRsThreads = 256;
-constexpr int kRsItems = 16;
-constexpr int kRsTile = kRsThreads * kRsItems;  // 4096 edges per tile
-constexpr int kRsBins = 256;
-constexpr int kRsWaves = kRsThreads / 64;
+constexpr int kMaxDigitBits = 8;
+constexpr int kMaxBins = 1 << kMaxDigitBits;
+constexpr int kRsWaves = 4;
+constexpr int kRsThreads = 64 * kRsWaves;
+constexpr int kRsRounds = 16;                    // 64-item rounds per wavefront
+constexpr int kRsWaveItems = 64 * kRsRounds;     // a wavefront's contiguous run of a tile
+constexpr int kRsTile = kRsThreads * kRsRounds;  // 4096 edges per tile
+// digits per thread in the tile scan: whole words of two 16-bit counters
+constexpr int kDigitsPerThread = kMaxBins / kRsThreads < 2 ? 2 : kMaxBins / kRsThreads;
 
 __global__ void count_bad(const int32_t* __restrict__ a, const int32_t* __restrict__ b, int64_t e, int32_t n,
                           int32_t* __restrict__ bad) {
@@ -29,120 +37,256 @@ __global__ void count_bad(const int32_t* __restrict__ a, const int32_t* __restri
     if (local) atomicAdd(bad, local);
 }
 
-__global__ void radix_upsweep(const int32_t* __restrict__ keys, int64_t e, int shift, uint32_t mask,
-                              int32_t* __restrict__ hist, int64_t nblocks) {
-    __shared__ int cnt[kRsBins];
-    cnt[threadIdx.x] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kRsTile;
-#pragma unroll 4
-    for (int k = 0; k < kRsItems; k++) {
-        int64_t i = base + k * kRsThreads + threadIdx.x;
-        if (i < e) atomicAdd(&cnt[((uint32_t)keys[i] >> shift) & mask], 1);
-    }
-    __syncthreads();
-    hist[(int64_t)threadIdx.x * nblocks + blockIdx.x] = cnt[threadIdx.x];
+__device__ __forceinline__ uint32_t digit_of(int32_t key, int shift, uint32_t mask) {
+    return ((uint32_t)key >> shift) & mask;
 }
 
-// vals_in == nullptr means the identity (COO index).  `offsets` is the digit-major exclusive
-// scan of the per-tile digit counts (offsets[d * nblocks + b]); `total` = e.
-__global__ __launch_bounds__(kRsThreads) void radix_downsweep(const int32_t* __restrict__ keys_in,
-                                                              const int32_t* __restrict__ vals_in,
-                                                              int32_t* __restrict__ keys_out,
-                                                              int32_t* __restrict__ vals_out, int64_t e, int shift,
-                                                              int bits, const int32_t* __restrict__ offsets,
-                                                              int64_t nblocks) {
-    __shared__ int run[kRsBins];    // items of each digit placed so far in this tile
-    __shared__ int tdo[kRsBins];    // tile-local start of each digit
-    __shared__ int gbase[kRsBins];  // global start of each digit's run of this tile
-    __shared__ int wc[kRsWaves][kRsBins];
-    __shared__ int wtot[kRsWaves];
-    __shared__ int32_t skey[kRsTile];
-    __shared__ int32_t sval[kRsTile];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint32_t mask = (1u << bits) - 1u;
+// Lanes of the wavefront whose item is valid and has digit d (as this lane's).
+__device__ __forceinline__ uint64_t same_digit_lanes(uint32_t d, bool valid, int bits) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; b++) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+    }
+    return peers;
+}
+
+// Per-tile digit counts: hist[d * nblocks + tile].
+__global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __restrict__ keys, int64_t e, int shift,
+                                                            int bits, int32_t* __restrict__ hist, int64_t nblocks) {
+    __shared__ int cnt[kMaxBins];
+    const int bins = 1 << bits;
+    const uint32_t mask = (uint32_t)bins - 1u;
+    for (int d = threadIdx.x; d < bins; d += kRsThreads) cnt[d] = 0;
+    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kRsTile;
-    const int tile_n = (int)((e - base) < kRsTile ? (e - base) : kRsTile);
-    // this tile's count of digit tid, from the scan's neighbour (the scan is over a flat array)
-    const int64_t oi = (int64_t)tid * nblocks + blockIdx.x;
-    const int g0 = offsets[oi];
-    const int g1 = (oi + 1 < (int64_t)kRsBins * nblocks) ? offsets[oi + 1] : (int)e;
-    const int cnt = g1 - g0;
-    gbase[tid] = g0;
-    run[tid] = 0;
-    {  // exclusive scan of the tile counts over the digits
-        int x = cnt;
+    int32_t k[kRsRounds];
+#pragma unroll
+    for (int r = 0; r < kRsRounds; r++) {
+        const int64_t i = base + r * kRsThreads + threadIdx.x;
+        k[r] = i < e ? keys[i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kRsRounds; r++) {
+        const int64_t i = base + r * kRsThreads + threadIdx.x;
+        if (i < e) atomicAdd(&cnt[digit_of(k[r], shift, mask)], 1);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < bins; d += kRsThreads) hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
+}
+
+// A wavefront's items of one tile, in order: round r, lane l holds item wbase + 64 r + l.
+struct TileItems {
+    int32_t key[kRsRounds], val[kRsRounds], oth[kRsRounds];
+};
+
+struct RadixArgs {
+    const int32_t* keys_in;
+    const int32_t* vals_in;  // null in the first pass: the values are the COO indices
+    const int32_t* oth_in;
+    int32_t* keys_out;  // may be null (keys not needed after this pass)
+    int32_t* vals_out;
+    int32_t* oth_out;
+    const int32_t* offsets;  // digit-major exclusive scan of the per-tile digit counts
+    int64_t e, nblocks;
+    int shift, bits;
+};
+
+struct RadixSmem {
+    // a wavefront's 16-bit per-digit counts, then its next tile position per digit; digit d
+    // sits in half d & 1 of word d / 2 (positions stay below 2^16, so halves never carry)
+    uint32_t wpos[kRsWaves][kMaxBins / 2];
+    uint16_t tdo[kMaxBins];   // tile-local start of each digit
+    int32_t gbase[kMaxBins];  // global start of each digit's run of this tile
+    int32_t wtot[kRsWaves];
+    int32_t skey[kRsTile];
+    int32_t sval[kRsTile];
+    int32_t soth[kRsTile];
+};
+
+__device__ __forceinline__ int tile_size(const RadixArgs& a, int64_t tile) {
+    const int64_t rest = a.e - tile * kRsTile;
+    return (int)(rest < kRsTile ? rest : kRsTile);
+}
+
+template <bool FIRST>
+__device__ __forceinline__ void load_tile(const RadixArgs& a, int64_t tile, TileItems& it) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t base = tile * kRsTile;
+    const int tile_n = tile_size(a, tile);
+#pragma unroll
+    for (int r = 0; r < kRsRounds; r++) {
+        const int li = wave * kRsWaveItems + r * 64 + lane;
+        const bool valid = li < tile_n;
+        it.key[r] = valid ? a.keys_in[base + li] : 0;
+        it.oth[r] = valid ? a.oth_in[base + li] : 0;
+        if constexpr (FIRST)
+            it.val[r] = (int32_t)(base + li);
+        else
+            it.val[r] = valid ? a.vals_in[base + li] : 0;
+    }
+}
+
+// Sorts one tile's items stably by the digit (key >> shift) & (2^bits - 1) and writes them
+// to their places.
+__device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, const TileItems& it, RadixSmem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bits = a.bits, shift = a.shift;
+    const int bins = 1 << bits;
+    const int words = (bins + 1) / 2;
+    const uint32_t mask = (uint32_t)bins - 1u;
+    const int64_t base = tile * kRsTile;
+    const int tile_n = tile_size(a, tile);
+    const int wbase = wave * kRsWaveItems;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    for (int i = tid; i < kRsWaves * (kMaxBins / 2); i += kRsThreads) {
+        const int w = i / (kMaxBins / 2), x = i % (kMaxBins / 2);
+        if (x < words) sm.wpos[w][x] = 0;
+    }
+    __syncthreads();  // (also: the previous tile's scatter has read tdo, gbase and the staging)
+
+    // each wavefront counts its digits (additions commute: no ordering needed)
+#pragma unroll
+    for (int r = 0; r < kRsRounds; r++) {
+        const bool valid = wbase + r * 64 + lane < tile_n;
+        const uint32_t d = digit_of(it.key[r], shift, mask);
+        if (valid) atomicAdd(&sm.wpos[wave][d >> 1], 1u << (16 * (d & 1)));
+    }
+    __syncthreads();
+
+    // tile-local digit starts (scan over digits), each wavefront's start per digit (in
+    // wavefront order), and the global start of each digit's run of this tile.  A thread
+    // owns kDigitsPerThread consecutive digits, i.e. whole words of wpos.
+    {
+        int c[kDigitsPerThread];
+        int tot = 0;
+#pragma unroll
+        for (int j = 0; j < kDigitsPerThread; j++) {
+            const int d = tid * kDigitsPerThread + j;
+            c[j] = 0;
+            if (d < bins)
+                for (int w = 0; w < kRsWaves; w++) c[j] += (sm.wpos[w][d >> 1] >> (16 * (d & 1))) & 0xffffu;
+            tot += c[j];
+        }
+        int x = tot;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(x, off, 64);
             if (lane >= off) x += y;
         }
-        if (lane == 63) wtot[wave] = x;
+        if (lane == 63) sm.wtot[wave] = x;
         __syncthreads();
-        int before = 0;
-        for (int w = 0; w < wave; w++) before += wtot[w];
-        tdo[tid] = before + x - cnt;
-    }
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int r = 0; r < kRsItems; r++) {
-        const int li = r * kRsThreads + tid;
-        const bool valid = li < tile_n;
-        const int32_t key = valid ? keys_in[base + li] : 0;
-        const int32_t val = valid ? (vals_in ? vals_in[base + li] : (int32_t)(base + li)) : 0;
-        const uint32_t d = ((uint32_t)key >> shift) & mask;
+        int run = x - tot;
+        for (int w = 0; w < wave; w++) run += sm.wtot[w];
 #pragma unroll
-        for (int w = 0; w < kRsWaves; w++) wc[w][tid] = 0;
-        __syncthreads();
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < bits; b++) {
-            const bool bit = (d >> b) & 1u;
-            const uint64_t bb = __ballot(bit);
-            peers &= bit ? bb : ~bb;
+        for (int m = 0; m < kDigitsPerThread / 2; m++) {
+            const int d0 = tid * kDigitsPerThread + 2 * m;
+            if (d0 < bins) {
+                uint32_t s0 = (uint32_t)run, s1 = (uint32_t)(run + c[2 * m]);
+                sm.tdo[d0] = (uint16_t)s0;
+                sm.gbase[d0] = a.offsets[(int64_t)d0 * a.nblocks + tile];
+                if (d0 + 1 < bins) {
+                    sm.tdo[d0 + 1] = (uint16_t)s1;
+                    sm.gbase[d0 + 1] = a.offsets[(int64_t)(d0 + 1) * a.nblocks + tile];
+                }
+                for (int w = 0; w < kRsWaves; w++) {
+                    const uint32_t cw = sm.wpos[w][d0 >> 1];
+                    sm.wpos[w][d0 >> 1] = s0 | (s1 << 16);
+                    s0 += cw & 0xffffu;
+                    s1 += cw >> 16;
+                }
+            }
+            run += c[2 * m] + c[2 * m + 1];
         }
-        const int rank = __popcll(peers & lt);
-        if (valid && rank == 0) wc[wave][d] = __popcll(peers);
-        __syncthreads();
-        if (valid) {
-            int pos = tdo[d] + run[d] + rank;
-            for (int w = 0; w < wave; w++) pos += wc[w][d];
-            skey[pos] = key;
-            sval[pos] = val;
-        }
-        __syncthreads();
-        int add = 0;
-#pragma unroll
-        for (int w = 0; w < kRsWaves; w++) add += wc[w][tid];
-        run[tid] += add;
     }
     __syncthreads();
+
+    // each wavefront places its items in order.  Per round the lowest lane of each group of
+    // equal digits takes the group's places with one atomic add that returns the digit's
+    // next position; a wavefront's LDS operations complete in issue order, so the rounds'
+    // adds follow one another and every group lands after the earlier rounds' items of its
+    // digit.  The group's members take the returned start from their lowest lane.
+    // (in two halves of kRsRounds / 2 rounds, to bound the registers holding the returns)
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        constexpr int kHalf = kRsRounds / 2;
+        uint32_t got[kHalf], rl[kHalf];  // rl: rank in the group | lowest lane << 8
+#pragma unroll
+        for (int q = 0; q < kHalf; q++) {
+            const int r = h * kHalf + q;
+            const bool valid = wbase + r * 64 + lane < tile_n;
+            const uint32_t d = digit_of(it.key[r], shift, mask);
+            const uint64_t peers = same_digit_lanes(d, valid, bits);
+            const uint32_t rank = (uint32_t)__popcll(peers & below);
+            got[q] = 0;
+            rl[q] = rank | ((uint32_t)(valid ? __ffsll((unsigned long long)peers) - 1 : lane) << 8);
+            if (valid && rank == 0)
+                got[q] = atomicAdd(&sm.wpos[wave][d >> 1], (uint32_t)__popcll(peers) << (16 * (d & 1)));
+        }
+#pragma unroll
+        for (int q = 0; q < kHalf; q++) {
+            const int r = h * kHalf + q;
+            const bool valid = wbase + r * 64 + lane < tile_n;
+            const uint32_t d = digit_of(it.key[r], shift, mask);
+            const uint32_t w0 = (uint32_t)__shfl((int)got[q], (int)(rl[q] >> 8), 64);
+            if (valid) {
+                const int pos = (int)((w0 >> (16 * (d & 1))) & 0xffffu) + (int)(rl[q] & 0xffu);
+                sm.skey[pos] = it.key[r];
+                sm.sval[pos] = it.val[r];
+                sm.soth[pos] = it.oth[r];
+            }
+        }
+    }
+    __syncthreads();
+
     // the tile now sits in LDS in (digit, original order); write each digit's run contiguously
     for (int li = tid; li < tile_n; li += kRsThreads) {
-        const int32_t key = skey[li];
-        const uint32_t d = ((uint32_t)key >> shift) & mask;
-        const int pos = gbase[d] + (li - tdo[d]);
-        if (keys_out) keys_out[pos] = key;
-        vals_out[pos] = sval[li];
+        const int32_t k = sm.skey[li];
+        const uint32_t d = digit_of(k, shift, mask);
+        const int64_t pos = (int64_t)sm.gbase[d] + (li - (int)sm.tdo[d]);
+        if (a.keys_out) a.keys_out[pos] = k;
+        a.vals_out[pos] = sm.sval[li];
+        a.oth_out[pos] = sm.soth[li];
     }
+    (void)base;
+}
+
+// One pass: one workgroup per tile.
+template <bool FIRST>
+__global__ __launch_bounds__(kRsThreads) void radix_downsweep(RadixArgs a) {
+    __shared__ RadixSmem sm;
+    TileItems x;
+    load_tile<FIRST>(a, blockIdx.x, x);
+    sort_tile(a, blockIdx.x, x, sm);
 }
 
 // row_ptr from the sorted keys: row_ptr[v] = first position whose key is >= v.  Position p
 // writes the rows v in (key[p-1], key[p]] (clamped to [0, n]); every write is in bounds even
-// when keys are out of range.
+// when keys are out of range.  A thread takes kRowPtrItems consecutive positions.
+constexpr int kRowPtrItems = 4;
+
 __global__ void row_ptr_from_sorted(const int32_t* __restrict__ skeys, int64_t e, int32_t n,
                                     int32_t* __restrict__ row_ptr) {
-    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p <= e; p += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t kp = p > 0 ? (int64_t)skeys[p - 1] : -1;
-        const int64_t kc = p < e ? (int64_t)skeys[p] : (int64_t)n;
-        const int64_t lo = kp + 1 < 0 ? 0 : kp + 1;
-        const int64_t hi = kc < n ? kc : n;
-        for (int64_t v = lo; v <= hi; v++) row_ptr[v] = (int32_t)p;
+    const int64_t groups = (e + 1 + kRowPtrItems - 1) / kRowPtrItems;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < groups;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p0 = t * kRowPtrItems;
+        int64_t kp = p0 > 0 ? (int64_t)skeys[p0 - 1] : -1;
+        int64_t kc[kRowPtrItems];
+#pragma unroll
+        for (int j = 0; j < kRowPtrItems; j++) kc[j] = p0 + j < e ? (int64_t)skeys[p0 + j] : (int64_t)n;
+#pragma unroll
+        for (int j = 0; j < kRowPtrItems; j++) {
+            const int64_t p = p0 + j;
+            if (p > e) break;
+            const int64_t lo = kp + 1 < 0 ? 0 : kp + 1;
+            const int64_t hi = kc[j] < n ? kc[j] : n;
+            for (int64_t v = lo; v <= hi; v++) row_ptr[v] = (int32_t)p;
+            kp = kc[j];
+        }
     }
-}
-
-__global__ void gather_col(const int32_t* __restrict__ other, const int32_t* __restrict__ eid, int64_t e,
-                           int32_t* __restrict__ col) {
-    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < e; p += (int64_t)gridDim.x * blockDim.x)
-        col[p] = other[eid[p]];
 }
 
 // Packs per-graph local COO ids into the block-diagonal list over the packed node axis.
@@ -210,24 +354,40 @@ int key_bits(int32_t n) {
     return 32 - __builtin_clz(m);
 }
 
+// Digit width of each pass: the key bits split into ceil(bits / 8) passes of equal width
+// (the last one narrower when they do not divide).
+struct Passes {
+    int count, width;
+};
+
+Passes passes_for(int32_t n) {
+    const int bits = key_bits(n);
+    Passes p;
+    p.count = bits == 0 ? 1 : (bits + kMaxDigitBits - 1) / kMaxDigitBits;
+    p.width = bits == 0 ? 0 : (bits + p.count - 1) / p.count;
+    return p;
+}
+
 struct CsrWs {
     int32_t* hist;
     int32_t* scan;
-    int32_t* keys_tmp;
+    int32_t* keys_tmp[2];
     int32_t* vals_tmp;
+    int32_t* oth_tmp;
     size_t bytes;
 };
 
 CsrWs carve(void* ws, int32_t n, int64_t e) {
     Carver c(ws);
     CsrWs w;
-    int64_t nblocks = (e + kRsTile - 1) / kRsTile;
-    int64_t hist_n = (int64_t)kRsBins * nblocks;
+    const int64_t nblocks = (e + kRsTile - 1) / kRsTile;
+    const int64_t hist_n = ((int64_t)1 << passes_for(n).width) * nblocks;
     w.hist = c.take<int32_t>((size_t)hist_n);
-    size_t sc = scan_workspace_elems(hist_n > n ? hist_n : n);
-    w.scan = c.take<int32_t>(sc);
-    w.keys_tmp = c.take<int32_t>((size_t)e);
+    w.scan = c.take<int32_t>(scan_workspace_elems(hist_n > n ? hist_n : n));
+    w.keys_tmp[0] = c.take<int32_t>((size_t)e);
+    w.keys_tmp[1] = c.take<int32_t>((size_t)e);
     w.vals_tmp = c.take<int32_t>((size_t)e);
+    w.oth_tmp = c.take<int32_t>((size_t)e);
     w.bytes = c.bytes();
     return w;
 }
@@ -277,28 +437,34 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
     }
 
     const int64_t nblocks = (e + kRsTile - 1) / kRsTile;
+    const Passes ps = passes_for(n);
     const int bits_total = key_bits(n);
-    const int passes = bits_total == 0 ? 1 : (bits_total + 7) / 8;
-    const int last = passes - 1;
-    int32_t* kbuf[2] = {w.keys_tmp, col};  // col is free until the final gather
+    const int last = ps.count - 1;
+    // values end in eid and others in col after the last pass: alternate so that they do
     int32_t* vbuf[2];
+    int32_t* obuf[2];
     vbuf[last & 1] = eid;
     vbuf[(last & 1) ^ 1] = w.vals_tmp;
-    for (int p = 0; p < passes; p++) {
-        const int shift = 8 * p;
-        const int bits = bits_total == 0 ? 0 : ((bits_total - shift) < 8 ? (bits_total - shift) : 8);
-        const uint32_t mask = (1u << bits) - 1u;
-        const int32_t* kin = p == 0 ? key : kbuf[(p - 1) & 1];
+    obuf[last & 1] = col;
+    obuf[(last & 1) ^ 1] = w.oth_tmp;
+    for (int p = 0; p < ps.count; p++) {
+        const int shift = ps.width * p;
+        const int bits = (bits_total - shift) < ps.width ? (bits_total - shift) : ps.width;
+        const int32_t* kin = p == 0 ? key : w.keys_tmp[(p - 1) & 1];
         const int32_t* vin = p == 0 ? nullptr : vbuf[(p - 1) & 1];
-        int32_t* kout = kbuf[p & 1];
-        int32_t* vout = vbuf[p & 1];
-        radix_upsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, e, shift, mask, w.hist, nblocks);
-        exclusive_scan_i32(w.hist, w.hist, (int64_t)kRsBins * nblocks, nullptr, w.scan, s);
-        radix_downsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, vin, kout, vout, e, shift, bits, w.hist,
-                                                                  nblocks);
+        const int32_t* oin = p == 0 ? other : obuf[(p - 1) & 1];
+        int32_t* kout = w.keys_tmp[p & 1];
+        radix_upsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, e, shift, bits, w.hist, nblocks);
+        exclusive_scan_i32(w.hist, w.hist, ((int64_t)1 << bits) * nblocks, nullptr, w.scan, s);
+        RadixArgs a{kin, vin, oin, kout, vbuf[p & 1], obuf[p & 1], w.hist, e, nblocks, shift, bits};
+        if (p == 0)
+            radix_downsweep<true><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
+        else
+            radix_downsweep<false><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
     }
-    if (n > 0) row_ptr_from_sorted<<<grid_for(e + 1), 256, 0, s>>>(kbuf[last & 1], e, n, row_ptr);
-    gather_col<<<grid_for(e), 256, 0, s>>>(other, eid, e, col);
+    if (n > 0)
+        row_ptr_from_sorted<<<grid_for((e + kRowPtrItems) / kRowPtrItems), 256, 0, s>>>(w.keys_tmp[last & 1], e, n,
+                                                                                      row_ptr);
     return launch_status();
 }
 
