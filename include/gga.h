@@ -302,13 +302,31 @@ int gga_global_linear_fwd(int32_t n, int32_t heads, int32_t r, const float *q, c
                           void *stream);
 
 /*
+ * The layer's projections in one product ("Gated Local-Global Graph Attention",
+ * Mathematical statement: Q = X W_Q, K = X W_K, V = X W_V; Key formulas: the node gate
+ * g_i = sigmoid(x_i . w_g + b_g)):
+ *   [Q | K | V | gate_logit] = X [W_Q | W_K | W_V | w_g] + [0 | 0 | 0 | b_g]
+ * x fp32 [n,d]; w_q, w_k, w_v fp32 [d,d]; w_g fp32 [d]; q, k, v fp32 [n,d] (each its own
+ * tensor, viewed [n,H,d/H] by the attention calls); gate_logit fp32 [n] (before the
+ * sigmoid).  With d a multiple of 128 and 16-byte aligned rows this is one launch on the
+ * matrix cores that reads X once, the gate logit formed from the X rows the first column
+ * tile loads; otherwise three gga_linear products and a row kernel (same results up to
+ * fp32 summation order).  Workspace: gga_qkv_gate_proj_workspace (for the second path).
+ */
+size_t gga_qkv_gate_proj_workspace(int32_t n, int32_t d);
+int gga_qkv_gate_proj(int32_t n, int32_t d, const float *x, const float *w_q, const float *w_k, const float *w_v,
+                      const float *w_g, float b_g, float *q, float *k, float *v, float *gate_logit, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/*
  * Node gate and combination ("Gated Local-Global Graph Attention", Key formulas):
- *   gate[i] = sigmoid(x[i,:] . w_g + b_g)          (x fp32 [n,d], w_g fp32 [d])
+ *   gate[i] = sigmoid(gate_logit[i])                 (gate_logit fp32 [n], from
+ *                                                     gga_qkv_gate_proj: x_i . w_g + b_g)
  *   y[i,:] = gate[i] l[i,:] + (1 - gate[i]) g[i,:]   (l, g, y fp32 [n,width])
  * gate_out may be NULL.
  */
-int gga_gated_combine(int32_t n, int32_t d, const float *x, const float *w_g, float b_g, int32_t width,
-                      const float *l, const float *g, float *gate_out, float *y, void *stream);
+int gga_gated_combine(int32_t n, int32_t width, const float *gate_logit, const float *l, const float *g,
+                      float *gate_out, float *y, void *stream);
 
 /*
  * Residual and LayerNorm of the layer output ("Gated Local-Global Graph
@@ -332,6 +350,18 @@ int gga_add_layernorm(int32_t n, int32_t d, const float *x, const float *y, cons
  */
 int gga_linear_accumulate(int32_t m, int32_t k, int32_t n, int32_t trans_a, int32_t trans_b, const float *a,
                           const float *b, float *c, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The input gradient of the three projections in one product:
+ *   d_x += [d_q | d_k | d_v] [W_Q | W_K | W_V]^T = d_q W_Q^T + d_k W_K^T + d_v W_V^T
+ * d_q, d_k, d_v fp32 [n,d]; w_q, w_k, w_v fp32 [d,d]; d_x fp32 [n,d], added to.  With
+ * d % 4 == 0 and 16-byte aligned rows, one accumulating launch (the three W^T staged in
+ * the workspace, the k ranges taken in the order q, k, v); otherwise three
+ * gga_linear_accumulate calls in that order.  Workspace: gga_qkv_proj_bwd_x_workspace.
+ */
+size_t gga_qkv_proj_bwd_x_workspace(int32_t n, int32_t d);
+int gga_qkv_proj_bwd_x(int32_t n, int32_t d, const float *d_q, const float *d_k, const float *d_v, const float *w_q,
+                       const float *w_k, const float *w_v, float *d_x, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Backward of out = LayerNorm(x + y) over rows of width d (gga_add_layernorm):

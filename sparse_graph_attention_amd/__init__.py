@@ -73,7 +73,11 @@ def _load() -> ctypes.CDLL:
         "gga_linear": ([i32, i32, i32, i32, i32, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_global_linear_workspace": ([i32, i32, i32], sz),
         "gga_global_linear_fwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
-        "gga_gated_combine": ([i32, i32, P, P, f32, i32, P, P, P, P, P], ctypes.c_int),
+        "gga_gated_combine": ([i32, i32, P, P, P, P, P, P], ctypes.c_int),
+        "gga_qkv_gate_proj_workspace": ([i32, i32], sz),
+        "gga_qkv_gate_proj": ([i32, i32, P, P, P, P, P, f32, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_qkv_proj_bwd_x_workspace": ([i32, i32], sz),
+        "gga_qkv_proj_bwd_x": ([i32, i32, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_add_layernorm": ([i32, i32, P, P, P, P, f32, P, P], ctypes.c_int),
         "gga_linear_accumulate": ([i32, i32, i32, i32, i32, P, P, P, P, sz, P], ctypes.c_int),
         "gga_add_layernorm_bwd_workspace": ([i32, i32], sz),
@@ -356,13 +360,37 @@ def gga_global_linear_fwd(q, k, v, eps=1e-6, s_out=None, z_out=None, g_out=None,
     return s_out, z_out, g_out
 
 
-def gga_gated_combine(x, w_g, b_g: float, l, g, gate_out=None, y=None, stream=None):
+def gga_qkv_gate_proj(x, w_q, w_k, w_v, w_g, b_g: float, heads: int, ws=None, stream=None):
+    """Q, K, V ([n, heads, d/heads] each) and the gate logit [n] from one product."""
     n, d = x.shape
+    dev = x.device
+    q, k, v = (torch.empty(n, heads, d // heads, dtype=torch.float32, device=dev) for _ in range(3))
+    logit = torch.empty(n, dtype=torch.float32, device=dev)
+    nb = lib.gga_qkv_gate_proj_workspace(n, d)
+    ws = _workspace(nb, dev, ws)
+    _check("gga_qkv_gate_proj", lib.gga_qkv_gate_proj(n, d, _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_g),
+                                                      float(b_g), _ptr(q), _ptr(k), _ptr(v), _ptr(logit), _ptr(ws),
+                                                      nb, _stream(stream)))
+    return q, k, v, logit
+
+
+def gga_qkv_proj_bwd_x(d_q, d_k, d_v, w_q, w_k, w_v, d_x, ws=None, stream=None):
+    """d_x += d_q W_Q^T + d_k W_K^T + d_v W_V^T (d_q, d_k, d_v viewed [n, d])."""
+    n, d = d_x.shape
+    nb = lib.gga_qkv_proj_bwd_x_workspace(n, d)
+    ws = _workspace(nb, d_x.device, ws)
+    _check("gga_qkv_proj_bwd_x", lib.gga_qkv_proj_bwd_x(n, d, _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(w_q), _ptr(w_k),
+                                                        _ptr(w_v), _ptr(d_x), _ptr(ws), nb, _stream(stream)))
+    return d_x
+
+
+def gga_gated_combine(gate_logit, l, g, gate_out=None, y=None, stream=None):
+    n = gate_logit.shape[0]
     width = _row_width(l)
-    y = torch.empty(n, width, dtype=torch.float32, device=x.device) if y is None else y
-    gate_out = torch.empty(n, dtype=torch.float32, device=x.device) if gate_out is None else gate_out
-    _check("gga_gated_combine", lib.gga_gated_combine(n, d, _ptr(x), _ptr(w_g), float(b_g), width, _ptr(l), _ptr(g),
-                                                      _ptr(gate_out), _ptr(y), _stream(stream)))
+    y = torch.empty(n, width, dtype=torch.float32, device=l.device) if y is None else y
+    gate_out = torch.empty(n, dtype=torch.float32, device=l.device) if gate_out is None else gate_out
+    _check("gga_gated_combine", lib.gga_gated_combine(n, width, _ptr(gate_logit), _ptr(l), _ptr(g), _ptr(gate_out),
+                                                      _ptr(y), _stream(stream)))
     return gate_out, y
 
 

@@ -13,31 +13,15 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// gate[i] = sigmoid(x[i].w_g + b_g); y[i] = gate[i] l[i] + (1 - gate[i]) g[i]
-__global__ __launch_bounds__(256) void gated_combine_kernel(int32_t n, int32_t d, const float* __restrict__ x,
-                                                            const float* __restrict__ w_g, float b_g, int32_t width,
+// gate[i] = sigmoid(gate_logit[i]); y[i] = gate[i] l[i] + (1 - gate[i]) g[i]
+__global__ __launch_bounds__(256) void gated_combine_kernel(int32_t n, const float* __restrict__ logit, int32_t width,
                                                             const float* __restrict__ l,
                                                             const float* __restrict__ gg, float* __restrict__ gate,
                                                             float* __restrict__ y, int vec) {
     const int lane = threadIdx.x & 63;
     const int64_t i = blockIdx.x * 4ll + (threadIdx.x >> 6);
     if (i >= n) return;
-    float t = 0.f;
-    if (vec) {
-        const float4* xr = reinterpret_cast<const float4*>(x + i * d);
-        const float4* wr = reinterpret_cast<const float4*>(w_g);
-        for (int j = lane; j < d / 4; j += 64) {
-            const float4 a = xr[j], b = wr[j];
-            t = fmaf(a.x, b.x, t);
-            t = fmaf(a.y, b.y, t);
-            t = fmaf(a.z, b.z, t);
-            t = fmaf(a.w, b.w, t);
-        }
-    } else {
-        for (int j = lane; j < d; j += 64) t = fmaf(x[i * d + j], w_g[j], t);
-    }
-    t = wave_sum(t) + b_g;
-    const float gv = 1.0f / (1.0f + __expf(-t));
+    const float gv = 1.0f / (1.0f + __expf(-logit[i]));
     if (gate && lane == 0) gate[i] = gv;
     const float hv = 1.0f - gv;
     if (vec) {
@@ -131,15 +115,14 @@ __global__ __launch_bounds__(256) void add_layernorm_generic(int32_t n, int32_t 
 
 using namespace gga;
 
-extern "C" int gga_gated_combine(int32_t n, int32_t d, const float* x, const float* w_g, float b_g, int32_t width,
-                                 const float* l, const float* g, float* gate_out, float* y, void* stream) {
-    if (n < 0 || d < 1 || width < 1) return GGA_EINVAL;
+extern "C" int gga_gated_combine(int32_t n, int32_t width, const float* gate_logit, const float* l, const float* g,
+                                 float* gate_out, float* y, void* stream) {
+    if (n < 0 || width < 1) return GGA_EINVAL;
     if (n == 0) return GGA_OK;
-    if (!x || !w_g || !l || !g || !y) return GGA_EINVAL;
-    const int vec = (d % 4 == 0) && (width % 4 == 0) && aligned16(x) && aligned16(w_g) && aligned16(l) &&
-                    aligned16(g) && aligned16(y);
-    gated_combine_kernel<<<(unsigned)(((int64_t)n + 3) / 4), 256, 0, as_stream(stream)>>>(n, d, x, w_g, b_g, width, l,
-                                                                                           g, gate_out, y, vec);
+    if (!gate_logit || !l || !g || !y) return GGA_EINVAL;
+    const int vec = (width % 4 == 0) && aligned16(l) && aligned16(g) && aligned16(y);
+    gated_combine_kernel<<<(unsigned)(((int64_t)n + 3) / 4), 256, 0, as_stream(stream)>>>(n, gate_logit, width, l, g,
+                                                                                           gate_out, y, vec);
     return launch_status();
 }
 

@@ -21,6 +21,8 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, KT = 16;
 
+constexpr int kMaxSegs = 4;
+
 struct GemmArgs {
     const float* a;
     const float* b;
@@ -30,6 +32,20 @@ struct GemmArgs {
     int32_t trans_a, trans_b;
     int32_t kchunk;  // K range per split
     int32_t accumulate;  // add into c instead of overwriting it
+    // Segmented operands (plain a and plain b only; seg_len a multiple of the 128-wide tile
+    // for column segments, of the 32-deep stage for k segments).  nseg > 1: the columns
+    // [s seg_len, (s+1) seg_len) of op(b) and c are the matrices seg_b[s] [K, seg_len] and
+    // seg_c[s] [M, seg_len].  kseg > 1: the k range [s seg_len, (s+1) seg_len) of a and b is
+    // seg_a[s] [M, seg_len] and seg_b[s] [seg_len, N], added in segment order.
+    int32_t nseg, kseg, seg_len;
+    const float* seg_a[kMaxSegs];
+    const float* seg_b[kMaxSegs];
+    float* seg_c[kMaxSegs];
+    // gate_out != null: the workgroups of column tile 0 also write gate_out[i] = a[i,:] . gate_w
+    // + gate_b for their rows, from the a values they load anyway (plain a only).
+    const float* gate_w;
+    float* gate_out;
+    float gate_b;
 };
 
 // Loads 4 consecutive floats of a row starting at column c0, zero beyond `lim` columns.
@@ -328,9 +344,25 @@ __device__ __forceinline__ void fast_fetch(const float* (&p)[4], int64_t step, v
 // The k loop of one tile: nk stages from kb through NB LDS buffers (with one, the stores of
 // the next stage wait at a barrier for every wavefront's reads of the current one).  FAST:
 // the tile and every stage lie inside the matrices, and rows are 16-byte aligned.
+// Adds this thread's a values of one stage (rows row0 + 32q, k = k0 + 4 (t % 8) .. +3; see
+// big_fetch) times gate_w to its four row sums (plain a only).
+__device__ __forceinline__ void gate_stage(const float* gw, int64_t k0, int64_t klim, bool vec, const v4f (&ra)[4],
+                                           float (&gs)[4]) {
+    const float4 w = load4(gw, k0 + (threadIdx.x & 7) * 4, klim, vec);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        gs[q] = fmaf(ra[q][0], w.x, gs[q]);
+        gs[q] = fmaf(ra[q][1], w.y, gs[q]);
+        gs[q] = fmaf(ra[q][2], w.z, gs[q]);
+        gs[q] = fmaf(ra[q][3], w.w, gs[q]);
+    }
+}
+
 template <bool AKM, bool BKM, bool FAST, int NB>
 __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kStageFloats], int64_t m0, int64_t n0,
-                                         int64_t kb, int64_t ke, bool a_vec, bool b_vec, v4f (&acc)[4][4]) {
+                                         int64_t kb, int64_t ke, bool a_vec, bool b_vec, v4f (&acc)[4][4],
+                                         const float* gw = nullptr, float* gsp = nullptr) {
+    // (gw == nullptr in every call of the plain instances: the gate code folds away)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int nk = (int)((ke - kb + TK2 - 1) / TK2);
@@ -347,8 +379,12 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
         big_fetch<AKM>(g.a, g.lda, m0, g.M, (k0), ke, false, a_vec, ra);       \
         big_fetch<BKM>(g.b, g.ldb, n0, g.N, (k0), ke, false, b_vec, rb);       \
     }
+    float gs[4] = {0.f, 0.f, 0.f, 0.f};
+    const bool gate = !AKM && gw != nullptr;
+    const bool gw_vec = gate && (reinterpret_cast<uintptr_t>(gw) & 15) == 0;
     if (nk > 0) {
         GGA_BIG_FETCH(kb)
+        if (gate) gate_stage(gw, kb, ke, gw_vec, ra, gs);
         big_stash<AKM>(lds[0][0], ra);
         big_stash<BKM>(lds[0][1], rb);
     }
@@ -376,6 +412,7 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][st], bf[j][st], acc[i][j], 0, 0, 0);
         }
         if (t + 1 < nk) {
+            if (gate) gate_stage(gw, kb + (int64_t)(t + 1) * TK2, ke, gw_vec, ra, gs);
             if constexpr (NB == 1) __syncthreads();
             big_stash<AKM>(lds[NB == 2 ? cur ^ 1 : 0][0], ra);
             big_stash<BKM>(lds[NB == 2 ? cur ^ 1 : 0][1], rb);
@@ -383,39 +420,18 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
         __syncthreads();
     }
 #undef GGA_BIG_FETCH
+    if (gate)
+#pragma unroll
+        for (int q = 0; q < 4; q++) gsp[q] += gs[q];
 }
 
-template <bool AKM, bool BKM>
-__global__ __launch_bounds__(kBigThreads, (BigCfg<AKM, BKM>::per_cu)) void gemm_f32_big(GemmArgs g) {
-    using Cfg = BigCfg<AKM, BKM>;
-    __shared__ float lds_raw[Cfg::lds_floats];
-    // [buffer][operand]; the epilogue reuses the same memory
-    float(*lds)[2][kStageFloats] = reinterpret_cast<float(*)[2][kStageFloats]>(lds_raw);
+// Epilogue of a 128 x 128 tile through LDS, 32 rows of the wavefront's 64 x 64 block at a
+// time: the accumulators go to a private [32][68] region, then each row leaves as 16-byte
+// stores, 16 lanes covering 64 consecutive columns.
+__device__ __forceinline__ void big_epilogue(const GemmArgs& g, float* lds_raw, const v4f (&acc)[4][4], int64_t m0,
+                                             int64_t n0, uint32_t bz) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const uint32_t gxy = gridDim.x * gridDim.y;
-    const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gxy * gridDim.z);
-    const uint32_t bz = tl / gxy, by = (tl % gxy) / gridDim.x, bx = tl % gridDim.x;
-    const int64_t m0 = (int64_t)by * TT, n0 = (int64_t)bx * TT;
-    const int64_t kb = (int64_t)bz * g.kchunk;
-    const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
-    const bool a_vec = (g.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
-    const bool b_vec = (g.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(g.b) & 15) == 0;
-    const bool fast = a_vec && b_vec && m0 + TT <= g.M && n0 + TT <= g.N && (ke - kb) % TK2 == 0;
-
-    v4f acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    if (fast)
-        big_loop<AKM, BKM, true, Cfg::buffers>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
-    else
-        big_loop<AKM, BKM, false, Cfg::buffers>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
-
-    // Epilogue through LDS, 32 rows of the wavefront's 64 x 64 block at a time: the
-    // accumulators go to a private [32][68] region, then each row leaves as 16-byte stores,
-    // 16 lanes covering 64 consecutive columns.
     float* cbase = g.c + (int64_t)bz * g.M * g.N;
     const bool add_bias = g.bias != nullptr && gridDim.z == 1;
     const bool acc_in = g.accumulate && gridDim.z == 1;
@@ -457,6 +473,150 @@ __global__ __launch_bounds__(kBigThreads, (BigCfg<AKM, BKM>::per_cu)) void gemm_
             }
         }
     }
+}
+
+template <bool AKM, bool BKM>
+__global__ __launch_bounds__(kBigThreads, (BigCfg<AKM, BKM>::per_cu)) void gemm_f32_big(GemmArgs g) {
+    using Cfg = BigCfg<AKM, BKM>;
+    __shared__ float lds_raw[Cfg::lds_floats];
+    // [buffer][operand]; the epilogue reuses the same memory
+    float(*lds)[2][kStageFloats] = reinterpret_cast<float(*)[2][kStageFloats]>(lds_raw);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t gxy = gridDim.x * gridDim.y;
+    const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gxy * gridDim.z);
+    const uint32_t bz = tl / gxy, by = (tl % gxy) / gridDim.x, bx = tl % gridDim.x;
+    const int64_t m0 = (int64_t)by * TT, n0 = (int64_t)bx * TT;
+    const int64_t kb = (int64_t)bz * g.kchunk;
+    const int64_t ke = kb + g.kchunk < g.K ? kb + g.kchunk : g.K;
+    const bool a_vec = (g.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(g.a) & 15) == 0;
+    const bool b_vec = (g.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(g.b) & 15) == 0;
+    const bool fast = a_vec && b_vec && m0 + TT <= g.M && n0 + TT <= g.N && (ke - kb) % TK2 == 0;
+
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (fast)
+        big_loop<AKM, BKM, true, Cfg::buffers>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
+    else
+        big_loop<AKM, BKM, false, Cfg::buffers>(g, lds, m0, n0, kb, ke, a_vec, b_vec, acc);
+
+    big_epilogue(g, lds_raw, acc, m0, n0, bz);
+}
+
+// Products with segmented operands (plain a and b), two workgroups per CU.
+//
+// Column segments (gemm_f32_seg_cols): each seg_len-wide column range of op(b) and c is its
+// own pair of matrices; with gate_out, the workgroups of column tile 0 also form
+// a . gate_w for their rows from the a values they load.
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_seg_cols(GemmArgs g) {
+    using Cfg = BigCfg<false, true>;
+    __shared__ float lds_raw[Cfg::lds_floats];
+    float(*lds)[2][kStageFloats] = reinterpret_cast<float(*)[2][kStageFloats]>(lds_raw);
+    const uint32_t gxy = gridDim.x * gridDim.y;
+    const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gxy);
+    const uint32_t by = tl / gridDim.x, bx = tl % gridDim.x;
+    const int64_t m0 = (int64_t)by * TT;
+    const int sg = (int)(((int64_t)bx * TT) / g.seg_len);
+    const int64_t n0 = (int64_t)bx * TT - (int64_t)sg * g.seg_len;
+    GemmArgs gv = g;  // the tile's own matrices
+    gv.b = g.seg_b[sg];
+    gv.c = g.seg_c[sg];
+    gv.N = g.seg_len;
+    gv.ldb = g.seg_len;
+    const bool do_gate = g.gate_out != nullptr && bx == 0;
+    float gsum[4] = {0.f, 0.f, 0.f, 0.f};
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    const bool a_vec = (gv.lda % 4) == 0 && (reinterpret_cast<uintptr_t>(gv.a) & 15) == 0;
+    const bool b_vec = (gv.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(gv.b) & 15) == 0;
+    const bool fast = a_vec && b_vec && m0 + TT <= gv.M && n0 + TT <= gv.N && gv.K % TK2 == 0;
+    const float* gw = do_gate ? g.gate_w : nullptr;
+    if (fast)
+        big_loop<false, true, true, Cfg::buffers>(gv, lds, m0, n0, 0, gv.K, a_vec, b_vec, acc, gw, gsum);
+    else
+        big_loop<false, true, false, Cfg::buffers>(gv, lds, m0, n0, 0, gv.K, a_vec, b_vec, acc, gw, gsum);
+    if (do_gate) {
+        // the eight threads of a row segment hold its eight k chunks: a fixed butterfly
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            float v = gsum[q];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            const int64_t row = m0 + (threadIdx.x >> 3) + 32 * q;
+            if ((threadIdx.x & 7) == 0 && row < g.M) g.gate_out[row] = v + g.gate_b;
+        }
+    }
+    big_epilogue(gv, lds_raw, acc, m0, n0, 0);
+}
+
+// k segments (gemm_f32_seg_k<S>): the k range [s seg_len, (s+1) seg_len) of a and b is the
+// pair seg_a[s] [M, seg_len], seg_b[s] [seg_len, N]; the segments run in order into the same
+// accumulators, so the sum is the one a single product over the concatenated k would form.
+template <int S>
+__global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_seg_k(GemmArgs g) {
+    using Cfg = BigCfg<false, true>;
+    __shared__ float lds_raw[Cfg::lds_floats];
+    float(*lds)[2][kStageFloats] = reinterpret_cast<float(*)[2][kStageFloats]>(lds_raw);
+    const uint32_t gxy = gridDim.x * gridDim.y;
+    const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gxy);
+    const uint32_t by = tl / gridDim.x, bx = tl % gridDim.x;
+    const int64_t m0 = (int64_t)by * TT, n0 = (int64_t)bx * TT;
+    v4f acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    bool fast = m0 + TT <= g.M && n0 + TT <= g.N && g.seg_len % TK2 == 0 && g.seg_len % 4 == 0 && g.ldb % 4 == 0;
+#pragma unroll
+    for (int kp = 0; kp < S; kp++)
+        fast = fast && (reinterpret_cast<uintptr_t>(g.seg_a[kp]) & 15) == 0 &&
+               (reinterpret_cast<uintptr_t>(g.seg_b[kp]) & 15) == 0;
+    if (fast) {
+#pragma unroll
+        for (int kp = 0; kp < S; kp++) {
+            GemmArgs gk = g;
+            gk.a = g.seg_a[kp];
+            gk.b = g.seg_b[kp];
+            gk.K = g.seg_len;
+            gk.lda = g.seg_len;
+            big_loop<false, true, true, Cfg::buffers>(gk, lds, m0, n0, 0, g.seg_len, true, true, acc);
+        }
+    } else {
+#pragma unroll
+        for (int kp = 0; kp < S; kp++) {
+            GemmArgs gk = g;
+            gk.a = g.seg_a[kp];
+            gk.b = g.seg_b[kp];
+            gk.K = g.seg_len;
+            gk.lda = g.seg_len;
+            const bool a_vec = (g.seg_len % 4) == 0 && (reinterpret_cast<uintptr_t>(gk.a) & 15) == 0;
+            const bool b_vec = (gk.ldb % 4) == 0 && (reinterpret_cast<uintptr_t>(gk.b) & 15) == 0;
+            big_loop<false, true, false, Cfg::buffers>(gk, lds, m0, n0, 0, g.seg_len, a_vec, b_vec, acc);
+        }
+    }
+    big_epilogue(g, lds_raw, acc, m0, n0, 0);
+}
+
+// gate[i] = x[i,:] . w + b, one wavefront per row, a fixed butterfly over the lanes (the
+// projections' path when the layer width is not a multiple of the 128-wide tile).
+__global__ __launch_bounds__(256) void gate_logit_kernel(int32_t n, int32_t d, const float* __restrict__ x,
+                                                         const float* __restrict__ w, float b,
+                                                         float* __restrict__ gate) {
+    const int lane = threadIdx.x & 63;
+    const int64_t i = blockIdx.x * 4ll + (threadIdx.x >> 6);
+    if (i >= n) return;
+    float t = 0.f;
+    for (int j = lane; j < d; j += 64) t = fmaf(x[i * d + j], w[j], t);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) t += __shfl_xor(t, o, 64);
+    if (lane == 0) gate[i] = t + b;
 }
 
 // dst[c][r] = src[r][c] for a rows x cols matrix, through a 32 x 32 LDS tile padded by one
@@ -1067,4 +1227,122 @@ extern "C" int gga_linear_accumulate(int32_t m, int32_t k, int32_t n, int32_t tr
                                      const float* a, const float* b, float* c, void* ws, size_t ws_bytes,
                                      void* stream) {
     return linear_impl(m, k, n, trans_a, trans_b, a, b, nullptr, c, 1, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- fused projections
+
+namespace gga {
+namespace {
+
+// The fused products run on the 128 x 128 tile kernel without a k split.
+bool fused_ok(int32_t m, int32_t k, int32_t n, int32_t seg, int32_t seg_mult) {
+    return m >= 1 && seg >= 1 && seg % seg_mult == 0 && pick_split(m, k, n).splits == 1 && (m + BM - 1) / BM <= 65535;
+}
+
+}  // namespace
+}  // namespace gga
+
+extern "C" size_t gga_qkv_gate_proj_workspace(int32_t n, int32_t d) { return gga_linear_workspace(n, d, d); }
+
+extern "C" int gga_qkv_gate_proj(int32_t n, int32_t d, const float* x, const float* w_q, const float* w_k,
+                                 const float* w_v, const float* w_g, float b_g, float* q, float* k, float* v,
+                                 float* gate_logit, void* ws, size_t ws_bytes, void* stream) {
+    if (n < 0 || d < 1) return GGA_EINVAL;
+    if (n == 0) return GGA_OK;
+    if (!x || !w_q || !w_k || !w_v || !w_g || !q || !k || !v || !gate_logit) return GGA_EINVAL;
+    if ((int64_t)n * d >= ((int64_t)1 << 40)) return GGA_ERANGE;
+    hipStream_t s = as_stream(stream);
+    bool aligned = true;
+    for (const void* p : {(const void*)x, (const void*)w_q, (const void*)w_k, (const void*)w_v, (const void*)q,
+                          (const void*)k, (const void*)v})
+        aligned = aligned && aligned16(p);
+    if (aligned && d % 4 == 0 && fused_ok(n, d, 3 * d, d, TT)) {
+        // one product X [W_Q | W_K | W_V] over three column segments; column tile 0 also forms
+        // the gate logit from the X rows it loads
+        GemmArgs g{};
+        g.a = x;
+        g.b = w_q;
+        g.c = q;
+        g.M = n;
+        g.K = d;
+        g.N = 3 * d;
+        g.lda = d;
+        g.ldb = d;
+        g.kchunk = d;
+        g.nseg = 3;
+        g.kseg = 1;
+        g.seg_len = d;
+        g.seg_b[0] = w_q;
+        g.seg_b[1] = w_k;
+        g.seg_b[2] = w_v;
+        g.seg_c[0] = q;
+        g.seg_c[1] = k;
+        g.seg_c[2] = v;
+        g.gate_w = w_g;
+        g.gate_out = gate_logit;
+        g.gate_b = b_g;
+        const dim3 grid((unsigned)((3 * (int64_t)d) / TT), (unsigned)((n + BM - 1) / BM), 1);
+        gemm_f32_seg_cols<<<grid, kBigThreads, 0, s>>>(g);
+        return launch_status();
+    }
+    int st = gga_linear(n, d, d, 0, 0, x, w_q, nullptr, q, ws, ws_bytes, stream);
+    if (st == GGA_OK) st = gga_linear(n, d, d, 0, 0, x, w_k, nullptr, k, ws, ws_bytes, stream);
+    if (st == GGA_OK) st = gga_linear(n, d, d, 0, 0, x, w_v, nullptr, v, ws, ws_bytes, stream);
+    if (st != GGA_OK) return st;
+    gate_logit_kernel<<<(unsigned)(((int64_t)n + 3) / 4), 256, 0, s>>>(n, d, x, w_g, b_g, gate_logit);
+    return launch_status();
+}
+
+extern "C" size_t gga_qkv_proj_bwd_x_workspace(int32_t n, int32_t d) {
+    if (n < 0 || d < 1) return 0;
+    const size_t wt = align_up((size_t)3 * d * d * sizeof(float), 256);
+    const size_t lin = gga_linear_workspace(n, d, d);
+    return wt > lin ? wt : lin;
+}
+
+extern "C" int gga_qkv_proj_bwd_x(int32_t n, int32_t d, const float* d_q, const float* d_k, const float* d_v,
+                                  const float* w_q, const float* w_k, const float* w_v, float* d_x, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    if (n < 0 || d < 1) return GGA_EINVAL;
+    if (n == 0) return GGA_OK;
+    if (!d_q || !d_k || !d_v || !w_q || !w_k || !w_v || !d_x) return GGA_EINVAL;
+    if ((int64_t)n * d >= ((int64_t)1 << 40)) return GGA_ERANGE;
+    if (ws_bytes < gga_qkv_proj_bwd_x_workspace(n, d) || !ws) return GGA_EWORKSPACE;
+    hipStream_t s = as_stream(stream);
+    bool aligned = true;
+    for (const void* p : {(const void*)d_q, (const void*)d_k, (const void*)d_v, (const void*)d_x, (const void*)ws})
+        aligned = aligned && aligned16(p);
+    if (aligned && d % 4 == 0 && fused_ok(n, 3 * d, d, d, TK2)) {
+        // W^T of each projection into the workspace, then one product [dQ | dK | dV] [W_Q | W_K | W_V]^T
+        // over three k segments, added into dX
+        float* wt = static_cast<float*>(ws);
+        const float* w[3] = {w_q, w_k, w_v};
+        const dim3 tg((unsigned)((d + 31) / 32), (unsigned)((d + 31) / 32));
+        for (int i = 0; i < 3; i++) transpose_f32<<<tg, 256, 0, s>>>(w[i], d, d, wt + (size_t)i * d * d);
+        GemmArgs g{};
+        g.a = d_q;
+        g.b = wt;
+        g.c = d_x;
+        g.M = n;
+        g.K = 3 * d;
+        g.N = d;
+        g.lda = d;
+        g.ldb = d;
+        g.kchunk = 3 * d;
+        g.accumulate = 1;
+        g.nseg = 1;
+        g.kseg = 3;
+        g.seg_len = d;
+        g.seg_a[0] = d_q;
+        g.seg_a[1] = d_k;
+        g.seg_a[2] = d_v;
+        for (int i = 0; i < 3; i++) g.seg_b[i] = wt + (size_t)i * d * d;
+        const dim3 grid((unsigned)((d + TT - 1) / TT), (unsigned)((n + BM - 1) / BM), 1);
+        gemm_f32_seg_k<3><<<grid, kBigThreads, 0, s>>>(g);
+        return launch_status();
+    }
+    int st = gga_linear_accumulate(n, d, d, 0, 1, d_q, w_q, d_x, ws, ws_bytes, stream);
+    if (st == GGA_OK) st = gga_linear_accumulate(n, d, d, 0, 1, d_k, w_k, d_x, ws, ws_bytes, stream);
+    if (st == GGA_OK) st = gga_linear_accumulate(n, d, d, 0, 1, d_v, w_v, d_x, ws, ws_bytes, stream);
+    return st;
 }

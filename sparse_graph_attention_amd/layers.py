@@ -22,6 +22,7 @@ import torch
 from . import (GGA_BF16, GGA_F32, GGA_SCORE_ADDITIVE, GGA_SCORE_DOT, GGA_SCORE_MEAN, Topology, gga_add_layernorm,
                gga_add_layernorm_bwd, gga_gat_coef_bwd, gga_gat_coef_fwd, gga_gated_combine, gga_gated_combine_bwd,
                gga_head_mean, gga_head_mean_bwd, gga_local_attn_bwd_edge, gga_local_attn_fwd_edge,
+               gga_qkv_gate_proj, gga_qkv_proj_bwd_x,
                gga_global_linear_batch_bwd, gga_global_linear_batch_fwd, gga_global_linear_bwd,
                gga_global_linear_fwd, gga_linear, gga_linear_accumulate, gga_local_attn_bwd, gga_local_attn_fwd,
                gga_relation_sources, make_desc)
@@ -91,16 +92,15 @@ def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, 
     x = p["x"]
     n, d = x.shape
     r = d // heads
-    q = gga_linear(x, p["w_q"]).view(n, heads, r)
-    k = gga_linear(x, p["w_k"]).view(n, heads, r)
-    v = gga_linear(x, p["w_v"]).view(n, heads, r)
+    # [Q | K | V | gate logit] = X [W_Q | W_K | W_V | w_g] + [0 | 0 | 0 | b_g], X read once
+    q, k, v, logit = gga_qkv_gate_proj(x, p["w_q"], p["w_k"], p["w_v"], p["w_g"], p["b_g"], heads)
     desc = make_desc(n, topo.e, heads, r, GGA_SCORE_DOT, dtype, r ** -0.5)
     loc, lse = gga_local_attn_fwd(desc, q, k, v, topo.row_ptr, topo.col, topo.plan)
     if node_ptr is None:
         s, z, glob = gga_global_linear_fwd(q, k, v, eps)
     else:
         s, z, glob = gga_global_linear_batch_fwd(node_ptr, q, k, v, eps)
-    gate, y = gga_gated_combine(x, p["w_g"], p["b_g"], loc.view(n, d), glob.view(n, d))
+    gate, y = gga_gated_combine(logit, loc.view(n, d), glob.view(n, d))
     zo = gga_linear(y, p["w_o"])
     out = gga_add_layernorm(x, zo, p["gamma"], p["beta"], ln_eps)
     return dict(q=q, k=k, v=v, local=loc.view(n, d), local3=loc, lse=lse, S=s, z=z, glob=glob.view(n, d), gate=gate,
@@ -130,9 +130,9 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
                                     d_glob.view(n, heads, r), d_q, d_k, d_v, eps)
     grads = dict(d_w_o=d_wo, d_w_g=d_wg, d_b_g=d_bg, d_gamma=d_gamma, d_beta=d_beta)
     for name, g in (("q", d_q), ("k", d_k), ("v", d_v)):
-        g2 = g.view(n, d)
-        grads["d_w_" + name] = gga_linear(x, g2, trans_a=True)
-        gga_linear_accumulate(g2, p["w_" + name], d_x, trans_b=True)
+        grads["d_w_" + name] = gga_linear(x, g.view(n, d), trans_a=True)
+    # d_x += [dQ | dK | dV] [W_Q | W_K | W_V]^T in one product
+    gga_qkv_proj_bwd_x(d_q, d_k, d_v, p["w_q"], p["w_k"], p["w_v"], d_x)
     grads["d_x"] = d_x
     return grads
 

@@ -210,3 +210,19 @@ def test_noalloc_forward_refuses_inputs_beyond_its_scratch():
     assert g.lib.gga_local_attn_fwd_workspace(ctypes.byref(d)) > 96 << 20
     assert g.lib.gga_local_attn_fwd_noalloc(ctypes.byref(d), a, a, a, a, a, a, a, a, None) == g.GGA_ESCRATCH
     assert g.lib.gga_status_string(g.GGA_ESCRATCH) != g.lib.gga_status_string(99)
+
+
+def test_fused_projection_checks():
+    import sparse_graph_attention_amd as g
+
+    L = g.lib
+    a = ctypes.c_void_p(4096)
+    assert L.gga_qkv_gate_proj(-1, 256, a, a, a, a, a, ctypes.c_float(0.0), a, a, a, a, None, 0, None) == 1
+    assert L.gga_qkv_gate_proj(10, 256, a, a, None, a, a, ctypes.c_float(0.0), a, a, a, a, None, 0, None) == 1
+    assert L.gga_qkv_gate_proj(0, 256, None, None, None, None, None, ctypes.c_float(0.0), None, None, None, None,
+                               None, 0, None) == 0
+    need = L.gga_qkv_proj_bwd_x_workspace(1000, 256)
+    assert need >= 3 * 256 * 256 * 4
+    assert L.gga_qkv_proj_bwd_x(1000, 256, a, a, a, a, a, a, a, a, need - 1, None) == 4
+    assert L.gga_qkv_proj_bwd_x(1000, 0, a, a, a, a, a, a, a, a, need, None) == 1
+    assert L.gga_gated_combine(10, 4, None, a, a, None, a, None) == 1

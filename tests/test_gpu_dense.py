@@ -88,14 +88,46 @@ def test_global_linear(g, n, h, r):
     assert_close(gg.cpu().numpy(), rg, "f32", "G")
 
 
+@pytest.mark.parametrize("n,d,heads", [(1000, 256, 4), (3000, 384, 4), (77, 100, 4), (5, 8, 2)])
+def test_qkv_gate_projection(g, n, d, heads):
+    """[Q | K | V | gate logit] = X [W_Q | W_K | W_V | w_g] + b_g: one launch for d a multiple
+    of 128 (ragged row tiles included), the per-product path otherwise."""
+    rng = np.random.default_rng(n + d)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    ws = [(rng.standard_normal((d, d)) * 0.05).astype(np.float32) for _ in range(3)]
+    wg = (rng.standard_normal(d) * 0.1).astype(np.float32)
+    q, k, v, logit = g.gga_qkv_gate_proj(_t(x), *(_t(w) for w in ws), _t(wg), 0.25, heads)
+    torch.cuda.synchronize()
+    x64 = x.astype(np.float64)
+    for got, w in zip((q, k, v), ws):
+        assert_close(got.reshape(n, d).cpu().numpy(), x64 @ w, "f32", "projection", atol=1e-5 * np.sqrt(d))
+    assert_close(logit.cpu().numpy(), x64 @ wg + 0.25, "f32", "gate logit", atol=1e-5 * np.sqrt(d))
+
+
+@pytest.mark.parametrize("n,d", [(3000, 256), (1000, 128), (77, 100)])
+def test_qkv_projection_input_gradient(g, n, d):
+    """d_x += dQ W_Q^T + dK W_K^T + dV W_V^T, one launch (k ranges q, k, v) or three."""
+    rng = np.random.default_rng(7 * n + d)
+    grads = [rng.standard_normal((n, d)).astype(np.float32) for _ in range(3)]
+    ws = [(rng.standard_normal((d, d)) * 0.05).astype(np.float32) for _ in range(3)]
+    dx0 = rng.standard_normal((n, d)).astype(np.float32)
+    dx = _t(dx0)
+    g.gga_qkv_proj_bwd_x(*(_t(a) for a in grads), *(_t(w) for w in ws), dx)
+    torch.cuda.synchronize()
+    want = dx0.astype(np.float64) + sum(a.astype(np.float64) @ w.T.astype(np.float64) for a, w in zip(grads, ws))
+    assert_close(dx.cpu().numpy(), want, "f32", "d_x", atol=1e-5 * np.sqrt(3 * d))
+
+
 def test_gate_combine_and_limits(g):
     rng = np.random.default_rng(5)
     n, d, w = 1000, 256, 256
     x = rng.standard_normal((n, d)).astype(np.float32)
     wg = (rng.standard_normal(d) * 0.1).astype(np.float32)
+    wz = np.zeros((d, d), np.float32)
     loc, glob = rng.standard_normal((n, w)).astype(np.float32), rng.standard_normal((n, w)).astype(np.float32)
     for b_g in (0.3, 80.0, -80.0):
-        gate, y = g.gga_gated_combine(_t(x), _t(wg), b_g, _t(loc), _t(glob))
+        *_, logit = g.gga_qkv_gate_proj(_t(x), _t(wz), _t(wz), _t(wz), _t(wg), b_g, 4)
+        gate, y = g.gga_gated_combine(logit, _t(loc), _t(glob))
         torch.cuda.synchronize()
         rg = oracle.gate(x, wg, b_g)
         assert_close(gate.cpu().numpy(), rg, "f32", "gate")
@@ -104,7 +136,8 @@ def test_gate_combine_and_limits(g):
     x2 = rng.standard_normal((37, 5)).astype(np.float32)
     wg2 = rng.standard_normal(5).astype(np.float32)
     l2, g2 = rng.standard_normal((37, 3)).astype(np.float32), rng.standard_normal((37, 3)).astype(np.float32)
-    gate, y = g.gga_gated_combine(_t(x2), _t(wg2), -0.2, _t(l2), _t(g2))
+    logit2 = _t(x2.astype(np.float64) @ wg2.astype(np.float64) - 0.2)
+    gate, y = g.gga_gated_combine(logit2, _t(l2), _t(g2))
     torch.cuda.synchronize()
     rg = oracle.gate(x2, wg2, -0.2)
     assert_close(y.cpu().numpy(), oracle.combine(rg, l2, g2), "f32", "y")
