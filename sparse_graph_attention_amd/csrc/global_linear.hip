@@ -83,35 +83,59 @@ struct Seg {
     }
 };
 
-// Calls f(b, r0, r1, slot) for the pieces tile t handles, in graph order: slot 0 or 1 for a
-// piece of a long graph (rows of the tile), -1 for a whole short graph (its rows may run
-// past the tile).  Depends only on t, so it is uniform across a workgroup.
-template <class F>
-__device__ __forceinline__ void for_each_segment(const Seg& sg, int64_t t, F&& f) {
-    const int64_t a = t * sg.rs;
-    const int64_t e = a + sg.rs < sg.n ? a + sg.rs : sg.n;
-    if (a >= e) return;
-    int32_t b = sg.graph_of(a);
-    {
-        const int64_t lo = sg.node(b), hi = sg.node(b + 1);
-        if (lo <= a && a < hi) {
-            if (hi - lo > sg.rs) {
-                f(b, a, hi < e ? hi : e, 0);
-                b++;
-            } else if (lo < a) {
-                b++;  // a short graph that started in an earlier tile
+struct Piece {
+    int32_t b;
+    int64_t r0, r1;
+    int slot;
+};
+
+// The pieces of tile t in order, one per call of next(): the first test covers a long graph
+// that began before (or at) the tile's first row, the loop the graphs starting inside it.
+struct PieceIter {
+    const Seg& sg;
+    int64_t a, e;
+    int32_t b;
+    bool first;
+    __device__ __forceinline__ PieceIter(const Seg& s, int64_t t) : sg(s), first(true) {
+        a = t * sg.rs;
+        e = a + sg.rs < sg.n ? a + sg.rs : sg.n;
+        b = a < e ? sg.graph_of(a) : sg.batch;
+    }
+    __device__ __forceinline__ bool next(Piece& p) {
+        if (a >= e) return false;
+        if (first) {
+            first = false;
+            const int64_t lo = sg.node(b), hi = sg.node(b + 1);
+            if (lo <= a && a < hi) {
+                if (hi - lo > sg.rs) {
+                    p = Piece{b, a, hi < e ? hi : e, 0};
+                    b++;
+                    return true;
+                }
+                if (lo < a) b++;  // a short graph that started in an earlier tile
             }
         }
+        for (; b < sg.batch; b++) {
+            const int64_t lo = sg.node(b), hi = sg.node(b + 1);
+            if (lo >= e) return false;
+            if (lo < a || hi <= lo) continue;
+            p = hi - lo > sg.rs ? Piece{b, lo, hi < e ? hi : e, 1} : Piece{b, lo, hi, -1};
+            b++;
+            return true;
+        }
+        return false;
     }
-    for (; b < sg.batch; b++) {
-        const int64_t lo = sg.node(b), hi = sg.node(b + 1);
-        if (lo >= e) break;
-        if (lo < a || hi <= lo) continue;
-        if (hi - lo > sg.rs)
-            f(b, lo, hi < e ? hi : e, 1);
-        else
-            f(b, lo, hi, -1);
-    }
+};
+
+// Calls f(b, r0, r1, slot) for the pieces tile t handles, in graph order: slot 0 or 1 for a
+// piece of a long graph (rows of the tile), -1 for a whole short graph (its rows may run
+// past the tile).  Depends only on t, so it is uniform across a workgroup.  One call site,
+// so f's body is compiled once.
+template <class F>
+__device__ __forceinline__ void for_each_segment(const Seg& sg, int64_t t, F&& f) {
+    PieceIter it(sg, t);
+    Piece p;
+    while (it.next(p)) f(p.b, p.r0, p.r1, p.slot);
 }
 
 // The long graph whose first row lies in tile t, or -1.
