@@ -684,9 +684,10 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
 // wavefronts take the piece's 16-row tiles in turn:
 //   dphi(K)^T = dS V^T: A = dS^T rows, B = the lane's own v;
 //   dV^T = dS^T phi(K)^T: A = dS rows, B = the lane's own phi(k).
-// The next tile's k, v and the current tile's dk, dv (which it adds to) are loaded before
-// the current tile's products; registers are held to two wavefronts per SIMD so that one
-// wavefront's loads overlap the other's products.
+// The next tile's k and v are loaded before the current tile's products, the dk, dv it adds
+// to after them (holding them through the products cost registers and measured 3.5% slower);
+// registers are held to two wavefronts per SIMD so that one wavefront's loads overlap the
+// other's products.
 template <int TR>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void dkv_mfma(
     Seg sg, int32_t H, const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ ds,
@@ -727,14 +728,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             const int64_t off = row * W + h * R + gq * KQ;
             float pk[KQ], vv[KQ];
             uint32_t pos = 0;              // bit t: k feature t > 0, where dphi = 1
-            v4f odk[KQ / 4], odv[KQ / 4];  // the dk, dv this tile adds to, also in flight during the products
 #pragma unroll
             for (int c = 0; c < KQ / 4; c++) {
-                odk[c] = odv[c] = v4f{0.f, 0.f, 0.f, 0.f};
-                if (valid) {
-                    odk[c] = *reinterpret_cast<const v4f*>(dk + off + 4 * c);
-                    odv[c] = *reinterpret_cast<const v4f*>(dv + off + 4 * c);
-                }
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const float x = kx[c][e];
@@ -761,6 +756,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             }
             // ak[ct][q4] = (dS v)[row li][gq*KQ + q4*TR + ct]; av likewise for dS^T phi(k)
             if (valid) {
+                v4f odk[KQ / 4], odv[KQ / 4];
+#pragma unroll
+                for (int c = 0; c < KQ / 4; c++) {
+                    odk[c] = *reinterpret_cast<const v4f*>(dk + off + 4 * c);
+                    odv[c] = *reinterpret_cast<const v4f*>(dv + off + 4 * c);
+                }
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
                     v4f ok, ov;
