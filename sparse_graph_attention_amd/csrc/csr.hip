@@ -1,13 +1,14 @@
 // COO -> CSR by key: a stable least-significant-digit radix sort of (key, COO index,
 // other endpoint).
 //
-// A build takes ceil(bits / 8) passes over the key bits (three for n <= 2^24), each sorting
-// by one digit of at most 8 bits.  A pass is stable by construction: each wavefront of a
-// tile ranks its own contiguous run of items in their original order (64 at a time, the
-// lanes with equal digits found by ballots, a per-digit running count in LDS carrying over
-// from one 64-item round to the next), the wavefronts' runs are placed in wavefront order
-// (per-digit counts of each wavefront, scanned in LDS), and tiles are ordered by a
-// digit-major exclusive scan of per-tile histograms.  The result therefore equals a stable
+// A build takes ceil(bits / 7) passes over the key bits (three for n <= 2^21), each sorting
+// by one digit of at most 7 bits.  A pass is stable by construction: each wavefront of a
+// 4096-item tile ranks its own contiguous run of items in their original order (64 at a
+// time, the lanes with equal digits found through a per-digit lane mask in LDS, a per-digit
+// running count in LDS carrying over from one 64-item round to the next), the wavefronts'
+// runs are placed in wavefront order (per-digit counts of each wavefront, scanned in LDS),
+// and tiles are ordered by each digit's exclusive scan of its per-tile counts over the
+// tiles, offset by the totals of the smaller digits.  The result therefore equals a stable
 // sort, independent of scheduling: within a row the COO indices ascend, bit-exact across
 // runs and devices.  The other endpoint travels with each item, so the last pass writes
 // col directly.  Each tile is staged in LDS in digit order before it is written, so the
@@ -19,11 +20,11 @@ namespace gga {
 
 namespace {
 
-constexpr int kMaxDigitBits = 8;
+constexpr int kMaxDigitBits = 7;
 constexpr int kMaxBins = 1 << kMaxDigitBits;
-constexpr int kRsWaves = 4;
+constexpr int kRsWaves = 8;
 constexpr int kRsThreads = 64 * kRsWaves;
-constexpr int kRsRounds = 16;                    // 64-item rounds per wavefront
+constexpr int kRsRounds = 8;                     // 64-item rounds per wavefront
 constexpr int kRsWaveItems = 64 * kRsRounds;     // a wavefront's contiguous run of a tile
 constexpr int kRsTile = kRsThreads * kRsRounds;  // 4096 edges per tile
 // digits per thread in the tile scan: whole words of two 16-bit counters
@@ -41,39 +42,116 @@ __device__ __forceinline__ uint32_t digit_of(int32_t key, int shift, uint32_t ma
     return ((uint32_t)key >> shift) & mask;
 }
 
-// Lanes of the wavefront whose item is valid and has digit d (as this lane's).
-__device__ __forceinline__ uint64_t same_digit_lanes(uint32_t d, bool valid, int bits) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < bits; b++) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bb = __ballot(bit);
-        peers &= bit ? bb : ~bb;
+// Lanes of the wavefront whose item is valid and has digit d (as this lane's), for a valid
+// lane.  `mask` is the wavefront's table of one 64-bit lane mask per digit, all zero on entry
+// and on return: every valid lane ORs its bit into its digit's mask, reads the mask back and
+// clears it.  The three are single instructions of the whole wavefront, and a wavefront's LDS
+// operations complete in issue order, so each read sees the bits of every lane of the round
+// and each clear comes after every read of the round.
+__device__ __forceinline__ uint64_t same_digit_lanes(uint64_t* mask, uint32_t d, bool valid, uint64_t bit) {
+    uint64_t peers = 0;
+    if (valid) {
+        __hip_atomic_fetch_or(mask + d, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        peers = __hip_atomic_load(mask + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+        __hip_atomic_store(mask + d, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
     }
     return peers;
 }
 
-// Per-tile digit counts: hist[d * nblocks + tile].
+// Per-tile digit counts: hist[d * nblocks + tile].  Each wavefront counts into its own
+// histogram (fewer conflicting LDS additions), and the wavefronts' histograms are summed at
+// the end.  A whole tile of 16-byte aligned keys is read as 16-byte vectors.
 __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __restrict__ keys, int64_t e, int shift,
                                                             int bits, int32_t* __restrict__ hist, int64_t nblocks) {
-    __shared__ int cnt[kMaxBins];
+    __shared__ int cnt[kRsWaves][kMaxBins];
     const int bins = 1 << bits;
     const uint32_t mask = (uint32_t)bins - 1u;
-    for (int d = threadIdx.x; d < bins; d += kRsThreads) cnt[d] = 0;
-    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (each wavefront clears and fills only its own histogram before the barrier)
+    for (int d = lane; d < bins; d += 64) cnt[wave][d] = 0;
     const int64_t base = (int64_t)blockIdx.x * kRsTile;
-    int32_t k[kRsRounds];
+    static_assert(kRsRounds % 4 == 0, "whole 16-byte vectors per thread");
+    if (base + kRsTile <= e && (reinterpret_cast<uintptr_t>(keys) & 15) == 0) {
+        const int4* kv = reinterpret_cast<const int4*>(keys + base);
+        int4 k[kRsRounds / 4];
 #pragma unroll
-    for (int r = 0; r < kRsRounds; r++) {
-        const int64_t i = base + r * kRsThreads + threadIdx.x;
-        k[r] = i < e ? keys[i] : 0;
-    }
+        for (int r = 0; r < kRsRounds / 4; r++) k[r] = kv[r * kRsThreads + tid];
 #pragma unroll
-    for (int r = 0; r < kRsRounds; r++) {
-        const int64_t i = base + r * kRsThreads + threadIdx.x;
-        if (i < e) atomicAdd(&cnt[digit_of(k[r], shift, mask)], 1);
+        for (int r = 0; r < kRsRounds / 4; r++) {
+            atomicAdd(&cnt[wave][digit_of(k[r].x, shift, mask)], 1);
+            atomicAdd(&cnt[wave][digit_of(k[r].y, shift, mask)], 1);
+            atomicAdd(&cnt[wave][digit_of(k[r].z, shift, mask)], 1);
+            atomicAdd(&cnt[wave][digit_of(k[r].w, shift, mask)], 1);
+        }
+    } else {
+        int32_t k[kRsRounds];
+#pragma unroll
+        for (int r = 0; r < kRsRounds; r++) {
+            const int64_t i = base + r * kRsThreads + tid;
+            k[r] = i < e ? keys[i] : 0;
+        }
+#pragma unroll
+        for (int r = 0; r < kRsRounds; r++) {
+            const int64_t i = base + r * kRsThreads + tid;
+            if (i < e) atomicAdd(&cnt[wave][digit_of(k[r], shift, mask)], 1);
+        }
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < bins; d += kRsThreads) hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
+    for (int d = tid; d < bins; d += kRsThreads) {
+        int c = 0;
+#pragma unroll
+        for (int w = 0; w < kRsWaves; w++) c += cnt[w][d];
+        hist[(int64_t)d * nblocks + blockIdx.x] = c;
+    }
+}
+
+// Each digit's row of per-tile counts hist[d * nblocks + t] becomes its exclusive scan over
+// the tiles, in place, and totals[d] the digit's count.  One workgroup per digit; a thread
+// takes kDsItems consecutive tiles of each kDsThreads * kDsItems.
+constexpr int kDsThreads = 1024;
+constexpr int kDsItems = 4;
+
+__global__ __launch_bounds__(kDsThreads) void digit_rows_scan(int32_t* __restrict__ hist, int64_t nblocks,
+                                                              int32_t* __restrict__ totals) {
+    __shared__ int32_t wtot[kDsThreads / 64];
+    int32_t* row = hist + (int64_t)blockIdx.x * nblocks;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int32_t carry = 0;
+    for (int64_t base = 0; base < nblocks; base += (int64_t)kDsThreads * kDsItems) {
+        int32_t v[kDsItems];
+        int32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < kDsItems; j++) {
+            const int64_t i = base + (int64_t)tid * kDsItems + j;
+            v[j] = i < nblocks ? row[i] : 0;
+            sum += v[j];
+        }
+        int32_t x = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) wtot[wave] = x;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kDsThreads / 64; w++) {
+            const int32_t t = wtot[w];
+            before += w < wave ? t : 0;
+            total += t;
+        }
+        __syncthreads();  // (wtot is rewritten by the next chunk)
+        int32_t run = carry + before + x - sum;
+#pragma unroll
+        for (int j = 0; j < kDsItems; j++) {
+            const int64_t i = base + (int64_t)tid * kDsItems + j;
+            if (i < nblocks) row[i] = run;
+            run += v[j];
+        }
+        carry += total;
+    }
+    if (tid == 0) totals[blockIdx.x] = carry;
 }
 
 // A wavefront's items of one tile, in order: round r, lane l holds item wbase + 64 r + l.
@@ -88,7 +166,8 @@ struct RadixArgs {
     int32_t* keys_out;  // may be null (keys not needed after this pass)
     int32_t* vals_out;
     int32_t* oth_out;
-    const int32_t* offsets;  // digit-major exclusive scan of the per-tile digit counts
+    const int32_t* offsets;  // per digit, the exclusive scan of its per-tile counts over the tiles
+    const int32_t* totals;   // per digit, its count over all tiles
     int64_t e, nblocks;
     int shift, bits;
 };
@@ -100,9 +179,17 @@ struct RadixSmem {
     uint16_t tdo[kMaxBins];   // tile-local start of each digit
     int32_t gbase[kMaxBins];  // global start of each digit's run of this tile
     int32_t wtot[kRsWaves];
-    int32_t skey[kRsTile];
-    int32_t sval[kRsTile];
-    int32_t soth[kRsTile];
+    int32_t wtot_all[kRsWaves];
+    union {
+        // while the wavefronts rank their items: each one's lane mask per digit
+        uint64_t lanes[kRsWaves][kMaxBins];
+        // then the tile in (digit, original order)
+        struct {
+            int32_t skey[kRsTile];
+            int32_t sval[kRsTile];
+            int32_t soth[kRsTile];
+        };
+    };
 };
 
 __device__ __forceinline__ int tile_size(const RadixArgs& a, int64_t tile) {
@@ -139,20 +226,44 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
     const int64_t base = tile * kRsTile;
     const int tile_n = tile_size(a, tile);
     const int wbase = wave * kRsWaveItems;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
+    // the starts of this tile's runs of the thread's digits among the digits' runs of all
+    // tiles, and the digits' totals (used after the ranking; loaded first, so their latency
+    // passes under it)
+    int32_t gb[kDigitsPerThread], dt[kDigitsPerThread];
+#pragma unroll
+    for (int j = 0; j < kDigitsPerThread; j++) {
+        const int d = tid * kDigitsPerThread + j;
+        gb[j] = d < bins ? a.offsets[(int64_t)d * a.nblocks + tile] : 0;
+        dt[j] = d < bins ? a.totals[d] : 0;
+    }
     for (int i = tid; i < kRsWaves * (kMaxBins / 2); i += kRsThreads) {
         const int w = i / (kMaxBins / 2), x = i % (kMaxBins / 2);
         if (x < words) sm.wpos[w][x] = 0;
     }
-    __syncthreads();  // (also: the previous tile's scatter has read tdo, gbase and the staging)
+    // (each wavefront clears its own lane masks, so they need no barrier before its ranking)
+    for (int x = lane; x < bins; x += 64) sm.lanes[wave][x] = 0;
+    __syncthreads();
 
-    // each wavefront counts its digits (additions commute: no ordering needed)
+    // each wavefront ranks its items among the equal digits of their 64-item round, and the
+    // first lane of each group adds the group's size to the wavefront's count of the digit
+    // (additions commute: no ordering needed).  rl[r]: rank in the group | group size << 16.
+    uint32_t rl[kRsRounds];
+    {
+        const uint64_t bit = 1ull << lane;
 #pragma unroll
-    for (int r = 0; r < kRsRounds; r++) {
-        const bool valid = wbase + r * 64 + lane < tile_n;
-        const uint32_t d = digit_of(it.key[r], shift, mask);
-        if (valid) atomicAdd(&sm.wpos[wave][d >> 1], 1u << (16 * (d & 1)));
+        for (int r = 0; r < kRsRounds; r++) {
+            const bool valid = wbase + r * 64 + lane < tile_n;
+            const uint32_t d = digit_of(it.key[r], shift, mask);
+            const uint64_t peers = same_digit_lanes(sm.lanes[wave], d, valid, bit);
+            const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+            const uint32_t size = (uint32_t)__popcll(peers);
+            rl[r] = rank | (size << 16);
+            // (materialise the packed word here, so the 64-bit masks do not stay live)
+            asm volatile("" : "+v"(rl[r]));
+            if (valid && rank == 0) atomicAdd(&sm.wpos[wave][d >> 1], size << (16 * (d & 1)));
+        }
     }
     __syncthreads();
 
@@ -161,7 +272,7 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
     // owns kDigitsPerThread consecutive digits, i.e. whole words of wpos.
     {
         int c[kDigitsPerThread];
-        int tot = 0;
+        int tot = 0, tot_all = 0;
 #pragma unroll
         for (int j = 0; j < kDigitsPerThread; j++) {
             const int d = tid * kDigitsPerThread + j;
@@ -169,27 +280,37 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
             if (d < bins)
                 for (int w = 0; w < kRsWaves; w++) c[j] += (sm.wpos[w][d >> 1] >> (16 * (d & 1))) & 0xffffu;
             tot += c[j];
+            tot_all += dt[j];
         }
-        int x = tot;
+        int x = tot, xa = tot_all;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
+            const int y = __shfl_up(x, off, 64), ya = __shfl_up(xa, off, 64);
+            if (lane >= off) {
+                x += y;
+                xa += ya;
+            }
         }
-        if (lane == 63) sm.wtot[wave] = x;
+        if (lane == 63) {
+            sm.wtot[wave] = x;
+            sm.wtot_all[wave] = xa;
+        }
         __syncthreads();
-        int run = x - tot;
-        for (int w = 0; w < wave; w++) run += sm.wtot[w];
+        int run = x - tot, run_all = xa - tot_all;  // run_all: the first position of the thread's first digit
+        for (int w = 0; w < wave; w++) {
+            run += sm.wtot[w];
+            run_all += sm.wtot_all[w];
+        }
 #pragma unroll
         for (int m = 0; m < kDigitsPerThread / 2; m++) {
             const int d0 = tid * kDigitsPerThread + 2 * m;
             if (d0 < bins) {
                 uint32_t s0 = (uint32_t)run, s1 = (uint32_t)(run + c[2 * m]);
                 sm.tdo[d0] = (uint16_t)s0;
-                sm.gbase[d0] = a.offsets[(int64_t)d0 * a.nblocks + tile];
+                sm.gbase[d0] = run_all + gb[2 * m];
                 if (d0 + 1 < bins) {
                     sm.tdo[d0 + 1] = (uint16_t)s1;
-                    sm.gbase[d0 + 1] = a.offsets[(int64_t)(d0 + 1) * a.nblocks + tile];
+                    sm.gbase[d0 + 1] = run_all + dt[2 * m] + gb[2 * m + 1];
                 }
                 for (int w = 0; w < kRsWaves; w++) {
                     const uint32_t cw = sm.wpos[w][d0 >> 1];
@@ -199,44 +320,32 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
                 }
             }
             run += c[2 * m] + c[2 * m + 1];
+            run_all += dt[2 * m] + dt[2 * m + 1];
         }
     }
     __syncthreads();
 
-    // each wavefront places its items in order.  Per round the lowest lane of each group of
-    // equal digits takes the group's places with one atomic add that returns the digit's
-    // next position; a wavefront's LDS operations complete in issue order, so the rounds'
-    // adds follow one another and every group lands after the earlier rounds' items of its
-    // digit.  The group's members take the returned start from their lowest lane.
-    // (in two halves of kRsRounds / 2 rounds, to bound the registers holding the returns)
+    // each wavefront places its items in order.  Per round every item reads its digit's next
+    // position and the first lane of each group of equal digits then adds the group's size;
+    // a wavefront's LDS operations complete in issue order, so the reads see the earlier
+    // rounds' additions and not this round's, and every group lands after the earlier
+    // rounds' items of its digit.  (The staging overlays the lane masks, whose last use is
+    // before the barrier above.)
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-        constexpr int kHalf = kRsRounds / 2;
-        uint32_t got[kHalf], rl[kHalf];  // rl: rank in the group | lowest lane << 8
-#pragma unroll
-        for (int q = 0; q < kHalf; q++) {
-            const int r = h * kHalf + q;
-            const bool valid = wbase + r * 64 + lane < tile_n;
+    for (int r = 0; r < kRsRounds; r++) {
+        const bool valid = wbase + r * 64 + lane < tile_n;
+        if (valid) {
             const uint32_t d = digit_of(it.key[r], shift, mask);
-            const uint64_t peers = same_digit_lanes(d, valid, bits);
-            const uint32_t rank = (uint32_t)__popcll(peers & below);
-            got[q] = 0;
-            rl[q] = rank | ((uint32_t)(valid ? __ffsll((unsigned long long)peers) - 1 : lane) << 8);
-            if (valid && rank == 0)
-                got[q] = atomicAdd(&sm.wpos[wave][d >> 1], (uint32_t)__popcll(peers) << (16 * (d & 1)));
-        }
-#pragma unroll
-        for (int q = 0; q < kHalf; q++) {
-            const int r = h * kHalf + q;
-            const bool valid = wbase + r * 64 + lane < tile_n;
-            const uint32_t d = digit_of(it.key[r], shift, mask);
-            const uint32_t w0 = (uint32_t)__shfl((int)got[q], (int)(rl[q] >> 8), 64);
-            if (valid) {
-                const int pos = (int)((w0 >> (16 * (d & 1))) & 0xffffu) + (int)(rl[q] & 0xffu);
-                sm.skey[pos] = it.key[r];
-                sm.sval[pos] = it.val[r];
-                sm.soth[pos] = it.oth[r];
-            }
+            uint32_t* wp = &sm.wpos[wave][d >> 1];
+            const uint32_t w0 = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+            const uint32_t rank = rl[r] & 0xffffu;
+            if (rank == 0)
+                __hip_atomic_fetch_add(wp, (rl[r] >> 16) << (16 * (d & 1)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
+            const int pos = (int)((w0 >> (16 * (d & 1))) & 0xffffu) + (int)rank;
+            sm.skey[pos] = it.key[r];
+            sm.sval[pos] = it.val[r];
+            sm.soth[pos] = it.oth[r];
         }
     }
     __syncthreads();
@@ -264,19 +373,29 @@ __global__ __launch_bounds__(kRsThreads) void radix_downsweep(RadixArgs a) {
 
 // row_ptr from the sorted keys: row_ptr[v] = first position whose key is >= v.  Position p
 // writes the rows v in (key[p-1], key[p]] (clamped to [0, n]); every write is in bounds even
-// when keys are out of range.  A thread takes kRowPtrItems consecutive positions.
-constexpr int kRowPtrItems = 4;
+// when keys are out of range.  A thread takes kRowPtrItems consecutive positions, read as one
+// 16-byte vector when they are whole and aligned.
+constexpr int kRowPtrItems = 4;  // one 16-byte vector
 
 __global__ void row_ptr_from_sorted(const int32_t* __restrict__ skeys, int64_t e, int32_t n,
                                     int32_t* __restrict__ row_ptr) {
     const int64_t groups = (e + 1 + kRowPtrItems - 1) / kRowPtrItems;
+    const bool vec = (reinterpret_cast<uintptr_t>(skeys) & 15) == 0;
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < groups;
          t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p0 = t * kRowPtrItems;
         int64_t kp = p0 > 0 ? (int64_t)skeys[p0 - 1] : -1;
         int64_t kc[kRowPtrItems];
+        if (vec && p0 + kRowPtrItems <= e) {
+            const int4 v = reinterpret_cast<const int4*>(skeys)[t];
+            kc[0] = v.x;
+            kc[1] = v.y;
+            kc[2] = v.z;
+            kc[3] = v.w;
+        } else {
 #pragma unroll
-        for (int j = 0; j < kRowPtrItems; j++) kc[j] = p0 + j < e ? (int64_t)skeys[p0 + j] : (int64_t)n;
+            for (int j = 0; j < kRowPtrItems; j++) kc[j] = p0 + j < e ? (int64_t)skeys[p0 + j] : (int64_t)n;
+        }
 #pragma unroll
         for (int j = 0; j < kRowPtrItems; j++) {
             const int64_t p = p0 + j;
@@ -370,7 +489,7 @@ Passes passes_for(int32_t n) {
 
 struct CsrWs {
     int32_t* hist;
-    int32_t* scan;
+    int32_t* totals;
     int32_t* keys_tmp[2];
     int32_t* vals_tmp;
     int32_t* oth_tmp;
@@ -383,7 +502,7 @@ CsrWs carve(void* ws, int32_t n, int64_t e) {
     const int64_t nblocks = (e + kRsTile - 1) / kRsTile;
     const int64_t hist_n = ((int64_t)1 << passes_for(n).width) * nblocks;
     w.hist = c.take<int32_t>((size_t)hist_n);
-    w.scan = c.take<int32_t>(scan_workspace_elems(hist_n > n ? hist_n : n));
+    w.totals = c.take<int32_t>((size_t)kMaxBins);
     w.keys_tmp[0] = c.take<int32_t>((size_t)e);
     w.keys_tmp[1] = c.take<int32_t>((size_t)e);
     w.vals_tmp = c.take<int32_t>((size_t)e);
@@ -455,8 +574,8 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
         const int32_t* oin = p == 0 ? other : obuf[(p - 1) & 1];
         int32_t* kout = w.keys_tmp[p & 1];
         radix_upsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, e, shift, bits, w.hist, nblocks);
-        exclusive_scan_i32(w.hist, w.hist, ((int64_t)1 << bits) * nblocks, nullptr, w.scan, s);
-        RadixArgs a{kin, vin, oin, kout, vbuf[p & 1], obuf[p & 1], w.hist, e, nblocks, shift, bits};
+        digit_rows_scan<<<1u << bits, kDsThreads, 0, s>>>(w.hist, nblocks, w.totals);
+        RadixArgs a{kin, vin, oin, kout, vbuf[p & 1], obuf[p & 1], w.hist, w.totals, e, nblocks, shift, bits};
         if (p == 0)
             radix_downsweep<true><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
         else
