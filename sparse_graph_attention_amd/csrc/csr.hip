@@ -58,6 +58,19 @@ __device__ __forceinline__ uint64_t same_digit_lanes(uint64_t* mask, uint32_t d,
     return peers;
 }
 
+// Workgroups go to the eight XCDs in turn (workgroup b to XCD b % 8); the tile of workgroup
+// b is chosen so that each XCD takes one contiguous range of tiles, in order.  Runs of one
+// digit from neighbouring tiles are neighbours in the output, and so are neighbouring tiles'
+// entries of a digit's histogram row: the cache line shared by two tiles' writes is then
+// written by one XCD's L2, close in time, and leaves it whole rather than as partial lines.
+// (Any mapping is correct: this one is a bijection of [0, nblocks).)
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nblocks) {
+    const int64_t x = b % kXcds, k = b / kXcds, q = nblocks / kXcds, r = nblocks % kXcds;
+    return x * q + (x < r ? x : r) + k;
+}
+
 // Per-tile digit counts: hist[d * nblocks + tile].  Each wavefront counts into its own
 // histogram (fewer conflicting LDS additions), and the wavefronts' histograms are summed at
 // the end.  A whole tile of 16-byte aligned keys is read as 16-byte vectors.
@@ -69,7 +82,8 @@ __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __res
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // (each wavefront clears and fills only its own histogram before the barrier)
     for (int d = lane; d < bins; d += 64) cnt[wave][d] = 0;
-    const int64_t base = (int64_t)blockIdx.x * kRsTile;
+    const int64_t tile = xcd_tile(blockIdx.x, nblocks);
+    const int64_t base = tile * kRsTile;
     static_assert(kRsRounds % 4 == 0, "whole 16-byte vectors per thread");
     if (base + kRsTile <= e && (reinterpret_cast<uintptr_t>(keys) & 15) == 0) {
         const int4* kv = reinterpret_cast<const int4*>(keys + base);
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __res
         int c = 0;
 #pragma unroll
         for (int w = 0; w < kRsWaves; w++) c += cnt[w][d];
-        hist[(int64_t)d * nblocks + blockIdx.x] = c;
+        hist[(int64_t)d * nblocks + tile] = c;
     }
 }
 
@@ -367,8 +381,9 @@ template <bool FIRST>
 __global__ __launch_bounds__(kRsThreads) void radix_downsweep(RadixArgs a) {
     __shared__ RadixSmem sm;
     TileItems x;
-    load_tile<FIRST>(a, blockIdx.x, x);
-    sort_tile(a, blockIdx.x, x, sm);
+    const int64_t tile = xcd_tile(blockIdx.x, a.nblocks);
+    load_tile<FIRST>(a, tile, x);
+    sort_tile(a, tile, x, sm);
 }
 
 // row_ptr from the sorted keys: row_ptr[v] = first position whose key is >= v.  Position p
