@@ -168,6 +168,15 @@ __global__ __launch_bounds__(kDsThreads) void digit_rows_scan(int32_t* __restric
     if (tid == 0) totals[blockIdx.x] = carry;
 }
 
+// row_ptr[v] = p for the rows v in (prev, key], clamped to [0, n]: position p holds the first
+// item of those rows when the keys are sorted and the item before it has key prev.  Every
+// write stays in bounds, whatever the keys.
+__device__ __forceinline__ void fill_rows(int32_t* row_ptr, int32_t n, int64_t prev, int64_t key, int64_t p) {
+    const int64_t lo = prev + 1 < 0 ? 0 : prev + 1;
+    const int64_t hi = key < n ? key : n;
+    for (int64_t v = lo; v <= hi; v++) row_ptr[v] = (int32_t)p;
+}
+
 // A wavefront's items of one tile, in order: round r, lane l holds item wbase + 64 r + l.
 struct TileItems {
     int32_t key[kRsRounds], val[kRsRounds], oth[kRsRounds];
@@ -184,6 +193,14 @@ struct RadixArgs {
     const int32_t* totals;   // per digit, its count over all tiles
     int64_t e, nblocks;
     int shift, bits;
+    // last pass only (null otherwise): row_ptr is written from the tile's sorted keys.  Each
+    // tile's run of each digit leaves its first key and global start in run_key / run_pos
+    // ([digit * nblocks + tile]; start -1 for an empty run), and keys_out holds only the key
+    // of each run's last item; row_ptr_gaps fills the rows between runs.
+    int32_t* row_ptr;
+    int32_t* run_key;
+    int32_t* run_pos;
+    int32_t n;
 };
 
 struct RadixSmem {
@@ -191,6 +208,7 @@ struct RadixSmem {
     // sits in half d & 1 of word d / 2 (positions stay below 2^16, so halves never carry)
     uint32_t wpos[kRsWaves][kMaxBins / 2];
     uint16_t tdo[kMaxBins];   // tile-local start of each digit
+    uint16_t tcnt[kMaxBins];  // the tile's count of each digit
     int32_t gbase[kMaxBins];  // global start of each digit's run of this tile
     int32_t wtot[kRsWaves];
     int32_t wtot_all[kRsWaves];
@@ -321,10 +339,14 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
             if (d0 < bins) {
                 uint32_t s0 = (uint32_t)run, s1 = (uint32_t)(run + c[2 * m]);
                 sm.tdo[d0] = (uint16_t)s0;
+                sm.tcnt[d0] = (uint16_t)c[2 * m];
                 sm.gbase[d0] = run_all + gb[2 * m];
+                if (a.row_ptr && c[2 * m] == 0) a.run_pos[(int64_t)d0 * a.nblocks + tile] = -1;
                 if (d0 + 1 < bins) {
                     sm.tdo[d0 + 1] = (uint16_t)s1;
+                    sm.tcnt[d0 + 1] = (uint16_t)c[2 * m + 1];
                     sm.gbase[d0 + 1] = run_all + dt[2 * m] + gb[2 * m + 1];
+                    if (a.row_ptr && c[2 * m + 1] == 0) a.run_pos[(int64_t)(d0 + 1) * a.nblocks + tile] = -1;
                 }
                 for (int w = 0; w < kRsWaves; w++) {
                     const uint32_t cw = sm.wpos[w][d0 >> 1];
@@ -368,10 +390,26 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
     for (int li = tid; li < tile_n; li += kRsThreads) {
         const int32_t k = sm.skey[li];
         const uint32_t d = digit_of(k, shift, mask);
-        const int64_t pos = (int64_t)sm.gbase[d] + (li - (int)sm.tdo[d]);
-        if (a.keys_out) a.keys_out[pos] = k;
+        const int first = sm.tdo[d], last = first + (int)sm.tcnt[d] - 1;
+        const int64_t pos = (int64_t)sm.gbase[d] + (li - first);
         a.vals_out[pos] = sm.sval[li];
         a.oth_out[pos] = sm.soth[li];
+        if (!a.row_ptr) {
+            if (a.keys_out) a.keys_out[pos] = k;
+            continue;
+        }
+        // after the last pass the keys are sorted: within a run the rows between the previous
+        // key and this one start here; a run's first item leaves that to row_ptr_gaps
+        if (li == first) {
+            a.run_key[(int64_t)d * a.nblocks + tile] = k;
+            a.run_pos[(int64_t)d * a.nblocks + tile] = (int32_t)pos;
+        } else {
+            fill_rows(a.row_ptr, a.n, sm.skey[li - 1], k, pos);
+        }
+        if (li == last) {
+            a.keys_out[pos] = k;
+            if (pos == a.e - 1) fill_rows(a.row_ptr, a.n, k, a.n, a.e);  // the rows after the largest key
+        }
     }
     (void)base;
 }
@@ -386,40 +424,15 @@ __global__ __launch_bounds__(kRsThreads) void radix_downsweep(RadixArgs a) {
     sort_tile(a, tile, x, sm);
 }
 
-// row_ptr from the sorted keys: row_ptr[v] = first position whose key is >= v.  Position p
-// writes the rows v in (key[p-1], key[p]] (clamped to [0, n]); every write is in bounds even
-// when keys are out of range.  A thread takes kRowPtrItems consecutive positions, read as one
-// 16-byte vector when they are whole and aligned.
-constexpr int kRowPtrItems = 4;  // one 16-byte vector
-
-__global__ void row_ptr_from_sorted(const int32_t* __restrict__ skeys, int64_t e, int32_t n,
-                                    int32_t* __restrict__ row_ptr) {
-    const int64_t groups = (e + 1 + kRowPtrItems - 1) / kRowPtrItems;
-    const bool vec = (reinterpret_cast<uintptr_t>(skeys) & 15) == 0;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < groups;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p0 = t * kRowPtrItems;
-        int64_t kp = p0 > 0 ? (int64_t)skeys[p0 - 1] : -1;
-        int64_t kc[kRowPtrItems];
-        if (vec && p0 + kRowPtrItems <= e) {
-            const int4 v = reinterpret_cast<const int4*>(skeys)[t];
-            kc[0] = v.x;
-            kc[1] = v.y;
-            kc[2] = v.z;
-            kc[3] = v.w;
-        } else {
-#pragma unroll
-            for (int j = 0; j < kRowPtrItems; j++) kc[j] = p0 + j < e ? (int64_t)skeys[p0 + j] : (int64_t)n;
-        }
-#pragma unroll
-        for (int j = 0; j < kRowPtrItems; j++) {
-            const int64_t p = p0 + j;
-            if (p > e) break;
-            const int64_t lo = kp + 1 < 0 ? 0 : kp + 1;
-            const int64_t hi = kc[j] < n ? kc[j] : n;
-            for (int64_t v = lo; v <= hi; v++) row_ptr[v] = (int32_t)p;
-            kp = kc[j];
-        }
+// row_ptr_gaps: the rows between a tile-run's first key and the key of the item before it
+// (the last item of the previous non-empty run, whose key the last pass left in keys_last)
+// start at the run's first position.
+__global__ void row_ptr_gaps(const int32_t* __restrict__ run_key, const int32_t* __restrict__ run_pos, int64_t runs,
+                             const int32_t* __restrict__ keys_last, int32_t n, int32_t* __restrict__ row_ptr) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs; i += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t p = run_pos[i];
+        if (p < 0) continue;
+        fill_rows(row_ptr, n, p > 0 ? keys_last[p - 1] : -1, run_key[i], p);
     }
 }
 
@@ -505,6 +518,8 @@ Passes passes_for(int32_t n) {
 struct CsrWs {
     int32_t* hist;
     int32_t* totals;
+    int32_t* run_key;
+    int32_t* run_pos;
     int32_t* keys_tmp[2];
     int32_t* vals_tmp;
     int32_t* oth_tmp;
@@ -518,6 +533,8 @@ CsrWs carve(void* ws, int32_t n, int64_t e) {
     const int64_t hist_n = ((int64_t)1 << passes_for(n).width) * nblocks;
     w.hist = c.take<int32_t>((size_t)hist_n);
     w.totals = c.take<int32_t>((size_t)kMaxBins);
+    w.run_key = c.take<int32_t>((size_t)hist_n);
+    w.run_pos = c.take<int32_t>((size_t)hist_n);
     w.keys_tmp[0] = c.take<int32_t>((size_t)e);
     w.keys_tmp[1] = c.take<int32_t>((size_t)e);
     w.vals_tmp = c.take<int32_t>((size_t)e);
@@ -590,15 +607,19 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
         int32_t* kout = w.keys_tmp[p & 1];
         radix_upsweep<<<(unsigned)nblocks, kRsThreads, 0, s>>>(kin, e, shift, bits, w.hist, nblocks);
         digit_rows_scan<<<1u << bits, kDsThreads, 0, s>>>(w.hist, nblocks, w.totals);
-        RadixArgs a{kin, vin, oin, kout, vbuf[p & 1], obuf[p & 1], w.hist, w.totals, e, nblocks, shift, bits};
+        // the last pass also writes row_ptr (n > 0; with no rows there is nothing to write)
+        const bool rows = p == last && n > 0;
+        RadixArgs a{kin, vin, oin, kout, vbuf[p & 1], obuf[p & 1], w.hist, w.totals, e, nblocks, shift, bits,
+                    rows ? row_ptr : nullptr, w.run_key, w.run_pos, n};
         if (p == 0)
             radix_downsweep<true><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
         else
             radix_downsweep<false><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
+        if (rows) {
+            const int64_t runs = ((int64_t)1 << bits) * nblocks;
+            row_ptr_gaps<<<grid_for(runs), 256, 0, s>>>(w.run_key, w.run_pos, runs, w.keys_tmp[last & 1], n, row_ptr);
+        }
     }
-    if (n > 0)
-        row_ptr_from_sorted<<<grid_for((e + kRowPtrItems) / kRowPtrItems), 256, 0, s>>>(w.keys_tmp[last & 1], e, n,
-                                                                                      row_ptr);
     return launch_status();
 }
 
