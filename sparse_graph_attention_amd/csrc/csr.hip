@@ -43,12 +43,17 @@ __device__ __forceinline__ uint32_t digit_of(int32_t key, int shift, uint32_t ma
 }
 
 // Lanes of the wavefront whose item is valid and has digit d (as this lane's), for a valid
-// lane.  `mask` is the wavefront's table of one 64-bit lane mask per digit, all zero on entry
-// and on return: every valid lane ORs its bit into its digit's mask, reads the mask back and
+// lane (the valid lanes are a prefix of the wavefront).  When every valid lane has lane 0's
+// digit (a round inside a long row of one key) they are the valid lanes.  Otherwise `mask`,
+// the wavefront's table of one 64-bit lane mask per digit, all zero on entry and on return,
+// finds them: every valid lane ORs its bit into its digit's mask, reads the mask back and
 // clears it.  The three are single instructions of the whole wavefront, and a wavefront's LDS
 // operations complete in issue order, so each read sees the bits of every lane of the round
 // and each clear comes after every read of the round.
 __device__ __forceinline__ uint64_t same_digit_lanes(uint64_t* mask, uint32_t d, bool valid, uint64_t bit) {
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+    const uint64_t vm = __ballot(valid);
+    if (__all(!valid || d == d0)) return valid ? vm : 0ull;
     uint64_t peers = 0;
     if (valid) {
         __hip_atomic_fetch_or(mask + d, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
@@ -69,6 +74,18 @@ constexpr int kXcds = 8;
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nblocks) {
     const int64_t x = b % kXcds, k = b / kXcds, q = nblocks / kXcds, r = nblocks % kXcds;
     return x * q + (x < r ? x : r) + k;
+}
+
+// Adds one item of digit d per lane of the (whole) wavefront to its histogram: a single
+// addition when all lanes have the same digit (rounds inside a long row of one key, which
+// would otherwise queue 64 additions on one LDS address).
+__device__ __forceinline__ void count_digit(int* cnt, uint32_t d, int lane) {
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+    if (__all(d == d0)) {
+        if (lane == 0) atomicAdd(&cnt[d0], 64);
+    } else {
+        atomicAdd(&cnt[d], 1);
+    }
 }
 
 // Per-tile digit counts: hist[d * nblocks + tile].  Each wavefront counts into its own
@@ -92,10 +109,10 @@ __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __res
         for (int r = 0; r < kRsRounds / 4; r++) k[r] = kv[r * kRsThreads + tid];
 #pragma unroll
         for (int r = 0; r < kRsRounds / 4; r++) {
-            atomicAdd(&cnt[wave][digit_of(k[r].x, shift, mask)], 1);
-            atomicAdd(&cnt[wave][digit_of(k[r].y, shift, mask)], 1);
-            atomicAdd(&cnt[wave][digit_of(k[r].z, shift, mask)], 1);
-            atomicAdd(&cnt[wave][digit_of(k[r].w, shift, mask)], 1);
+            count_digit(cnt[wave], digit_of(k[r].x, shift, mask), lane);
+            count_digit(cnt[wave], digit_of(k[r].y, shift, mask), lane);
+            count_digit(cnt[wave], digit_of(k[r].z, shift, mask), lane);
+            count_digit(cnt[wave], digit_of(k[r].w, shift, mask), lane);
         }
     } else {
         int32_t k[kRsRounds];
