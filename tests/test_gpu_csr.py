@@ -61,6 +61,36 @@ def test_csr_workloads(g, ident):
         _csr_exact(g, n, src, dst)
 
 
+@pytest.mark.parametrize("case", ["one_target", "last_target", "sorted", "reversed", "sparse_keys"])
+def test_csr_key_patterns(g, case):
+    """Key layouts that stress the radix passes and the row_ptr written with the last pass:
+    every edge on one row (each 64-item round of one digit), keys already sorted or
+    reversed, and a few keys spread over many rows (most tile runs empty, long gaps of empty
+    rows between runs and after the largest key)."""
+    rng = np.random.default_rng(17)
+    n, e = 300_000, 200_000
+    other = rng.integers(0, n, e).astype(np.int32)
+    if case == "one_target":
+        key = np.zeros(e, np.int32)
+    elif case == "last_target":
+        key = np.full(e, n - 1, np.int32)
+    elif case == "sorted":
+        key = np.sort(rng.integers(0, n, e)).astype(np.int32)
+    elif case == "reversed":
+        key = np.sort(rng.integers(0, n, e))[::-1].astype(np.int32)
+    else:
+        key = rng.choice(np.array([3, 4096, 77_777, 150_001, 262_143], np.int32), e)
+    _csr_exact(g, n, key, other)
+
+
+@pytest.mark.parametrize("n", [127, 128, 129, 16_384, 16_385, (1 << 21) + 1])
+def test_csr_pass_counts(g, n):
+    """Node counts at the edges of the digit-pass counts (key bits 7, 8, 14, 15 and 22:
+    one to four passes of at most 7 bits)."""
+    src, dst = synth.random_multigraph(n, 150_000, 23, isolated=n // 10)
+    _csr_exact(g, n, dst, src)
+
+
 def test_validate_coo(g):
     src = np.array([0, 1, 5, -1, 2], np.int32)
     dst = np.array([1, 7, 2, 0, 2], np.int32)
