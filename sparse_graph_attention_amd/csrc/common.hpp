@@ -169,10 +169,18 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 void fill_i32(int32_t* p, int64_t n, int32_t value, hipStream_t s);
 void fill_f32(float* p, int64_t n, float value, hipStream_t s);
 
-// Exclusive prefix sum of in[0..n) into out[0..n); if total != nullptr, *total (device) = sum.
-// out may alias in.  Needs scan_workspace_elems(n) int32 of scratch.
+// Exclusive prefix sums, in place, of up to kScanMaxCols int32 columns of n entries each,
+// all in the same three launches; column c's total goes to *total[c] (device) when total[c]
+// is not null.  Needs scan_workspace_elems(n) int32 of scratch.
+constexpr int kScanMaxCols = 5;
+
+struct ScanCols {
+    int32_t* col[kScanMaxCols];
+    int32_t* total[kScanMaxCols];
+    int ncols;
+};
+
 size_t scan_workspace_elems(int64_t n);
-void exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total, int32_t* scratch,
-                        hipStream_t s);
+void exclusive_scan_cols(const ScanCols& sc, int64_t n, int32_t* scratch, hipStream_t s);
 
 }  // namespace gga

@@ -76,12 +76,16 @@ __global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, int64_
     }
 }
 
+// Every field of the header: the sizes, and zero counts and status (the counts come from
+// the scans that follow).
 __global__ void plan_header(PlanHeader* hdr, int32_t n, int64_t e) {
-    hdr->n = n;
-    hdr->e = (int32_t)e;
-    hdr->light_edges = kLightEdges;
-    hdr->chunk_edges = kChunkEdges;
-    hdr->magic = kPlanMagic;
+    PlanHeader h{};
+    h.n = n;
+    h.e = (int32_t)e;
+    h.light_edges = kLightEdges;
+    h.chunk_edges = kChunkEdges;
+    h.magic = kPlanMagic;
+    *hdr = h;
 }
 
 int grid_for(int64_t n) {
@@ -120,16 +124,13 @@ extern "C" int gga_plan_build(int32_t n, int64_t e, const int32_t* row_ptr, void
     pv = plan_view(plan, n, e);
     w = carve_ws(ws, n);
     hipStream_t s = as_stream(stream);
-    int32_t* hdr_i = reinterpret_cast<int32_t*>(pv.hdr);
-    fill_i32(hdr_i, sizeof(PlanHeader) / 4, 0, s);
     plan_header<<<1, 1, 0, s>>>(pv.hdr, n, e);
     if (n == 0) return launch_status();
     plan_classify<<<grid_for(n), 256, 0, s>>>(row_ptr, n, w.a, w.b, w.c, w.d, w.e);
-    exclusive_scan_i32(w.a, w.a, n, &pv.hdr->n_light, w.scan, s);
-    exclusive_scan_i32(w.b, w.b, n, &pv.hdr->n_chunks, w.scan, s);
-    exclusive_scan_i32(w.c, w.c, n, &pv.hdr->n_slots, w.scan, s);
-    exclusive_scan_i32(w.d, w.d, n, &pv.hdr->n_heavy, w.scan, s);
-    exclusive_scan_i32(w.e, w.e, n, &pv.hdr->light_sum, w.scan, s);
+    ScanCols sc{{w.a, w.b, w.c, w.d, w.e},
+                {&pv.hdr->n_light, &pv.hdr->n_chunks, &pv.hdr->n_slots, &pv.hdr->n_heavy, &pv.hdr->light_sum},
+                5};
+    exclusive_scan_cols(sc, n, w.scan, s);
     plan_fill<<<grid_for(n), 256, 0, s>>>(row_ptr, n, e, plan_bounds(e), w.a, w.b, w.c, w.d, pv);
     return launch_status();
 }

@@ -49,8 +49,10 @@ __device__ int block_exclusive(int x, int* excl, int* wave_tot) {
     return total;
 }
 
-__global__ void scan_reduce(const int32_t* in, int64_t n, int32_t* bsum) {
+// Column blockIdx.y of the scan: each launch scans all columns of a ScanCols together.
+__global__ void scan_reduce(ScanCols sc, int64_t n, int32_t* bsum, int64_t nb) {
     __shared__ int wave_tot[kScanThreads / 64];
+    const int32_t* in = sc.col[blockIdx.y];
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
     int s = 0;
 #pragma unroll
@@ -60,12 +62,14 @@ __global__ void scan_reduce(const int32_t* in, int64_t n, int32_t* bsum) {
     }
     int excl;
     int tot = block_exclusive(s, &excl, wave_tot);
-    if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
+    if (threadIdx.x == 0) bsum[blockIdx.y * nb + blockIdx.x] = tot;
 }
 
-// Single block: exclusive scan of bsum[0..nb) in place, total to *total.
-__global__ void scan_block_sums(int32_t* bsum, int64_t nb, int32_t* total) {
+// One block per column: exclusive scan of that column's block sums in place, its total
+// to total[column] when given.
+__global__ void scan_block_sums(ScanCols sc, int32_t* bsum_all, int64_t nb) {
     __shared__ int wave_tot[kScanThreads / 64];
+    int32_t* bsum = bsum_all + blockIdx.x * nb;
     int carry = 0;
     for (int64_t base = 0; base < nb; base += kScanThreads) {
         int64_t i = base + threadIdx.x;
@@ -76,18 +80,19 @@ __global__ void scan_block_sums(int32_t* bsum, int64_t nb, int32_t* total) {
         carry += tot;
         __syncthreads();
     }
-    if (threadIdx.x == 0 && total) *total = carry;
+    if (threadIdx.x == 0 && sc.total[blockIdx.x]) *sc.total[blockIdx.x] = carry;
 }
 
-__global__ void scan_down(const int32_t* in, int32_t* out, int64_t n, const int32_t* bsum) {
+__global__ void scan_down(ScanCols sc, int64_t n, const int32_t* bsum, int64_t nb) {
     __shared__ int lds[kScanTile + kScanTile / 16];
     __shared__ int wave_tot[kScanThreads / 64];
+    int32_t* col = sc.col[blockIdx.y];
     const int64_t base = (int64_t)blockIdx.x * kScanTile;
 #pragma unroll
     for (int k = 0; k < kScanItems; k++) {
         int idx = k * kScanThreads + threadIdx.x;
         int64_t i = base + idx;
-        lds[pad(idx)] = (i < n) ? in[i] : 0;
+        lds[pad(idx)] = (i < n) ? col[i] : 0;
     }
     __syncthreads();
     int s = 0;
@@ -95,7 +100,7 @@ __global__ void scan_down(const int32_t* in, int32_t* out, int64_t n, const int3
     for (int j = 0; j < kScanItems; j++) s += lds[pad(threadIdx.x * kScanItems + j)];
     int excl;
     block_exclusive(s, &excl, wave_tot);
-    int run = bsum[blockIdx.x] + excl;
+    int run = bsum[blockIdx.y * nb + blockIdx.x] + excl;
 #pragma unroll
     for (int j = 0; j < kScanItems; j++) {
         int p = pad(threadIdx.x * kScanItems + j);
@@ -108,7 +113,7 @@ __global__ void scan_down(const int32_t* in, int32_t* out, int64_t n, const int3
     for (int k = 0; k < kScanItems; k++) {
         int idx = k * kScanThreads + threadIdx.x;
         int64_t i = base + idx;
-        if (i < n) out[i] = lds[pad(idx)];
+        if (i < n) col[i] = lds[pad(idx)];
     }
 }
 
@@ -131,18 +136,20 @@ void fill_f32(float* p, int64_t n, float value, hipStream_t s) {
     fill_f32_kernel<<<grid_for(n, 256), 256, 0, s>>>(p, n, value);
 }
 
-size_t scan_workspace_elems(int64_t n) { return (size_t)((n + kScanTile - 1) / kScanTile) + 1; }
+size_t scan_workspace_elems(int64_t n) { return (size_t)kScanMaxCols * ((n + kScanTile - 1) / kScanTile) + 1; }
 
-void exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, int32_t* total, int32_t* scratch,
-                        hipStream_t s) {
+void exclusive_scan_cols(const ScanCols& sc, int64_t n, int32_t* scratch, hipStream_t s) {
+    if (sc.ncols <= 0) return;
     if (n <= 0) {
-        if (total) fill_i32(total, 1, 0, s);
+        for (int c = 0; c < sc.ncols; c++)
+            if (sc.total[c]) fill_i32(sc.total[c], 1, 0, s);
         return;
     }
     int64_t nb = (n + kScanTile - 1) / kScanTile;
-    scan_reduce<<<(unsigned)nb, kScanThreads, 0, s>>>(in, n, scratch);
-    scan_block_sums<<<1, kScanThreads, 0, s>>>(scratch, nb, total);
-    scan_down<<<(unsigned)nb, kScanThreads, 0, s>>>(in, out, n, scratch);
+    const dim3 grid((unsigned)nb, (unsigned)sc.ncols);
+    scan_reduce<<<grid, kScanThreads, 0, s>>>(sc, n, scratch, nb);
+    scan_block_sums<<<(unsigned)sc.ncols, kScanThreads, 0, s>>>(sc, scratch, nb);
+    scan_down<<<grid, kScanThreads, 0, s>>>(sc, n, scratch, nb);
 }
 
 }  // namespace gga
