@@ -58,11 +58,11 @@ KERNEL_SOURCES = {
 }
 COUNTED = {
     "fwd_w3": {"gb": 39.86, "profile": "profiles/local_fwd_dot_n1m_h8_r64_bf16.md", "sources": "fwd",
-               "digest": "842453ba8b038b16"},
+               "digest": "0f70097d25f36865"},
     "fwd_w5": {"gb": 72.56, "profile": "profiles/local_fwd_bwd_dot_n2m_zipf_h8_c32_bf16.md", "sources": "fwd",
-               "digest": "842453ba8b038b16"},
-    "bwd_w5": {"gb": 157.60, "profile": "profiles/local_fwd_bwd_dot_n2m_zipf_h8_c32_bf16.md", "sources": "bwd",
-               "digest": "542611b50cd4e571"},
+               "digest": "0f70097d25f36865"},
+    "bwd_w5": {"gb": 157.63, "profile": "profiles/local_fwd_bwd_dot_n2m_zipf_h8_c32_bf16.md", "sources": "bwd",
+               "digest": "94fbeb65e5cdd369"},
 }
 
 
