@@ -76,21 +76,10 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t nblocks) {
     return x * q + (x < r ? x : r) + k;
 }
 
-// Adds one item of digit d per lane of the (whole) wavefront to its histogram: a single
-// addition when all lanes have the same digit (rounds inside a long row of one key, which
-// would otherwise queue 64 additions on one LDS address).
-__device__ __forceinline__ void count_digit(int* cnt, uint32_t d, int lane) {
-    const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
-    if (__all(d == d0)) {
-        if (lane == 0) atomicAdd(&cnt[d0], 64);
-    } else {
-        atomicAdd(&cnt[d], 1);
-    }
-}
-
 // Per-tile digit counts: hist[d * nblocks + tile].  Each wavefront counts into its own
 // histogram (fewer conflicting LDS additions), and the wavefronts' histograms are summed at
-// the end.  A whole tile of 16-byte aligned keys is read as 16-byte vectors.
+// the end.  A whole tile of 16-byte aligned keys is read as 16-byte vectors, a lane taking
+// consecutive keys; a wavefront whose keys all share one digit adds once.
 __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __restrict__ keys, int64_t e, int shift,
                                                             int bits, int32_t* __restrict__ hist, int64_t nblocks) {
     __shared__ int cnt[kRsWaves][kMaxBins];
@@ -103,16 +92,38 @@ __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __res
     const int64_t base = tile * kRsTile;
     static_assert(kRsRounds % 4 == 0, "whole 16-byte vectors per thread");
     if (base + kRsTile <= e && (reinterpret_cast<uintptr_t>(keys) & 15) == 0) {
-        const int4* kv = reinterpret_cast<const int4*>(keys + base);
-        int4 k[kRsRounds / 4];
-#pragma unroll
-        for (int r = 0; r < kRsRounds / 4; r++) k[r] = kv[r * kRsThreads + tid];
+        // each lane counts kRsRounds consecutive keys: runs of one digit (long rows of one
+        // key, or keys sorted by earlier passes) become one addition each
+        const int4* kv = reinterpret_cast<const int4*>(keys + base) + tid * (kRsRounds / 4);
+        uint32_t d[kRsRounds];
 #pragma unroll
         for (int r = 0; r < kRsRounds / 4; r++) {
-            count_digit(cnt[wave], digit_of(k[r].x, shift, mask), lane);
-            count_digit(cnt[wave], digit_of(k[r].y, shift, mask), lane);
-            count_digit(cnt[wave], digit_of(k[r].z, shift, mask), lane);
-            count_digit(cnt[wave], digit_of(k[r].w, shift, mask), lane);
+            const int4 k = kv[r];
+            d[4 * r] = digit_of(k.x, shift, mask);
+            d[4 * r + 1] = digit_of(k.y, shift, mask);
+            d[4 * r + 2] = digit_of(k.z, shift, mask);
+            d[4 * r + 3] = digit_of(k.w, shift, mask);
+        }
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(d[0]);
+        bool same = true;
+#pragma unroll
+        for (int r = 0; r < kRsRounds; r++) same = same && d[r] == d0;
+        if (__all(same)) {
+            if (lane == 0) atomicAdd(&cnt[wave][d0], 64 * kRsRounds);
+        } else {
+            uint32_t cur = d[0];
+            int c = 1;
+#pragma unroll
+            for (int r = 1; r < kRsRounds; r++) {
+                if (d[r] == cur) {
+                    c++;
+                } else {
+                    atomicAdd(&cnt[wave][cur], c);
+                    cur = d[r];
+                    c = 1;
+                }
+            }
+            atomicAdd(&cnt[wave][cur], c);
         }
     } else {
         int32_t k[kRsRounds];
@@ -212,11 +223,12 @@ struct RadixArgs {
     int shift, bits;
     // last pass only (null otherwise): row_ptr is written from the tile's sorted keys.  Each
     // tile's run of each digit leaves its first key and global start in run_key / run_pos
-    // ([digit * nblocks + tile]; start -1 for an empty run), and keys_out holds only the key
-    // of each run's last item; row_ptr_gaps fills the rows between runs.
+    // ([digit * nblocks + tile]; start -1 for an empty run), and its last key in run_lkey;
+    // row_ptr_gaps fills the rows between runs.
     int32_t* row_ptr;
     int32_t* run_key;
     int32_t* run_pos;
+    int32_t* run_lkey;  // the key of each run's last item
     int32_t n;
 };
 
@@ -424,7 +436,7 @@ __device__ __forceinline__ void sort_tile(const RadixArgs& a, int64_t tile, cons
             fill_rows(a.row_ptr, a.n, sm.skey[li - 1], k, pos);
         }
         if (li == last) {
-            a.keys_out[pos] = k;
+            a.run_lkey[(int64_t)d * a.nblocks + tile] = k;
             if (pos == a.e - 1) fill_rows(a.row_ptr, a.n, k, a.n, a.e);  // the rows after the largest key
         }
     }
@@ -441,15 +453,58 @@ __global__ __launch_bounds__(kRsThreads) void radix_downsweep(RadixArgs a) {
     sort_tile(a, tile, x, sm);
 }
 
-// row_ptr_gaps: the rows between a tile-run's first key and the key of the item before it
-// (the last item of the previous non-empty run, whose key the last pass left in keys_last)
-// start at the run's first position.
-__global__ void row_ptr_gaps(const int32_t* __restrict__ run_key, const int32_t* __restrict__ run_pos, int64_t runs,
-                             const int32_t* __restrict__ keys_last, int32_t n, int32_t* __restrict__ row_ptr) {
+// row_ptr_gaps: the rows between a tile run's first key and the key of the item before it
+// start at the run's first position p.  That item is the last of the closest earlier
+// non-empty run in digit-major order (the order of the output): found by stepping back over
+// empty runs, or, past kGapSteps of them, by a binary search of the runs' starts
+// (dbase[d] + offsets[d][t], non-decreasing) for the run that holds position p - 1.
+constexpr int kGapSteps = 32;
+
+__global__ __launch_bounds__(256) void row_ptr_gaps(const int32_t* __restrict__ run_key,
+                                                    const int32_t* __restrict__ run_pos,
+                                                    const int32_t* __restrict__ run_lkey,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ totals, int bits, int64_t nblocks,
+                                                    int32_t n, int32_t* __restrict__ row_ptr) {
+    __shared__ int32_t dbase[kMaxBins];
+    const int bins = 1 << bits;
+    if (threadIdx.x < 64) {  // exclusive scan of the digits' totals, two digits per lane
+        const int lane = threadIdx.x;
+        const int32_t t0 = 2 * lane < bins ? totals[2 * lane] : 0, t1 = 2 * lane + 1 < bins ? totals[2 * lane + 1] : 0;
+        int32_t x = t0 + t1;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int32_t y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        const int32_t ex = x - t0 - t1;
+        if (2 * lane < bins) dbase[2 * lane] = ex;
+        if (2 * lane + 1 < bins) dbase[2 * lane + 1] = ex + t0;
+    }
+    __syncthreads();
+    const int64_t runs = (int64_t)bins * nblocks;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs; i += (int64_t)gridDim.x * blockDim.x) {
         const int32_t p = run_pos[i];
         if (p < 0) continue;
-        fill_rows(row_ptr, n, p > 0 ? keys_last[p - 1] : -1, run_key[i], p);
+        int64_t prev = -1;
+        if (p > 0) {
+            int64_t j = i - 1;
+            for (int step = 0; step < kGapSteps && j >= 0 && run_pos[j] < 0; step++) j--;
+            if (j < 0 || run_pos[j] < 0) {
+                // the largest j < i whose run starts at or before p - 1 (run 0 starts at 0)
+                int64_t lo = 0, hi = i - 1;
+                while (lo < hi) {
+                    const int64_t mid = (lo + hi + 1) / 2;
+                    if ((int64_t)dbase[mid / nblocks] + offsets[mid] <= (int64_t)p - 1)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                j = lo;
+            }
+            prev = run_lkey[j];
+        }
+        fill_rows(row_ptr, n, prev, run_key[i], p);
     }
 }
 
@@ -537,6 +592,7 @@ struct CsrWs {
     int32_t* totals;
     int32_t* run_key;
     int32_t* run_pos;
+    int32_t* run_lkey;
     int32_t* keys_tmp[2];
     int32_t* vals_tmp;
     int32_t* oth_tmp;
@@ -552,6 +608,7 @@ CsrWs carve(void* ws, int32_t n, int64_t e) {
     w.totals = c.take<int32_t>((size_t)kMaxBins);
     w.run_key = c.take<int32_t>((size_t)hist_n);
     w.run_pos = c.take<int32_t>((size_t)hist_n);
+    w.run_lkey = c.take<int32_t>((size_t)hist_n);
     w.keys_tmp[0] = c.take<int32_t>((size_t)e);
     w.keys_tmp[1] = c.take<int32_t>((size_t)e);
     w.vals_tmp = c.take<int32_t>((size_t)e);
@@ -627,14 +684,15 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
         // the last pass also writes row_ptr (n > 0; with no rows there is nothing to write)
         const bool rows = p == last && n > 0;
         RadixArgs a{kin, vin, oin, kout, vbuf[p & 1], obuf[p & 1], w.hist, w.totals, e, nblocks, shift, bits,
-                    rows ? row_ptr : nullptr, w.run_key, w.run_pos, n};
+                    rows ? row_ptr : nullptr, w.run_key, w.run_pos, w.run_lkey, n};
         if (p == 0)
             radix_downsweep<true><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
         else
             radix_downsweep<false><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
         if (rows) {
             const int64_t runs = ((int64_t)1 << bits) * nblocks;
-            row_ptr_gaps<<<grid_for(runs), 256, 0, s>>>(w.run_key, w.run_pos, runs, w.keys_tmp[last & 1], n, row_ptr);
+            row_ptr_gaps<<<grid_for(runs), 256, 0, s>>>(w.run_key, w.run_pos, w.run_lkey, w.hist, w.totals, bits,
+                                                        nblocks, n, row_ptr);
         }
     }
     return launch_status();
