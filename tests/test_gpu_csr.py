@@ -100,20 +100,54 @@ def test_validate_coo(g):
     assert int(bad.item()) == 1
 
 
-def test_plan_counts(g):
-    """The plan's header counts follow from the degree histogram."""
-    n = 6000
-    src, dst = synth.mixed_degree_graph(n, 2, hubs=(50000, 4097, 1025, 1024, 700, 65, 64))
+def _plan_tables(plan, n, e):
+    """The header, light list, chunk table and heavy list of a plan buffer (layout of
+    plan.hpp: 256-byte aligned tables after the header)."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    words = plan.view(torch.int32).cpu().numpy()
+    max_chunks = e // 65 + e // 1024 + 1
+    off_light = 256
+    off_chunks = al(off_light + n * 16)
+    off_heavy = al(off_chunks + max_chunks * 16)
+    hdr = words[:12]
+    light = words[off_light // 4: off_light // 4 + 4 * hdr[0]].reshape(-1, 4)
+    chunks = words[off_chunks // 4: off_chunks // 4 + 4 * hdr[1]].reshape(-1, 4)
+    heavy = words[off_heavy // 4: off_heavy // 4 + 4 * hdr[2]].reshape(-1, 4)
+    return hdr, light, chunks, heavy
+
+
+@pytest.mark.parametrize("n", [1, 4095, 4096, 4097, 6000, 70_000])
+def test_plan_counts(g, n):
+    """The plan's header counts and every entry of its tables follow from the degree
+    histogram (node counts around the scan's 4096-row blocks)."""
+    hubs = (50000, 4097, 1025, 1024, 700, 65, 64) if n > 8 else ()
+    src, dst = synth.mixed_degree_graph(n, 2, hubs=hubs, isolated=3 if n > 8 else 0)
+    e = int(src.size)
     t = g.Topology(n, i32(src), i32(dst))
-    hdr = t.plan[:36].view(torch.int32).cpu().numpy()
+    torch.cuda.synchronize()
+    hdr, light, chunks, heavy = _plan_tables(t.plan, n, e)
     deg = np.bincount(dst, minlength=n)
-    light = (deg <= 64).sum()
-    chunks = np.where(deg > 64, (deg + 1023) // 1024, 0)
-    assert hdr[0] == light
-    assert hdr[1] == chunks.sum()
-    assert hdr[2] == (chunks > 1).sum()
-    assert hdr[3] == chunks[chunks > 1].sum()
+    rp = np.concatenate([[0], np.cumsum(deg)])
+    nchunk = np.where(deg > 64, (deg + 1023) // 1024, 0)
+    assert hdr[0] == (deg <= 64).sum()
+    assert hdr[1] == nchunk.sum()
+    assert hdr[2] == (nchunk > 1).sum()
+    assert hdr[3] == nchunk[nchunk > 1].sum()
+    assert hdr[4] == n and hdr[9] == e and hdr[10] == 0 and hdr[11] == 0
     assert hdr[8] == deg[deg <= 64].sum()  # edges of the light rows
+    lv = np.nonzero(deg <= 64)[0]
+    np.testing.assert_array_equal(light, np.stack([lv, rp[lv], rp[lv + 1], np.zeros_like(lv)], 1))
+    want_chunks, want_heavy, slot = [], [], 0
+    for v in np.nonzero(deg > 64)[0]:
+        k = int(nchunk[v])
+        for j in range(k):
+            cb = rp[v] + 1024 * j
+            want_chunks.append((v, cb, min(cb + 1024, rp[v + 1]), slot + j if k > 1 else -1))
+        if k > 1:
+            want_heavy.append((v, slot, k, 0))
+            slot += k
+    np.testing.assert_array_equal(chunks, np.array(want_chunks, np.int64).reshape(-1, 4))
+    np.testing.assert_array_equal(heavy, np.array(want_heavy, np.int64).reshape(-1, 4))
 
 
 def test_plan_guard(g):
