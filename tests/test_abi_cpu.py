@@ -54,6 +54,21 @@ def test_binding_names_match_header():
             assert callable(getattr(g, s)), s
 
 
+def test_binding_refuses_to_import_without_the_library(tmp_path):
+    """The binding has no fallback: a copy of the package without libgga.so fails to import."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = tmp_path / "sparse_graph_attention_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "sparse_graph_attention_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import sparse_graph_attention_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libgga.so is missing" in r.stderr
+
+
 def test_version_and_status(lib):
     lib.gga_abi_version.restype = ctypes.c_int
     lib.gga_status_string.restype = ctypes.c_char_p
