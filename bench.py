@@ -388,6 +388,38 @@ def bench_heavy_tail(args, g, torch, synth):
                        bwd_gbs_algorithmic=ba / bms / 1e6))
 
 
+def bench_edge_values(g, torch, topo, n, e, width, dev, reps=20):
+    """The endpoint projection primitive at this graph's shape, timed alone: out[e] =
+    x[src[e]] over an [n, width] fp32 table, and its backward dx[u] = the sum of d_edge over
+    the out-edges of u, walked through the CSR by source.  The rates count each byte that
+    has to move once: the table (or dx), the endpoints (or eid and row_ptr) and the
+    [e, width] field."""
+    x = torch.randn(n, width, device=dev)
+    d_edge = torch.randn(e, width, device=dev)
+    out = torch.empty(e, width, device=dev)
+    dx = torch.empty(n, width, device=dev)
+
+    def timed(f):
+        f()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            f()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    fms = timed(lambda: g.gga_edge_values(x, topo.src, out=out))
+    bms = timed(lambda: g.gga_edge_values_bwd(n, d_edge, topo.row_ptr_s, topo.eid_s, dx=dx))
+    fb = 4 * n * width + 4 * e + 4 * e * width
+    bb = 4 * (n + 1) + 4 * e + 4 * e * width + 4 * n * width
+    log(f"edge_values [{e}, {width}] fp32: fwd {fms * 1e3:.1f} us ({fb / fms / 1e6:.0f} GB/s), "
+        f"bwd {bms * 1e3:.1f} us ({bb / bms / 1e6:.0f} GB/s)")
+    return {"width": width, "dtype": "f32", "reps": reps, "fwd_ms": fms, "fwd_bytes": fb,
+            "fwd_gbs": fb / fms / 1e6, "bwd_ms": bms, "bwd_bytes": bb, "bwd_gbs": bb / bms / 1e6}
+
+
 def bench_gat(args, g, torch, synth, ident):
     """The GAT layer, forward + first-order gradients; the edge-feature workload adds 16
     learned features per edge to every logit and averages the heads."""
@@ -445,7 +477,10 @@ def bench_gat(args, g, torch, synth, ident):
            "heads_combined": "concatenated" if concat else "averaged",
            "edge_features": 0 if edge is None else int(edge["f"].shape[1]),
            "step": "forward + first-order gradients", "seq_len": n}
-    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
+    extra = dict(tt, fwd_ms=fms, bwd_ms=bms)
+    if ident == 2:
+        extra["edge_values"] = bench_edge_values(g, torch, topo, n, e, heads, dev)
+    return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, extra)
 
 
 def bench_layer(args, g, torch, synth, ident):
