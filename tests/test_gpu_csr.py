@@ -116,18 +116,12 @@ def _plan_tables(plan, n, e):
     return hdr, light, chunks, heavy
 
 
-@pytest.mark.parametrize("n", [1, 4095, 4096, 4097, 6000, 70_000])
-def test_plan_counts(g, n):
-    """The plan's header counts and every entry of its tables follow from the degree
-    histogram (node counts around the scan's 4096-row blocks)."""
-    hubs = (50000, 4097, 1025, 1024, 700, 65, 64) if n > 8 else ()
-    src, dst = synth.mixed_degree_graph(n, 2, hubs=hubs, isolated=3 if n > 8 else 0)
-    e = int(src.size)
-    t = g.Topology(n, i32(src), i32(dst))
-    torch.cuda.synchronize()
-    hdr, light, chunks, heavy = _plan_tables(t.plan, n, e)
-    deg = np.bincount(dst, minlength=n)
-    rp = np.concatenate([[0], np.cumsum(deg)])
+def _plan_check(plan, n, e, rp):
+    """The plan's header counts and every entry of its tables, from the row lengths: rows of
+    at most 64 edges in the light list, longer rows cut into 1024-edge chunks, rows of more
+    than one chunk in the heavy list with consecutive partial-state slots."""
+    hdr, light, chunks, heavy = _plan_tables(plan, n, e)
+    deg = np.diff(rp)
     nchunk = np.where(deg > 64, (deg + 1023) // 1024, 0)
     assert hdr[0] == (deg <= 64).sum()
     assert hdr[1] == nchunk.sum()
@@ -137,17 +131,31 @@ def test_plan_counts(g, n):
     assert hdr[8] == deg[deg <= 64].sum()  # edges of the light rows
     lv = np.nonzero(deg <= 64)[0]
     np.testing.assert_array_equal(light, np.stack([lv, rp[lv], rp[lv + 1], np.zeros_like(lv)], 1))
-    want_chunks, want_heavy, slot = [], [], 0
-    for v in np.nonzero(deg > 64)[0]:
-        k = int(nchunk[v])
-        for j in range(k):
-            cb = rp[v] + 1024 * j
-            want_chunks.append((v, cb, min(cb + 1024, rp[v + 1]), slot + j if k > 1 else -1))
-        if k > 1:
-            want_heavy.append((v, slot, k, 0))
-            slot += k
-    np.testing.assert_array_equal(chunks, np.array(want_chunks, np.int64).reshape(-1, 4))
-    np.testing.assert_array_equal(heavy, np.array(want_heavy, np.int64).reshape(-1, 4))
+    cv = np.nonzero(deg > 64)[0]
+    k = nchunk[cv]
+    v = np.repeat(cv, k)
+    j = np.arange(v.size) - np.repeat(np.cumsum(k) - k, k)
+    cb = rp[v] + 1024 * j
+    hv = cv[k > 1]
+    first = np.cumsum(nchunk[hv]) - nchunk[hv]  # each heavy row's first slot
+    slot_of = np.full(n, -1, np.int64)
+    slot_of[hv] = first
+    slot = np.where(nchunk[v] > 1, slot_of[v] + j, -1)
+    np.testing.assert_array_equal(chunks, np.stack([v, cb, np.minimum(cb + 1024, rp[v + 1]), slot], 1).reshape(-1, 4))
+    np.testing.assert_array_equal(heavy, np.stack([hv, first, nchunk[hv], np.zeros_like(hv)], 1).reshape(-1, 4))
+
+
+@pytest.mark.parametrize("n", [1, 4095, 4096, 4097, 6000, 70_000])
+def test_plan_counts(g, n):
+    """The plan's tables follow from the degree histogram (node counts around the scan's
+    4096-row blocks)."""
+    hubs = (50000, 4097, 1025, 1024, 700, 65, 64) if n > 8 else ()
+    src, dst = synth.mixed_degree_graph(n, 2, hubs=hubs, isolated=3 if n > 8 else 0)
+    e = int(src.size)
+    t = g.Topology(n, i32(src), i32(dst))
+    torch.cuda.synchronize()
+    rp = np.concatenate([[0], np.cumsum(np.bincount(dst, minlength=n))])
+    _plan_check(t.plan, n, e, rp)
 
 
 def test_plan_guard(g):
@@ -193,3 +201,75 @@ def test_plan_guard(g):
     # rows that overlap (row_ptr not monotone)
     rp = i32(np.array([0, 100, 50, 150], np.int32))
     assert int(g.gga_plan_status(g.gga_plan_build(3, 150, rp), 3, 150).item()) == g.GGA_ERANGE
+
+
+# ---- the largest inputs the boundary takes (e < INT32_MAX; n up to INT32_MAX - 1)
+
+
+def _csr_properties(n, e, key, other, rp, col, eid, chunk=1 << 28):
+    """The unique stable CSR, checked through properties that hold at any size: row_ptr
+    runs from 0 to e without decreasing; every position lies in the row of its edge's key;
+    col is the other endpoint of that edge; eid is a permutation of [0, e) that ascends
+    within each row."""
+    rp64 = rp.long()
+    assert rp64[0].item() == 0 and rp64[-1].item() == e
+    assert bool((rp64[1:] >= rp64[:-1]).all())
+    seen = torch.zeros(e, dtype=torch.bool, device=key.device)
+    prev_key = prev_id = None
+    for p0 in range(0, e, chunk):
+        p1 = min(e, p0 + chunk)
+        ids = eid[p0:p1].long()
+        assert bool(((ids >= 0) & (ids < e)).all())
+        seen[ids] = True
+        k = key[ids].long()
+        pos = torch.arange(p0, p1, dtype=torch.long, device=key.device)
+        assert bool(((rp64[k] <= pos) & (pos < rp64[k + 1])).all())
+        assert bool((col[p0:p1] == other[ids]).all())
+        same = k[1:] == k[:-1]
+        assert bool((ids[1:][same] > ids[:-1][same]).all())
+        if prev_key is not None and k[0].item() == prev_key:
+            assert ids[0].item() > prev_id
+        prev_key, prev_id = k[-1].item(), ids[-1].item()
+        del ids, k, pos, same
+    assert bool(seen.all())
+
+
+@pytest.mark.timeout(900)
+def test_csr_max_edges(g):
+    # 2^31 - 2 edges over 2^21 rows: positions, COO indices and row_ptr values up to the
+    # largest int32 the boundary accepts
+    n, e = 1 << 21, (1 << 31) - 2
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    key = torch.randint(0, n, (e,), generator=gen, dtype=torch.int32, device="cuda")
+    other = torch.randint(0, n, (e,), generator=gen, dtype=torch.int32, device="cuda")
+    print(f"csr at the largest edge count: n={n} e={e}", flush=True)
+    rp, col, eid = g.gga_coo_to_csr(n, key, other)
+    torch.cuda.synchronize()
+    _csr_properties(n, e, key, other, rp, col, eid)
+    del key, other, col, eid
+    # the degree plan over the same row_ptr (rows of about 1024 edges: one or two chunks)
+    print(f"plan at the largest edge count: n={n} e={e}", flush=True)
+    plan = g.gga_plan_build(n, e, rp)
+    torch.cuda.synchronize()
+    _plan_check(plan, n, e, rp.cpu().numpy().astype(np.int64))
+    del rp, plan
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_csr_max_rows(g):
+    # 2^31 - 2 rows (31-bit keys: five passes) and 2^20 edges, bit-exact against the oracle
+    n, e = (1 << 31) - 2, 1 << 20
+    rng = np.random.default_rng(8)
+    key = rng.integers(0, n, e, dtype=np.int64).astype(np.int32)
+    key[:4] = (0, n - 1, n - 1, 0)
+    other = rng.integers(0, n, e, dtype=np.int64).astype(np.int32)
+    print(f"csr at the largest row count: n={n} e={e}", flush=True)
+    rp, col, eid = g.gga_coo_to_csr(n, i32(key), i32(other))
+    torch.cuda.synchronize()
+    ref = oracle.coo_to_csr(n, key, other)
+    np.testing.assert_array_equal(eid.cpu().numpy(), ref[2])
+    np.testing.assert_array_equal(col.cpu().numpy(), ref[1])
+    assert torch.equal(rp, torch.from_numpy(ref[0]).to(rp.device))
+    del rp, col, eid, ref
+    torch.cuda.empty_cache()
