@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void edge_scatter_sum(int32_t n, int32_t width
     for (int x0 = 0; x0 < width; x0 += lw) {
         const int x = x0 + li;
         float acc = 0.f;
-        for (int32_t p = beg + g; p < end; p += G) {
+        for (int64_t p = beg + g; p < end; p += G) {  // (64-bit: end may lie within G of INT32_MAX)
             const int64_t ed = eid[p];
             if (x < width) acc += d_edge[ed * width + x];
         }

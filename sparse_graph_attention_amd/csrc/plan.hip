@@ -33,14 +33,16 @@ PlanWs carve_ws(void* ws, int32_t n) {
 __global__ void plan_classify(const int32_t* __restrict__ row_ptr, int32_t n, int32_t* a, int32_t* b, int32_t* c,
                               int32_t* d, int32_t* e) {
     for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < n; v += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t deg = row_ptr[v + 1] - row_ptr[v];
+        // (64-bit: a row may hold up to 2^31 - 2 edges, and a corrupt row_ptr any difference;
+        // plan_fill reports a row with a negative length)
+        const int64_t deg = (int64_t)row_ptr[v + 1] - row_ptr[v];
         const bool light = deg <= kLightEdges;
-        const int32_t chunks = light ? 0 : (deg + kChunkEdges - 1) / kChunkEdges;
+        const int32_t chunks = light ? 0 : (int32_t)((deg + kChunkEdges - 1) / kChunkEdges);
         a[v] = light;
         b[v] = chunks;
         c[v] = chunks > 1 ? chunks : 0;
         d[v] = chunks > 1;
-        e[v] = light ? deg : 0;
+        e[v] = light && deg > 0 ? (int32_t)deg : 0;
     }
 }
 
@@ -55,15 +57,18 @@ __global__ void plan_fill(const int32_t* __restrict__ row_ptr, int32_t n, int64_
             pv.hdr->status = GGA_ERANGE;
             continue;
         }
-        const int32_t deg = end - beg;
+        const int64_t deg = (int64_t)end - beg;
         if (deg <= kLightEdges) {
             pv.light[a[v]] = make_int4((int32_t)v, beg, end, 0);
             continue;
         }
-        const int32_t chunks = (deg + kChunkEdges - 1) / kChunkEdges;
+        const int32_t chunks = (int32_t)((deg + kChunkEdges - 1) / kChunkEdges);
         const bool heavy = chunks > 1;
-        if ((int64_t)b[v] + chunks > bnd.max_chunks ||
-            (heavy && ((int64_t)d[v] >= bnd.max_heavy || (int64_t)c[v] + chunks > bnd.max_slots))) {
+        // the scans' positions are checked at both ends: other rows of a corrupt row_ptr
+        // (reported above) may have pushed them out of the tables
+        if (b[v] < 0 || (int64_t)b[v] + chunks > bnd.max_chunks ||
+            (heavy && (d[v] < 0 || (int64_t)d[v] >= bnd.max_heavy || c[v] < 0 ||
+                       (int64_t)c[v] + chunks > bnd.max_slots))) {
             pv.hdr->status = GGA_ERANGE;
             continue;
         }

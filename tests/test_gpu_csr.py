@@ -203,6 +203,33 @@ def test_plan_guard(g):
     assert int(g.gga_plan_status(g.gga_plan_build(3, 150, rp), 3, 150).item()) == g.GGA_ERANGE
 
 
+def test_plan_corrupt_row_ptr(g):
+    """A row_ptr with 1100 entries set near INT32_MAX: the rows before them claim about 2^21
+    chunks each, so the chunk counts add up past 2^31 in the 32-bit scans.  Every table
+    position is checked at both ends before it is written; the plan reports GGA_ERANGE and
+    a forward handed it writes nothing."""
+    n, e, heads, c = 4096, 300_000, 2, 16
+    rng = np.random.default_rng(0)
+    deg = rng.integers(0, 2 * e // n, n)
+    deg = (deg * (e / deg.sum())).astype(np.int64)
+    deg[-1] += e - deg.sum()
+    rp = np.concatenate([[0], np.cumsum(deg)]).astype(np.int64)
+    rp[rng.choice(np.arange(1, n), 1100, replace=False)] = np.iinfo(np.int32).max - 1
+    print(f"plan over a corrupt row_ptr: n={n} e={e}", flush=True)
+    plan = g.gga_plan_build(n, e, i32(rp))
+    torch.cuda.synchronize()
+    assert int(g.gga_plan_status(plan, n, e).item()) == g.GGA_ERANGE
+    # the edges themselves are valid: a forward over them with this plan leaves its outputs
+    col = i32(rng.integers(0, n, e))
+    q, k, v = (torch.from_numpy(rng.standard_normal((n, heads, c)).astype(np.float32)).cuda() for _ in range(3))
+    desc = g.make_desc(n, e, heads, c, g.GGA_SCORE_DOT, g.GGA_F32)
+    out = torch.full((n, heads, c), 7.0, device="cuda")
+    lse = torch.full((n, heads), 7.0, device="cuda")
+    g.gga_local_attn_fwd(desc, q, k, v, i32(rp), col, plan, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()) and bool((lse == 7.0).all())
+
+
 # ---- the largest inputs the boundary takes (e < INT32_MAX; n up to INT32_MAX - 1)
 
 
