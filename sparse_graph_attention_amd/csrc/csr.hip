@@ -149,9 +149,10 @@ __global__ __launch_bounds__(kRsThreads) void radix_upsweep(const int32_t* __res
 
 // Each digit's row of per-tile counts hist[d * nblocks + t] becomes its exclusive scan over
 // the tiles, in place, and totals[d] the digit's count.  One workgroup per digit; a thread
-// takes kDsItems consecutive tiles of each kDsThreads * kDsItems.
+// takes kDsItems consecutive tiles of each kDsThreads * kDsItems (6144: one round for up to
+// 25M edges, where a round's barriers and latency are most of the kernel's time).
 constexpr int kDsThreads = 1024;
-constexpr int kDsItems = 4;
+constexpr int kDsItems = 6;
 
 __global__ __launch_bounds__(kDsThreads) void digit_rows_scan(int32_t* __restrict__ hist, int64_t nblocks,
                                                               int32_t* __restrict__ totals) {
