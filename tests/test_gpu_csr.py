@@ -300,3 +300,29 @@ def test_csr_max_rows(g):
     assert torch.equal(rp, torch.from_numpy(ref[0]).to(rp.device))
     del rp, col, eid, ref
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_edge_values_bwd_max_edges(g):
+    # the endpoint projection's backward walks the CSR keyed by the endpoint with 64-bit
+    # positions: the last row ends at 2^31 - 2, where a 32-bit step past it would wrap
+    n, e = 1 << 21, (1 << 31) - 2
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    key = torch.randint(0, n, (e,), generator=gen, dtype=torch.int32, device="cuda")
+    print(f"edge_values_bwd at the largest edge count: n={n} e={e}", flush=True)
+    rp, _, eid = g.gga_coo_to_csr(n, key, key)
+    d_edge = torch.rand(e, 1, generator=gen, device="cuda")
+    dx = g.gga_edge_values_bwd(n, d_edge, rp, eid)
+    torch.cuda.synchronize()
+    del eid
+    ref = torch.zeros(n, dtype=torch.float64, device="cuda")
+    chunk = 1 << 28
+    for p0 in range(0, e, chunk):
+        p1 = min(e, p0 + chunk)
+        ref.index_add_(0, key[p0:p1].long(), d_edge[p0:p1, 0].double())
+    deg = (rp[1:] - rp[:-1]).double()
+    # fp32 sums of deg terms: rtol 1e-4 and atol 1e-5 sqrt(deg) (sums over long axes)
+    err = (dx[:, 0].double() - ref).abs()
+    assert bool((err <= 1e-4 * ref.abs() + 1e-5 * deg.clamp(min=1.0).sqrt()).all()), float(err.max())
+    del key, rp, d_edge, dx, ref, deg, err
+    torch.cuda.empty_cache()
