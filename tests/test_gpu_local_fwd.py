@@ -154,3 +154,46 @@ def test_workload_1m_full(g):
 
 def test_workload_heavy_tail_full(g):
     _workload_dot(g, 5)
+
+
+@pytest.mark.timeout(900)
+def test_local_fwd_max_edges(g):
+    """The largest edge count the attention calls take (e <= INT32_MAX - 4096: a row's
+    positions plus a loop step stay in int32), over 2^21 rows of about 1024 edges (one or two
+    chunks each, partial states merged).  Sampled rows -- the first, the last (their edges at
+    the largest positions), the longest and 64 at random -- against the oracle, which gets
+    those rows' in-edges filtered from the seeded COO in COO order."""
+    n, heads, c = 1 << 21, 1, 4
+    e = (1 << 31) - 1 - 4096
+    gen = torch.Generator(device="cuda").manual_seed(10)
+    dst = torch.randint(0, n, (e,), generator=gen, dtype=torch.int32, device="cuda")
+    src = torch.randint(0, n, (e,), generator=gen, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(10)
+    q32, k32, v32 = (rng.standard_normal((n, heads, c)).astype(np.float32) for _ in range(3))
+    print(f"fwd at the largest edge count: n={n} e={e} H={heads} C={c} f32", flush=True)
+    topo = g.Topology(n, src, dst)
+    scale = c ** -0.5
+    desc = g.make_desc(n, e, heads, c, g.GGA_SCORE_DOT, g.GGA_F32, scale)
+    out, lse = g.gga_local_attn_fwd(desc, *(torch.from_numpy(x).cuda() for x in (q32, k32, v32)), topo.row_ptr,
+                                    topo.col, topo.plan)
+    torch.cuda.synchronize()
+    del topo
+    deg = torch.zeros(n, dtype=torch.long, device="cuda")
+    for p0 in range(0, e, 1 << 28):
+        deg += torch.bincount(dst[p0:p0 + (1 << 28)].long(), minlength=n)
+    rows = np.unique(np.concatenate([[0, 1, n - 3, n - 2, n - 1, int(deg.argmax())],
+                                     rng.integers(0, n, 64)])).astype(np.int32)
+    sel = torch.zeros(n, dtype=torch.bool, device="cuda")
+    sel[torch.from_numpy(rows).long().cuda()] = True
+    sub_s, sub_d = [], []
+    for p0 in range(0, e, 1 << 28):
+        d = dst[p0:p0 + (1 << 28)]
+        idx = sel[d.long()].nonzero()[:, 0]
+        sub_s.append(src[p0:p0 + (1 << 28)][idx].cpu())
+        sub_d.append(d[idx].cpu())
+    del dst, src, deg, sel
+    torch.cuda.empty_cache()
+    og = oracle.Graph(n, torch.cat(sub_s).numpy(), torch.cat(sub_d).numpy())
+    ref_out, ref_lse = oracle.local_fwd_dot(q32, k32, v32, og, scale, rows=rows)
+    assert_close(out.cpu().numpy()[rows], ref_out, "f32", "out")
+    assert_close(lse.cpu().numpy()[rows], ref_lse, "f32", "lse")
