@@ -456,10 +456,13 @@ __global__ __launch_bounds__(kRsThreads) void radix_downsweep(RadixArgs a) {
 
 // row_ptr_gaps: the rows between a tile run's first key and the key of the item before it
 // start at the run's first position p.  That item is the last of the closest earlier
-// non-empty run in digit-major order (the order of the output): found by stepping back over
-// empty runs, or, past kGapSteps of them, by a binary search of the runs' starts
-// (dbase[d] + offsets[d][t], non-decreasing) for the run that holds position p - 1.
+// non-empty run in digit-major order (the order of the output).  A thread takes kGapRuns
+// consecutive runs, their loads issued together: within the group that run is the previous
+// non-empty one of the group, and only the group's first non-empty run looks further back,
+// stepping back over empty runs or, past kGapSteps of them, by a binary search of the runs'
+// starts (dbase[d] + offsets[d][t], non-decreasing) for the run that holds position p - 1.
 constexpr int kGapSteps = 32;
+constexpr int kGapRuns = 4;
 
 __global__ __launch_bounds__(256) void row_ptr_gaps(const int32_t* __restrict__ run_key,
                                                     const int32_t* __restrict__ run_pos,
@@ -484,12 +487,28 @@ __global__ __launch_bounds__(256) void row_ptr_gaps(const int32_t* __restrict__ 
     }
     __syncthreads();
     const int64_t runs = (int64_t)bins * nblocks;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs; i += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t p = run_pos[i];
-        if (p < 0) continue;
+    const int64_t groups = (runs + kGapRuns - 1) / kGapRuns;
+    for (int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; gi < groups;
+         gi += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i0 = gi * kGapRuns;
+        int32_t pos[kGapRuns], key[kGapRuns], lkey[kGapRuns];
+#pragma unroll
+        for (int r = 0; r < kGapRuns; r++) {  // (an empty run's keys are never used)
+            const bool in = i0 + r < runs;
+            pos[r] = in ? run_pos[i0 + r] : -1;
+            key[r] = in ? run_key[i0 + r] : 0;
+            lkey[r] = in ? run_lkey[i0 + r] : 0;
+        }
+        int first = kGapRuns;
+#pragma unroll
+        for (int r = kGapRuns - 1; r >= 0; r--)
+            if (pos[r] >= 0) first = r;
+        if (first == kGapRuns) continue;
         int64_t prev = -1;
+        const int32_t p = pos[first];
         if (p > 0) {
-            int64_t j = i - 1;
+            const int64_t i = i0 + first;
+            int64_t j = i0 - 1;  // the runs i0 .. i - 1 are empty
             for (int step = 0; step < kGapSteps && j >= 0 && run_pos[j] < 0; step++) j--;
             if (j < 0 || run_pos[j] < 0) {
                 // the largest j < i whose run starts at or before p - 1 (run 0 starts at 0)
@@ -505,7 +524,12 @@ __global__ __launch_bounds__(256) void row_ptr_gaps(const int32_t* __restrict__ 
             }
             prev = run_lkey[j];
         }
-        fill_rows(row_ptr, n, prev, run_key[i], p);
+#pragma unroll
+        for (int r = 0; r < kGapRuns; r++) {
+            if (r < first || pos[r] < 0) continue;
+            fill_rows(row_ptr, n, prev, key[r], pos[r]);
+            prev = lkey[r];
+        }
     }
 }
 
@@ -692,7 +716,7 @@ extern "C" int gga_coo_to_csr(int32_t n, int64_t e, const int32_t* key, const in
             radix_downsweep<false><<<(unsigned)nblocks, kRsThreads, 0, s>>>(a);
         if (rows) {
             const int64_t runs = ((int64_t)1 << bits) * nblocks;
-            row_ptr_gaps<<<grid_for(runs), 256, 0, s>>>(w.run_key, w.run_pos, w.run_lkey, w.hist, w.totals, bits,
+            row_ptr_gaps<<<grid_for((runs + kGapRuns - 1) / kGapRuns), 256, 0, s>>>(w.run_key, w.run_pos, w.run_lkey, w.hist, w.totals, bits,
                                                         nblocks, n, row_ptr);
         }
     }
