@@ -47,6 +47,11 @@ def _t(a):
     (2000, 0, 80, 0, 0, True),  # empty contraction beside the streaming shapes: c is the bias
     # transposed a over a long k (split-k), ragged k, with bias
     (128, 170001, 64, 1, 0, True), (48, 20000, 64, 1, 0, False), (64, 16384, 112, 1, 0, True),
+    # few outputs over a long k with a transposed a: split k at every tile count of m and n in
+    # {32, 64, 128}, k at and just past 4096, ragged k ranges, a k of two million
+    (32, 4096, 32, 1, 0, True), (32, 5000, 64, 1, 0, False), (32, 9001, 128, 1, 0, True), (64, 4097, 32, 1, 0, False),
+    (64, 33333, 64, 1, 0, True), (64, 6000, 128, 1, 0, False), (128, 12345, 32, 1, 0, True),
+    (128, 4100, 64, 1, 0, False), (128, 2100000, 64, 1, 0, False),
 ])
 def test_linear(g, m, k, n, ta, tb, bias):
     print(f"linear m={m} k={k} n={n} ta={ta} tb={tb}", flush=True)
@@ -61,6 +66,18 @@ def test_linear(g, m, k, n, ta, tb, bias):
         ref = ref + bv
     # fp32 accumulation over k terms of size ~1: allow sqrt(k) growth of the absolute error
     assert_close(c.cpu().numpy(), ref, "f32", "c", atol=1e-5 * max(1.0, np.sqrt(k)))
+
+
+def test_linear_split_k_accumulate(g):
+    """c += a^T b over a long k: the split-k partials are added into c in a fixed order."""
+    rng = np.random.default_rng(5)
+    a, b = rng.standard_normal((70000, 128)).astype(np.float32), rng.standard_normal((70000, 64)).astype(np.float32)
+    c0 = rng.standard_normal((128, 64)).astype(np.float32)
+    acc = _t(c0)
+    g.gga_linear_accumulate(_t(a), _t(b), acc, trans_a=True)
+    torch.cuda.synchronize()
+    ref = a.T.astype(np.float64) @ b.astype(np.float64) + c0
+    assert_close(acc.cpu().numpy(), ref, "f32", "c+=", atol=1e-5 * np.sqrt(70000))
 
 
 def test_linear_deterministic(g):
