@@ -647,8 +647,19 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float* __restrict__ 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t i = (int64_t)blockIdx.x * 64 + lane;
     float s = 0.f;
-    if (i < mn)
-        for (int z = wave; z < splits; z += 16) s += part[(int64_t)z * mn + i];
+    if (i < mn) {
+        // eight of the wavefront's splits are requested at a time and added in split order
+        // (the same sums as one at a time)
+        int z = wave;
+        for (; z + 7 * 16 < splits; z += 8 * 16) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = part[(int64_t)(z + 16 * j) * mn + i];
+#pragma unroll
+            for (int j = 0; j < 8; j++) s += v[j];
+        }
+        for (; z < splits; z += 16) s += part[(int64_t)z * mn + i];
+    }
     sm[wave][lane] = s;
     __syncthreads();
     if (wave == 0 && i < mn) {
