@@ -317,11 +317,25 @@ __global__ __launch_bounds__(NW * 64) void seg_reduce(Seg sg, int32_t H, int32_t
         const int32_t b = ent.y;
         const int64_t t1 = (hi - 1) / sg.rs;
         float a = 0.f;
-        if (x < tot)
-            for (int64_t tt = t0 + wave; tt <= t1; tt += NW) {
+        if (x < tot) {
+            // eight of the wavefront's tiles are requested at a time and added in tile order
+            int64_t tt = t0 + wave;
+            for (; tt + 7 * NW <= t1; tt += 8 * NW) {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const int64_t u = tt + (int64_t)j * NW;
+                    const int slot = (u == t0 && lo != t0 * sg.rs) ? 1 : 0;
+                    v[j] = part[((u * 2 + slot) * H + h) * per + e];
+                }
+#pragma unroll
+                for (int j = 0; j < 8; j++) a += v[j];
+            }
+            for (; tt <= t1; tt += NW) {
                 const int slot = (tt == t0 && lo != t0 * sg.rs) ? 1 : 0;
                 a += part[((tt * 2 + slot) * H + h) * per + e];
             }
+        }
         __syncthreads();
         sm[wave][lane] = a;
         __syncthreads();

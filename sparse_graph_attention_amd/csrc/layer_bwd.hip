@@ -284,8 +284,19 @@ __global__ __launch_bounds__(1024) void colsum_reduce(int nb, int ncols, const f
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int c = blockIdx.x * 64 + lane;
     float a = 0.f;
-    if (c < ncols)
-        for (int b = wave; b < nb; b += 16) a += part[(int64_t)b * ncols + c];
+    if (c < ncols) {
+        // eight of the wavefront's ranges are requested at a time and added in range order
+        // (the same sums as one at a time)
+        int b = wave;
+        for (; b + 7 * 16 < nb; b += 8 * 16) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = part[(int64_t)(b + 16 * j) * ncols + c];
+#pragma unroll
+            for (int j = 0; j < 8; j++) a += v[j];
+        }
+        for (; b < nb; b += 16) a += part[(int64_t)b * ncols + c];
+    }
     sm[wave][lane] = a;
     __syncthreads();
     if (wave != 0 || c >= ncols) return;
