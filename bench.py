@@ -63,6 +63,8 @@ COUNTED = {
                "digest": "0f70097d25f36865"},
     "bwd_w5": {"gb": 157.63, "profile": "profiles/local_fwd_bwd_dot_n2m_zipf_h8_c32_bf16.md", "sources": "bwd",
                "digest": "94fbeb65e5cdd369"},
+    "bwd_w4": {"gb": 39.69, "profile": "profiles/gated_layer_n262k_d256_h4.md", "sources": "bwd",
+               "digest": "94fbeb65e5cdd369"},
 }
 
 
@@ -517,7 +519,8 @@ def bench_layer(args, g, torch, synth, ident):
         _mark(tm, "f0")
         f = layers.gated_layer_forward(pd, topo, heads, node_ptr=node_ptr_d)
         _mark(tm, "f1")
-        layers.gated_layer_backward(pd, f, topo, heads, dod, node_ptr=node_ptr_d)
+        layers.gated_layer_backward(pd, f, topo, heads, dod, node_ptr=node_ptr_d,
+                                    mark=None if tm is None else (lambda name: _mark(tm, name)))
         _mark(tm, "b1")
 
     tm = Timer(torch, torch.cuda.current_stream())
@@ -541,8 +544,21 @@ def bench_layer(args, g, torch, synth, ident):
         cpu = {"value": e / dt / 1e9, "unit": "GEdges/s", "cores": oracle.threads(), "kind": "oracle",
                "sample": f"the whole step (layer forward + first-order gradients), fp64 (numpy matmuls for the "
                          f"dense products), {dt:.1f} s"}
-    roof = roofline("mfma", flops / (ms * 1e-3) / 1e12, MFMA_F32_PEAK_TFLOPS, "TFLOP/s", None,
-                    kernel="whole layer step (fp32 GEMMs dominate the flops)", flops_per_step=flops, launch_ms=ms)
+    kms = tm.phase_ms("local_bwd0", "local_bwd1")
+    if node_ptr is None:
+        # the dominant call of the step: the local attention's backward (pass A over the CSR
+        # by destination, pass B over the CSR by source, the merges), HBM bound
+        alg = bwd_bytes(n, e, heads, c, 4)
+        roof = roofline("hbm", alg / (kms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s", counted_traffic("bwd_w4"),
+                        kernel="local attention backward call (bwd_dst_kernel, bwd_src_kernel, bwd_merge)",
+                        alg_bytes_per_launch=alg, launch_ms=kms, step_share=kms / ms,
+                        dense_tflops_per_step=flops / (ms * 1e-3) / 1e12)
+    else:
+        # small graphs: each graph's key and value rows stay in the caches, so a per-edge byte
+        # count is no HBM count; the step's dense contractions are its roofline
+        roof = roofline("mfma", flops / (ms * 1e-3) / 1e12, MFMA_F32_PEAK_TFLOPS, "TFLOP/s", None,
+                        kernel="whole layer step (fp32 GEMMs dominate the flops)", flops_per_step=flops,
+                        launch_ms=ms, local_bwd_ms=kms)
     cfg = {"nodes": n, "edges": e, "heads": heads, "head_dim": c, "d_model": d, "graphs": w.batch,
            "storage": "fp32", "step": "layer forward + first-order gradients", "seq_len": n}
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))

@@ -108,10 +108,12 @@ def gated_layer_forward(p: dict, topo: Topology, heads: int, eps: float = 1e-6, 
 
 
 def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: torch.Tensor, eps: float = 1e-6,
-                         ln_eps: float = 1e-5, node_ptr: torch.Tensor | None = None):
+                         ln_eps: float = 1e-5, node_ptr: torch.Tensor | None = None, mark=None):
     """First-order gradients of sum(out * d_out) for every input and parameter of the gated
     local-global layer, from the forward's intermediates.  topo must hold the CSR by source
-    (Topology(..., backward=True)); the forward must have run in fp32."""
+    (Topology(..., backward=True)); the forward must have run in fp32.  mark (optional) is
+    called with "local_bwd0" and "local_bwd1" on the host right before and after the local
+    attention's backward call is enqueued (a benchmark records stream events there)."""
     x = p["x"]
     n, d = x.shape
     r = d // heads
@@ -120,8 +122,12 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
     d_wo = gga_linear(fwd["y"], d_pre, trans_a=True)
     d_loc, d_glob, d_x, d_wg, d_bg = gga_gated_combine_bwd(x, p["w_g"], p["b_g"], fwd["local"], fwd["glob"], d_y,
                                                            d_pre)
+    if mark is not None:
+        mark("local_bwd0")
     d_q, d_k, d_v = gga_local_attn_bwd(fwd["desc"], fwd["q"], fwd["k"], fwd["v"], fwd["local3"], fwd["lse"],
                                        d_loc.view(n, heads, r), topo)
+    if mark is not None:
+        mark("local_bwd1")
     if node_ptr is None:
         gga_global_linear_bwd(fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"], d_glob.view(n, heads, r), d_q, d_k,
                               d_v, eps)
