@@ -143,3 +143,49 @@ def test_edge_gradient_finite_differences():
             if abs(z) < 1e-3:  # the LeakyReLU kink
                 continue
             assert abs((loss(sp) - loss(sm)) / (2 * h) - b["d_s_edge"][e_i, k]) < 1e-7
+
+
+def test_coefficients_select_columns_for_identity_weights():
+    """Closed-form special case of both coefficient maps: with W = I and a one-hot attention
+    vector per head (entry j_k of head k), the coefficient of row n and head k is the input's
+    column k*C + j_k (Tinymesh "Composition": one coefficient per node and head of X W)."""
+    rng = np.random.default_rng(3)
+    n, heads, c = 7, 3, 4
+    x = rng.standard_normal((n, heads * c))
+    j = np.array([2, 0, 3])
+    a = np.zeros((heads, c))
+    a[np.arange(heads), j] = 1.0
+    b = np.zeros((heads, c))
+    b[np.arange(heads), (j + 1) % c] = 1.0
+    hf, s_src, s_dst = oracle.gat_coefficients(x, np.eye(heads * c), a, b)
+    np.testing.assert_array_equal(hf.reshape(n, -1), x)
+    np.testing.assert_array_equal(s_src, x[:, np.arange(heads) * c + j])
+    np.testing.assert_array_equal(s_dst, x[:, np.arange(heads) * c + (j + 1) % c])
+    he, s_edge = oracle.edge_coefficients(x, np.eye(heads * c), a)
+    np.testing.assert_array_equal(he.reshape(n, -1), x)
+    np.testing.assert_array_equal(s_edge, x[:, np.arange(heads) * c + j])
+
+
+def test_coefficients_follow_a_head_permutation():
+    """Permuting the heads (W's column blocks with the rows of a_s, a_t) permutes the
+    coefficients' head axis the same way."""
+    rng = np.random.default_rng(4)
+    n, fin, heads, c = 9, 5, 4, 3
+    x, w = rng.standard_normal((n, fin)), rng.standard_normal((fin, heads * c))
+    a_s, a_t = rng.standard_normal((heads, c)), rng.standard_normal((heads, c))
+    perm = np.array([2, 0, 3, 1])
+    wp = w.reshape(fin, heads, c)[:, perm].reshape(fin, heads * c)
+    _, s1, d1 = oracle.gat_coefficients(x, w, a_s, a_t)
+    _, s2, d2 = oracle.gat_coefficients(x, wp, a_s[perm], a_t[perm])
+    np.testing.assert_allclose(s2, s1[:, perm], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(d2, d1[:, perm], rtol=1e-12, atol=1e-12)
+
+
+def test_phi_grad_matches_finite_differences():
+    """d phi / dx (phi = elu + 1) against central differences of the oracle's phi, away from
+    the kink at 0 where the one-sided derivatives (1 and e^0 = 1) agree anyway."""
+    x = np.concatenate([np.linspace(-6, -0.01, 50), np.linspace(0.01, 6, 50)])
+    h = 1e-6
+    fd = (oracle.phi(x + h) - oracle.phi(x - h)) / (2 * h)
+    np.testing.assert_allclose(oracle.phi_grad(x), fd, rtol=1e-7, atol=1e-8)
+    assert oracle.phi_grad(np.array([0.0]))[0] == 1.0
