@@ -1057,10 +1057,11 @@ Split pick_split(int32_t m, int32_t k, int32_t n) {
     const int64_t tiles = (int64_t)((m + BM - 1) / BM) * ((n + bn - 1) / bn);
     Split s{1, k};
     if (tiles < 512 && k > 1024) {
-        // about 2048 workgroups in all; outputs of at most four tiles take 512 (longer k
-        // ranges, one round of resident workgroups: measured 4-9% faster on [128 x 170000]^T
-        // [170000 x 64] and [256 x 262144]^T [262144 x 256], slower with twelve tiles)
-        const int64_t target = tiles <= 4 ? 512 : 2048;
+        // one round of resident workgroups in all: 512 for outputs of at most four tiles, 768
+        // (three 128 x 128 workgroups per CU) for larger ones.  Against 2048: 4-9% faster on
+        // [128 x 170000]^T [170000 x 64] and [256 x 262144]^T [262144 x 256], 0-11% on the
+        // 256 x 768, 256 x 512, 512 x 512 and 512 x 1536 outputs (512 there was slower)
+        const int64_t target = tiles <= 4 ? 512 : 768;
         int64_t want = (target + tiles - 1) / tiles;
         int64_t by_k = k / 256;
         int64_t sp = want < by_k ? want : by_k;
