@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SCRIPT = r'''
 import sys
 import numpy as np
-sys.path.insert(0, sys.argv[1])
+sys.path.insert(0, globals().get("ROOT_DIR") or sys.argv[1])
 import oracle, synth
 
 def run():
@@ -89,14 +89,16 @@ def test_oracle_under_sanitizers(tmp_path):
         if not os.path.isabs(p):
             pytest.skip(f"{name} is not available")
         runtimes.append(p)
-    env = dict(os.environ, ORACLE_LIB=lib, LD_PRELOAD=" ".join(runtimes), OMP_NUM_THREADS="2",
+    # the sanitizer runtimes go first; whatever the environment already preloads stays after them
+    preload = " ".join(runtimes + [p for p in [os.environ.get("LD_PRELOAD", "")] if p])
+    env = dict(os.environ, ORACLE_LIB=lib, LD_PRELOAD=preload, OMP_NUM_THREADS="2",
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([sys.executable, str(script), ROOT, str(out)], env=env, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0, f"sanitized oracle failed:\n{r.stderr[-4000:]}"
     assert "runtime error" not in r.stderr, r.stderr[-4000:]
     san = np.load(out)
-    ns = {}
+    ns = {"ROOT_DIR": ROOT}
     exec(compile(SCRIPT.replace('if __name__ == "__main__":', "if False:"), "drive", "exec"), ns)
     sys.path.insert(0, ROOT)
     plain = ns["run"]()
