@@ -397,11 +397,15 @@ int gga_gated_combine_bwd(int32_t n, int32_t d, const float *x, const float *w_g
  * The results are ADDED to d_q, d_k, d_v (fp32 [n,H,r]), so the local branch's
  * gradients can be written there first.  Requires r <= 64.  dS, dz sums over nodes use
  * a fixed range order (deterministic).
+ * g_fw (fp32 [n,H,r], device, may be NULL): the G this forward wrote.  num_i enters the
+ * gradients only through dG_i . G_i; given g_fw, that term reads it and num_i is not
+ * formed again (a third fewer matrix products); NULL forms it from S.  The two agree to
+ * rounding.  Not checked against q, S, z: a G from other inputs gives other gradients.
  */
 size_t gga_global_linear_bwd_workspace(int32_t n, int32_t heads, int32_t r);
 int gga_global_linear_bwd(int32_t n, int32_t heads, int32_t r, const float *q, const float *k, const float *v,
-                          float eps, const float *s, const float *z, const float *d_g, float *d_q, float *d_k,
-                          float *d_v, void *ws, size_t ws_bytes, void *stream);
+                          float eps, const float *s, const float *z, const float *d_g, const float *g_fw,
+                          float *d_q, float *d_k, float *d_v, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Batches of graphs ("Gated Local-Global Graph Attention", Implementation notes
@@ -442,13 +446,13 @@ int gga_global_linear_batch_fwd(int32_t n, int32_t batch, const int32_t *node_pt
 
 /*
  * Its backward (gga_global_linear_bwd per graph, with s [batch,H,r,r] and
- * z [batch,H,r] from the forward): adds the gradients into d_q, d_k, d_v.
- * Requires r <= 64.  Workspace: gga_global_linear_batch_workspace.
+ * z [batch,H,r] from the forward, and g_fw as there): adds the gradients into d_q,
+ * d_k, d_v.  Requires r <= 64.  Workspace: gga_global_linear_batch_workspace.
  */
 int gga_global_linear_batch_bwd(int32_t n, int32_t batch, const int32_t *node_ptr, int32_t heads, int32_t r,
                                 const float *q, const float *k, const float *v, float eps, const float *s,
-                                const float *z, const float *d_g, float *d_q, float *d_k, float *d_v, void *ws,
-                                size_t ws_bytes, void *stream);
+                                const float *z, const float *d_g, const float *g_fw, float *d_q, float *d_k,
+                                float *d_v, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * GAT variants the Tinymesh page ("Evidence and limits") lists as not yet

@@ -85,7 +85,7 @@ def _load() -> ctypes.CDLL:
         "gga_gated_combine_bwd_workspace": ([i32, i32], sz),
         "gga_gated_combine_bwd": ([i32, i32, P, P, f32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_global_linear_bwd_workspace": ([i32, i32, i32], sz),
-        "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_batch_edges": ([i32, P, P, i64, P, P, P, P, P, P], ctypes.c_int),
         "gga_relation_sources": ([i32, i32, i64, P, P, i32, P, P, P, P], ctypes.c_int),
         "gga_local_attn_fwd_edge_workspace": ([D], sz),
@@ -96,7 +96,7 @@ def _load() -> ctypes.CDLL:
         "gga_head_mean_bwd": ([i32, i32, i32, P, P, P], ctypes.c_int),
         "gga_global_linear_batch_workspace": ([i32, i32, i32, i32], sz),
         "gga_global_linear_batch_fwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, sz, P], ctypes.c_int),
-        "gga_global_linear_batch_bwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, sz, P],
+        "gga_global_linear_batch_bwd": ([i32, i32, P, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, P, sz, P],
                                         ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -450,14 +450,15 @@ def gga_gated_combine_bwd(x, w_g, b_g: float, l, g, d_y, d_x_in, d_l=None, d_g=N
     return d_l, d_g, d_x_out, d_w_g, d_b_g
 
 
-def gga_global_linear_bwd(q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None):
-    """Adds the global branch's gradients into d_q, d_k, d_v (all [n, H, r] fp32)."""
+def gga_global_linear_bwd(q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None, g_fw=None):
+    """Adds the global branch's gradients into d_q, d_k, d_v (all [n, H, r] fp32).  g_fw:
+    the forward's G ([n, H, r] fp32), or None to form it again from S."""
     n, heads, r = q.shape
     nb = lib.gga_global_linear_bwd_workspace(n, heads, r)
     ws = _workspace(nb, q.device, ws)
     _check("gga_global_linear_bwd", lib.gga_global_linear_bwd(n, heads, r, _ptr(q), _ptr(k), _ptr(v), eps, _ptr(s),
-                                                              _ptr(z), _ptr(d_g), _ptr(d_q), _ptr(d_k), _ptr(d_v),
-                                                              _ptr(ws), nb, _stream(stream)))
+                                                              _ptr(z), _ptr(d_g), _ptr(g_fw), _ptr(d_q), _ptr(d_k),
+                                                              _ptr(d_v), _ptr(ws), nb, _stream(stream)))
     return d_q, d_k, d_v
 
 
@@ -509,16 +510,18 @@ def gga_global_linear_batch_fwd(node_ptr, q, k, v, eps=1e-6, s_out=None, z_out=N
     return s_out, z_out, g_out
 
 
-def gga_global_linear_batch_bwd(node_ptr, q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None):
-    """Adds the per-graph global branch's gradients into d_q, d_k, d_v."""
+def gga_global_linear_batch_bwd(node_ptr, q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None,
+                                g_fw=None):
+    """Adds the per-graph global branch's gradients into d_q, d_k, d_v (g_fw as in
+    gga_global_linear_bwd)."""
     n, heads, r = q.shape
     batch = node_ptr.numel() - 1
     nb = lib.gga_global_linear_batch_workspace(n, batch, heads, r)
     ws = _workspace(nb, q.device, ws)
     _check("gga_global_linear_batch_bwd",
            lib.gga_global_linear_batch_bwd(n, batch, _ptr(node_ptr), heads, r, _ptr(q), _ptr(k), _ptr(v), eps,
-                                           _ptr(s), _ptr(z), _ptr(d_g), _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(ws),
-                                           nb, _stream(stream)))
+                                           _ptr(s), _ptr(z), _ptr(d_g), _ptr(g_fw), _ptr(d_q), _ptr(d_k), _ptr(d_v),
+                                           _ptr(ws), nb, _stream(stream)))
     return d_q, d_k, d_v
 
 

@@ -491,17 +491,20 @@ __device__ __forceinline__ void stage_both(const float* __restrict__ m, float* m
 // workgroup, all on head blockIdx.y; for each piece of the tile the wavefronts take its
 // 16-row tiles in turn.  Per tile, with the lane layout of apply_mfma (lane group gq owns the
 // KQ consecutive features gq*KQ .. of the row li = lane%16):
-//   1. num^T = S^T phi(Q)^T: A = S read from LDS, B = phi(q) of the lane's own row, so the
-//      output lands with row li in lane li and columns gq*KQ + (q4*TR + jt) in group gq;
+//   1. dG . G, the one place num enters: with the forward's G given (HG), read beside dG;
+//      otherwise num^T = S^T phi(Q)^T formed again: A = S read from LDS, B = phi(q) of the
+//      lane's own row, so the output lands with row li in lane li and columns
+//      gq*KQ + (q4*TR + jt) in group gq;
 //   2. dphi(Q)^T = S dnum^T: A = S^T from LDS, B = the lane's own dnum;
 //   3. dS += phi(Q)^T dnum: the tile's phi(q) and dnum go through LDS to put rows on the
 //      contraction axis.
 // The wavefronts' dS, dz sums are added in wavefront order and written as the piece's
 // partial (same layout as the statistics), or as the graph's dS, dz for a short graph.
-template <int TR>
+template <int TR, bool HG>
 __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, const float* __restrict__ q,
                                                const float* __restrict__ s, const float* __restrict__ z,
-                                               const float* __restrict__ dg, float* __restrict__ dq,
+                                               const float* __restrict__ dg, const float* __restrict__ gfw,
+                                               float* __restrict__ dq,
                                                float* __restrict__ part, float* __restrict__ ds_out,
                                                float* __restrict__ dz_out) {
     constexpr int R = TR * 16, KQ = R / 4;
@@ -537,10 +540,10 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             const int64_t row = r0 + tl * 16 + li;
             const bool valid = tl < ntile && row < r1;
             const int64_t off = row * W + h * R + gq * KQ;
-            // q, dG and the dq being accumulated into are requested together, so the dq
-            // values arrive during the products instead of after them; q itself is kept only
-            // as phi(q) and a sign mask (phi'(q) is 1 where q > 0 and phi(q) elsewhere).
-            float a[KQ], dgl[KQ], dqo[KQ];
+            // q, dG (G with HG) and the dq being accumulated into are requested together, so
+            // the dq values arrive during the products instead of after them; q itself is kept
+            // only as phi(q) and a sign mask (phi'(q) is 1 where q > 0 and phi(q) elsewhere).
+            float a[KQ], dgl[KQ], dqo[KQ], gv[HG ? KQ : 1];
             uint32_t pos = 0;
             if (valid) {
                 float qr[KQ];
@@ -552,6 +555,10 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
                     qr[4 * c + 0] = t4.x; qr[4 * c + 1] = t4.y; qr[4 * c + 2] = t4.z; qr[4 * c + 3] = t4.w;
                     dgl[4 * c + 0] = g4.x; dgl[4 * c + 1] = g4.y; dgl[4 * c + 2] = g4.z; dgl[4 * c + 3] = g4.w;
                     dqo[4 * c + 0] = o4.x; dqo[4 * c + 1] = o4.y; dqo[4 * c + 2] = o4.z; dqo[4 * c + 3] = o4.w;
+                    if constexpr (HG) {
+                        const float4 f4 = *reinterpret_cast<const float4*>(gfw + off + 4 * c);
+                        gv[4 * c + 0] = f4.x; gv[4 * c + 1] = f4.y; gv[4 * c + 2] = f4.z; gv[4 * c + 3] = f4.w;
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < KQ; t++) {
@@ -561,6 +568,8 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             } else {
 #pragma unroll
                 for (int t = 0; t < KQ; t++) a[t] = dgl[t] = dqo[t] = 0.f;
+#pragma unroll
+                for (int t = 0; t < (HG ? KQ : 1); t++) gv[t] = 0.f;
             }
             float d = 0.f;
 #pragma unroll
@@ -568,29 +577,37 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             d += __shfl_xor(d, 16, 64);
             d += __shfl_xor(d, 32, 64);
             const float inv = 1.0f / (d + eps);
-            // 1. num^T
-            v4f acc1[TR];
-#pragma unroll
-            for (int j = 0; j < TR; j++) acc1[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int t = 0; t < KQ; t++) {
-                float sa[TR];
-                lds_load_n<TR>(sl + (gq * KQ + t) * R + TR * li, sa);
-#pragma unroll
-                for (int j = 0; j < TR; j++)
-                    acc1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], a[t], acc1[j], 0, 0, 0);
-            }
-            // acc1[jt][q4] = num[row li][gq*KQ + q4*TR + jt]
+            // 1. dG . G over the lane's features
             float dn[KQ];
             float dd = 0.f;
+            if constexpr (HG) {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; q4++)
-#pragma unroll
-                for (int j = 0; j < TR; j++) {
-                    const int idx = q4 * TR + j;
-                    dd = fmaf(dgl[idx], acc1[j][q4] * inv, dd);
-                    dn[idx] = dgl[idx] * inv;
+                for (int t = 0; t < KQ; t++) {
+                    dd = fmaf(dgl[t], gv[t], dd);
+                    dn[t] = dgl[t] * inv;
                 }
+            } else {
+                v4f acc1[TR];
+#pragma unroll
+                for (int j = 0; j < TR; j++) acc1[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < KQ; t++) {
+                    float sa[TR];
+                    lds_load_n<TR>(sl + (gq * KQ + t) * R + TR * li, sa);
+#pragma unroll
+                    for (int j = 0; j < TR; j++)
+                        acc1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], a[t], acc1[j], 0, 0, 0);
+                }
+                // acc1[jt][q4] = num[row li][gq*KQ + q4*TR + jt]
+#pragma unroll
+                for (int q4 = 0; q4 < 4; q4++)
+#pragma unroll
+                    for (int j = 0; j < TR; j++) {
+                        const int idx = q4 * TR + j;
+                        dd = fmaf(dgl[idx], acc1[j][q4] * inv, dd);
+                        dn[idx] = dgl[idx] * inv;
+                    }
+            }
             dd += __shfl_xor(dd, 16, 64);
             dd += __shfl_xor(dd, 32, 64);
             const float dden = -dd * inv;
@@ -799,7 +816,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 // the piece's dS, dz as above.
 __global__ __launch_bounds__(256) void dq_scalar(Seg sg, int32_t H, int32_t R, float eps, const float* __restrict__ q,
                                                  const float* __restrict__ s, const float* __restrict__ z,
-                                                 const float* __restrict__ dg, float* __restrict__ dq,
+                                                 const float* __restrict__ dg, const float* __restrict__ gfw,
+                                                 float* __restrict__ dq,
                                                  float* __restrict__ part, float* __restrict__ ds_out,
                                                  float* __restrict__ dz_out) {
     __shared__ float buf[64 * 64 + 64];
@@ -824,10 +842,16 @@ __global__ __launch_bounds__(256) void dq_scalar(Seg sg, int32_t H, int32_t R, f
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) d += __shfl_xor(d, o, 64);
             const float inv = 1.0f / (d + eps);
-            float num = 0.f;
-            for (int c = 0; c < R; c++) num = fmaf(__shfl(pc, c, 64), on ? sh[c * R + lane] : 0.f, num);
+            float gj;  // G of this feature: the forward's, or num / den formed again
+            if (gfw) {
+                gj = on ? gfw[off] : 0.f;
+            } else {
+                float num = 0.f;
+                for (int c = 0; c < R; c++) num = fmaf(__shfl(pc, c, 64), on ? sh[c * R + lane] : 0.f, num);
+                gj = num * inv;
+            }
             const float dgj = on ? dg[off] : 0.f;
-            float dd = dgj * (num * inv);
+            float dd = dgj * gj;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) dd += __shfl_xor(dd, o, 64);
             const float dden = -dd * inv;
@@ -995,8 +1019,8 @@ int gl_fwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
 }
 
 int gl_bwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float* k, const float* v, float eps,
-           const float* s_in, const float* z_in, const float* d_g, float* d_q, float* d_k, float* d_v, void* ws,
-           size_t ws_bytes, hipStream_t st) {
+           const float* s_in, const float* z_in, const float* d_g, const float* g_fw, float* d_q, float* d_k,
+           float* d_v, void* ws, size_t ws_bytes, hipStream_t st) {
     const GlWs need = carve_gl(nullptr, sg.n, sg.batch, heads, r);
     if (ws_bytes < need.bytes || !ws) return GGA_EWORKSPACE;
     if (sg.n == 0) return GGA_OK;
@@ -1007,17 +1031,23 @@ int gl_bwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
     }
     const int64_t tiles = tile_count(sg.n, sg.rs);
     const bool mfma = mfma_ok(r) && aligned16(q) && aligned16(k) && aligned16(v) && aligned16(d_g) &&
-                      aligned16(d_q) && aligned16(d_k) && aligned16(d_v);
+                      aligned16(d_q) && aligned16(d_k) && aligned16(d_v) && aligned16(g_fw);
     const dim3 ga((unsigned)tiles, (unsigned)heads);
     if (mfma) {
+#define GGA_DQ(TR)                                                                                              \
+    if (g_fw)                                                                                                   \
+        dq_mfma<TR, true><<<ga, 256, 0, st>>>(sg, heads, eps, q, s_in, z_in, d_g, g_fw, d_q, w.part, w.s, w.z);  \
+    else                                                                                                        \
+        dq_mfma<TR, false><<<ga, 256, 0, st>>>(sg, heads, eps, q, s_in, z_in, d_g, g_fw, d_q, w.part, w.s, w.z)
         switch (r / 16) {
-            case 1: dq_mfma<1><<<ga, 256, 0, st>>>(sg, heads, eps, q, s_in, z_in, d_g, d_q, w.part, w.s, w.z); break;
-            case 2: dq_mfma<2><<<ga, 256, 0, st>>>(sg, heads, eps, q, s_in, z_in, d_g, d_q, w.part, w.s, w.z); break;
-            case 3: dq_mfma<3><<<ga, 256, 0, st>>>(sg, heads, eps, q, s_in, z_in, d_g, d_q, w.part, w.s, w.z); break;
-            default: dq_mfma<4><<<ga, 256, 0, st>>>(sg, heads, eps, q, s_in, z_in, d_g, d_q, w.part, w.s, w.z); break;
+            case 1: GGA_DQ(1); break;
+            case 2: GGA_DQ(2); break;
+            case 3: GGA_DQ(3); break;
+            default: GGA_DQ(4); break;
         }
+#undef GGA_DQ
     } else {
-        dq_scalar<<<ga, 256, 0, st>>>(sg, heads, r, eps, q, s_in, z_in, d_g, d_q, w.part, w.s, w.z);
+        dq_scalar<<<ga, 256, 0, st>>>(sg, heads, r, eps, q, s_in, z_in, d_g, g_fw, d_q, w.part, w.s, w.z);
     }
     launch_list_and_reduce(sg, heads, r, w, w.s, w.z, st);
     if (mfma) {
@@ -1064,13 +1094,14 @@ extern "C" size_t gga_global_linear_bwd_workspace(int32_t n, int32_t heads, int3
 
 extern "C" int gga_global_linear_bwd(int32_t n, int32_t heads, int32_t r, const float* q, const float* k,
                                      const float* v, float eps, const float* s_in, const float* z_in, const float* d_g,
-                                     float* d_q, float* d_k, float* d_v, void* ws, size_t ws_bytes, void* stream) {
+                                     const float* g_fw, float* d_q, float* d_k, float* d_v, void* ws, size_t ws_bytes,
+                                     void* stream) {
     if (n < 0 || heads < 1 || r < 1) return GGA_EINVAL;
     if (r > 64) return GGA_EUNSUPPORTED;
     if (heads > 65535) return GGA_ERANGE;
     if (n == 0) return GGA_OK;
     if (!q || !k || !v || !s_in || !z_in || !d_g || !d_q || !d_k || !d_v) return GGA_EINVAL;
-    return gl_bwd(one_graph(n, heads), heads, r, q, k, v, eps, s_in, z_in, d_g, d_q, d_k, d_v, ws, ws_bytes,
+    return gl_bwd(one_graph(n, heads), heads, r, q, k, v, eps, s_in, z_in, d_g, g_fw, d_q, d_k, d_v, ws, ws_bytes,
                   as_stream(stream));
 }
 
@@ -1093,13 +1124,15 @@ extern "C" int gga_global_linear_batch_fwd(int32_t n, int32_t batch, const int32
 
 extern "C" int gga_global_linear_batch_bwd(int32_t n, int32_t batch, const int32_t* node_ptr, int32_t heads,
                                            int32_t r, const float* q, const float* k, const float* v, float eps,
-                                           const float* s_in, const float* z_in, const float* d_g, float* d_q,
-                                           float* d_k, float* d_v, void* ws, size_t ws_bytes, void* stream) {
+                                           const float* s_in, const float* z_in, const float* d_g,
+                                           const float* g_fw, float* d_q, float* d_k, float* d_v, void* ws,
+                                           size_t ws_bytes, void* stream) {
     if (n < 0 || batch < 1 || heads < 1 || r < 1) return GGA_EINVAL;
     if (r > 64) return GGA_EUNSUPPORTED;
     if (heads > 65535) return GGA_ERANGE;
     if (n == 0) return GGA_OK;
     if (!node_ptr || !q || !k || !v || !s_in || !z_in || !d_g || !d_q || !d_k || !d_v) return GGA_EINVAL;
     const Seg sg{node_ptr, batch, n, tile_rows(n, heads)};
-    return gl_bwd(sg, heads, r, q, k, v, eps, s_in, z_in, d_g, d_q, d_k, d_v, ws, ws_bytes, as_stream(stream));
+    return gl_bwd(sg, heads, r, q, k, v, eps, s_in, z_in, d_g, g_fw, d_q, d_k, d_v, ws, ws_bytes,
+                  as_stream(stream));
 }

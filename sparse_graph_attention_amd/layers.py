@@ -130,10 +130,10 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
         mark("local_bwd1")
     if node_ptr is None:
         gga_global_linear_bwd(fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"], d_glob.view(n, heads, r), d_q, d_k,
-                              d_v, eps)
+                              d_v, eps, g_fw=fwd["glob"].view(n, heads, r))
     else:
         gga_global_linear_batch_bwd(node_ptr, fwd["q"], fwd["k"], fwd["v"], fwd["S"], fwd["z"],
-                                    d_glob.view(n, heads, r), d_q, d_k, d_v, eps)
+                                    d_glob.view(n, heads, r), d_q, d_k, d_v, eps, g_fw=fwd["glob"].view(n, heads, r))
     grads = dict(d_w_o=d_wo, d_w_g=d_wg, d_b_g=d_bg, d_gamma=d_gamma, d_beta=d_beta)
     for name, g in (("q", d_q), ("k", d_k), ("v", d_v)):
         grads["d_w_" + name] = gga_linear(x, g.view(n, d), trans_a=True)

@@ -108,9 +108,12 @@ def test_global_batch_bwd(g, name, heads, r):
     names = ("d_q", "d_k", "d_v")
     np_d = i32(node_ptr)
     qd, kd, vd, gd = _t(q), _t(k), _t(v), _t(d_g)
-    s, z, _ = g.gga_global_linear_batch_fwd(np_d, qd, kd, vd, 1e-6)
+    s, z, gfw = g.gga_global_linear_batch_fwd(np_d, qd, kd, vd, 1e-6)
     grads = [torch.zeros(n, heads, r, device="cuda") for _ in names]
     g.gga_global_linear_batch_bwd(np_d, qd, kd, vd, s, z, gd, *grads, 1e-6)
+    # with the forward's G the query pass reads dG . G instead of forming num again
+    grads_g = [torch.zeros(n, heads, r, device="cuda") for _ in names]
+    g.gga_global_linear_batch_bwd(np_d, qd, kd, vd, s, z, gd, *grads_g, 1e-6, g_fw=gfw)
     # the kernels add into what is there: from a nonzero start the result is that start plus
     # the same contribution (the addition may be fused with the last product, so the two
     # differ by at most a rounding of each)
@@ -118,6 +121,8 @@ def test_global_batch_bwd(g, name, heads, r):
     acc = [b.clone() for b in base]
     g.gga_global_linear_batch_bwd(np_d, qd, kd, vd, s, z, gd, *acc, 1e-6)
     torch.cuda.synchronize()
+    for got, nm in zip(grads_g, names):
+        assert_close(got.cpu().numpy(), ref[nm], "f32", nm + " (forward G)", atol=1e-5 * scale[nm])
     for got, b, a, nm in zip(grads, base, acc, names):
         assert_close(got.cpu().numpy(), ref[nm], "f32", nm, atol=1e-5 * scale[nm])
         lim = 2.0 ** -23 * (b.abs() + 2 * got.abs())
@@ -136,9 +141,13 @@ def test_global_batch_of_one_equals_plain(g):
     b = [torch.zeros(n, heads, r, device="cuda") for _ in range(3)]
     g.gga_global_linear_bwd(q, k, v, s1, z1, d_g, *a, 1e-6)
     g.gga_global_linear_batch_bwd(np_d, q, k, v, s2, z2, d_g, *b, 1e-6)
+    ag = [torch.zeros(n, heads, r, device="cuda") for _ in range(3)]
+    bg = [torch.zeros(n, heads, r, device="cuda") for _ in range(3)]
+    g.gga_global_linear_bwd(q, k, v, s1, z1, d_g, *ag, 1e-6, g_fw=g1)
+    g.gga_global_linear_batch_bwd(np_d, q, k, v, s2, z2, d_g, *bg, 1e-6, g_fw=g2)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2[0]) and torch.equal(z1, z2[0]) and torch.equal(g1, g2)
-    for x, y in zip(a, b):
+    for x, y in zip(a + ag, b + bg):
         assert torch.equal(x, y)
 
 

@@ -95,9 +95,12 @@ def test_global_linear_bwd(g, n, heads, r):
     ref = oracle.global_linear_bwd(q, k, v, d_g, 1e-6)
     names = ("d_q", "d_k", "d_v")
     qd, kd, vd, gd = _t(q), _t(k), _t(v), _t(d_g)
-    s, z, _ = g.gga_global_linear_fwd(qd, kd, vd, 1e-6)
+    s, z, gfw = g.gga_global_linear_fwd(qd, kd, vd, 1e-6)
     grads = [torch.zeros(n, heads, r, device="cuda") for _ in names]
     g.gga_global_linear_bwd(qd, kd, vd, s, z, gd, *grads, 1e-6)
+    # with the forward's G the query pass reads dG . G instead of forming num again
+    grads_g = [torch.zeros(n, heads, r, device="cuda") for _ in names]
+    g.gga_global_linear_bwd(qd, kd, vd, s, z, gd, *grads_g, 1e-6, g_fw=gfw)
     # the kernels add into what is there: from a nonzero start the result is that start plus
     # the same contribution (the addition may be fused with the last product, so the two
     # differ by at most a rounding of each)
@@ -106,6 +109,8 @@ def test_global_linear_bwd(g, n, heads, r):
     g.gga_global_linear_bwd(qd, kd, vd, s, z, gd, *acc, 1e-6)
     torch.cuda.synchronize()
     scale = global_term_scales(q, k, v, d_g, 1e-6)
+    for got, nm in zip(grads_g, names):
+        assert_close(got.cpu().numpy(), ref[nm], "f32", nm + " (forward G)", atol=1e-5 * scale[nm])
     for got, b, a, nm in zip(grads, base, acc, names):
         assert_close(got.cpu().numpy(), ref[nm], "f32", nm, atol=1e-5 * scale[nm])
         lim = 2.0 ** -23 * (b.abs() + 2 * got.abs())
