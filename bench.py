@@ -665,6 +665,29 @@ def bench_relation(args, g, torch, synth, ident):
     return record(args, w.name, e / (ms * 1e-3) / 1e9, ms, "f32", cfg, roof, cpu, dict(tt, fwd_ms=fms, bwd_ms=bms))
 
 
+def stream_rates(torch, n=262144 * 256, reps=20):
+    """Best-of-reps rates of torch's own elementwise kernels on [2^18, 256] fp32 tensors (the
+    gated layer's row tensors): the streaming rate a row-wise kernel of that size can reach
+    here, for one, two and three reads per write."""
+    dev = torch.device("cuda:0")
+    a, b, c, d = (torch.randn(n, device=dev) for _ in range(4))
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nb = n * 4
+    for name, fn, moved in (("copy (1 read, 1 write)", lambda: c.copy_(a), 2 * nb),
+                            ("add (2 reads, 1 write)", lambda: torch.add(a, b, out=c), 3 * nb),
+                            ("addcmul (3 reads, 1 write)", lambda: torch.addcmul(a, b, d, out=c), 4 * nb)):
+        for _ in range(3):
+            fn()
+        best = float("inf")
+        for _ in range(reps):
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            best = min(best, s.elapsed_time(e))
+        log(f"stream rate {name}: {best * 1e3:.1f} us, {moved / best / 1e9:.2f} TB/s")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -674,6 +697,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--stream-rates", action="store_true",
+                    help="also time plain torch elementwise kernels (copy, add, addcmul) over 268 MB "
+                         "fp32 tensors: the streaming rates of read/write mixes on this device")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures a single GPU; --gpus above 1 is not supported",
@@ -702,6 +728,8 @@ def main() -> int:
             b.copy_(a)
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
+    if args.stream_rates:
+        stream_rates(torch)
     print(json.dumps(rec), flush=True)
     return 0
 

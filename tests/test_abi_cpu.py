@@ -241,3 +241,30 @@ def test_fused_projection_checks():
     assert L.gga_qkv_proj_bwd_x(1000, 256, a, a, a, a, a, a, a, a, need - 1, None) == 4
     assert L.gga_qkv_proj_bwd_x(1000, 0, a, a, a, a, a, a, a, a, need, None) == 1
     assert L.gga_gated_combine(10, 4, None, a, a, None, a, None) == 1
+
+
+def test_global_branch_backward_checks():
+    """The global branch's backward (with or without the forward's G) refuses bad shapes,
+    missing tensors and a short workspace before launching anything; n = 0 is a no-op."""
+    import sparse_graph_attention_amd as g
+
+    L = g.lib
+    a = ctypes.c_void_p(4096)
+    eps = ctypes.c_float(1e-6)
+    need = L.gga_global_linear_bwd_workspace(1000, 4, 64)
+    assert need > 0
+    for gfw in (None, a):
+        assert L.gga_global_linear_bwd(-1, 4, 64, a, a, a, eps, a, a, a, gfw, a, a, a, a, need, None) == g.GGA_EINVAL
+        assert L.gga_global_linear_bwd(1000, 4, 65, a, a, a, eps, a, a, a, gfw, a, a, a, a, need, None) == \
+            g.GGA_EUNSUPPORTED
+        assert L.gga_global_linear_bwd(1000, 4, 64, a, a, a, eps, a, a, None, gfw, a, a, a, a, need, None) == \
+            g.GGA_EINVAL
+        assert L.gga_global_linear_bwd(1000, 4, 64, a, a, a, eps, a, a, a, gfw, a, a, a, a, need - 1, None) == \
+            g.GGA_EWORKSPACE
+        assert L.gga_global_linear_bwd(0, 4, 64, None, None, None, eps, None, None, None, gfw, None, None, None,
+                                       None, 0, None) == g.GGA_OK
+        bneed = L.gga_global_linear_batch_workspace(1000, 3, 4, 64)
+        assert L.gga_global_linear_batch_bwd(1000, 3, None, 4, 64, a, a, a, eps, a, a, a, gfw, a, a, a, a, bneed,
+                                             None) == g.GGA_EINVAL
+        assert L.gga_global_linear_batch_bwd(1000, 3, a, 4, 64, a, a, a, eps, a, a, a, gfw, a, a, a, a, bneed - 1,
+                                             None) == g.GGA_EWORKSPACE
