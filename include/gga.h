@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GGA_ABI_VERSION 2
+#define GGA_ABI_VERSION 3
 
 /* status codes */
 #define GGA_OK 0

@@ -43,6 +43,9 @@ class gga_local_desc(ctypes.Structure):
     ]
 
 
+ABI_VERSION = 3
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_graph_attention_amd/build.py`")
@@ -103,6 +106,11 @@ def _load() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = args
         fn.restype = res
+    # the signatures above are those of this ABI version; a library built from other sources
+    # would take the arguments differently
+    if L.gga_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {L.gga_abi_version()}, this binding expects {ABI_VERSION}: "
+                          "rebuild it with `python sparse_graph_attention_amd/build.py`")
     return L
 
 

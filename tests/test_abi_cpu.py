@@ -72,7 +72,7 @@ def test_binding_refuses_to_import_without_the_library(tmp_path):
 def test_version_and_status(lib):
     lib.gga_abi_version.restype = ctypes.c_int
     lib.gga_status_string.restype = ctypes.c_char_p
-    assert lib.gga_abi_version() == 2
+    assert lib.gga_abi_version() == 3
     assert lib.gga_status_string(0) == b"ok"
     assert lib.gga_status_string(4).startswith(b"workspace")
 
