@@ -352,12 +352,21 @@ __global__ __launch_bounds__(NW * 64) void seg_reduce(Seg sg, int32_t H, int32_t
 
 // ---------------------------------------------------------------- G = phi(Q) S / (phi(Q) z + eps)
 
+// Lane layout of the row passes (apply_mfma and the two backward passes): lane group
+// gq = lane / 16 of row li = lane % 16 holds, as its t-th value (t = 4c + e), feature
+// feat(gq, t) = 16c + 4gq + e of the head, so the c-th 16-byte load or store of the four
+// groups covers 64 contiguous bytes of the row (one memory request, not four 16-byte ones
+// 64 bytes apart).  An MFMA output tile j covers features 16j .. 16j+15 of which group gq
+// holds positions 4gq .. 4gq+3, the same features as its t = 4j .. 4j+3: inputs and outputs
+// of a lane line up.
+__device__ __forceinline__ int feat(int gq, int t) { return 16 * (t >> 2) + 4 * gq + (t & 3); }
+
 // Matrix-core path.  grid (tiles), up to 8 wavefronts; wavefront w serves head w % hp and every P-th 16-row
 // tile of a piece from tile w / hp (hp = min(H, wavefronts), P = wavefronts / hp; more heads
-// than wavefronts loop).  The contraction index is permuted so that in MFMA step t the lane
-// group gq = lane/16 supplies k = gq*(R/4) + t: each lane's A operands over the R/4 steps are
-// R/4 consecutive elements of its row (16-byte loads), and its B operands S[k][j] are held in
-// registers for the whole piece.  Output columns are permuted too (MFMA tile j, position
+// than wavefronts loop).  The contraction index follows feat: in MFMA step t the lane group
+// gq = lane/16 supplies k = feat(gq, t), so each lane's A operands over the R/4 steps come
+// from 16-byte loads that together read 64 contiguous bytes of the row, and its B operands
+// S[k][j] are held in registers for the whole piece.  Output columns are permuted too (MFMA tile j, position
 // li <-> column TR*li + j), so each lane ends with TR consecutive outputs of a row.  The
 // next tile's q is loaded (and kept raw until used) before the current one is multiplied.
 template <int TR>
@@ -380,19 +389,19 @@ __global__ __launch_bounds__(512) void apply_mfma(Seg sg, int32_t H, float eps, 
             float sreg[KQ][TR], zreg[KQ];
 #pragma unroll
             for (int t = 0; t < KQ; t++) {
-                const int kk = gq * KQ + t;
+                const int kk = feat(gq, t);
                 zreg[t] = zh[kk];
 #pragma unroll
                 for (int j = 0; j < TR; j++) sreg[t][j] = sh[kk * R + TR * li + j];
             }
-            const int64_t col = h * R + gq * KQ;
+            const int64_t col = h * R + 4 * gq;  // chunk c of the lane: features 16c + 4gq ..
             // the next tile's q rows stay raw until used, so their loads overlap this tile's
             // MFMAs; rows past the piece read its last row and are zeroed by a select
             v4f qn[KQ / 4];
             auto fetch = [&](int64_t rowt) {
                 const int64_t row = rowt + li < r1 ? rowt + li : r1 - 1;
 #pragma unroll
-                for (int c = 0; c < KQ / 4; c++) qn[c] = *reinterpret_cast<const v4f*>(q + row * W + col + 4 * c);
+                for (int c = 0; c < KQ / 4; c++) qn[c] = *reinterpret_cast<const v4f*>(q + row * W + col + 16 * c);
             };
             int64_t row0 = r0 + 16 * p0;
             if (row0 < r1) fetch(row0);
@@ -477,24 +486,29 @@ __device__ __forceinline__ void lds_load_n(const float* p, float* out) {
     }
 }
 
-// Loads the R x R matrix m into LDS both as is (mr[c][j]) and transposed (mt[j][c]).
-template <int R>
+// Loads the R x R matrix m into LDS both as is and transposed, the columns of each copy
+// permuted so that the TR entries a lane multiplies at MFMA position li of tiles 0..TR-1
+// (columns li, 16 + li, ..) sit side by side: mr[c][TR*(j%16) + j/16] = m[c][j] and
+// mt[j][TR*(c%16) + c/16] = m[c][j].
+template <int TR>
 __device__ __forceinline__ void stage_both(const float* __restrict__ m, float* mr, float* mt) {
+    constexpr int R = TR * 16;
     for (int x = threadIdx.x; x < R * R; x += blockDim.x) {
         const float val = m[x];
-        mr[x] = val;
-        mt[(x % R) * R + x / R] = val;
+        const int c = x / R, j = x % R;
+        mr[c * R + TR * (j & 15) + (j >> 4)] = val;
+        mt[j * R + TR * (c & 15) + (c >> 4)] = val;
     }
 }
 
 // ---- pass over the query rows, matrix-core path.  grid (tiles, H), 4 wavefronts per
 // workgroup, all on head blockIdx.y; for each piece of the tile the wavefronts take its
-// 16-row tiles in turn.  Per tile, with the lane layout of apply_mfma (lane group gq owns the
-// KQ consecutive features gq*KQ .. of the row li = lane%16):
+// 16-row tiles in turn.  Per tile, with the lane layout feat (lane group gq holds features
+// feat(gq, t) of the row li = lane%16):
 //   1. dG . G, the one place num enters: with the forward's G given (HG), read beside dG;
 //      otherwise num^T = S^T phi(Q)^T formed again: A = S read from LDS, B = phi(q) of the
-//      lane's own row, so the output lands with row li in lane li and columns
-//      gq*KQ + (q4*TR + jt) in group gq;
+//      lane's own row, so the output lands with row li in lane li and features
+//      16jt + 4gq + q4 in group gq;
 //   2. dphi(Q)^T = S dnum^T: A = S^T from LDS, B = the lane's own dnum;
 //   3. dS += phi(Q)^T dnum: the tile's phi(q) and dnum go through LDS to put rows on the
 //      contraction axis.
@@ -518,10 +532,10 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
     for_each_segment(sg, tile, [&](int32_t b, int64_t r0, int64_t r1, int slot) {
         const int64_t bh = (int64_t)b * H + h;
         __syncthreads();  // the previous piece is done with sl, st
-        stage_both<R>(s + bh * R * R, sl, st);
+        stage_both<TR>(s + bh * R * R, sl, st);
         float zreg[KQ];
 #pragma unroll
-        for (int t = 0; t < KQ; t++) zreg[t] = z[bh * R + gq * KQ + t];
+        for (int t = 0; t < KQ; t++) zreg[t] = z[bh * R + feat(gq, t)];
         __syncthreads();
 
         v4f dsacc[TR][TR];
@@ -539,7 +553,7 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             const int64_t tl = it * 4 + wave;
             const int64_t row = r0 + tl * 16 + li;
             const bool valid = tl < ntile && row < r1;
-            const int64_t off = row * W + h * R + gq * KQ;
+            const int64_t off = row * W + h * R + 4 * gq;  // chunk c at off + 16c
             // q, dG (G with HG) and the dq being accumulated into are requested together, so
             // the dq values arrive during the products instead of after them; q itself is kept
             // only as phi(q) and a sign mask (phi'(q) is 1 where q > 0 and phi(q) elsewhere).
@@ -549,14 +563,14 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
                 float qr[KQ];
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
-                    const float4 t4 = *reinterpret_cast<const float4*>(q + off + 4 * c);
-                    const float4 g4 = *reinterpret_cast<const float4*>(dg + off + 4 * c);
-                    const float4 o4 = *reinterpret_cast<const float4*>(dq + off + 4 * c);
+                    const float4 t4 = *reinterpret_cast<const float4*>(q + off + 16 * c);
+                    const float4 g4 = *reinterpret_cast<const float4*>(dg + off + 16 * c);
+                    const float4 o4 = *reinterpret_cast<const float4*>(dq + off + 16 * c);
                     qr[4 * c + 0] = t4.x; qr[4 * c + 1] = t4.y; qr[4 * c + 2] = t4.z; qr[4 * c + 3] = t4.w;
                     dgl[4 * c + 0] = g4.x; dgl[4 * c + 1] = g4.y; dgl[4 * c + 2] = g4.z; dgl[4 * c + 3] = g4.w;
                     dqo[4 * c + 0] = o4.x; dqo[4 * c + 1] = o4.y; dqo[4 * c + 2] = o4.z; dqo[4 * c + 3] = o4.w;
                     if constexpr (HG) {
-                        const float4 f4 = *reinterpret_cast<const float4*>(gfw + off + 4 * c);
+                        const float4 f4 = *reinterpret_cast<const float4*>(gfw + off + 16 * c);
                         gv[4 * c + 0] = f4.x; gv[4 * c + 1] = f4.y; gv[4 * c + 2] = f4.z; gv[4 * c + 3] = f4.w;
                     }
                 }
@@ -593,17 +607,17 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
 #pragma unroll
                 for (int t = 0; t < KQ; t++) {
                     float sa[TR];
-                    lds_load_n<TR>(sl + (gq * KQ + t) * R + TR * li, sa);
+                    lds_load_n<TR>(sl + feat(gq, t) * R + TR * li, sa);
 #pragma unroll
                     for (int j = 0; j < TR; j++)
                         acc1[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], a[t], acc1[j], 0, 0, 0);
                 }
-                // acc1[jt][q4] = num[row li][gq*KQ + q4*TR + jt]
+                // acc1[jt][q4] = num[row li][16jt + 4gq + q4], the lane's value t = 4jt + q4
 #pragma unroll
-                for (int q4 = 0; q4 < 4; q4++)
+                for (int j = 0; j < TR; j++)
 #pragma unroll
-                    for (int j = 0; j < TR; j++) {
-                        const int idx = q4 * TR + j;
+                    for (int q4 = 0; q4 < 4; q4++) {
+                        const int idx = 4 * j + q4;
                         dd = fmaf(dgl[idx], acc1[j][q4] * inv, dd);
                         dn[idx] = dgl[idx] * inv;
                     }
@@ -618,12 +632,12 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
 #pragma unroll
             for (int t = 0; t < KQ; t++) {
                 float sa[TR];
-                lds_load_n<TR>(st + (gq * KQ + t) * R + TR * li, sa);
+                lds_load_n<TR>(st + feat(gq, t) * R + TR * li, sa);
 #pragma unroll
                 for (int c = 0; c < TR; c++)
                     acc2[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[c], dn[t], acc2[c], 0, 0, 0);
             }
-            // acc2[ct][q4] = (S dnum)[row li][gq*KQ + q4*TR + ct]
+            // acc2[ct][q4] = (S dnum)[row li][16ct + 4gq + q4], the lane's value t = 4ct + q4
             if (valid) {
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
@@ -631,10 +645,10 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
                         const int idx = 4 * c + e;
-                        const float gv = acc2[idx % TR][idx / TR] + zreg[idx] * dden;
+                        const float gv = acc2[c][e] + zreg[idx] * dden;
                         u[e] = dqo[idx] + gv * ((pos >> idx) & 1u ? 1.f : a[idx]);
                     }
-                    *reinterpret_cast<float4*>(dq + off + 4 * c) = make_float4(u[0], u[1], u[2], u[3]);
+                    *reinterpret_cast<float4*>(dq + off + 16 * c) = make_float4(u[0], u[1], u[2], u[3]);
                 }
             }
 #pragma unroll
@@ -644,9 +658,9 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
             float* dw = dn_l[wave];
 #pragma unroll
             for (int c = 0; c < KQ / 4; c++) {
-                *reinterpret_cast<float4*>(pw + li * R + gq * KQ + 4 * c) =
+                *reinterpret_cast<float4*>(pw + li * R + 16 * c + 4 * gq) =
                     make_float4(a[4 * c], a[4 * c + 1], a[4 * c + 2], a[4 * c + 3]);
-                *reinterpret_cast<float4*>(dw + li * R + gq * KQ + 4 * c) =
+                *reinterpret_cast<float4*>(dw + li * R + 16 * c + 4 * gq) =
                     make_float4(dn[4 * c], dn[4 * c + 1], dn[4 * c + 2], dn[4 * c + 3]);
             }
             wave_lds_sync();  // pq[wave], dn_l[wave] belong to this wavefront alone
@@ -691,7 +705,7 @@ __global__ __launch_bounds__(256) void dq_mfma(Seg sg, int32_t H, float eps, con
                         }
                 if (li == 0) {
 #pragma unroll
-                    for (int t = 0; t < KQ; t++) zbuf[gq * KQ + t] = (w == 0 ? 0.f : zbuf[gq * KQ + t]) + dzacc[t];
+                    for (int t = 0; t < KQ; t++) zbuf[feat(gq, t)] = (w == 0 ? 0.f : zbuf[feat(gq, t)]) + dzacc[t];
                 }
             }
             __syncthreads();
@@ -732,22 +746,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for_each_segment(sg, blockIdx.x, [&](int32_t b, int64_t r0, int64_t r1, int) {
         const int64_t bh = (int64_t)b * H + h;
         __syncthreads();
-        stage_both<R>(ds + bh * R * R, sl, st);
+        stage_both<TR>(ds + bh * R * R, sl, st);
         float zreg[KQ];
 #pragma unroll
-        for (int t = 0; t < KQ; t++) zreg[t] = dz[bh * R + gq * KQ + t];
+        for (int t = 0; t < KQ; t++) zreg[t] = dz[bh * R + feat(gq, t)];
         __syncthreads();
         // the next tile's k and v, loaded during the current tile's products
         v4f kx[KQ / 4], vx[KQ / 4];
         auto fetch = [&](int64_t row0) {
             const int64_t row = row0 + li;
-            const int64_t off = row * W + h * R + gq * KQ;
+            const int64_t off = row * W + h * R + 4 * gq;  // chunk c at off + 16c
 #pragma unroll
             for (int c = 0; c < KQ / 4; c++) {
                 kx[c] = vx[c] = v4f{0.f, 0.f, 0.f, 0.f};
                 if (row < r1) {
-                    kx[c] = *reinterpret_cast<const v4f*>(k + off + 4 * c);
-                    vx[c] = *reinterpret_cast<const v4f*>(v + off + 4 * c);
+                    kx[c] = *reinterpret_cast<const v4f*>(k + off + 16 * c);
+                    vx[c] = *reinterpret_cast<const v4f*>(v + off + 16 * c);
                 }
             }
         };
@@ -756,7 +770,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         for (; row0 < r1; row0 += 64) {
             const int64_t row = row0 + li;
             const bool valid = row < r1;
-            const int64_t off = row * W + h * R + gq * KQ;
+            const int64_t off = row * W + h * R + 4 * gq;  // chunk c at off + 16c
             float pk[KQ], vv[KQ];
             uint32_t pos = 0;              // bit t: k feature t > 0, where dphi = 1
 #pragma unroll
@@ -776,8 +790,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
             for (int t = 0; t < KQ; t++) {
                 float sa[TR], sb[TR];
-                lds_load_n<TR>(st + (gq * KQ + t) * R + TR * li, sa);
-                lds_load_n<TR>(sl + (gq * KQ + t) * R + TR * li, sb);
+                lds_load_n<TR>(st + feat(gq, t) * R + TR * li, sa);
+                lds_load_n<TR>(sl + feat(gq, t) * R + TR * li, sb);
 #pragma unroll
                 for (int j = 0; j < TR; j++) {
                     ak[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sa[j], vv[t], ak[j], 0, 0, 0);
@@ -785,13 +799,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
                 }
                 if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // at most four steps' dS loads live
             }
-            // ak[ct][q4] = (dS v)[row li][gq*KQ + q4*TR + ct]; av likewise for dS^T phi(k)
+            // ak[ct][q4] = (dS v)[row li][16ct + 4gq + q4], the lane's value t = 4ct + q4; av
+            // likewise for dS^T phi(k)
             if (valid) {
                 v4f odk[KQ / 4], odv[KQ / 4];
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
-                    odk[c] = *reinterpret_cast<const v4f*>(dk + off + 4 * c);
-                    odv[c] = *reinterpret_cast<const v4f*>(dv + off + 4 * c);
+                    odk[c] = *reinterpret_cast<const v4f*>(dk + off + 16 * c);
+                    odv[c] = *reinterpret_cast<const v4f*>(dv + off + 16 * c);
                 }
 #pragma unroll
                 for (int c = 0; c < KQ / 4; c++) {
@@ -800,11 +815,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
                     for (int e = 0; e < 4; e++) {
                         const int idx = 4 * c + e;
                         const float dp = (pos >> idx) & 1u ? 1.f : pk[idx];  // dphi
-                        ok[e] = odk[c][e] + (ak[idx % TR][idx / TR] + zreg[idx]) * dp;
-                        ov[e] = odv[c][e] + av[idx % TR][idx / TR];
+                        ok[e] = odk[c][e] + (ak[c][e] + zreg[idx]) * dp;
+                        ov[e] = odv[c][e] + av[c][e];
                     }
-                    *reinterpret_cast<v4f*>(dk + off + 4 * c) = ok;
-                    *reinterpret_cast<v4f*>(dv + off + 4 * c) = ov;
+                    *reinterpret_cast<v4f*>(dk + off + 16 * c) = ok;
+                    *reinterpret_cast<v4f*>(dv + off + 16 * c) = ov;
                 }
             }
         }
