@@ -361,83 +361,97 @@ __global__ __launch_bounds__(NW * 64) void seg_reduce(Seg sg, int32_t H, int32_t
 // of a lane line up.
 __device__ __forceinline__ int feat(int gq, int t) { return 16 * (t >> 2) + 4 * gq + (t & 3); }
 
-// Matrix-core path.  grid (tiles), up to 8 wavefronts; wavefront w serves head w % hp and every P-th 16-row
-// tile of a piece from tile w / hp (hp = min(H, wavefronts), P = wavefronts / hp; more heads
-// than wavefronts loop).  The contraction index follows feat: in MFMA step t the lane group
-// gq = lane/16 supplies k = feat(gq, t), so each lane's A operands over the R/4 steps come
-// from 16-byte loads that together read 64 contiguous bytes of the row, and its B operands
-// S[k][j] are held in registers for the whole piece.  Output columns are permuted too (MFMA tile j, position
-// li <-> column TR*li + j), so each lane ends with TR consecutive outputs of a row.  The
-// next tile's q is loaded (and kept raw until used) before the current one is multiplied.
+// N consecutive floats from LDS as one vector read where N allows.
+template <int N>
+__device__ __forceinline__ void lds_load_n(const float* p, float* out) {
+    if constexpr (N == 4) {
+        const float4 t = *reinterpret_cast<const float4*>(p);
+        out[0] = t.x; out[1] = t.y; out[2] = t.z; out[3] = t.w;
+    } else if constexpr (N == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(p);
+        out[0] = t.x; out[1] = t.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; i++) out[i] = p[i];
+    }
+}
+
+// Matrix-core path.  grid (tiles, H), four wavefronts on head blockIdx.y; the piece's S and z
+// sit in LDS and the wavefronts take its 16-row tiles in turn.  The contraction index follows
+// feat: in MFMA step t the lane group gq = lane/16 supplies k = feat(gq, t), so each lane's A
+// operands over the R/4 steps come from 16-byte loads that together read 64 contiguous bytes
+// of the row; its B operands S[k][TR*li .. TR*li+TR-1] are one LDS vector per step.  Output
+// columns are permuted too (MFMA tile j, position li <-> column TR*li + j), so each lane ends
+// with TR consecutive outputs of a row.  The next tile's q is loaded (and kept raw until
+// used) before the current one is multiplied.  (S held in registers for a whole piece took
+// 256 registers: two wavefronts per SIMD, each with one tile's loads in flight.)
 template <int TR>
-__global__ __launch_bounds__(512) void apply_mfma(Seg sg, int32_t H, float eps, const float* __restrict__ q,
+__global__ __launch_bounds__(256) void apply_mfma(Seg sg, int32_t H, float eps, const float* __restrict__ q,
                                                    const float* __restrict__ s, const float* __restrict__ z,
                                                    float* __restrict__ g) {
     constexpr int R = TR * 16;
     constexpr int KQ = R / 4;  // MFMA steps per row tile
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    __shared__ __align__(16) float sl[R * R], zl[R];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int gq = lane >> 4, li = lane & 15;
+    const int h = blockIdx.y;
     const int64_t W = (int64_t)H * R;
-    const int hp = H < nw ? H : nw;
-    const int P = nw / hp;
-    const int h0 = wave % hp, p0 = wave / hp;
-    if (p0 >= P) return;
     for_each_segment(sg, blockIdx.x, [&](int32_t b, int64_t r0, int64_t r1, int) {
-        for (int h = h0; h < H; h += hp) {
-            const float* sh = s + ((int64_t)b * H + h) * R * R;
-            const float* zh = z + ((int64_t)b * H + h) * R;
-            float sreg[KQ][TR], zreg[KQ];
+        const int64_t bh = (int64_t)b * H + h;
+        __syncthreads();  // the previous piece is done with sl, zl
+        for (int x = threadIdx.x; x < R * R; x += blockDim.x) sl[x] = s[bh * R * R + x];
+        if (threadIdx.x < R) zl[threadIdx.x] = z[bh * R + threadIdx.x];
+        __syncthreads();
+        float zreg[KQ];
+#pragma unroll
+        for (int t = 0; t < KQ; t++) zreg[t] = zl[feat(gq, t)];
+        const int64_t col = h * R + 4 * gq;  // chunk c of the lane: features 16c + 4gq ..
+        // the next tile's q rows stay raw until used, so their loads overlap this tile's
+        // MFMAs; rows past the piece read its last row and are zeroed by a select
+        v4f qn[KQ / 4];
+        auto fetch = [&](int64_t rowt) {
+            const int64_t row = rowt + li < r1 ? rowt + li : r1 - 1;
+#pragma unroll
+            for (int c = 0; c < KQ / 4; c++) qn[c] = *reinterpret_cast<const v4f*>(q + row * W + col + 16 * c);
+        };
+        int64_t row0 = r0 + 16 * wave;
+        if (row0 < r1) fetch(row0);
+        for (; row0 < r1; row0 += 64) {
+            float a[KQ];
+            const bool ok = row0 + li < r1;
+#pragma unroll
+            for (int c = 0; c < KQ / 4; c++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) a[4 * c + e] = ok ? phi(qn[c][e]) : 0.f;
+            const int64_t nxt = row0 + 64;
+            if (nxt < r1) fetch(nxt);
+            float d = 0.f;
+#pragma unroll
+            for (int t = 0; t < KQ; t++) d = fmaf(a[t], zreg[t], d);
+            d += __shfl_xor(d, 16, 64);
+            d += __shfl_xor(d, 32, 64);  // every lane li now holds the dot for row row0 + li
+            v4f acc[TR];
+#pragma unroll
+            for (int j = 0; j < TR; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < KQ; t++) {
-                const int kk = feat(gq, t);
-                zreg[t] = zh[kk];
+                float sb[TR];
+                lds_load_n<TR>(sl + feat(gq, t) * R + TR * li, sb);
 #pragma unroll
-                for (int j = 0; j < TR; j++) sreg[t][j] = sh[kk * R + TR * li + j];
+                for (int j = 0; j < TR; j++)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], sb[j], acc[j], 0, 0, 0);
+                if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // at most four steps' S loads live
             }
-            const int64_t col = h * R + 4 * gq;  // chunk c of the lane: features 16c + 4gq ..
-            // the next tile's q rows stay raw until used, so their loads overlap this tile's
-            // MFMAs; rows past the piece read its last row and are zeroed by a select
-            v4f qn[KQ / 4];
-            auto fetch = [&](int64_t rowt) {
-                const int64_t row = rowt + li < r1 ? rowt + li : r1 - 1;
 #pragma unroll
-                for (int c = 0; c < KQ / 4; c++) qn[c] = *reinterpret_cast<const v4f*>(q + row * W + col + 16 * c);
-            };
-            int64_t row0 = r0 + 16 * p0;
-            if (row0 < r1) fetch(row0);
-            for (; row0 < r1; row0 += 16 * P) {
-                float a[KQ];
-                const bool ok = row0 + li < r1;
+            for (int q4 = 0; q4 < 4; q4++) {
+                const int rr = gq * 4 + q4;  // output row of this lane within the tile
+                const float inv = 1.0f / (__shfl(d, rr, 64) + eps);
+                const int64_t orow = row0 + rr;
+                if (orow < r1) {
+                    float o[TR];
 #pragma unroll
-                for (int c = 0; c < KQ / 4; c++)
-#pragma unroll
-                    for (int e = 0; e < 4; e++) a[4 * c + e] = ok ? phi(qn[c][e]) : 0.f;
-                const int64_t nxt = row0 + 16 * P;
-                if (nxt < r1) fetch(nxt);
-                float d = 0.f;
-#pragma unroll
-                for (int t = 0; t < KQ; t++) d = fmaf(a[t], zreg[t], d);
-                d += __shfl_xor(d, 16, 64);
-                d += __shfl_xor(d, 32, 64);  // every lane li now holds the dot for row row0 + li
-                v4f acc[TR];
-#pragma unroll
-                for (int j = 0; j < TR; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < KQ; t++)
-#pragma unroll
-                    for (int j = 0; j < TR; j++)
-                        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t], sreg[t][j], acc[j], 0, 0, 0);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; q4++) {
-                    const int rr = gq * 4 + q4;  // output row of this lane within the tile
-                    const float inv = 1.0f / (__shfl(d, rr, 64) + eps);
-                    const int64_t orow = row0 + rr;
-                    if (orow < r1) {
-                        float o[TR];
-#pragma unroll
-                        for (int j = 0; j < TR; j++) o[j] = acc[j][q4] * inv;
-                        store_n<TR>(g + orow * W + h * R + TR * li, o);
-                    }
+                    for (int j = 0; j < TR; j++) o[j] = acc[j][q4] * inv;
+                    store_n<TR>(g + orow * W + h * R + TR * li, o);
                 }
             }
         }
@@ -471,20 +485,6 @@ __global__ void apply_scalar(Seg sg, int32_t H, int32_t R, float eps, const floa
 //   dphi(q_i) = S dnum_i + z dden_i,   dS = sum_i phi(q_i) dnum_i^T,  dz = sum_i phi(q_i) dden_i,
 //   dphi(k_j) = dS v_j + dz,           dv_j = dS^T phi(k_j),
 // with the sums over the rows of the graph.  dq, dk, dv are accumulated (+=).
-
-template <int N>
-__device__ __forceinline__ void lds_load_n(const float* p, float* out) {
-    if constexpr (N == 4) {
-        const float4 t = *reinterpret_cast<const float4*>(p);
-        out[0] = t.x; out[1] = t.y; out[2] = t.z; out[3] = t.w;
-    } else if constexpr (N == 2) {
-        const float2 t = *reinterpret_cast<const float2*>(p);
-        out[0] = t.x; out[1] = t.y;
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; i++) out[i] = p[i];
-    }
-}
 
 // Loads the R x R matrix m into LDS both as is and transposed, the columns of each copy
 // permuted so that the TR entries a lane multiplies at MFMA position li of tiles 0..TR-1
@@ -1016,14 +1016,12 @@ int gl_fwd(const Seg& sg, int32_t heads, int32_t r, const float* q, const float*
     }
     launch_list_and_reduce(sg, heads, r, w, s, z, st);
     if (mfma) {
-        // up to 8 wavefronts: every head, and as many row-tile streams per head as fit
-        const int per_head = heads < 8 ? 8 / heads : 1;
-        const unsigned grid = (unsigned)tiles, threads = 64u * (unsigned)(heads < 8 ? heads * per_head : 8);
+        const dim3 ga((unsigned)tiles, (unsigned)heads);
         switch (r / 16) {
-            case 1: apply_mfma<1><<<grid, threads, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
-            case 2: apply_mfma<2><<<grid, threads, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
-            case 3: apply_mfma<3><<<grid, threads, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
-            default: apply_mfma<4><<<grid, threads, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
+            case 1: apply_mfma<1><<<ga, 256, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
+            case 2: apply_mfma<2><<<ga, 256, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
+            case 3: apply_mfma<3><<<ga, 256, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
+            default: apply_mfma<4><<<ga, 256, 0, st>>>(sg, heads, eps, q, s, z, g_out); break;
         }
     } else {
         int64_t blocks = ((int64_t)sg.n * heads * r + 255) / 256;
