@@ -90,6 +90,7 @@ def test_linear_deterministic(g):
 
 
 @pytest.mark.parametrize("n,h,r", [(1, 1, 16), (1000, 2, 16), (5000, 4, 64), (3001, 3, 32), (777, 2, 48),
+                                   (2000, 8, 64), (3000, 12, 16),
                                    (500, 2, 5), (20000, 1, 8),
                                    # tiles longer than 256 rows: 592 at 4 heads, 272 at one head
                                    (150001, 4, 64), (270001, 1, 16)])
