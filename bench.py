@@ -668,14 +668,23 @@ def bench_relation(args, g, torch, synth, ident):
 def stream_rates(torch, n=262144 * 256, reps=20):
     """Best-of-reps rates of torch's own elementwise kernels on [2^18, 256] fp32 tensors (the
     gated layer's row tensors): the streaming rate a row-wise kernel of that size can reach
-    here, for one, two and three reads per write."""
+    here, for one, two and three reads per write, and for a copy that moves one head's
+    256-byte segment of every row at a time (the access pattern of the global branch's
+    per-head passes)."""
     dev = torch.device("cuda:0")
     a, b, c, d = (torch.randn(n, device=dev) for _ in range(4))
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nb = n * 4
+    a4, c4 = a.view(-1, 4, 64), c.view(-1, 4, 64)
+
+    def head_slices():  # one head's 256-byte segment of each 1 KiB row, the four heads in turn
+        for h in range(4):
+            c4[:, h].copy_(a4[:, h])
+
     for name, fn, moved in (("copy (1 read, 1 write)", lambda: c.copy_(a), 2 * nb),
                             ("add (2 reads, 1 write)", lambda: torch.add(a, b, out=c), 3 * nb),
-                            ("addcmul (3 reads, 1 write)", lambda: torch.addcmul(a, b, d, out=c), 4 * nb)):
+                            ("addcmul (3 reads, 1 write)", lambda: torch.addcmul(a, b, d, out=c), 4 * nb),
+                            ("copy by head slices (1 read, 1 write)", head_slices, 2 * nb)):
         for _ in range(3):
             fn()
         best = float("inf")
