@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GGA_ABI_VERSION 3
+#define GGA_ABI_VERSION 4
 
 /* status codes */
 #define GGA_OK 0
@@ -352,16 +352,20 @@ int gga_linear_accumulate(int32_t m, int32_t k, int32_t n, int32_t trans_a, int3
                           const float *b, float *c, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * The input gradient of the three projections in one product:
- *   d_x += [d_q | d_k | d_v] [W_Q | W_K | W_V]^T = d_q W_Q^T + d_k W_K^T + d_v W_V^T
- * d_q, d_k, d_v fp32 [n,d]; w_q, w_k, w_v fp32 [d,d]; d_x fp32 [n,d], added to.  With
- * d % 4 == 0 and 16-byte aligned rows, one accumulating launch (the three W^T staged in
- * the workspace, the k ranges taken in the order q, k, v); otherwise three
- * gga_linear_accumulate calls in that order.  Workspace: gga_qkv_proj_bwd_x_workspace.
+ * The input gradient of the three projections (and of the gate logit) in one product:
+ *   d_x += [d_q | d_k | d_v] [W_Q | W_K | W_V]^T (+ d_logit w_g^T)
+ *        = d_q W_Q^T + d_k W_K^T + d_v W_V^T (+ d_logit w_g^T)
+ * d_q, d_k, d_v fp32 [n,d]; w_q, w_k, w_v fp32 [d,d]; d_x fp32 [n,d], added to.  d_logit
+ * fp32 [n] and w_g fp32 [d] are both given or both NULL: the gate logit's share of the input
+ * gradient (gga_gated_combine_bwd's d_logit), added in the same epilogue.  With d % 4 == 0
+ * and 16-byte aligned rows, one accumulating launch (the three W^T staged in the workspace,
+ * the k ranges taken in the order q, k, v); otherwise three gga_linear_accumulate calls in
+ * that order, then the d_logit term.  Workspace: gga_qkv_proj_bwd_x_workspace.
  */
 size_t gga_qkv_proj_bwd_x_workspace(int32_t n, int32_t d);
 int gga_qkv_proj_bwd_x(int32_t n, int32_t d, const float *d_q, const float *d_k, const float *d_v, const float *w_q,
-                       const float *w_k, const float *w_v, float *d_x, void *ws, size_t ws_bytes, void *stream);
+                       const float *w_k, const float *w_v, const float *d_logit, const float *w_g, float *d_x,
+                       void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Backward of out = LayerNorm(x + y) over rows of width d (gga_add_layernorm):
@@ -379,14 +383,18 @@ int gga_add_layernorm_bwd(int32_t n, int32_t d, const float *x, const float *y, 
  * Backward of the gate and combination (gga_gated_combine), with g_i recomputed:
  *   d_l = g dY,  d_g = (1 - g) dY,  dt_i = g_i (1 - g_i) sum_c dY[i,c] (l[i,c] - g[i,c])
  *   d_x_out = d_x_in + dt w_g^T   (d_x_out may alias d_x_in)
+ *   d_logit = dt                  (fp32 [n], may be NULL)
  *   d_w_g = sum_i dt_i x_i,  d_b_g = sum_i dt_i   (fixed two-level order)
- * x [n,d]; l, g_glob, d_y, d_l, d_g [n,width]; d_w_g [d]; d_b_g one float.
+ * x [n,d]; l, g_glob, d_y, d_l, d_g [n,width]; d_w_g [d]; d_b_g one float.  d_x_in and
+ * d_x_out are both given or both NULL; with both NULL, d_logit must be given and the caller
+ * adds dt w_g^T into its input gradient elsewhere (gga_qkv_proj_bwd_x takes d_logit), which
+ * saves reading and writing an [n,d] gradient here.
  */
 size_t gga_gated_combine_bwd_workspace(int32_t n, int32_t d);
 int gga_gated_combine_bwd(int32_t n, int32_t d, const float *x, const float *w_g, float b_g, int32_t width,
                           const float *l, const float *g_glob, const float *d_y, float *d_l, float *d_g,
-                          const float *d_x_in, float *d_x_out, float *d_w_g, float *d_b_g, void *ws,
-                          size_t ws_bytes, void *stream);
+                          const float *d_x_in, float *d_x_out, float *d_logit, float *d_w_g, float *d_b_g,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Backward of the global branch (gga_global_linear_fwd), per head, given its S and z:

@@ -43,7 +43,7 @@ class gga_local_desc(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def _load() -> ctypes.CDLL:
@@ -80,13 +80,13 @@ def _load() -> ctypes.CDLL:
         "gga_qkv_gate_proj_workspace": ([i32, i32], sz),
         "gga_qkv_gate_proj": ([i32, i32, P, P, P, P, P, f32, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_qkv_proj_bwd_x_workspace": ([i32, i32], sz),
-        "gga_qkv_proj_bwd_x": ([i32, i32, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_qkv_proj_bwd_x": ([i32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_add_layernorm": ([i32, i32, P, P, P, P, f32, P, P], ctypes.c_int),
         "gga_linear_accumulate": ([i32, i32, i32, i32, i32, P, P, P, P, sz, P], ctypes.c_int),
         "gga_add_layernorm_bwd_workspace": ([i32, i32], sz),
         "gga_add_layernorm_bwd": ([i32, i32, P, P, P, f32, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_gated_combine_bwd_workspace": ([i32, i32], sz),
-        "gga_gated_combine_bwd": ([i32, i32, P, P, f32, i32, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
+        "gga_gated_combine_bwd": ([i32, i32, P, P, f32, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_global_linear_bwd_workspace": ([i32, i32, i32], sz),
         "gga_global_linear_bwd": ([i32, i32, i32, P, P, P, f32, P, P, P, P, P, P, P, P, sz, P], ctypes.c_int),
         "gga_batch_edges": ([i32, P, P, i64, P, P, P, P, P, P], ctypes.c_int),
@@ -382,13 +382,15 @@ def gga_qkv_gate_proj(x, w_q, w_k, w_v, w_g, b_g: float, heads: int, ws=None, st
     return q, k, v, logit
 
 
-def gga_qkv_proj_bwd_x(d_q, d_k, d_v, w_q, w_k, w_v, d_x, ws=None, stream=None):
-    """d_x += d_q W_Q^T + d_k W_K^T + d_v W_V^T (d_q, d_k, d_v viewed [n, d])."""
+def gga_qkv_proj_bwd_x(d_q, d_k, d_v, w_q, w_k, w_v, d_x, ws=None, stream=None, d_logit=None, w_g=None):
+    """d_x += d_q W_Q^T + d_k W_K^T + d_v W_V^T (+ d_logit w_g^T when both are given;
+    d_q, d_k, d_v viewed [n, d])."""
     n, d = d_x.shape
     nb = lib.gga_qkv_proj_bwd_x_workspace(n, d)
     ws = _workspace(nb, d_x.device, ws)
     _check("gga_qkv_proj_bwd_x", lib.gga_qkv_proj_bwd_x(n, d, _ptr(d_q), _ptr(d_k), _ptr(d_v), _ptr(w_q), _ptr(w_k),
-                                                        _ptr(w_v), _ptr(d_x), _ptr(ws), nb, _stream(stream)))
+                                                        _ptr(w_v), _ptr(d_logit), _ptr(w_g), _ptr(d_x), _ptr(ws), nb,
+                                                        _stream(stream)))
     return d_x
 
 
@@ -440,22 +442,28 @@ def gga_add_layernorm_bwd(x, y, gamma, d_out, eps=1e-5, d_pre=None, d_gamma=None
 
 
 def gga_gated_combine_bwd(x, w_g, b_g: float, l, g, d_y, d_x_in, d_l=None, d_g=None, d_x_out=None, d_w_g=None,
-                          d_b_g=None, ws=None, stream=None):
+                          d_b_g=None, ws=None, stream=None, d_logit=None, want_logit=False):
+    """Returns (d_l, d_g, d_x_out, d_w_g, d_b_g, d_logit).  With d_x_in None no input gradient is
+    formed (d_x_out is None) and the [n] logit gradients are returned for the caller to add
+    d_logit w_g^T itself; want_logit also returns them beside d_x_out."""
     n, d = x.shape
     dev = x.device
     width = _row_width(l)
     d_l = torch.empty(n, width, dtype=torch.float32, device=dev) if d_l is None else d_l
     d_g = torch.empty(n, width, dtype=torch.float32, device=dev) if d_g is None else d_g
-    d_x_out = torch.empty_like(x) if d_x_out is None else d_x_out
+    if d_x_in is not None and d_x_out is None:
+        d_x_out = torch.empty_like(x)
+    if (d_x_in is None or want_logit) and d_logit is None:
+        d_logit = torch.empty(n, dtype=torch.float32, device=dev)
     d_w_g = torch.empty(d, dtype=torch.float32, device=dev) if d_w_g is None else d_w_g
     d_b_g = torch.empty(1, dtype=torch.float32, device=dev) if d_b_g is None else d_b_g
     nb = lib.gga_gated_combine_bwd_workspace(n, d)
     ws = _workspace(nb, dev, ws)
     _check("gga_gated_combine_bwd", lib.gga_gated_combine_bwd(n, d, _ptr(x), _ptr(w_g), float(b_g), width, _ptr(l),
                                                               _ptr(g), _ptr(d_y), _ptr(d_l), _ptr(d_g), _ptr(d_x_in),
-                                                              _ptr(d_x_out), _ptr(d_w_g), _ptr(d_b_g), _ptr(ws), nb,
-                                                              _stream(stream)))
-    return d_l, d_g, d_x_out, d_w_g, d_b_g
+                                                              _ptr(d_x_out), _ptr(d_logit), _ptr(d_w_g), _ptr(d_b_g),
+                                                              _ptr(ws), nb, _stream(stream)))
+    return d_l, d_g, d_x_out, d_w_g, d_b_g, d_logit
 
 
 def gga_global_linear_bwd(q, k, v, s, z, d_g, d_q, d_k, d_v, eps=1e-6, ws=None, stream=None, g_fw=None):

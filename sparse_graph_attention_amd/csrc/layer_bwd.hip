@@ -189,13 +189,16 @@ __global__ __launch_bounds__(1024) void ln_bwd_generic(int32_t n, int32_t d, int
 }
 
 // ---- gate and combination backward.  acc row: [0, d) d_w_g, [d] d_b_g.
+// XOUT: write d_x_out = d_x_in + dt w_g^T; otherwise only the logit gradients dt (d_logit,
+// when given) leave, and the caller adds dt w_g^T into dX elsewhere.
+template <bool XOUT>
 __global__ __launch_bounds__(1024) void combine_bwd_kernel(int32_t n, int32_t d, int32_t per, const float* __restrict__ x,
                                                            const float* __restrict__ w_g, float b_g, int32_t width,
                                                            const float* __restrict__ l, const float* __restrict__ gg,
                                                            const float* __restrict__ d_y, float* __restrict__ d_l,
                                                            float* __restrict__ d_g, const float* d_x_in,
-                                                           float* d_x_out, float* __restrict__ part,
-                                                           int vec) {
+                                                           float* d_x_out, float* __restrict__ d_logit,
+                                                           float* __restrict__ part, int vec) {
     extern __shared__ float acc_lds[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
     const int ncols = d + 1;
@@ -246,15 +249,18 @@ __global__ __launch_bounds__(1024) void combine_bwd_kernel(int32_t n, int32_t d,
             }
         }
         const float dt = wave_sum(s) * (gv * hv);
+        if (d_logit && lane == 0) d_logit[i] = dt;
         // input gradient and the parameter partials
         if (vec) {
             const float4* xr = reinterpret_cast<const float4*>(x + i * d);
             const float4* wr = reinterpret_cast<const float4*>(w_g);
-            const float4* ir = reinterpret_cast<const float4*>(d_x_in + i * d);
-            float4* orow = reinterpret_cast<float4*>(d_x_out + i * d);
             for (int j = lane; j < d / 4; j += 64) {
-                const float4 a = xr[j], w = wr[j], p = ir[j];
-                orow[j] = make_float4(fmaf(dt, w.x, p.x), fmaf(dt, w.y, p.y), fmaf(dt, w.z, p.z), fmaf(dt, w.w, p.w));
+                const float4 a = xr[j];
+                if constexpr (XOUT) {
+                    const float4 w = wr[j], p = reinterpret_cast<const float4*>(d_x_in + i * d)[j];
+                    reinterpret_cast<float4*>(d_x_out + i * d)[j] =
+                        make_float4(fmaf(dt, w.x, p.x), fmaf(dt, w.y, p.y), fmaf(dt, w.z, p.z), fmaf(dt, w.w, p.w));
+                }
                 float4* ap = reinterpret_cast<float4*>(acc + 4 * j);
                 float4 c = *ap;
                 c.x = fmaf(dt, a.x, c.x);
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(1024) void combine_bwd_kernel(int32_t n, int32_t d,
         } else {
             for (int j = lane; j < d; j += 64) {
                 const int64_t o = i * d + j;
-                d_x_out[o] = fmaf(dt, w_g[j], d_x_in[o]);
+                if constexpr (XOUT) d_x_out[o] = fmaf(dt, w_g[j], d_x_in[o]);
                 acc[j] = fmaf(dt, x[o], acc[j]);
             }
         }
@@ -361,11 +367,13 @@ extern "C" size_t gga_gated_combine_bwd_workspace(int32_t n, int32_t d) {
 
 extern "C" int gga_gated_combine_bwd(int32_t n, int32_t d, const float* x, const float* w_g, float b_g, int32_t width,
                                      const float* l, const float* g_glob, const float* d_y, float* d_l, float* d_g,
-                                     const float* d_x_in, float* d_x_out, float* d_w_g, float* d_b_g, void* ws,
-                                     size_t ws_bytes, void* stream) {
+                                     const float* d_x_in, float* d_x_out, float* d_logit, float* d_w_g, float* d_b_g,
+                                     void* ws, size_t ws_bytes, void* stream) {
     if (n < 0 || d < 1 || width < 1) return GGA_EINVAL;
     if (!w_g || !d_w_g || !d_b_g) return GGA_EINVAL;
-    if (n > 0 && (!x || !l || !g_glob || !d_y || !d_l || !d_g || !d_x_in || !d_x_out)) return GGA_EINVAL;
+    // d_x_in and d_x_out come together; without them d_logit must be given (rows only)
+    if (n > 0 && ((d_x_in == nullptr) != (d_x_out == nullptr) || (!d_x_out && !d_logit))) return GGA_EINVAL;
+    if (n > 0 && (!x || !l || !g_glob || !d_y || !d_l || !d_g)) return GGA_EINVAL;
     const int ncols = d + 1;
     const RowSplit rs = row_split(n, ncols);
     if (rs.wpb < 1) return GGA_EUNSUPPORTED;
@@ -378,9 +386,14 @@ extern "C" int gga_gated_combine_bwd(int32_t n, int32_t d, const float* x, const
                     aligned16(d_x_out);
     if (n == 0)
         fill_f32(part, (int64_t)rs.nb * ncols, 0.f, s);
+    else if (d_x_out)
+        combine_bwd_kernel<true><<<(unsigned)rs.nb, 64u * rs.wpb, (size_t)rs.wpb * acc_stride(ncols) * sizeof(float),
+                                   s>>>(n, d, rs.per, x, w_g, b_g, width, l, g_glob, d_y, d_l, d_g, d_x_in, d_x_out,
+                                        d_logit, part, vec);
     else
-        combine_bwd_kernel<<<(unsigned)rs.nb, 64u * rs.wpb, (size_t)rs.wpb * acc_stride(ncols) * sizeof(float), s>>>(
-            n, d, rs.per, x, w_g, b_g, width, l, g_glob, d_y, d_l, d_g, d_x_in, d_x_out, part, vec);
+        combine_bwd_kernel<false><<<(unsigned)rs.nb, 64u * rs.wpb, (size_t)rs.wpb * acc_stride(ncols) * sizeof(float),
+                                    s>>>(n, d, rs.per, x, w_g, b_g, width, l, g_glob, d_y, d_l, d_g, nullptr, nullptr,
+                                         d_logit, part, vec);
     colsum_reduce<<<(unsigned)((ncols + 63) / 64), 1024, 0, s>>>(rs.nb, ncols, part, d, d_w_g, d_b_g);
     return launch_status();
 }

@@ -46,6 +46,10 @@ struct GemmArgs {
     const float* gate_w;
     float* gate_out;
     float gate_b;
+    // r1_row != null (gemm_f32_seg_k only): c also gets the outer product r1_row r1_col^T
+    // (r1_row [M], r1_col [N]), added in the epilogue with the accumulation.
+    const float* r1_row;
+    const float* r1_col;
 };
 
 // Loads 4 consecutive floats of a row starting at column c0, zero beyond `lim` columns.
@@ -427,14 +431,44 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
 
 // Epilogue of a 128 x 128 tile through LDS, 32 rows of the wavefront's 64 x 64 block at a
 // time: the accumulators go to a private [32][68] region, then each row leaves as 16-byte
-// stores, 16 lanes covering 64 consecutive columns.
+// stores, 16 lanes covering 64 consecutive columns.  R1: the outer-product term of GemmArgs
+// is added when its pointers are set (only the instance that takes it compiles it).
+// The outer-product term's values for one lane of a 128 x 128 tile: its 16 rows (two halves
+// of 8) and 4 columns.
+struct R1Vals {
+    float u[2][8];
+    v4f w;
+};
+
+// Requested at the start of the kernel that takes the term, so the loads are long done when
+// the epilogue uses them.
+__device__ __forceinline__ R1Vals load_r1(const GemmArgs& g, int64_t m0, int64_t n0) {
+    R1Vals r;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1, cl = lane & 15;
+    const bool on = g.r1_row != nullptr;
+    const int64_t col = n0 + wn * 64 + cl * 4;
+#pragma unroll
+    for (int e = 0; e < 4; e++) r.w[e] = on && col + e < g.N ? g.r1_col[col + e] : 0.f;
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+        for (int it = 0; it < 8; it++) {
+            const int64_t row = m0 + wm * 64 + hh * 32 + it * 4 + (lane >> 4);
+            r.u[hh][it] = on && row < g.M ? g.r1_row[row] : 0.f;
+        }
+    return r;
+}
+
+template <bool R1 = false>
 __device__ __forceinline__ void big_epilogue(const GemmArgs& g, float* lds_raw, const v4f (&acc)[4][4], int64_t m0,
-                                             int64_t n0, uint32_t bz) {
+                                             int64_t n0, uint32_t bz, const R1Vals* r1 = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     float* cbase = g.c + (int64_t)bz * g.M * g.N;
     const bool add_bias = g.bias != nullptr && gridDim.z == 1;
     const bool acc_in = g.accumulate && gridDim.z == 1;
+    const bool add_r1 = R1 && g.r1_row != nullptr && gridDim.z == 1;
     const bool c_vec = (g.N % 4) == 0 && (reinterpret_cast<uintptr_t>(g.c) & 15) == 0 &&
                        (!add_bias || (reinterpret_cast<uintptr_t>(g.bias) & 15) == 0);
     constexpr int EP = kEpPitch;
@@ -458,16 +492,22 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, float* lds_raw, 
             if (row >= g.M) continue;
             const v4f v = *reinterpret_cast<const v4f*>(ep + rl * EP + cl * 4);
             float* dst = cbase + row * g.N + col;
+            const float ur = R1 && add_r1 ? r1->u[hh][it] : 0.f;
             if (c_vec && col + 3 < g.N) {
                 v4f o = v;
                 if (add_bias) o += *reinterpret_cast<const v4f*>(g.bias + col);
+                if (R1 && add_r1) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) o[e] = fmaf(ur, r1->w[e], o[e]);
+                }
                 if (acc_in) o = *reinterpret_cast<const v4f*>(dst) + o;
                 *reinterpret_cast<v4f*>(dst) = o;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     if (col + e >= g.N) continue;
-                    const float o = v[e] + (add_bias ? g.bias[col + e] : 0.f);
+                    float o = v[e] + (add_bias ? g.bias[col + e] : 0.f);
+                    if (R1 && add_r1) o = fmaf(ur, r1->w[e], o);
                     dst[e] = acc_in ? dst[e] + o : o;
                 }
             }
@@ -568,6 +608,7 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_seg_k(GemmArgs g) {
     const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * blockIdx.y, gxy);
     const uint32_t by = tl / gridDim.x, bx = tl % gridDim.x;
     const int64_t m0 = (int64_t)by * TT, n0 = (int64_t)bx * TT;
+    const R1Vals r1 = load_r1(g, m0, n0);  // zeros when the term is absent
     v4f acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -601,7 +642,16 @@ __global__ __launch_bounds__(kBigThreads, 2) void gemm_f32_seg_k(GemmArgs g) {
             big_loop<false, true, false, Cfg::buffers>(gk, lds, m0, n0, 0, g.seg_len, a_vec, b_vec, acc);
         }
     }
-    big_epilogue(g, lds_raw, acc, m0, n0, 0);
+    big_epilogue<true>(g, lds_raw, acc, m0, n0, 0, &r1);
+}
+
+// c[i,j] += u[i] v[j] over an n x d matrix (the outer-product term of the k-segmented dX
+// product when that product cannot take it in its epilogue).
+__global__ __launch_bounds__(256) void rank1_add(int32_t n, int32_t d, const float* __restrict__ u,
+                                                 const float* __restrict__ v, float* __restrict__ c) {
+    const int64_t total = (int64_t)n * d;
+    for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < total; x += (int64_t)gridDim.x * blockDim.x)
+        c[x] = fmaf(u[x / d], v[x % d], c[x]);
 }
 
 // gate[i] = x[i,:] . w + b, one wavefront per row, a fixed butterfly over the lanes (the
@@ -1317,9 +1367,10 @@ extern "C" size_t gga_qkv_proj_bwd_x_workspace(int32_t n, int32_t d) {
 }
 
 extern "C" int gga_qkv_proj_bwd_x(int32_t n, int32_t d, const float* d_q, const float* d_k, const float* d_v,
-                                  const float* w_q, const float* w_k, const float* w_v, float* d_x, void* ws,
-                                  size_t ws_bytes, void* stream) {
+                                  const float* w_q, const float* w_k, const float* w_v, const float* d_logit,
+                                  const float* w_g, float* d_x, void* ws, size_t ws_bytes, void* stream) {
     if (n < 0 || d < 1) return GGA_EINVAL;
+    if ((d_logit == nullptr) != (w_g == nullptr)) return GGA_EINVAL;
     if (n == 0) return GGA_OK;
     if (!d_q || !d_k || !d_v || !w_q || !w_k || !w_v || !d_x) return GGA_EINVAL;
     if ((int64_t)n * d >= ((int64_t)1 << 40)) return GGA_ERANGE;
@@ -1353,6 +1404,8 @@ extern "C" int gga_qkv_proj_bwd_x(int32_t n, int32_t d, const float* d_q, const 
         g.seg_a[1] = d_k;
         g.seg_a[2] = d_v;
         for (int i = 0; i < 3; i++) g.seg_b[i] = wt + (size_t)i * d * d;
+        g.r1_row = d_logit;  // + d_logit w_g^T in the same epilogue (null: none)
+        g.r1_col = w_g;
         const dim3 grid((unsigned)((d + TT - 1) / TT), (unsigned)((n + BM - 1) / BM), 1);
         gemm_f32_seg_k<3><<<grid, kBigThreads, 0, s>>>(g);
         return launch_status();
@@ -1360,5 +1413,11 @@ extern "C" int gga_qkv_proj_bwd_x(int32_t n, int32_t d, const float* d_q, const 
     int st = gga_linear_accumulate(n, d, d, 0, 1, d_q, w_q, d_x, ws, ws_bytes, stream);
     if (st == GGA_OK) st = gga_linear_accumulate(n, d, d, 0, 1, d_k, w_k, d_x, ws, ws_bytes, stream);
     if (st == GGA_OK) st = gga_linear_accumulate(n, d, d, 0, 1, d_v, w_v, d_x, ws, ws_bytes, stream);
+    if (st == GGA_OK && d_logit) {
+        const int64_t total = (int64_t)n * d;
+        const int64_t blocks = (total + 255) / 256;
+        rank1_add<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(n, d, d_logit, w_g, d_x);
+        st = launch_status();
+    }
     return st;
 }

@@ -120,8 +120,12 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
     d_pre, d_gamma, d_beta = gga_add_layernorm_bwd(x, fwd["zo"], p["gamma"], d_out, ln_eps)
     d_y = gga_linear(d_pre, p["w_o"], trans_b=True)
     d_wo = gga_linear(fwd["y"], d_pre, trans_a=True)
-    d_loc, d_glob, d_x, d_wg, d_bg = gga_gated_combine_bwd(x, p["w_g"], p["b_g"], fwd["local"], fwd["glob"], d_y,
-                                                           d_pre)
+    # the gate logit's share of dX (d_logit w_g^T) is added by the dX product below, into
+    # d_pre, the residual's share; the combine backward does not read or write an [n, d]
+    # gradient for it
+    d_loc, d_glob, _, d_wg, d_bg, d_logit = gga_gated_combine_bwd(x, p["w_g"], p["b_g"], fwd["local"], fwd["glob"],
+                                                                  d_y, None)
+    d_x = d_pre
     if mark is not None:
         mark("local_bwd0")
     d_q, d_k, d_v = gga_local_attn_bwd(fwd["desc"], fwd["q"], fwd["k"], fwd["v"], fwd["local3"], fwd["lse"],
@@ -137,8 +141,8 @@ def gated_layer_backward(p: dict, fwd: dict, topo: Topology, heads: int, d_out: 
     grads = dict(d_w_o=d_wo, d_w_g=d_wg, d_b_g=d_bg, d_gamma=d_gamma, d_beta=d_beta)
     for name, g in (("q", d_q), ("k", d_k), ("v", d_v)):
         grads["d_w_" + name] = gga_linear(x, g.view(n, d), trans_a=True)
-    # d_x += [dQ | dK | dV] [W_Q | W_K | W_V]^T in one product
-    gga_qkv_proj_bwd_x(d_q, d_k, d_v, p["w_q"], p["w_k"], p["w_v"], d_x)
+    # d_x += [dQ | dK | dV] [W_Q | W_K | W_V]^T + d_logit w_g^T in one product
+    gga_qkv_proj_bwd_x(d_q, d_k, d_v, p["w_q"], p["w_k"], p["w_v"], d_x, d_logit=d_logit, w_g=p["w_g"])
     grads["d_x"] = d_x
     return grads
 

@@ -72,7 +72,7 @@ def test_binding_refuses_to_import_without_the_library(tmp_path):
 def test_version_and_status(lib):
     lib.gga_abi_version.restype = ctypes.c_int
     lib.gga_status_string.restype = ctypes.c_char_p
-    assert lib.gga_abi_version() == 3
+    assert lib.gga_abi_version() == 4
     assert lib.gga_status_string(0) == b"ok"
     assert lib.gga_status_string(4).startswith(b"workspace")
 
@@ -238,8 +238,19 @@ def test_fused_projection_checks():
                                None, 0, None) == 0
     need = L.gga_qkv_proj_bwd_x_workspace(1000, 256)
     assert need >= 3 * 256 * 256 * 4
-    assert L.gga_qkv_proj_bwd_x(1000, 256, a, a, a, a, a, a, a, a, need - 1, None) == 4
-    assert L.gga_qkv_proj_bwd_x(1000, 0, a, a, a, a, a, a, a, a, need, None) == 1
+    assert L.gga_qkv_proj_bwd_x(1000, 256, a, a, a, a, a, a, None, None, a, a, need - 1, None) == 4
+    assert L.gga_qkv_proj_bwd_x(1000, 0, a, a, a, a, a, a, None, None, a, a, need, None) == 1
+    # the gate logit's share needs both its vectors
+    assert L.gga_qkv_proj_bwd_x(1000, 256, a, a, a, a, a, a, a, None, a, a, need, None) == 1
+    assert L.gga_qkv_proj_bwd_x(1000, 256, a, a, a, a, a, a, None, a, a, a, need, None) == 1
+    # the combine backward: d_x_in and d_x_out together, or neither and d_logit
+    cneed = L.gga_gated_combine_bwd_workspace(1000, 256)
+    f0 = ctypes.c_float(0.0)
+    assert L.gga_gated_combine_bwd(1000, 256, a, a, f0, 256, a, a, a, a, a, a, None, a, a, a, a, cneed, None) == 1
+    assert L.gga_gated_combine_bwd(1000, 256, a, a, f0, 256, a, a, a, a, a, None, None, None, a, a, a, cneed,
+                                   None) == 1
+    assert L.gga_gated_combine_bwd(1000, 256, a, a, f0, 256, a, a, a, a, a, None, None, a, a, a, a, cneed - 1,
+                                   None) == 4
     assert L.gga_gated_combine(10, 4, None, a, a, None, a, None) == 1
 
 

@@ -134,6 +134,15 @@ def test_qkv_projection_input_gradient(g, n, d):
     torch.cuda.synchronize()
     want = dx0.astype(np.float64) + sum(a.astype(np.float64) @ w.T.astype(np.float64) for a, w in zip(grads, ws))
     assert_close(dx.cpu().numpy(), want, "f32", "d_x", atol=1e-5 * np.sqrt(3 * d))
+    # with the gate logit's share: + d_logit w_g^T in the same call (the product's epilogue, or
+    # a separate pass after the three products)
+    d_logit = rng.standard_normal(n).astype(np.float32)
+    w_g = (rng.standard_normal(d) * 0.1).astype(np.float32)
+    dx = _t(dx0)
+    g.gga_qkv_proj_bwd_x(*(_t(a) for a in grads), *(_t(w) for w in ws), dx, d_logit=_t(d_logit), w_g=_t(w_g))
+    torch.cuda.synchronize()
+    want = want + np.outer(d_logit.astype(np.float64), w_g)
+    assert_close(dx.cpu().numpy(), want, "f32", "d_x with d_logit", atol=1e-5 * np.sqrt(3 * d + 1))
 
 
 def test_gate_combine_and_limits(g):

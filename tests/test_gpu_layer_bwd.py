@@ -61,15 +61,24 @@ def test_gated_combine_bwd(g, n, d, width):
     b_g = 0.1
     l, gl, d_y, d_in = _rand((n, width), 7), _rand((n, width), 8), _rand((n, width), 9), _rand((n, d), 10)
     print(f"combine bwd n={n} d={d} width={width}", flush=True)
-    d_l, d_g, d_x, d_wg, d_bg = g.gga_gated_combine_bwd(_t(x), _t(w_g), b_g, _t(l), _t(gl), _t(d_y), _t(d_in))
+    d_l, d_g, d_x, d_wg, d_bg, d_lg = g.gga_gated_combine_bwd(_t(x), _t(w_g), b_g, _t(l), _t(gl), _t(d_y), _t(d_in),
+                                                              want_logit=True)
+    # without an input gradient: only the logit gradients leave (the caller adds d_logit w_g^T)
+    d_l2, d_g2, none, d_wg2, d_bg2, d_lg2 = g.gga_gated_combine_bwd(_t(x), _t(w_g), b_g, _t(l), _t(gl), _t(d_y),
+                                                                     None)
     torch.cuda.synchronize()
+    assert none is None
     gv = oracle.gate(x, w_g, b_g)
     dt = (d_y.astype(np.float64) * (l.astype(np.float64) - gl)).sum(-1) * gv * (1.0 - gv)
     _close(d_l, gv[:, None] * d_y, "d_l")
     _close(d_g, (1.0 - gv)[:, None] * d_y, "d_g")
     _close(d_x, d_in + np.outer(dt, w_g), "d_x")
+    _close(d_lg, dt, "d_logit")
     _close(d_wg, x.astype(np.float64).T @ dt, "d_w_g")
     _close(d_bg, np.array([dt.sum()]), "d_b_g")
+    # the two modes run the same arithmetic: identical bits
+    for a, b in ((d_l, d_l2), (d_g, d_g2), (d_wg, d_wg2), (d_bg, d_bg2), (d_lg, d_lg2)):
+        assert torch.equal(a, b)
 
 
 def test_gated_combine_bwd_in_place(g):
@@ -80,7 +89,7 @@ def test_gated_combine_bwd_in_place(g):
     d_in = _rand((n, d), 16)
     buf = _t(d_in)
     g.gga_gated_combine_bwd(_t(x), _t(w_g), 0.0, _t(l), _t(gl), _t(d_y), buf, d_x_out=buf)
-    _, _, ref, _, _ = g.gga_gated_combine_bwd(_t(x), _t(w_g), 0.0, _t(l), _t(gl), _t(d_y), _t(d_in))
+    _, _, ref, _, _, _ = g.gga_gated_combine_bwd(_t(x), _t(w_g), 0.0, _t(l), _t(gl), _t(d_y), _t(d_in))
     torch.cuda.synchronize()
     assert torch.equal(buf, ref)
 
