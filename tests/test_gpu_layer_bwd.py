@@ -54,7 +54,8 @@ def test_add_layernorm_bwd(g, n, d):
     _close(d_beta, db if n else np.zeros(d), "d_beta")
 
 
-@pytest.mark.parametrize("n,d,width", [(1000, 256, 256), (513, 100, 36), (64, 64, 64), (0, 32, 32)])
+@pytest.mark.parametrize("n,d,width", [(1000, 256, 256), (513, 100, 36), (64, 64, 64), (0, 32, 32),
+                                       (257, 30, 22)])  # widths off the 4-float vectors: the scalar loops
 def test_gated_combine_bwd(g, n, d, width):
     x = _rand((n, d), 5)
     w_g = _rand(d, 6, 0.3)
