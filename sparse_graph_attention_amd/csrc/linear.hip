@@ -429,10 +429,6 @@ __device__ __forceinline__ void big_loop(const GemmArgs& g, float (*lds)[2][kSta
         for (int q = 0; q < 4; q++) gsp[q] += gs[q];
 }
 
-// Epilogue of a 128 x 128 tile through LDS, 32 rows of the wavefront's 64 x 64 block at a
-// time: the accumulators go to a private [32][68] region, then each row leaves as 16-byte
-// stores, 16 lanes covering 64 consecutive columns.  R1: the outer-product term of GemmArgs
-// is added when its pointers are set (only the instance that takes it compiles it).
 // The outer-product term's values for one lane of a 128 x 128 tile: its 16 rows (two halves
 // of 8) and 4 columns.
 struct R1Vals {
@@ -460,6 +456,11 @@ __device__ __forceinline__ R1Vals load_r1(const GemmArgs& g, int64_t m0, int64_t
     return r;
 }
 
+// Epilogue of a 128 x 128 tile through LDS, 32 rows of the wavefront's 64 x 64 block at a
+// time: the accumulators go to a private [32][68] region, then each row leaves as 16-byte
+// stores, 16 lanes covering 64 consecutive columns.  R1: the outer-product term of GemmArgs
+// (values from load_r1) is added when its pointers are set; only the instance that takes it
+// compiles it.
 template <bool R1 = false>
 __device__ __forceinline__ void big_epilogue(const GemmArgs& g, float* lds_raw, const v4f (&acc)[4][4], int64_t m0,
                                              int64_t n0, uint32_t bz, const R1Vals* r1 = nullptr) {
@@ -521,8 +522,6 @@ __global__ __launch_bounds__(kBigThreads, (BigCfg<AKM, BKM>::per_cu)) void gemm_
     __shared__ float lds_raw[Cfg::lds_floats];
     // [buffer][operand]; the epilogue reuses the same memory
     float(*lds)[2][kStageFloats] = reinterpret_cast<float(*)[2][kStageFloats]>(lds_raw);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
     const uint32_t gxy = gridDim.x * gridDim.y;
     const uint32_t tl = xcd_order(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), gxy * gridDim.z);
     const uint32_t bz = tl / gxy, by = (tl % gxy) / gridDim.x, bx = tl % gridDim.x;
