@@ -180,6 +180,15 @@ def test_layer_bwd_narrow_heads(g):
     _layer(g, n, src, dst, heads, p, _rand((n, d), 51))
 
 
+def test_layer_bwd_odd_width(g):
+    """d = 80 (4 heads of 20): the projections' per-product paths, dX through three
+    accumulating products and the separate outer-product pass, the scalar global branch."""
+    n, d, heads = 1200, 80, 4
+    src, dst = synth.mixed_degree_graph(n, 35, hubs=(900, 70))
+    p = synth.gated_layer_inputs(n, d=d)
+    _layer(g, n, src, dst, heads, p, _rand((n, d), 53))
+
+
 def test_layer_bwd_workload(g):
     w = synth.WORKLOADS[4]
     n = w.n
